@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Throughput of the W4A16 linear forward (awq_gemm) on one MI355X.
+
+Headline workload (the decode target): M=1, K=8192, N=7168, group_size=128,
+no bias -- one awq_gemm call per step, algorithmic bytes per step =
+qweight + qzeros + scales + x + y.  The metric also names prefill TFLOP/s; the
+prefill fused-QKV workload (M=2048, K=4096, N=12288, group_size=128, bias) is
+measured in the same run and reported under "prefill" on the same line.
+
+Timing: inputs are resident in HBM before the timed region.  The weights,
+zeros, scales, x and y of each step rotate through enough distinct copies to
+exceed twice the 256 MiB Infinity Cache, so every step streams its weights
+from HBM.  W warmup steps, then exactly K steps recorded in a HIP graph and
+replayed once between device synchronisations (this removes host launch
+gaps, which are comparable to a decode kernel's duration).  The kernel's
+average duration is measured separately with HIP events around each launch on
+the launching stream; the roofline figures use it.
+
+Prints one JSON line on stdout.  --gpus above 1 is refused: this build is the
+single-GPU share of the path.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores
+ROTATE_BYTES = 512 << 20        # two Infinity Caches
+
+DECODE = dict(workload="decode_m1_k8192_n7168_g128", source="decode_sweep_k8192_n7168",
+              M=1, group_size=128)
+PREFILL = dict(workload="prefill_qkv_m2048_k4096_n12288_g128",
+               source="prefill_qkv_m2048_k4096_n12288", M=2048, group_size=128)
+
+
+def algorithmic_bytes(M, K, N, G, bias):
+    """qweight + qzeros + scales + x + y (+ bias), each read or written once."""
+    return K * N // 2 + G * N // 2 + G * N * 2 + M * K * 2 + M * N * 2 + (2 * N if bias else 0)
+
+
+def problem_dims(p):
+    K = p["qweight"].shape[0]
+    N = p["qweight"].shape[1] * 8
+    G = p["qzeros"].shape[0]
+    return K, N, G
+
+
+def make_copies(torch, p, R, dev):
+    base = {k: torch.from_numpy(v).to(dev) for k, v in p.items()
+            if k in ("qweight", "qzeros", "scales", "x")}
+    bias = torch.from_numpy(p["bias"]).to(dev) if p["bias"] is not None else None
+    M = p["x"].shape[0]
+    _, N, _ = problem_dims(p)
+    copies = []
+    for _ in range(R):
+        c = {k: v.clone() for k, v in base.items()}
+        c["bias"] = bias
+        c["y"] = torch.empty((M, N), dtype=torch.float16, device=dev)
+        copies.append(c)
+    return copies
+
+
+def run_leg(torch, awq, spec, steps, warmup, dev):
+    import awq_inputs
+    p = awq_inputs.workload_inputs(spec["source"], spec["M"], spec["group_size"])
+    M = spec["M"]
+    g = spec["group_size"]
+    K, N, G = problem_dims(p)
+    nbytes = algorithmic_bytes(M, K, N, G, p["bias"] is not None)
+    nflops = 2 * M * N * K
+    R = max(2, -(-ROTATE_BYTES // nbytes))
+    copies = make_copies(torch, p, R, dev)
+    ws_bytes = awq.gemm_workspace_size(M, K, N, g)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    path, need = awq.gemm_plan(M, K, N, g, copies[0]["x"].data_ptr(),
+                               copies[0]["scales"].data_ptr())
+    assert need <= ws_bytes
+
+    def step(i):
+        c = copies[i % R]
+        awq.gemm(c["x"], c["qweight"], c["qzeros"], c["scales"], c["bias"], g, out=c["y"],
+                 workspace=ws)
+
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step(i)
+    torch.cuda.synchronize()
+
+    # Kernel duration: HIP events around each launch, on the launching stream.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            ev[i][0].record(stream)
+            step(i)
+            ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_avg_ms = statistics.fmean(kern_ms)
+
+    # Whole job: exactly `steps` steps captured in one graph, replayed once.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(steps):
+            step(i)
+    torch.cuda.synchronize()
+    graph.replay()                      # first replay uploads the graph
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    with torch.cuda.stream(stream):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / steps
+
+    # Eager loop for reference (host launch overhead included).
+    torch.cuda.synchronize()
+    e0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            step(i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - e0) * 1e3 / steps
+
+    return dict(p=p, M=M, K=K, N=N, G=G, g=g, nbytes=nbytes, nflops=nflops, R=R,
+                path=awq.PATH_NAMES[path], ms_per_step=ms_per_step, kern_avg_ms=kern_avg_ms,
+                kern_min_ms=min(kern_ms), eager_ms=eager_ms, ws_bytes=ws_bytes)
+
+
+def cpu_baseline(p, g, budget_s, sample_rows=None):
+    """The oracle, as it stands, on the host cores (rank 0 only)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    x = p["x"] if sample_rows is None else p["x"][:sample_rows]
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.awq_linear_ref(x, p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 20:
+            break
+    del np
+    return statistics.median(times), len(times), blas_threads
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--legs", default="decode,prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (for profiler runs)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the multi-GPU (sharded) path is not part of "
+              "this build; rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_weight_quantized_awq_amd as awq
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    awq.lib()
+    legs = args.legs.split(",")
+    res = {}
+    for name, spec in (("decode", DECODE), ("prefill", PREFILL)):
+        if name in legs:
+            print(f"[bench] {name} leg: {spec['workload']}", file=sys.stderr, flush=True)
+            res[name] = run_leg(torch, awq, spec, args.steps, args.warmup, dev)
+
+    def decode_fields(r):
+        gbs = r["nbytes"] / (r["ms_per_step"] * 1e-3) / 1e9
+        kgbs = r["nbytes"] / (r["kern_avg_ms"] * 1e-3) / 1e9
+        return gbs, kgbs
+
+    out = {
+        "metric": "W4A16 GEMM: decode GB/s (% HBM peak) at M=1; prefill TFLOP/s (% MFMA peak)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+    }
+    if "decode" in res:
+        r = res["decode"]
+        gbs, kgbs = decode_fields(r)
+        out.update({
+            "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": r["ms_per_step"],
+            "config": {"workload": DECODE["workload"], "M": r["M"], "K": r["K"], "N": r["N"],
+                       "group_size": r["g"], "bias": False, "kernel": r["path"],
+                       "weight_copies_rotated": r["R"], "bytes_per_step": r["nbytes"],
+                       "hbm_peak_frac_whole_job": round(gbs / HBM_PEAK_GBS, 4),
+                       "eager_ms_per_step": r["eager_ms"]},
+            "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel_avg_us": round(r["kern_avg_ms"] * 1e3, 3),
+                         "kernel_min_us": round(r["kern_min_ms"] * 1e3, 3)},
+        })
+    if "prefill" in res:
+        r = res["prefill"]
+        tf = r["nflops"] / (r["ms_per_step"] * 1e-3) / 1e12
+        ktf = r["nflops"] / (r["kern_avg_ms"] * 1e-3) / 1e12
+        pre = {"workload": PREFILL["workload"], "value": round(tf, 1), "unit": "TFLOP/s",
+               "ms_per_step": r["ms_per_step"], "kernel": r["path"],
+               "M": r["M"], "K": r["K"], "N": r["N"], "group_size": r["g"], "bias": True,
+               "roofline": {"bound": "mfma", "achieved": round(ktf, 1),
+                            "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(ktf / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                            "kernel_avg_us": round(r["kern_avg_ms"] * 1e3, 3)}}
+        if "decode" not in res:
+            out.update({"value": pre["value"], "unit": "TFLOP/s",
+                        "ms_per_step": pre["ms_per_step"],
+                        "config": {"workload": pre["workload"]}, "roofline": pre["roofline"]})
+        out["prefill"] = pre
+
+    if not args.no_cpu_baseline and "decode" in res:
+        r = res["decode"]
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        t, n, cores = cpu_baseline(r["p"], r["g"], budget_s=12.0)
+        out["cpu_baseline"] = {
+            "value": round(r["nbytes"] / t / 1e9, 3), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"the full decode problem (M=1, K=8192, N=7168, g=128) through the "
+                      f"numpy oracle (unpack, float16 dequant, float64 matmul), median of {n} "
+                      f"runs of {t:.2f} s; elementwise steps single-threaded, BLAS on "
+                      f"{cores} threads"}
+    if not args.no_cpu_baseline and "prefill" in res:
+        r = res["prefill"]
+        rows = 128
+        t, n, cores = cpu_baseline(r["p"], r["g"], budget_s=12.0, sample_rows=rows)
+        out["prefill"]["cpu_baseline"] = {
+            "value": round(2 * rows * r["K"] * r["N"] / t / 1e12, 5), "unit": "TFLOP/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"first {rows} of the 2048 rows of the prefill problem through the numpy "
+                      f"oracle (full dequant + float64 matmul), median of {n} runs of {t:.2f} s"}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

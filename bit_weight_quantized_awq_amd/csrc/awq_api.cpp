@@ -1,0 +1,118 @@
+// C-ABI entry points (include/awq.h): host validation, planning, launch.
+#include <hip/hip_runtime.h>
+
+#include "awq.h"
+#include "awq_device.h"
+#include "awq_plan.h"
+
+using awq::Plan;
+using awq::Problem;
+
+extern "C" {
+
+int awq_abi_version(void) { return AWQ_ABI_VERSION; }
+
+const char* awq_status_string(int status) {
+  switch (status) {
+    case AWQ_SUCCESS: return "success";
+    case AWQ_ERROR_INVALID_VALUE:
+      return "invalid value (NULL pointer, negative or zero size, bad group_size, "
+             "or a kernel path that cannot run this problem)";
+    case AWQ_ERROR_SHAPE:
+      return "shape error (out_features % 8 != 0, in_features % group_size != 0, "
+             "or an operand with 2^31 or more elements)";
+    case AWQ_ERROR_MISALIGNED: return "pointer not aligned to its element size";
+    case AWQ_ERROR_WORKSPACE: return "workspace missing or smaller than awq_gemm_workspace_size";
+    case AWQ_ERROR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t awq_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size) {
+  Problem p;
+  if (awq::validate_shape(M, K, N, group_size, &p) != AWQ_SUCCESS) return 0;
+  if (!awq::decode_supported(p, true, true)) return 0;
+  Plan pl;
+  if (awq::make_plan(p, true, true, AWQ_PATH_DECODE, &pl) != AWQ_SUCCESS) return 0;
+  return pl.ws_bytes;
+}
+
+int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size, const void* x,
+                  const void* scales, int* path, size_t* workspace_bytes) {
+  Problem p;
+  int st = awq::validate_shape(M, K, N, group_size, &p);
+  if (st != AWQ_SUCCESS) return st;
+  const int force = awq::force_path_from_env();
+  if (force < 0) return AWQ_ERROR_INVALID_VALUE;
+  Plan pl;
+  st = awq::make_plan(p, awq::aligned(x, 16), awq::aligned(scales, 16), force, &pl);
+  if (st != AWQ_SUCCESS) return st;
+  if (path) *path = pl.path;
+  if (workspace_bytes) *workspace_bytes = pl.ws_bytes;
+  return AWQ_SUCCESS;
+}
+
+int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void* scales,
+             const void* bias, void* y, int64_t M, int64_t K, int64_t N, int64_t group_size,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  Problem p;
+  int st = awq::validate_shape(M, K, N, group_size, &p);
+  if (st != AWQ_SUCCESS) return st;
+  st = awq::validate_gemm_pointers(x, qweight, qzeros, scales, bias, y, M);
+  if (st != AWQ_SUCCESS) return st;
+  if (M == 0) return AWQ_SUCCESS;
+  const int force = awq::force_path_from_env();
+  if (force < 0) return AWQ_ERROR_INVALID_VALUE;
+  Plan pl;
+  st = awq::make_plan(p, awq::aligned(x, 16), awq::aligned(scales, 16), force, &pl);
+  if (st != AWQ_SUCCESS) return st;
+  if (pl.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < pl.ws_bytes) return AWQ_ERROR_WORKSPACE;
+    if (!awq::aligned(workspace, 16)) return AWQ_ERROR_MISALIGNED;
+  }
+
+  const auto* xh = static_cast<const _Float16*>(x);
+  const auto* qw = static_cast<const uint32_t*>(qweight);
+  const auto* qz = static_cast<const uint32_t*>(qzeros);
+  const auto* sc = static_cast<const _Float16*>(scales);
+  const auto* bh = static_cast<const _Float16*>(bias);
+  auto* yh = static_cast<_Float16*>(y);
+  const int iM = static_cast<int>(p.M), iK = static_cast<int>(p.K), iN = static_cast<int>(p.N);
+  const int ig = static_cast<int>(p.g), iG = static_cast<int>(p.G);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  hipError_t e = hipErrorInvalidValue;
+  switch (pl.path) {
+    case AWQ_PATH_DECODE:
+      e = awq::launch_decode(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, iG, pl.steps, pl.splits,
+                             pl.n_tiles, workspace, pl.ticket_bytes, s);
+      break;
+    case AWQ_PATH_PREFILL:
+      e = awq::launch_prefill(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, pl.m_tiles, pl.n_tiles, s);
+      break;
+    case AWQ_PATH_GENERIC:
+      e = awq::launch_generic(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, s);
+      break;
+    default:
+      return AWQ_ERROR_INVALID_VALUE;
+  }
+  return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP;
+}
+
+int awq_dequant(const void* qweight, const void* qzeros, const void* scales, void* w,
+                int64_t K, int64_t N, int64_t group_size, void* stream) {
+  Problem p;
+  int st = awq::validate_shape(0, K, N, group_size, &p);
+  if (st != AWQ_SUCCESS) return st;
+  st = awq::validate_dequant_pointers(qweight, qzeros, scales, w);
+  if (st != AWQ_SUCCESS) return st;
+  hipError_t e = awq::launch_dequant(static_cast<const uint32_t*>(qweight),
+                                     static_cast<const uint32_t*>(qzeros),
+                                     static_cast<const _Float16*>(scales),
+                                     static_cast<_Float16*>(w), static_cast<int>(p.K),
+                                     static_cast<int>(p.N), static_cast<int>(p.g),
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP;
+}
+
+}  // extern "C"

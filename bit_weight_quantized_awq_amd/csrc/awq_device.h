@@ -1,0 +1,68 @@
+// Device helpers shared by the gfx950 kernels: vector types, nibble unpacking
+// into packed float16 pairs, and the launch entry points of each kernel file.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// float16 1024.0 is 0x6400; its ulp is 1, so OR-ing a nibble q into the low
+// mantissa bits yields exactly 1024 + q.  Two such values sit in one 32-bit
+// register as a packed pair.
+constexpr uint32_t kMagicPair = 0x64006400u;
+constexpr uint32_t kNibblePairMask = 0x000F000Fu;
+
+// Byte shuffles that place, for two words a (low half) and b (high half),
+// bytes {a.b0, a.b1, b.b0, b.b1} (lo) or {a.b2, a.b3, b.b2, b.b3} (hi) in one
+// register.  Nibble j < 4 of a and b then sits at bit 4j of each 16-bit half
+// of `lo`, nibble j >= 4 at bit 4(j-4) of each half of `hi`.
+__device__ __forceinline__ uint32_t pair_bytes_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_bytes_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// (1024 + nibble, 1024 + nibble) float16 pair from a pair_bytes_* register.
+__device__ __forceinline__ uint32_t magic_pair(uint32_t paired, int shift) {
+  return ((paired >> shift) & kNibblePairMask) | kMagicPair;
+}
+
+__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+__device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// (1024 + z_j) in both halves, for nibble j of zero word zw.
+__device__ __forceinline__ uint32_t zero_pair(uint32_t zw, int j) {
+  const uint32_t dup = (j < 4) ? pair_bytes_lo(zw, zw) : pair_bytes_hi(zw, zw);
+  return magic_pair(dup, 4 * (j & 3));
+}
+
+}  // namespace awq
+
+// Launchers implemented in the .hip files; called by awq_api.cpp.
+namespace awq {
+struct Problem;
+struct Plan;
+hipError_t launch_dequant(const uint32_t* qweight, const uint32_t* qzeros,
+                          const _Float16* scales, _Float16* w, int K, int N, int g,
+                          hipStream_t stream);
+hipError_t launch_generic(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
+                          const _Float16* scales, const _Float16* bias, _Float16* y,
+                          int M, int K, int N, int g, hipStream_t stream);
+hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
+                         const _Float16* scales, const _Float16* bias, _Float16* y,
+                         int M, int K, int N, int g, int G, int steps, int splits,
+                         int n_tiles, void* workspace, size_t ticket_bytes,
+                         hipStream_t stream);
+hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
+                          const _Float16* scales, const _Float16* bias, _Float16* y,
+                          int M, int K, int N, int g, int m_tiles, int n_tiles,
+                          hipStream_t stream);
+}  // namespace awq

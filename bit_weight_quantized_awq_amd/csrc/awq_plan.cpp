@@ -1,0 +1,130 @@
+// Host-side validation and kernel planning (HIP-free).
+#include "awq_plan.h"
+
+#include <stdlib.h>
+#include <string.h>
+
+#include "awq.h"
+
+namespace awq {
+
+namespace {
+constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;
+// Work-groups to aim for in the decode grid: enough resident waves on 256
+// CUs to keep many weight loads in flight, without multiplying the split-K
+// partial sums more than needed.
+constexpr int64_t kDecodeTargetWGs = 800;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+}  // namespace
+
+int validate_shape(int64_t M, int64_t K, int64_t N, int64_t group_size, Problem* out) {
+  if (M < 0 || K <= 0 || N <= 0) return AWQ_ERROR_INVALID_VALUE;
+  if (group_size == 0 || group_size < -1) return AWQ_ERROR_INVALID_VALUE;
+  if (N % 8 != 0) return AWQ_ERROR_SHAPE;
+  const int64_t g = (group_size == -1) ? K : group_size;
+  if (K % g != 0) return AWQ_ERROR_SHAPE;
+  if (K > kMaxElems || N > kMaxElems || M > kMaxElems) return AWQ_ERROR_SHAPE;
+  if (K * N > kMaxElems) return AWQ_ERROR_SHAPE;
+  if (M * K > kMaxElems || M * N > kMaxElems) return AWQ_ERROR_SHAPE;
+  if (out) {
+    out->M = M;
+    out->K = K;
+    out->N = N;
+    out->g = g;
+    out->G = K / g;
+  }
+  return AWQ_SUCCESS;
+}
+
+int validate_gemm_pointers(const void* x, const void* qweight, const void* qzeros,
+                           const void* scales, const void* bias, const void* y, int64_t M) {
+  if (!qweight || !qzeros || !scales) return AWQ_ERROR_INVALID_VALUE;
+  if (M > 0 && (!x || !y)) return AWQ_ERROR_INVALID_VALUE;
+  if (!aligned(qweight, 4) || !aligned(qzeros, 4)) return AWQ_ERROR_MISALIGNED;
+  if (!aligned(scales, 2)) return AWQ_ERROR_MISALIGNED;
+  if (bias && !aligned(bias, 2)) return AWQ_ERROR_MISALIGNED;
+  if (x && !aligned(x, 2)) return AWQ_ERROR_MISALIGNED;
+  if (y && !aligned(y, 2)) return AWQ_ERROR_MISALIGNED;
+  return AWQ_SUCCESS;
+}
+
+int validate_dequant_pointers(const void* qweight, const void* qzeros,
+                              const void* scales, const void* w) {
+  if (!qweight || !qzeros || !scales || !w) return AWQ_ERROR_INVALID_VALUE;
+  if (!aligned(qweight, 4) || !aligned(qzeros, 4)) return AWQ_ERROR_MISALIGNED;
+  if (!aligned(scales, 2) || !aligned(w, 2)) return AWQ_ERROR_MISALIGNED;
+  return AWQ_SUCCESS;
+}
+
+bool decode_supported(const Problem& p, bool x_al16, bool scales_al16) {
+  // 16-byte x loads need K % 8 == 0; a group must not change inside a wave's
+  // 32-row step.
+  return p.M <= kDecodeMaxM && p.K % 8 == 0 && x_al16 && scales_al16 &&
+         (p.g % kDecodeRowsPerStep == 0 || p.G == 1);
+}
+
+bool prefill_supported(const Problem& p, bool x_al16, bool scales_al16) {
+  // Dequantisation works on 4-row blocks that must share a group.
+  return p.K % 8 == 0 && x_al16 && scales_al16 && p.g % 4 == 0;
+}
+
+static int decode_steps_override() {
+  const char* s = getenv("AWQ_DECODE_STEPS");
+  if (!s) return 0;
+  int v = atoi(s);
+  return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 0;
+}
+
+int make_plan(const Problem& p, bool x_al16, bool scales_al16, int force, Plan* out) {
+  Plan pl;
+  memset(&pl, 0, sizeof(pl));
+  const bool dec = decode_supported(p, x_al16, scales_al16);
+  const bool pre = prefill_supported(p, x_al16, scales_al16);
+  int path;
+  if (force == 0) {
+    path = dec ? AWQ_PATH_DECODE : (pre ? AWQ_PATH_PREFILL : AWQ_PATH_GENERIC);
+  } else {
+    path = force;
+    if ((force == AWQ_PATH_DECODE && !dec) || (force == AWQ_PATH_PREFILL && !pre))
+      return AWQ_ERROR_INVALID_VALUE;
+    if (force != AWQ_PATH_DECODE && force != AWQ_PATH_PREFILL && force != AWQ_PATH_GENERIC)
+      return AWQ_ERROR_INVALID_VALUE;
+  }
+  pl.path = path;
+  if (path == AWQ_PATH_DECODE) {
+    pl.n_tiles = static_cast<int>(ceil_div(p.N, kDecodeCols));
+    int steps = decode_steps_override();
+    if (steps == 0) {
+      steps = 1;
+      for (int s = 8; s >= 1; s /= 2) {
+        const int64_t splits = ceil_div(p.K, 2 * kDecodeRowsPerStep * s);
+        if (pl.n_tiles * splits >= kDecodeTargetWGs) { steps = s; break; }
+      }
+    }
+    pl.steps = steps;
+    pl.splits = static_cast<int>(ceil_div(p.K, 2 * kDecodeRowsPerStep * steps));
+    if (pl.splits > 1) {
+      pl.ticket_bytes = round_up(static_cast<size_t>(pl.n_tiles) * 4, 256);
+      pl.ws_bytes = pl.ticket_bytes +
+                    static_cast<size_t>(pl.splits) * p.M * p.N * sizeof(float);
+    }
+  } else if (path == AWQ_PATH_PREFILL) {
+    pl.m_tiles = static_cast<int>(ceil_div(p.M, kPrefillBM));
+    pl.n_tiles = static_cast<int>(ceil_div(p.N, kPrefillBN));
+  }
+  *out = pl;
+  return AWQ_SUCCESS;
+}
+
+int force_path_from_env() {
+  const char* s = getenv("AWQ_FORCE_PATH");
+  if (!s || !*s) return 0;
+  if (!strcmp(s, "decode")) return AWQ_PATH_DECODE;
+  if (!strcmp(s, "prefill")) return AWQ_PATH_PREFILL;
+  if (!strcmp(s, "generic")) return AWQ_PATH_GENERIC;
+  return -1;
+}
+
+}  // namespace awq

@@ -1,0 +1,62 @@
+// Host-side validation and kernel planning for the W4A16 linear forward.
+// HIP-free: this translation unit is compiled with a plain host compiler too,
+// so every argument check can be exercised (and sanitised) without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace awq {
+
+// Decode kernel geometry: a work-group is 4 waves; waves 0/1 and 2/3 split
+// the K range of the work-group, waves 0/2 and 1/3 split its 256 columns.
+constexpr int kDecodeCols = 256;         // columns per work-group
+constexpr int kDecodeRowsPerStep = 32;   // rows one wave consumes per step
+constexpr int kDecodeMaxM = 16;          // rows of the 16x16 MFMA output
+
+// Prefill kernel tile.
+constexpr int kPrefillBM = 256;
+constexpr int kPrefillBN = 128;
+constexpr int kPrefillBK = 64;
+
+struct Problem {
+  int64_t M, K, N;
+  int64_t g;   // resolved group size (K when -1 was passed)
+  int64_t G;   // number of groups
+};
+
+struct Plan {
+  int path;          // awq_path value
+  int steps;         // decode: 32-row steps per wave
+  int splits;        // decode: work-groups along K per column tile
+  int n_tiles;       // column tiles
+  int m_tiles;       // prefill: row tiles
+  size_t ws_bytes;   // workspace bytes
+  size_t ticket_bytes;  // decode: counter area at the start of the workspace
+};
+
+// Checks of the page's WQLinear construction (K % g == 0, N % 8 == 0, the -1
+// rule) plus this library's argument rules.  Returns an awq_status value.
+int validate_shape(int64_t M, int64_t K, int64_t N, int64_t group_size, Problem* out);
+
+// Pointer checks: required pointers non-NULL, element alignment.
+int validate_gemm_pointers(const void* x, const void* qweight, const void* qzeros,
+                           const void* scales, const void* bias, const void* y, int64_t M);
+int validate_dequant_pointers(const void* qweight, const void* qzeros,
+                              const void* scales, const void* w);
+
+bool decode_supported(const Problem& p, bool x_al16, bool scales_al16);
+bool prefill_supported(const Problem& p, bool x_al16, bool scales_al16);
+
+// force: 0 = automatic, otherwise an awq_path value.  Returns an awq_status.
+int make_plan(const Problem& p, bool x_al16, bool scales_al16, int force, Plan* out);
+
+// Parses AWQ_FORCE_PATH.  Returns 0 (unset/automatic), an awq_path value, or
+// -1 for an unrecognised value.
+int force_path_from_env();
+
+inline bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+}  // namespace awq

@@ -1,0 +1,119 @@
+/*
+ * awq.h -- C ABI of the MI355X (gfx950) W4A16 weight-quantised linear forward.
+ *
+ * The operation is the forward of the AWQ WQLinear layer described on the page
+ * "Predibase Lorax AWQ WQLinear" (sections Description and I/O Contract):
+ *
+ *     y[M, N] = x[M, K] . W[K, N] (+ bias[N]),
+ *     W[k, n] = float16_RNE((q[k, n] - z[k / g, n]) * s[k / g, n])
+ *
+ * with K = in_features, N = out_features, g = group_size (g = K when -1 is
+ * passed, G = K / g groups).  Data formats (row-major, contiguous):
+ *
+ *   x        float16  (M, K)
+ *   qweight  int32    (K, N / 8)  eight unsigned 4-bit values per word along
+ *                                 the output dimension; bits [4j, 4j+3] of
+ *                                 word (k, c) hold q[k, 8c + j]
+ *   qzeros   int32    (G, N / 8)  zero points z, packed like qweight
+ *   scales   float16  (G, N)      scales s
+ *   bias     float16  (N) or NULL
+ *   y        float16  (M, N)
+ *
+ * The page fixes the packing (eight 4-bit values per int32 along the output
+ * dimension), the shape of qweight, the -1 rule for group_size and the checks
+ * K % group_size == 0 and N % 8 == 0.  It does not fix the nibble order inside
+ * a word, the layouts of qzeros and scales, or the dequantisation rounding;
+ * the readings above are the ones this library implements.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named x, qweight, qzeros, scales, bias, y, w and workspace are
+ *     DEVICE pointers owned by the caller.  The library allocates nothing and
+ *     keeps no pointer after the call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; nothing synchronises.
+ *   - Arguments are validated on the host before any HIP call.  On a non-zero
+ *     return nothing was enqueued and no output was written, except
+ *     AWQ_ERROR_HIP, which reports a failed launch.
+ *   - Element alignment is required (2 bytes for float16 pointers, 4 bytes for
+ *     int32 pointers).  Faster kernels are chosen when x and scales are 16-byte
+ *     aligned and K % 8 == 0; other legal inputs take a general kernel.
+ *   - Every operand must hold fewer than 2^31 elements (M*K, M*N, K*N).
+ */
+#ifndef AWQ_MI355X_AWQ_H_
+#define AWQ_MI355X_AWQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AWQ_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+enum awq_status {
+  AWQ_SUCCESS = 0,
+  AWQ_ERROR_INVALID_VALUE = 1, /* NULL required pointer, M < 0, K <= 0, N <= 0,
+                                  group_size == 0 or < -1, unknown path request */
+  AWQ_ERROR_SHAPE = 2,         /* N % 8 != 0, K % group_size != 0 (page checks),
+                                  or an operand with 2^31 or more elements */
+  AWQ_ERROR_MISALIGNED = 3,    /* a pointer not aligned to its element size */
+  AWQ_ERROR_WORKSPACE = 4,     /* workspace smaller than awq_gemm_workspace_size */
+  AWQ_ERROR_HIP = 5            /* a HIP launch reported an error */
+};
+
+/* Kernel families that awq_gemm can run (see awq_gemm_plan). */
+enum awq_path {
+  AWQ_PATH_DECODE = 1,  /* split-K MFMA skinny GEMM, M <= 16 */
+  AWQ_PATH_PREFILL = 2, /* LDS-tiled MFMA GEMM with dequantisation into LDS */
+  AWQ_PATH_GENERIC = 3  /* any legal shape or alignment; slow */
+};
+
+/* AWQ_ABI_VERSION of the built library. */
+int awq_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* awq_status_string(int status);
+
+/* Bytes of workspace awq_gemm needs for this problem when x and scales are
+ * 16-byte aligned (the most any pointer alignment needs).  0 means none.
+ * Returns 0 for invalid shapes (awq_gemm then reports the error). */
+size_t awq_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size);
+
+/* Host-only planning, no HIP call and no dereference of x or scales (only
+ * their addresses' alignment is inspected).  Writes the kernel family awq_gemm
+ * would run to *path and its workspace need to *workspace_bytes (either may be
+ * NULL).  The environment variable AWQ_FORCE_PATH = decode | prefill | generic
+ * overrides the choice for testing; a forced family that cannot run the
+ * problem yields AWQ_ERROR_INVALID_VALUE. */
+int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size,
+                  const void* x, const void* scales, int* path,
+                  size_t* workspace_bytes);
+
+/* The WQLinear forward (page "Predibase Lorax AWQ WQLinear", Description,
+ * forward steps 1-3), with the bias addition fused into the kernel epilogue:
+ * y = float16_RNE(fp32 accumulation of x . W + bias).
+ *
+ * workspace: device memory of at least awq_gemm_workspace_size(...) bytes, or
+ * NULL when that is 0.  It must be zero-filled once before its first use; the
+ * kernels leave it re-usable (all counters back at zero) on exit, so the same
+ * buffer serves later calls on the same stream.  Two calls that may run
+ * concurrently (different streams) must not share a workspace.
+ * M == 0 is a no-op that returns AWQ_SUCCESS (x and y may then be NULL). */
+int awq_gemm(const void* x, const void* qweight, const void* qzeros,
+             const void* scales, const void* bias, void* y,
+             int64_t M, int64_t K, int64_t N, int64_t group_size,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* The dequantised weight on its own: w[K, N] float16 with
+ * w[k, n] = float16_RNE((q[k, n] - z[k / g, n]) * s[k / g, n]), bit-exact
+ * (the page's "per-group dequantization", Description). */
+int awq_dequant(const void* qweight, const void* qzeros, const void* scales,
+                void* w, int64_t K, int64_t N, int64_t group_size, void* stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* AWQ_MI355X_AWQ_H_ */

@@ -1,0 +1,87 @@
+// Drives the HIP-free validation and planning code over a grid of arguments,
+// including every error path and extreme sizes, under ASan/UBSan.  Prints
+// "plan_check ok" and exits 0 when every expectation holds.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "awq.h"
+#include "awq_plan.h"
+
+static int failures = 0;
+#define EXPECT(cond)                                                   \
+  do {                                                                 \
+    if (!(cond)) {                                                     \
+      fprintf(stderr, "%s:%d: expectation failed: %s\n", __FILE__,    \
+              __LINE__, #cond);                                        \
+      ++failures;                                                      \
+    }                                                                  \
+  } while (0)
+
+int main() {
+  using namespace awq;
+  Problem p;
+  EXPECT(validate_shape(4, 256, 128, 64, &p) == AWQ_SUCCESS);
+  EXPECT(p.g == 64 && p.G == 4);
+  EXPECT(validate_shape(4, 256, 128, -1, &p) == AWQ_SUCCESS && p.g == 256 && p.G == 1);
+  EXPECT(validate_shape(-1, 256, 128, 64, &p) == AWQ_ERROR_INVALID_VALUE);
+  EXPECT(validate_shape(4, 0, 128, 64, &p) == AWQ_ERROR_INVALID_VALUE);
+  EXPECT(validate_shape(4, 256, 0, 64, &p) == AWQ_ERROR_INVALID_VALUE);
+  EXPECT(validate_shape(4, 256, 128, 0, &p) == AWQ_ERROR_INVALID_VALUE);
+  EXPECT(validate_shape(4, 256, 128, -7, &p) == AWQ_ERROR_INVALID_VALUE);
+  EXPECT(validate_shape(4, 256, 130, 64, &p) == AWQ_ERROR_SHAPE);
+  EXPECT(validate_shape(4, 256, 128, 48, &p) == AWQ_ERROR_SHAPE);
+  EXPECT(validate_shape(INT64_MAX, INT64_MAX, 8, -1, &p) == AWQ_ERROR_SHAPE);
+  EXPECT(validate_shape(1, INT64_MAX - 7, 8, -1, &p) == AWQ_ERROR_SHAPE);
+  EXPECT(validate_shape(1, (int64_t)1 << 40, (int64_t)1 << 40, -1, &p) == AWQ_ERROR_SHAPE);
+
+  int x;
+  EXPECT(validate_gemm_pointers(&x, &x, &x, &x, nullptr, &x, 1) == AWQ_SUCCESS);
+  EXPECT(validate_gemm_pointers(nullptr, &x, &x, &x, nullptr, nullptr, 0) == AWQ_SUCCESS);
+  EXPECT(validate_gemm_pointers(nullptr, &x, &x, &x, nullptr, &x, 1) == AWQ_ERROR_INVALID_VALUE);
+  EXPECT(validate_gemm_pointers(&x, (char*)&x + 2, &x, &x, nullptr, &x, 1) ==
+         AWQ_ERROR_MISALIGNED);
+  EXPECT(validate_dequant_pointers(&x, &x, &x, nullptr) == AWQ_ERROR_INVALID_VALUE);
+
+  // Every shape in a grid plans without overflow, and a plan's workspace
+  // covers its split-K partials.
+  const int64_t Ms[] = {0, 1, 2, 15, 16, 17, 255, 256, 4096};
+  const int64_t Ks[] = {8, 32, 40, 96, 256, 4096, 8192, 14336};
+  const int64_t Ns[] = {8, 24, 128, 1280, 7168, 12288};
+  const int64_t gs[] = {-1, 1, 4, 8, 32, 64, 128};
+  for (int64_t M : Ms)
+    for (int64_t K : Ks)
+      for (int64_t N : Ns)
+        for (int64_t g : gs) {
+          if (validate_shape(M, K, N, g, &p) != AWQ_SUCCESS) continue;
+          for (int force = 0; force <= 3; ++force) {
+            for (int al = 0; al < 4; ++al) {
+              Plan pl;
+              const int st = make_plan(p, al & 1, al & 2, force, &pl);
+              if (st != AWQ_SUCCESS) {
+                EXPECT(force != 0 && force != AWQ_PATH_GENERIC);
+                continue;
+              }
+              if (pl.path == AWQ_PATH_DECODE) {
+                EXPECT(M <= kDecodeMaxM);
+                EXPECT(pl.splits >= 1 && pl.n_tiles * kDecodeCols >= N);
+                EXPECT((int64_t)pl.splits * 2 * kDecodeRowsPerStep * pl.steps >= K);
+                if (pl.splits > 1)
+                  EXPECT(pl.ws_bytes >= pl.ticket_bytes + (size_t)pl.splits * M * N * 4);
+                else
+                  EXPECT(pl.ws_bytes == 0);
+              } else if (pl.path == AWQ_PATH_PREFILL) {
+                EXPECT((int64_t)pl.m_tiles * kPrefillBM >= M);
+                EXPECT((int64_t)pl.n_tiles * kPrefillBN >= N);
+                EXPECT(pl.ws_bytes == 0);
+              }
+            }
+          }
+        }
+  if (failures) {
+    fprintf(stderr, "%d failures\n", failures);
+    return 1;
+  }
+  printf("plan_check ok\n");
+  return 0;
+}

@@ -1,0 +1,216 @@
+"""Host-side tests of the C-ABI library: it loads without a GPU, exports every
+symbol include/awq.h declares, and rejects every invalid argument before any
+HIP call.  No compute runs here (no GPU in this environment)."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import bit_weight_quantized_awq_amd as awq
+from bit_weight_quantized_awq_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq.h")
+
+# Fake device addresses: never dereferenced, every call below returns before
+# any HIP call.
+A = 0x10000
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(awq_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert header_functions() == sorted(binding.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = awq.lib()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", binding.LIB_PATH],
+                             capture_output=True, text=True, check=True).stdout
+        exported = set(re.findall(r"\b(awq_\w+)\b", out))
+        assert set(header_functions()) <= exported
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define AWQ_ABI_VERSION (\d+)", open(HEADER).read())
+    assert awq.abi_version() == int(m.group(1))
+
+
+def test_status_strings():
+    for s in range(6):
+        assert awq.status_string(s)
+    assert awq.status_string(0) == "success"
+    assert awq.status_string(99) == "unknown status"
+
+
+def _gemm(x=A, qw=A, qz=A, sc=A, bias=None, y=A, M=4, K=256, N=128, g=64, ws=None, wsb=0):
+    return awq.lib().awq_gemm(x, qw, qz, sc, bias, y, M, K, N, g, ws, wsb, None)
+
+
+def _dequant(qw=A, qz=A, sc=A, w=A, K=256, N=128, g=64):
+    return awq.lib().awq_dequant(qw, qz, sc, w, K, N, g, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(qw=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(qz=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(sc=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(x=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(y=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(M=-1), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(K=0), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(N=0), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(N=-8), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(g=0), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(g=-2), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(N=100), binding.AWQ_ERROR_SHAPE),           # out_features % 8
+    (dict(g=96), binding.AWQ_ERROR_SHAPE),            # in_features % group_size
+    (dict(g=512), binding.AWQ_ERROR_SHAPE),           # group larger than K
+    (dict(K=65536, N=65536, g=128), binding.AWQ_ERROR_SHAPE),  # K*N >= 2^31
+    (dict(M=1 << 20, K=4096, N=4096), binding.AWQ_ERROR_SHAPE),  # M*K >= 2^31
+    (dict(qw=A + 2), binding.AWQ_ERROR_MISALIGNED),
+    (dict(qz=A + 1), binding.AWQ_ERROR_MISALIGNED),
+    (dict(sc=A + 1), binding.AWQ_ERROR_MISALIGNED),
+    (dict(x=A + 1), binding.AWQ_ERROR_MISALIGNED),
+    (dict(y=A + 3), binding.AWQ_ERROR_MISALIGNED),
+    (dict(bias=A + 1), binding.AWQ_ERROR_MISALIGNED),
+    (dict(M=0, x=None, y=None), binding.AWQ_SUCCESS),  # empty batch: no launch
+])
+def test_gemm_validation(kwargs, status):
+    assert _gemm(**kwargs) == status
+
+
+def test_gemm_workspace_checked_before_launch():
+    M, K, N, g = 1, 8192, 7168, 128
+    need = awq.gemm_workspace_size(M, K, N, g)
+    assert need > 0
+    assert _gemm(M=M, K=K, N=N, g=g) == binding.AWQ_ERROR_WORKSPACE
+    assert _gemm(M=M, K=K, N=N, g=g, ws=A, wsb=need - 1) == binding.AWQ_ERROR_WORKSPACE
+    assert _gemm(M=M, K=K, N=N, g=g, ws=A + 8, wsb=need) == binding.AWQ_ERROR_MISALIGNED
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(qw=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(w=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(K=0), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(N=12), binding.AWQ_ERROR_SHAPE),
+    (dict(g=100), binding.AWQ_ERROR_SHAPE),
+    (dict(g=-5), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(w=A + 1), binding.AWQ_ERROR_MISALIGNED),
+    (dict(qz=A + 2), binding.AWQ_ERROR_MISALIGNED),
+])
+def test_dequant_validation(kwargs, status):
+    assert _dequant(**kwargs) == status
+
+
+@pytest.mark.parametrize("M,K,N,g,path", [
+    (4, 256, 128, 64, binding.AWQ_PATH_DECODE),
+    (1, 8192, 1280, 128, binding.AWQ_PATH_DECODE),
+    (16, 8192, 7168, 128, binding.AWQ_PATH_DECODE),
+    (2048, 4096, 12288, 128, binding.AWQ_PATH_PREFILL),
+    (1, 14336, 4096, -1, binding.AWQ_PATH_DECODE),
+    (4096, 14336, 4096, -1, binding.AWQ_PATH_PREFILL),
+    (256, 14336, 4096, 128, binding.AWQ_PATH_PREFILL),
+    (17, 4096, 4096, 128, binding.AWQ_PATH_PREFILL),
+    (4, 96, 64, 3, binding.AWQ_PATH_GENERIC),        # group size not a multiple of 4
+    (4, 100, 64, -1, binding.AWQ_PATH_GENERIC),      # K % 8 != 0
+    (4, 256, 64, 16, binding.AWQ_PATH_PREFILL),      # small groups: not decode
+])
+def test_plan_selects_kernel(M, K, N, g, path):
+    got, ws = awq.gemm_plan(M, K, N, g)
+    assert got == path
+    if path == binding.AWQ_PATH_DECODE:
+        assert ws == awq.gemm_workspace_size(M, K, N, g) or ws == 0
+    else:
+        assert ws == 0
+
+
+def test_plan_unaligned_x_falls_back_to_generic():
+    assert awq.gemm_plan(1, 8192, 7168, 128, x_ptr=A + 2, scales_ptr=A)[0] == \
+        binding.AWQ_PATH_GENERIC
+    assert awq.gemm_plan(1, 8192, 7168, 128, x_ptr=A, scales_ptr=A + 2)[0] == \
+        binding.AWQ_PATH_GENERIC
+
+
+def test_forced_path(monkeypatch):
+    monkeypatch.setenv("AWQ_FORCE_PATH", "prefill")
+    assert awq.gemm_plan(1, 8192, 7168, 128)[0] == binding.AWQ_PATH_PREFILL
+    monkeypatch.setenv("AWQ_FORCE_PATH", "generic")
+    assert awq.gemm_plan(2048, 4096, 12288, 128)[0] == binding.AWQ_PATH_GENERIC
+    monkeypatch.setenv("AWQ_FORCE_PATH", "decode")
+    with pytest.raises(awq.AwqError):
+        awq.gemm_plan(64, 4096, 4096, 128)          # decode handles M <= 16 only
+    monkeypatch.setenv("AWQ_FORCE_PATH", "bogus")
+    with pytest.raises(awq.AwqError):
+        awq.gemm_plan(1, 4096, 4096, 128)
+    assert _gemm(M=1, K=4096, N=4096, g=128) == binding.AWQ_ERROR_INVALID_VALUE
+
+
+def test_decode_workspace_size_formula():
+    """Tickets (one uint32 per 256-column tile, padded to 256 bytes) plus one
+    fp32 partial row per split per batch row."""
+    M, K, N, g = 4, 8192, 7168, 128
+    path, ws = awq.gemm_plan(M, K, N, g)
+    assert path == binding.AWQ_PATH_DECODE
+    n_tiles = -(-N // 256)
+    ticket = -(-(n_tiles * 4) // 256) * 256
+    partial = ws - ticket
+    assert partial % (M * N * 4) == 0
+    splits = partial // (M * N * 4)
+    assert any(splits == -(-K // (64 * steps)) for steps in (1, 2, 4, 8))
+
+
+def test_no_cpu_fallback():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((256, 16), dtype=torch.int32)
+    with pytest.raises(ValueError, match="HIP device"):
+        awq.gemm(torch.zeros((1, 256), dtype=torch.float16), q, torch.zeros((4, 16), dtype=torch.int32),
+                 torch.zeros((4, 128), dtype=torch.float16), None, 64)
+    with pytest.raises(ValueError, match="HIP device"):
+        awq.dequant(q, torch.zeros((4, 16), dtype=torch.int32),
+                    torch.zeros((4, 128), dtype=torch.float16), 64)
+
+
+def test_wqlinear_construction_checks():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((256, 16), dtype=torch.int32)
+    z = torch.zeros((4, 16), dtype=torch.int32)
+    s = torch.zeros((4, 128), dtype=torch.float16)
+    layer = awq.WQLinear(4, 64, q, z, s, None)
+    assert layer.in_features == 256 and layer.out_features == 128
+    assert layer.weight is layer.qweight
+    assert awq.WQLinear(4, -1, q, z[:1], s[:1], None).group_size == 256
+    with pytest.raises(ValueError):
+        awq.WQLinear(8, 64, q, z, s, None)
+    with pytest.raises(ValueError):
+        awq.WQLinear(4, 100, q, z, s, None)
+
+
+def test_validation_under_sanitizers(tmp_path):
+    """The HIP-free planning/validation translation unit, built with the host
+    compiler under AddressSanitizer + UBSan and driven over a grid of
+    arguments (including every error path and extreme sizes)."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    csrc = os.path.join(ROOT, "bit_weight_quantized_awq_amd", "csrc")
+    exe = tmp_path / "plan_check"
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", f"-I{os.path.join(ROOT, 'include')}", f"-I{csrc}",
+           os.path.join(csrc, "awq_plan.cpp"), os.path.join(ROOT, "tests", "native", "plan_check.cpp"),
+           "-o", str(exe)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "plan_check ok" in res.stdout
