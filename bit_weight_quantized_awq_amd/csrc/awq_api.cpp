@@ -85,7 +85,7 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void*
   switch (pl.path) {
     case AWQ_PATH_DECODE:
       e = awq::launch_decode(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, iG, pl.steps, pl.splits,
-                             pl.n_tiles, workspace, pl.ticket_bytes, s);
+                             pl.n_tiles, workspace, pl.ticket_stride, s);
       break;
     case AWQ_PATH_PREFILL:
       e = awq::launch_prefill(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, pl.m_tiles, pl.n_tiles, s);

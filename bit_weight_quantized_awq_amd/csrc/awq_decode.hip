@@ -31,20 +31,27 @@
 // * Reduction: the two K-halves of a work-group meet in LDS; work-groups write
 //   fp32 partials to the workspace, take a ticket on their column tile, and
 //   the last one sums the partials in split order (deterministic), adds the
-//   bias, rounds to float16 and resets the ticket.
+//   bias, rounds to float16 and resets the ticket.  Tickets sit up to 256
+//   bytes apart in a fixed region at the start of the workspace:
+//   device-scope atomics on one cache line are serialised, which costs
+//   ~0.2 us per arrival when every tile shares a line.
 #include "awq_device.h"
 #include "awq_plan.h"
 
 namespace awq {
 namespace {
 
-template <int STEPS>
-__global__ __launch_bounds__(256) void decode_kernel(
+// SINGLE_GROUP: every row a wave reads lies in one quantisation group (the
+// group size is a multiple of the wave's 32*STEPS rows, or there is one
+// group), so the scale is applied once after all steps.  Otherwise each
+// 32-row step (which never straddles a group) is scaled on its own.
+template <int STEPS, bool SINGLE_GROUP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_kernel(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
     const _Float16* __restrict__ bias, _Float16* __restrict__ y,
     float* __restrict__ partial, uint32_t* __restrict__ tickets,
-    int M, int K, int N, int g, int G, int splits) {
+    int M, int K, int N, int g, int G, int splits, int ticket_words) {
   extern __shared__ float red[];  // [2][M][256] fp32
   __shared__ int s_last;
 
@@ -61,33 +68,47 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const int c = n_tile * 32 + wn * 16 + col16;
   const bool cvalid = c < NW;
   const int kw0 = split * (64 * STEPS) + wk * (32 * STEPS);
-  const bool wave_has_rows = kw0 < K;
 
-  // Group parameters of the wave's first step, fetched first.
-  int cur = (G == 1) ? 0 : kw0 / g;
-  uint32_t zw = 0;
-  half8_t sv = {};
-  if (wave_has_rows && cvalid) {
-    zw = qz[cur * NW + c];
-    sv = *reinterpret_cast<const half8_t*>(sc + cur * N + 8 * c);
+  // Buffer resources: every load below is range-checked by the hardware and
+  // reads zero outside its tensor, so tails need no branches.  Steps at or
+  // past K read x == 0 and contribute exact zeros.
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qw, static_cast<uint32_t>(K) * NW * 4u);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(qz, static_cast<uint32_t>(G) * NW * 4u);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(sc, static_cast<uint32_t>(G) * N * 2u);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, static_cast<uint32_t>(M) * K * 2u);
+
+  // Group parameters first (one group, or one per step).
+  constexpr int NG = SINGLE_GROUP ? 1 : STEPS;
+  uint32_t zw[NG];
+  half8_t sv[NG];
+#pragma unroll
+  for (int s = 0; s < NG; ++s) {
+    const int k0 = kw0 + 32 * s;
+    const int grp = (G == 1) ? 0 : k0 / g;
+    const bool ok = cvalid && k0 < K;
+    zw[s] = buf_load_u32(rz, ok ? static_cast<uint32_t>(grp * NW + c) * 4u : kOutOfRange);
+    sv[s] = __builtin_bit_cast(
+        half8_t, buf_load_u32x4(rs, ok ? static_cast<uint32_t>(grp * N + 8 * c) * 2u
+                                       : kOutOfRange));
   }
 
-  // All x fragments and packed words of this wave.
+  // x fragments, then every packed word of this wave, all in flight at once.
   half8_t xa[STEPS];
-  uint32_t wv[STEPS][8];
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     const int kr = kw0 + 32 * s + 8 * kb;
-    xa[s] = (col16 < M && kr < K) ? *reinterpret_cast<const half8_t*>(x + col16 * K + kr)
-                                  : half8_t{};
+    const uint32_t xoff = (col16 < M && kr < K) ? static_cast<uint32_t>(col16 * K + kr) * 2u
+                                                : kOutOfRange;
+    xa[s] = __builtin_bit_cast(half8_t, buf_load_u32x4(rx, xoff));
   }
+  uint32_t wv[STEPS][8];
+  const uint32_t row_bytes = static_cast<uint32_t>(NW) * 4u;
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     const int kr = kw0 + 32 * s + 8 * kb;
-    const bool rv = cvalid && kr < K;
-    const uint32_t* src = qw + kr * NW + c;
+    const uint32_t off = cvalid ? static_cast<uint32_t>(kr * NW + c) * 4u : kOutOfRange;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) wv[s][r] = rv ? src[r * NW] : 0u;
+    for (int r = 0; r < 8; ++r) wv[s][r] = buf_load_u32(rq, off + r * row_bytes);
   }
 
   floatx4 acc[8], tot[8];
@@ -96,28 +117,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
     acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
     tot[j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  uint32_t zp[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) zp[j] = zero_pair(zw, j);
 
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
-    const int k0 = kw0 + 32 * s;
-    if (k0 >= K) break;
-    const int grp = (G == 1) ? 0 : k0 / g;
-    if (grp != cur) {
-      // Close the previous group: scale its fp32 partial into the total.
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        tot[j] += static_cast<float>(sv[j]) * acc[j];
-        acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
-      cur = grp;
-      zw = cvalid ? qz[grp * NW + c] : 0u;
-      sv = cvalid ? *reinterpret_cast<const half8_t*>(sc + grp * N + 8 * c) : half8_t{};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) zp[j] = zero_pair(zw, j);
-    }
+    const int gi = SINGLE_GROUP ? 0 : s;
     uint32_t plo[4], phi[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       half8_t b;
-      const half2_t z2 = as_h2(zp[j]);
+      const half2_t z2 = as_h2(zero_pair(zw[gi], j));
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const uint32_t src = (j < 4) ? plo[p] : phi[p];
@@ -137,9 +140,19 @@ __global__ __launch_bounds__(256) void decode_kernel(
       }
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], b, acc[j], 0, 0, 0);
     }
-  }
+    if (!SINGLE_GROUP) {
+      // Scale this step's fp32 partial by its group's scales.
 #pragma unroll
-  for (int j = 0; j < 8; ++j) tot[j] += static_cast<float>(sv[j]) * acc[j];
+      for (int j = 0; j < 8; ++j) {
+        tot[j] += static_cast<float>(sv[s][j]) * acc[j];
+        acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+  if (SINGLE_GROUP) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tot[j] = static_cast<float>(sv[0][j]) * acc[j];
+  }
 
   // tot[j][i] is row 4*kb + i, column 8*c + j.  Meet the other K-half in LDS.
   const int lcol = 8 * (wn * 16 + col16);
@@ -166,49 +179,72 @@ __global__ __launch_bounds__(256) void decode_kernel(
     return;
   }
 
+  // Split-K exchange.  Partials are written with device-coherent stores and
+  // read back with device-coherent loads (agent-scope atomic accesses: they
+  // bypass the per-XCD L2's non-coherent state instead of needing a whole-L2
+  // writeback and invalidate).  Each thread waits for its stores to be
+  // acknowledged before the barrier, so every partial of this work-group is
+  // in place before its ticket is taken; the work-group that takes the last
+  // ticket therefore sees all of them.
   if (nvalid) {
     for (int m = 0; m < M; ++m) {
       const float v = red[m * kDecodeCols + tid] + red[(M + m) * kDecodeCols + tid];
-      partial[(split * M + m) * N + n] = v;
+      __hip_atomic_store(partial + (split * M + m) * N + n, v, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __threadfence();  // release this work-group's partials device-wide
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&tickets[n_tile], 1u) == static_cast<unsigned>(splits - 1));
+  if (tid == 0)
+    s_last = (__hip_atomic_fetch_add(tickets + n_tile * ticket_words, 1u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) ==
+              static_cast<unsigned>(splits - 1));
   __syncthreads();
   if (!s_last) return;
-  __threadfence();  // acquire every other work-group's partials
 
   if (nvalid) {
     const float b = bias ? static_cast<float>(bias[n]) : 0.f;
+    const int stride = M * N;
     for (int m = 0; m < M; ++m) {
       const float* p = partial + m * N + n;
-      const int stride = M * N;
       float sum = 0.f;
       int sp = 0;
-      for (; sp + 8 <= splits; sp += 8) {
-        float v[8];
+      for (; sp + 16 <= splits; sp += 16) {
+        float v[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = p[(sp + u) * stride];
+        for (int u = 0; u < 16; ++u)
+          v[u] = __hip_atomic_load(p + (sp + u) * stride, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) sum += v[u];
+        for (int u = 0; u < 16; ++u) sum += v[u];
       }
-      for (; sp < splits; ++sp) sum += p[sp * stride];
+      for (; sp < splits; ++sp)
+        sum += __hip_atomic_load(p + sp * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       y[m * N + n] = static_cast<_Float16>(sum + b);
     }
   }
-  if (tid == 0) atomicExch(&tickets[n_tile], 0u);
+  if (tid == 0) __hip_atomic_store(tickets + n_tile * ticket_words, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int STEPS>
 hipError_t launch_steps(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                         const _Float16* scales, const _Float16* bias, _Float16* y,
                         int M, int K, int N, int g, int G, int splits, int n_tiles,
-                        float* partial, uint32_t* tickets, hipStream_t stream) {
+                        float* partial, uint32_t* tickets, int ticket_words,
+                        hipStream_t stream) {
   const size_t shmem = 2 * static_cast<size_t>(M) * kDecodeCols * sizeof(float);
-  hipLaunchKernelGGL(decode_kernel<STEPS>, dim3(n_tiles * splits), dim3(256), shmem, stream,
-                     x, qweight, qzeros, scales, bias, y, partial, tickets, M, K, N, g, G,
-                     splits);
+  // Work-group row ranges start at multiples of 64*STEPS, so every wave's
+  // 32*STEPS rows share a group exactly when g is a multiple of 32*STEPS.
+  const bool single = (G == 1) || (g % (kDecodeRowsPerStep * STEPS) == 0);
+  if (single)
+    hipLaunchKernelGGL((decode_kernel<STEPS, true>), dim3(n_tiles * splits), dim3(256), shmem,
+                       stream, x, qweight, qzeros, scales, bias, y, partial, tickets, M, K, N,
+                       g, G, splits, ticket_words);
+  else
+    hipLaunchKernelGGL((decode_kernel<STEPS, false>), dim3(n_tiles * splits), dim3(256), shmem,
+                       stream, x, qweight, qzeros, scales, bias, y, partial, tickets, M, K, N,
+                       g, G, splits, ticket_words);
   return hipGetLastError();
 }
 
@@ -217,21 +253,22 @@ hipError_t launch_steps(const _Float16* x, const uint32_t* qweight, const uint32
 hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                          const _Float16* scales, const _Float16* bias, _Float16* y,
                          int M, int K, int N, int g, int G, int steps, int splits,
-                         int n_tiles, void* workspace, size_t ticket_bytes,
+                         int n_tiles, void* workspace, int ticket_stride,
                          hipStream_t stream) {
   uint32_t* tickets = static_cast<uint32_t*>(workspace);
   float* partial = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                        ticket_bytes)
+                                                        kTicketRegionBytes)
                              : nullptr;
+  const int tw = ticket_stride / 4;
   switch (steps) {
     case 1: return launch_steps<1>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G, splits,
-                                   n_tiles, partial, tickets, stream);
+                                   n_tiles, partial, tickets, tw, stream);
     case 2: return launch_steps<2>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G, splits,
-                                   n_tiles, partial, tickets, stream);
+                                   n_tiles, partial, tickets, tw, stream);
     case 4: return launch_steps<4>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G, splits,
-                                   n_tiles, partial, tickets, stream);
+                                   n_tiles, partial, tickets, tw, stream);
     case 8: return launch_steps<8>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G, splits,
-                                   n_tiles, partial, tickets, stream);
+                                   n_tiles, partial, tickets, tw, stream);
     default: return hipErrorInvalidValue;
   }
 }

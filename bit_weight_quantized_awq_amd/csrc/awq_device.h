@@ -30,9 +30,35 @@ __device__ __forceinline__ uint32_t pair_bytes_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// (v & mask) | bits in one VALU instruction.  The compiler splits this
+// pattern into two when the operands are constants; gfx9 encodings allow at
+// most one scalar operand, so the mask travels in a vector register.
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t bits) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(v), "v"(mask), "s"(bits));
+  return d;
+}
+
 // (1024 + nibble, 1024 + nibble) float16 pair from a pair_bytes_* register.
 __device__ __forceinline__ uint32_t magic_pair(uint32_t paired, int shift) {
-  return ((paired >> shift) & kNibblePairMask) | kMagicPair;
+  return and_or(paired >> shift, kNibblePairMask, kMagicPair);
+}
+
+// Buffer resource over [base, base + bytes): loads at offsets outside that
+// range return zero instead of touching memory, so tails need no branches.
+// Offsets are in bytes and must stay below 2^32.
+constexpr uint32_t kOutOfRange = 0x80000000u;  // any offset >= the range reads 0
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                          0x00020000);
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t buf_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x4 buf_load_u32x4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
@@ -59,7 +85,7 @@ hipError_t launch_generic(const _Float16* x, const uint32_t* qweight, const uint
 hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                          const _Float16* scales, const _Float16* bias, _Float16* y,
                          int M, int K, int N, int g, int G, int steps, int splits,
-                         int n_tiles, void* workspace, size_t ticket_bytes,
+                         int n_tiles, void* workspace, int ticket_stride,
                          hipStream_t stream);
 hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                           const _Float16* scales, const _Float16* bias, _Float16* y,

@@ -18,11 +18,12 @@ __global__ __launch_bounds__(256) void generic_kernel(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
     const _Float16* __restrict__ bias, _Float16* __restrict__ y,
-    int M, int K, int N, int g) {
+    int M, int K, int N, int g, int n_tiles) {
   __shared__ float xs[kRows][kKChunk];
   const int NW = N / 8;
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  const int m0 = blockIdx.y * kRows;
+  const int mt = blockIdx.x / n_tiles;
+  const int n = (blockIdx.x - mt * n_tiles) * 256 + threadIdx.x;
+  const int m0 = mt * kRows;
   const int c = n >> 3;
   const int shift = 4 * (n & 7);
   float acc[kRows];
@@ -66,9 +67,10 @@ __global__ __launch_bounds__(256) void generic_kernel(
 hipError_t launch_generic(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                           const _Float16* scales, const _Float16* bias, _Float16* y,
                           int M, int K, int N, int g, hipStream_t stream) {
-  const dim3 grid((N + 255) / 256, (M + kRows - 1) / kRows);
-  hipLaunchKernelGGL(generic_kernel, grid, dim3(256), 0, stream,
-                     x, qweight, qzeros, scales, bias, y, M, K, N, g);
+  const int n_tiles = (N + 255) / 256;
+  const int m_tiles = (M + kRows - 1) / kRows;
+  hipLaunchKernelGGL(generic_kernel, dim3(n_tiles * m_tiles), dim3(256), 0, stream,
+                     x, qweight, qzeros, scales, bias, y, M, K, N, g, n_tiles);
   return hipGetLastError();
 }
 

@@ -58,16 +58,25 @@ int validate_dequant_pointers(const void* qweight, const void* qzeros,
   return AWQ_SUCCESS;
 }
 
+// The fast kernels address every operand with 32-bit byte offsets (buffer
+// loads whose out-of-range offsets read zero): keep each operand below 1 GiB.
+static bool fits_32bit_offsets(const Problem& p) {
+  const int64_t lim = int64_t{1} << 29;  // elements of 2 bytes
+  return p.M * p.K <= lim && p.M * p.N <= lim && p.K * p.N / 4 <= lim;
+}
+
 bool decode_supported(const Problem& p, bool x_al16, bool scales_al16) {
   // 16-byte x loads need K % 8 == 0; a group must not change inside a wave's
-  // 32-row step.
-  return p.M <= kDecodeMaxM && p.K % 8 == 0 && x_al16 && scales_al16 &&
+  // 32-row step; every column tile needs a 4-byte ticket slot.
+  const int64_t n_tiles = (p.N + kDecodeCols - 1) / kDecodeCols;
+  return fits_32bit_offsets(p) && n_tiles * 4 <= static_cast<int64_t>(kTicketRegionBytes) &&
+         p.M <= kDecodeMaxM && p.K % 8 == 0 && x_al16 && scales_al16 &&
          (p.g % kDecodeRowsPerStep == 0 || p.G == 1);
 }
 
 bool prefill_supported(const Problem& p, bool x_al16, bool scales_al16) {
   // Dequantisation works on 4-row blocks that must share a group.
-  return p.K % 8 == 0 && x_al16 && scales_al16 && p.g % 4 == 0;
+  return fits_32bit_offsets(p) && p.K % 8 == 0 && x_al16 && scales_al16 && p.g % 4 == 0;
 }
 
 static int decode_steps_override() {
@@ -97,17 +106,23 @@ int make_plan(const Problem& p, bool x_al16, bool scales_al16, int force, Plan* 
     pl.n_tiles = static_cast<int>(ceil_div(p.N, kDecodeCols));
     int steps = decode_steps_override();
     if (steps == 0) {
+      // At most 4 steps (32 outstanding word loads per lane plus x, zeros and
+      // scales stay under the 63 outstanding vector loads a wave can track);
+      // prefer step counts whose rows stay in one quantisation group, and the
+      // largest that still gives enough work-groups.
       steps = 1;
-      for (int s = 8; s >= 1; s /= 2) {
+      for (int s = 4; s >= 1; s /= 2) {
+        const bool single = p.G == 1 || p.g % (kDecodeRowsPerStep * s) == 0;
         const int64_t splits = ceil_div(p.K, 2 * kDecodeRowsPerStep * s);
-        if (pl.n_tiles * splits >= kDecodeTargetWGs) { steps = s; break; }
+        if (single && pl.n_tiles * splits >= kDecodeTargetWGs) { steps = s; break; }
       }
     }
     pl.steps = steps;
     pl.splits = static_cast<int>(ceil_div(p.K, 2 * kDecodeRowsPerStep * steps));
+    int stride = static_cast<int>(kTicketRegionBytes / pl.n_tiles) & ~3;
+    pl.ticket_stride = stride < kTicketMaxStrideBytes ? stride : kTicketMaxStrideBytes;
     if (pl.splits > 1) {
-      pl.ticket_bytes = round_up(static_cast<size_t>(pl.n_tiles) * 4, 256);
-      pl.ws_bytes = pl.ticket_bytes +
+      pl.ws_bytes = kTicketRegionBytes +
                     static_cast<size_t>(pl.splits) * p.M * p.N * sizeof(float);
     }
   } else if (path == AWQ_PATH_PREFILL) {

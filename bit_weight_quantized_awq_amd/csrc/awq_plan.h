@@ -13,6 +13,13 @@ namespace awq {
 constexpr int kDecodeCols = 256;         // columns per work-group
 constexpr int kDecodeRowsPerStep = 32;   // rows one wave consumes per step
 constexpr int kDecodeMaxM = 16;          // rows of the 16x16 MFMA output
+// Split-K tickets live in a fixed region at the start of every workspace, so
+// the partial sums of any call (which start after it) can never overwrite
+// the tickets of a later call with a different shape sharing the workspace.
+// Device-scope atomics to one cache line serialise, so each column tile's
+// ticket gets its own slot of up to 256 bytes.
+constexpr size_t kTicketRegionBytes = 65536;
+constexpr int kTicketMaxStrideBytes = 256;
 
 // Prefill kernel tile.
 constexpr int kPrefillBM = 256;
@@ -32,7 +39,7 @@ struct Plan {
   int n_tiles;       // column tiles
   int m_tiles;       // prefill: row tiles
   size_t ws_bytes;   // workspace bytes
-  size_t ticket_bytes;  // decode: counter area at the start of the workspace
+  int ticket_stride;  // decode: bytes between two tiles' tickets
 };
 
 // Checks of the page's WQLinear construction (K % g == 0, N % 8 == 0, the -1

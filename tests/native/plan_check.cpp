@@ -66,8 +66,10 @@ int main() {
                 EXPECT(M <= kDecodeMaxM);
                 EXPECT(pl.splits >= 1 && pl.n_tiles * kDecodeCols >= N);
                 EXPECT((int64_t)pl.splits * 2 * kDecodeRowsPerStep * pl.steps >= K);
+                EXPECT(pl.ticket_stride >= 4 && pl.ticket_stride % 4 == 0);
+                EXPECT((size_t)pl.ticket_stride * pl.n_tiles <= kTicketRegionBytes);
                 if (pl.splits > 1)
-                  EXPECT(pl.ws_bytes >= pl.ticket_bytes + (size_t)pl.splits * M * N * 4);
+                  EXPECT(pl.ws_bytes == kTicketRegionBytes + (size_t)pl.splits * M * N * 4);
                 else
                   EXPECT(pl.ws_bytes == 0);
               } else if (pl.path == AWQ_PATH_PREFILL) {

@@ -314,7 +314,8 @@ def test_deterministic_repeats(M):
 
 def test_workspace_reuse_across_shapes():
     """One workspace serves decode calls of different shapes back to back
-    (the kernels leave every ticket at zero)."""
+    (the kernels leave every ticket at zero).  Regression: a narrow call's
+    partial sums must not land on a wider call's tickets."""
     say("workspace reuse")
     ws = torch.zeros(awq.gemm_workspace_size(16, 8192, 7168, 128), dtype=torch.uint8, device=DEV)
     for (M, K, N) in [(16, 8192, 7168), (1, 8192, 1280), (4, 4096, 2048), (16, 8192, 7168)]:
@@ -323,7 +324,7 @@ def test_workspace_reuse_across_shapes():
         y = awq.gemm(d["x"], d["qweight"], d["qzeros"], d["scales"], None, 128, workspace=ws)
         ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], None, 128)
         assert_within_tol(y.cpu().numpy(), ref, f"reuse M={M} K={K} N={N}")
-    assert torch.count_nonzero(ws[:256]).item() == 0
+    assert torch.count_nonzero(ws[:65536]).item() == 0   # every ticket slot back at zero
 
 
 def test_wqlinear_module_forward():
