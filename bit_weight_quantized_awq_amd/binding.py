@@ -34,7 +34,7 @@ SIGNATURES = {
     "awq_abi_version": (ctypes.c_int, []),
     "awq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "awq_gemm_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64, _i64]),
-    "awq_gemm_plan": (ctypes.c_int, [_i64, _i64, _i64, _i64, _vp, _vp,
+    "awq_gemm_plan": (ctypes.c_int, [_i64, _i64, _i64, _i64, _vp, _vp, _vp,
                                      ctypes.POINTER(ctypes.c_int),
                                      ctypes.POINTER(ctypes.c_size_t)]),
     "awq_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
@@ -84,13 +84,13 @@ def gemm_workspace_size(M: int, K: int, N: int, group_size: int) -> int:
 
 
 def gemm_plan(M: int, K: int, N: int, group_size: int, x_ptr: int = 0,
-              scales_ptr: int = 0) -> tuple[int, int]:
+              scales_ptr: int = 0, qweight_ptr: int = 0) -> tuple[int, int]:
     """(path, workspace bytes) that awq_gemm would use; pointers are only
     inspected for alignment (0 counts as aligned)."""
     path = ctypes.c_int(0)
     ws = ctypes.c_size_t(0)
-    st = lib().awq_gemm_plan(M, K, N, group_size, x_ptr or None, scales_ptr or None,
-                             ctypes.byref(path), ctypes.byref(ws))
+    st = lib().awq_gemm_plan(M, K, N, group_size, x_ptr or None, qweight_ptr or None,
+                             scales_ptr or None, ctypes.byref(path), ctypes.byref(ws))
     if st != AWQ_SUCCESS:
         raise AwqError(st, "awq_gemm_plan")
     return path.value, ws.value
@@ -181,7 +181,8 @@ def gemm(x, qweight, qzeros, scales, bias=None, group_size: int = 128, out=None,
             raise ValueError("out must be a contiguous float16 (M, N) tensor")
     stream = torch.cuda.current_stream(device).cuda_stream
     if M > 0:
-        _, need = gemm_plan(M, K, N, group_size, x2.data_ptr(), scales.data_ptr())
+        _, need = gemm_plan(M, K, N, group_size, x2.data_ptr(), scales.data_ptr(),
+                            qweight.data_ptr())
     else:
         need = 0
     if workspace is None:

@@ -31,21 +31,25 @@ const char* awq_status_string(int status) {
 size_t awq_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size) {
   Problem p;
   if (awq::validate_shape(M, K, N, group_size, &p) != AWQ_SUCCESS) return 0;
-  if (!awq::decode_supported(p, true, true)) return 0;
+  const awq::Alignment al{true, true, true};
+  if (!awq::decode_supported(p, al)) return 0;
   Plan pl;
-  if (awq::make_plan(p, true, true, AWQ_PATH_DECODE, &pl) != AWQ_SUCCESS) return 0;
+  if (awq::make_plan(p, al, AWQ_PATH_DECODE, &pl) != AWQ_SUCCESS) return 0;
   return pl.ws_bytes;
 }
 
 int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size, const void* x,
-                  const void* scales, int* path, size_t* workspace_bytes) {
+                  const void* qweight, const void* scales, int* path,
+                  size_t* workspace_bytes) {
   Problem p;
   int st = awq::validate_shape(M, K, N, group_size, &p);
   if (st != AWQ_SUCCESS) return st;
   const int force = awq::force_path_from_env();
   if (force < 0) return AWQ_ERROR_INVALID_VALUE;
   Plan pl;
-  st = awq::make_plan(p, awq::aligned(x, 16), awq::aligned(scales, 16), force, &pl);
+  const awq::Alignment al{awq::aligned(x, 16), awq::aligned(scales, 16),
+                          awq::aligned(qweight, 16)};
+  st = awq::make_plan(p, al, force, &pl);
   if (st != AWQ_SUCCESS) return st;
   if (path) *path = pl.path;
   if (workspace_bytes) *workspace_bytes = pl.ws_bytes;
@@ -64,7 +68,9 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void*
   const int force = awq::force_path_from_env();
   if (force < 0) return AWQ_ERROR_INVALID_VALUE;
   Plan pl;
-  st = awq::make_plan(p, awq::aligned(x, 16), awq::aligned(scales, 16), force, &pl);
+  const awq::Alignment al{awq::aligned(x, 16), awq::aligned(scales, 16),
+                          awq::aligned(qweight, 16)};
+  st = awq::make_plan(p, al, force, &pl);
   if (st != AWQ_SUCCESS) return st;
   if (pl.ws_bytes > 0) {
     if (!workspace || workspace_bytes < pl.ws_bytes) return AWQ_ERROR_WORKSPACE;
@@ -85,7 +91,7 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void*
   switch (pl.path) {
     case AWQ_PATH_DECODE:
       e = awq::launch_decode(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, iG, pl.steps, pl.splits,
-                             pl.n_tiles, workspace, pl.ticket_stride, s);
+                             pl.n_tiles, pl.decode_lds, workspace, pl.ticket_stride, s);
       break;
     case AWQ_PATH_PREFILL:
       e = awq::launch_prefill(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, pl.m_tiles, pl.n_tiles, s);

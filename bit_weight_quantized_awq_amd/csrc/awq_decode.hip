@@ -227,6 +227,306 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   if (tid == 0) __hip_atomic_store(tickets + n_tile * ticket_words, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------------------
+// Streaming variant for N % 32 == 0 (rows are 16-byte aligned).  Each wave
+// copies its rows straight from HBM into a private LDS region with 16-byte
+// buffer loads (8 lanes cover one 128-byte row segment, one instruction moves
+// 8 rows), then every lane reads back, per 32-row step, the 8 rows of its
+// word column -- the transposition the MFMA operand layout needs -- without
+// the packed words ever occupying registers in flight.
+//
+// Work-group: 4 waves over the same 256 columns (two MFMA column sets of 16
+// words per wave) and consecutive 32*STEPS-row ranges; the four K-ranges
+// meet in LDS, the work-groups of a column tile meet through the split-K
+// exchange.  The 8-row blocks sit 1088 bytes apart in LDS so that the 64
+// lanes of a transposed read (16 word columns x 4 row blocks) hit 64 distinct
+// banks.
+constexpr int kLdsBlockPitch = 1088;  // 8 rows x 128 bytes + 64-byte skew
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int STEPS, bool SINGLE_GROUP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void
+decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
+                  const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
+                  const _Float16* __restrict__ bias, _Float16* __restrict__ y,
+                  float* __restrict__ partial, uint32_t* __restrict__ tickets,
+                  int M, int K, int N, int g, int G, int splits, int ticket_words) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_last;
+  constexpr int kWaveBytes = STEPS * 4 * kLdsBlockPitch;
+
+  const int NW = N >> 3;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_tile = blockIdx.x / splits;
+  const int split = blockIdx.x - n_tile * splits;
+  const int col16 = lane & 15;  // MFMA column (B) / row (A) of this lane
+  const int kb = lane >> 4;     // 8-row block within a 32-row step
+  const int c0 = n_tile * 32;   // first word column of the tile
+  const int kw0 = split * (128 * STEPS) + wave * (32 * STEPS);
+
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qw, static_cast<uint32_t>(K) * NW * 4u);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(qz, static_cast<uint32_t>(G) * NW * 4u);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(sc, static_cast<uint32_t>(G) * N * 2u);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, static_cast<uint32_t>(M) * K * 2u);
+
+  // Group parameters for the lane's two word columns c0 + col16 and
+  // c0 + 16 + col16 (one group, or one per step).
+  constexpr int NG = SINGLE_GROUP ? 1 : STEPS;
+  uint32_t zw[NG][2];
+  half8_t sv[NG][2];
+#pragma unroll
+  for (int s = 0; s < NG; ++s) {
+    const int k0 = kw0 + 32 * s;
+    const int grp = (G == 1) ? 0 : k0 / g;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = c0 + 16 * h + col16;
+      const bool ok = c < NW && k0 < K;
+      zw[s][h] = buf_load_u32(rz, offset_or_oob(ok, static_cast<uint32_t>(grp * NW + c) * 4u));
+      sv[s][h] = __builtin_bit_cast(
+          half8_t, buf_load_u32x4(rs, offset_or_oob(ok, static_cast<uint32_t>(grp * N + 8 * c) * 2u)));
+    }
+  }
+  half8_t xa[STEPS];
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    const int kr = kw0 + 32 * s + 8 * kb;
+    const uint32_t xoff =
+        offset_or_oob(col16 < M && kr < K, static_cast<uint32_t>(col16 * K + kr) * 2u);
+    xa[s] = __builtin_bit_cast(half8_t, buf_load_u32x4(rx, xoff));
+  }
+  // Nothing may be scheduled between here and the waits below except the
+  // LDS copies: the waits count outstanding copies.
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Packed words: HBM -> LDS, 4 instructions (4 x 8 rows) per step, issued
+  // last so that waiting for step s leaves later steps in flight.
+  char* wlds = smem + wave * kWaveBytes;
+  {
+    const int lrow = lane >> 3;   // row within an 8-row block
+    const int lword = c0 + 4 * (lane & 7);
+    const uint32_t row_bytes = static_cast<uint32_t>(NW) * 4u;
+    const bool cok = lword < NW;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int row = kw0 + 32 * s + 8 * b + lrow;
+        const uint32_t off = offset_or_oob(
+            cok, static_cast<uint32_t>(row) * row_bytes + static_cast<uint32_t>(lword) * 4u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rq, (__attribute__((address_space(3))) void*)(wlds + (4 * s + b) * kLdsBlockPitch),
+            16, off, 0, 0, 0);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Byte-pair contraction.  For byte b of a word (nibbles 2b and 2b+1,
+  // columns 8c+2b and 8c+2b+1), one byte shuffle per row pair places that
+  // byte of both rows, zero-extended, in the two halves of a register; OR-ing
+  // into float16 1024.0 gives the exact 1024 + (q_even + 16*q_odd), masking
+  // the high nibble first gives 1024 + q_even.  Subtracting the group's
+  // 1024 + (z_even + 16*z_odd) and 1024 + z_even (exact small integers) feeds
+  //   acc_f[b] = sum_k x*((q_e - z_e) + 16*(q_o - z_o)),  acc_e[b] = sum_k x*(q_e - z_e)
+  // to the matrix cores; the odd column is (acc_f - acc_e) / 16.  Five VALU
+  // ops per four weights; q == z and one-hot rows stay exact.
+  floatx4 acc_e[2][4], acc_f[2][4];
+  floatx4 tot[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc_e[h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+      acc_f[h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tot[h][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // (1024 + zero byte, 1024 + low zero nibble) pairs of byte b of zero word zw.
+  auto zero_pairs = [](uint32_t zw, int b, half2_t& zf, half2_t& ze) {
+    const uint32_t dup = __builtin_amdgcn_perm(zw, zw, 0x0C000C00u | ((4u + b) << 16) | b);
+    zf = as_h2(dup | kMagicPair);
+    ze = as_h2(and_or(dup, kNibblePairMask, kMagicPair));
+  };
+  // Scale the group partials of set h and add them to the totals.
+  auto fold = [&](int h, half8_t svh) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float se = static_cast<float>(svh[2 * q]);
+      const float so = static_cast<float>(svh[2 * q + 1]) * 0.0625f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        tot[h][2 * q][i] += se * acc_e[h][q][i];
+        tot[h][2 * q + 1][i] += so * (acc_f[h][q][i] - acc_e[h][q][i]);
+      }
+    }
+  };
+
+  half2_t zf[NG][2][4], ze[NG][2][4];
+#pragma unroll
+  for (int s = 0; s < NG; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) zero_pairs(zw[s][h], q, zf[s][h][q], ze[s][h][q]);
+
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    // Step s's four LDS copies are done once at most 4*(STEPS-1-s) loads
+    // (the later steps' copies) are outstanding.
+    switch (STEPS - 1 - s) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<4>(); break;
+      case 2: wait_vmcnt<8>(); break;
+      case 3: wait_vmcnt<12>(); break;
+      default: wait_vmcnt<0>(); break;
+    }
+    const int gi = SINGLE_GROUP ? 0 : s;
+    const char* blk = wlds + (4 * s + kb) * kLdsBlockPitch;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        w[r] = *reinterpret_cast<const uint32_t*>(blk + r * 128 + (16 * h + col16) * 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // [row 2p byte q, 0, row 2p+1 byte q, 0] for the four row pairs.
+        const uint32_t sel = 0x0C000C00u | ((4u + q) << 16) | q;
+        half8_t bf, be;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t pb = __builtin_amdgcn_perm(w[2 * p + 1], w[2 * p], sel);
+          const half2_t f = as_h2(pb | kMagicPair) - zf[gi][h][q];
+          const half2_t e = as_h2(and_or(pb, kNibblePairMask, kMagicPair)) - ze[gi][h][q];
+          bf[2 * p] = f[0];
+          bf[2 * p + 1] = f[1];
+          be[2 * p] = e[0];
+          be[2 * p + 1] = e[1];
+        }
+        acc_e[h][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], be, acc_e[h][q], 0, 0, 0);
+        acc_f[h][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], bf, acc_f[h][q], 0, 0, 0);
+      }
+      if (!SINGLE_GROUP) {
+        fold(h, sv[s][h]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc_e[h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+          acc_f[h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+  }
+  if (SINGLE_GROUP) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) fold(h, sv[0][h]);
+  }
+
+  // The four K-ranges meet in LDS (the copy regions are free once every wave
+  // is past its last step).  tot[h][j][i] is row 4*kb + i, local column
+  // 8*(16h + col16) + j.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int lcol = 8 * (16 * h + col16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * kb + i;
+        if (m < M) red[(wave * M + m) * kDecodeCols + lcol + j] = tot[h][j][i];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int n = n_tile * kDecodeCols + tid;
+  const bool nvalid = n < N;
+  auto wg_sum = [&](int m) {
+    float v = red[m * kDecodeCols + tid];
+    v += red[(M + m) * kDecodeCols + tid];
+    v += red[(2 * M + m) * kDecodeCols + tid];
+    v += red[(3 * M + m) * kDecodeCols + tid];
+    return v;
+  };
+  if (splits == 1) {
+    if (nvalid) {
+      const float b = bias ? static_cast<float>(bias[n]) : 0.f;
+      for (int m = 0; m < M; ++m) y[m * N + n] = static_cast<_Float16>(wg_sum(m) + b);
+    }
+    return;
+  }
+  // Split-K exchange (see the register variant above for the protocol).
+  if (nvalid) {
+    for (int m = 0; m < M; ++m)
+      __hip_atomic_store(partial + (split * M + m) * N + n, wg_sum(m), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = (__hip_atomic_fetch_add(tickets + n_tile * ticket_words, 1u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) ==
+              static_cast<unsigned>(splits - 1));
+  __syncthreads();
+  if (!s_last) return;
+  if (nvalid) {
+    const float b = bias ? static_cast<float>(bias[n]) : 0.f;
+    const int stride = M * N;
+    for (int m = 0; m < M; ++m) {
+      const float* p = partial + m * N + n;
+      float sum = 0.f;
+      int sp = 0;
+      for (; sp + 16 <= splits; sp += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          v[u] = __hip_atomic_load(p + (sp + u) * stride, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) sum += v[u];
+      }
+      for (; sp < splits; ++sp)
+        sum += __hip_atomic_load(p + sp * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      y[m * N + n] = static_cast<_Float16>(sum + b);
+    }
+  }
+  if (tid == 0)
+    __hip_atomic_store(tickets + n_tile * ticket_words, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int STEPS>
+hipError_t launch_lds_steps(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
+                            const _Float16* scales, const _Float16* bias, _Float16* y,
+                            int M, int K, int N, int g, int G, int splits, int n_tiles,
+                            float* partial, uint32_t* tickets, int ticket_words,
+                            hipStream_t stream) {
+  const size_t copy_bytes = 4 * STEPS * 4 * kLdsBlockPitch;
+  const size_t red_bytes = 4 * static_cast<size_t>(M) * kDecodeCols * sizeof(float);
+  const size_t shmem = copy_bytes > red_bytes ? copy_bytes : red_bytes;
+  const bool single = (G == 1) || (g % (kDecodeRowsPerStep * STEPS) == 0);
+  if (single)
+    hipLaunchKernelGGL((decode_lds_kernel<STEPS, true>), dim3(n_tiles * splits), dim3(256),
+                       shmem, stream, x, qweight, qzeros, scales, bias, y, partial, tickets, M,
+                       K, N, g, G, splits, ticket_words);
+  else
+    hipLaunchKernelGGL((decode_lds_kernel<STEPS, false>), dim3(n_tiles * splits), dim3(256),
+                       shmem, stream, x, qweight, qzeros, scales, bias, y, partial, tickets, M,
+                       K, N, g, G, splits, ticket_words);
+  return hipGetLastError();
+}
+
 template <int STEPS>
 hipError_t launch_steps(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                         const _Float16* scales, const _Float16* bias, _Float16* y,
@@ -253,13 +553,24 @@ hipError_t launch_steps(const _Float16* x, const uint32_t* qweight, const uint32
 hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                          const _Float16* scales, const _Float16* bias, _Float16* y,
                          int M, int K, int N, int g, int G, int steps, int splits,
-                         int n_tiles, void* workspace, int ticket_stride,
+                         int n_tiles, bool lds_variant, void* workspace, int ticket_stride,
                          hipStream_t stream) {
   uint32_t* tickets = static_cast<uint32_t*>(workspace);
   float* partial = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                         kTicketRegionBytes)
                              : nullptr;
   const int tw = ticket_stride / 4;
+  if (lds_variant) {
+    switch (steps) {
+      case 1: return launch_lds_steps<1>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G,
+                                         splits, n_tiles, partial, tickets, tw, stream);
+      case 2: return launch_lds_steps<2>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G,
+                                         splits, n_tiles, partial, tickets, tw, stream);
+      case 4: return launch_lds_steps<4>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G,
+                                         splits, n_tiles, partial, tickets, tw, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (steps) {
     case 1: return launch_steps<1>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G, splits,
                                    n_tiles, partial, tickets, tw, stream);

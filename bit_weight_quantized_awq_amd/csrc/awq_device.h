@@ -54,6 +54,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                           0x00020000);
 }
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Branch-free "offset if valid, else out of range": valid offsets are below
+// 2^31 (operands stay under 1 GiB), so setting bit 31 moves an invalid lane
+// past the end of every buffer.  A select written as a ternary may be turned
+// into divergent branches, each issuing its own load; this cannot.
+__device__ __forceinline__ uint32_t offset_or_oob(bool valid, uint32_t off) {
+  return off | (static_cast<uint32_t>(!valid) << 31);
+}
 __device__ __forceinline__ uint32_t buf_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
@@ -85,7 +93,7 @@ hipError_t launch_generic(const _Float16* x, const uint32_t* qweight, const uint
 hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                          const _Float16* scales, const _Float16* bias, _Float16* y,
                          int M, int K, int N, int g, int G, int steps, int splits,
-                         int n_tiles, void* workspace, int ticket_stride,
+                         int n_tiles, bool lds_variant, void* workspace, int ticket_stride,
                          hipStream_t stream);
 hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                           const _Float16* scales, const _Float16* bias, _Float16* y,

@@ -14,6 +14,7 @@ constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;
 // CUs to keep many weight loads in flight, without multiplying the split-K
 // partial sums more than needed.
 constexpr int64_t kDecodeTargetWGs = 800;
+constexpr int64_t kDecodeLdsTargetWGs = 384;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
@@ -65,18 +66,19 @@ static bool fits_32bit_offsets(const Problem& p) {
   return p.M * p.K <= lim && p.M * p.N <= lim && p.K * p.N / 4 <= lim;
 }
 
-bool decode_supported(const Problem& p, bool x_al16, bool scales_al16) {
+bool decode_supported(const Problem& p, const Alignment& al) {
   // 16-byte x loads need K % 8 == 0; a group must not change inside a wave's
-  // 32-row step; every column tile needs a 4-byte ticket slot.
+  // 32-row step; every column tile needs a 4-byte ticket slot; the
+  // LDS-streaming variant (N % 32 == 0) copies 16-byte row segments.
   const int64_t n_tiles = (p.N + kDecodeCols - 1) / kDecodeCols;
   return fits_32bit_offsets(p) && n_tiles * 4 <= static_cast<int64_t>(kTicketRegionBytes) &&
-         p.M <= kDecodeMaxM && p.K % 8 == 0 && x_al16 && scales_al16 &&
-         (p.g % kDecodeRowsPerStep == 0 || p.G == 1);
+         p.M <= kDecodeMaxM && p.K % 8 == 0 && al.x && al.scales &&
+         (p.N % 32 != 0 || al.qweight) && (p.g % kDecodeRowsPerStep == 0 || p.G == 1);
 }
 
-bool prefill_supported(const Problem& p, bool x_al16, bool scales_al16) {
+bool prefill_supported(const Problem& p, const Alignment& al) {
   // Dequantisation works on 4-row blocks that must share a group.
-  return fits_32bit_offsets(p) && p.K % 8 == 0 && x_al16 && scales_al16 && p.g % 4 == 0;
+  return fits_32bit_offsets(p) && p.K % 8 == 0 && al.x && al.scales && p.g % 4 == 0;
 }
 
 static int decode_steps_override() {
@@ -86,11 +88,11 @@ static int decode_steps_override() {
   return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 0;
 }
 
-int make_plan(const Problem& p, bool x_al16, bool scales_al16, int force, Plan* out) {
+int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
   Plan pl;
   memset(&pl, 0, sizeof(pl));
-  const bool dec = decode_supported(p, x_al16, scales_al16);
-  const bool pre = prefill_supported(p, x_al16, scales_al16);
+  const bool dec = decode_supported(p, al);
+  const bool pre = prefill_supported(p, al);
   int path;
   if (force == 0) {
     path = dec ? AWQ_PATH_DECODE : (pre ? AWQ_PATH_PREFILL : AWQ_PATH_GENERIC);
@@ -104,21 +106,27 @@ int make_plan(const Problem& p, bool x_al16, bool scales_al16, int force, Plan* 
   pl.path = path;
   if (path == AWQ_PATH_DECODE) {
     pl.n_tiles = static_cast<int>(ceil_div(p.N, kDecodeCols));
+    pl.decode_lds = (p.N % 32 == 0);
+    // Rows per work-group: 4 waves (LDS variant) or 2 waves (register
+    // variant) along K, 32 rows per step each.
+    const int waves_k = pl.decode_lds ? 4 : 2;
     int steps = decode_steps_override();
+    if (steps == 8 && pl.decode_lds) steps = 4;
     if (steps == 0) {
-      // At most 4 steps (32 outstanding word loads per lane plus x, zeros and
-      // scales stay under the 63 outstanding vector loads a wave can track);
-      // prefer step counts whose rows stay in one quantisation group, and the
-      // largest that still gives enough work-groups.
+      // At most 4 steps (the register variant keeps 32 word loads per lane
+      // in flight, under the 63 outstanding vector loads a wave can track);
+      // prefer step counts whose rows stay in one quantisation group, and
+      // the largest that still gives enough work-groups.
+      const int64_t target = pl.decode_lds ? kDecodeLdsTargetWGs : kDecodeTargetWGs;
       steps = 1;
       for (int s = 4; s >= 1; s /= 2) {
         const bool single = p.G == 1 || p.g % (kDecodeRowsPerStep * s) == 0;
-        const int64_t splits = ceil_div(p.K, 2 * kDecodeRowsPerStep * s);
-        if (single && pl.n_tiles * splits >= kDecodeTargetWGs) { steps = s; break; }
+        const int64_t splits = ceil_div(p.K, waves_k * kDecodeRowsPerStep * s);
+        if (single && pl.n_tiles * splits >= target) { steps = s; break; }
       }
     }
     pl.steps = steps;
-    pl.splits = static_cast<int>(ceil_div(p.K, 2 * kDecodeRowsPerStep * steps));
+    pl.splits = static_cast<int>(ceil_div(p.K, waves_k * kDecodeRowsPerStep * steps));
     int stride = static_cast<int>(kTicketRegionBytes / pl.n_tiles) & ~3;
     pl.ticket_stride = stride < kTicketMaxStrideBytes ? stride : kTicketMaxStrideBytes;
     if (pl.splits > 1) {

@@ -40,6 +40,7 @@ struct Plan {
   int m_tiles;       // prefill: row tiles
   size_t ws_bytes;   // workspace bytes
   int ticket_stride;  // decode: bytes between two tiles' tickets
+  bool decode_lds;    // decode: LDS-streaming variant (N % 32 == 0) or register variant
 };
 
 // Checks of the page's WQLinear construction (K % g == 0, N % 8 == 0, the -1
@@ -52,11 +53,16 @@ int validate_gemm_pointers(const void* x, const void* qweight, const void* qzero
 int validate_dequant_pointers(const void* qweight, const void* qzeros,
                               const void* scales, const void* w);
 
-bool decode_supported(const Problem& p, bool x_al16, bool scales_al16);
-bool prefill_supported(const Problem& p, bool x_al16, bool scales_al16);
+// Alignment flags: whether x, scales and qweight start on a 16-byte boundary.
+struct Alignment {
+  bool x, scales, qweight;
+};
+
+bool decode_supported(const Problem& p, const Alignment& al);
+bool prefill_supported(const Problem& p, const Alignment& al);
 
 // force: 0 = automatic, otherwise an awq_path value.  Returns an awq_status.
-int make_plan(const Problem& p, bool x_al16, bool scales_al16, int force, Plan* out);
+int make_plan(const Problem& p, const Alignment& al, int force, Plan* out);
 
 // Parses AWQ_FORCE_PATH.  Returns 0 (unset/automatic), an awq_path value, or
 // -1 for an unrecognised value.

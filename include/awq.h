@@ -35,8 +35,9 @@
  *     return nothing was enqueued and no output was written, except
  *     AWQ_ERROR_HIP, which reports a failed launch.
  *   - Element alignment is required (2 bytes for float16 pointers, 4 bytes for
- *     int32 pointers).  Faster kernels are chosen when x and scales are 16-byte
- *     aligned and K % 8 == 0; other legal inputs take a general kernel.
+ *     int32 pointers).  Faster kernels are chosen when x, scales and qweight
+ *     are 16-byte aligned and K % 8 == 0; other legal inputs take a general
+ *     kernel.
  *   - Every operand must hold fewer than 2^31 elements (M*K, M*N, K*N).
  */
 #ifndef AWQ_MI355X_AWQ_H_
@@ -81,14 +82,15 @@ const char* awq_status_string(int status);
  * Returns 0 for invalid shapes (awq_gemm then reports the error). */
 size_t awq_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size);
 
-/* Host-only planning, no HIP call and no dereference of x or scales (only
- * their addresses' alignment is inspected).  Writes the kernel family awq_gemm
- * would run to *path and its workspace need to *workspace_bytes (either may be
- * NULL).  The environment variable AWQ_FORCE_PATH = decode | prefill | generic
- * overrides the choice for testing; a forced family that cannot run the
- * problem yields AWQ_ERROR_INVALID_VALUE. */
+/* Host-only planning, no HIP call and no dereference of x, qweight or scales
+ * (only their addresses' alignment is inspected; NULL counts as aligned).
+ * Writes the kernel family awq_gemm would run to *path and its workspace need
+ * to *workspace_bytes (either may be NULL).  The environment variable
+ * AWQ_FORCE_PATH = decode | prefill | generic overrides the choice for
+ * testing; a forced family that cannot run the problem yields
+ * AWQ_ERROR_INVALID_VALUE. */
 int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size,
-                  const void* x, const void* scales, int* path,
+                  const void* x, const void* qweight, const void* scales, int* path,
                   size_t* workspace_bytes);
 
 /* The WQLinear forward (page "Predibase Lorax AWQ WQLinear", Description,

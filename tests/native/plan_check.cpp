@@ -55,9 +55,10 @@ int main() {
         for (int64_t g : gs) {
           if (validate_shape(M, K, N, g, &p) != AWQ_SUCCESS) continue;
           for (int force = 0; force <= 3; ++force) {
-            for (int al = 0; al < 4; ++al) {
+            for (int al = 0; al < 8; ++al) {
               Plan pl;
-              const int st = make_plan(p, al & 1, al & 2, force, &pl);
+              const Alignment a{(al & 1) != 0, (al & 2) != 0, (al & 4) != 0};
+              const int st = make_plan(p, a, force, &pl);
               if (st != AWQ_SUCCESS) {
                 EXPECT(force != 0 && force != AWQ_PATH_GENERIC);
                 continue;
@@ -65,7 +66,11 @@ int main() {
               if (pl.path == AWQ_PATH_DECODE) {
                 EXPECT(M <= kDecodeMaxM);
                 EXPECT(pl.splits >= 1 && pl.n_tiles * kDecodeCols >= N);
-                EXPECT((int64_t)pl.splits * 2 * kDecodeRowsPerStep * pl.steps >= K);
+                EXPECT(pl.decode_lds == (N % 32 == 0));
+                EXPECT(!pl.decode_lds || a.qweight);
+                const int waves_k = pl.decode_lds ? 4 : 2;
+                EXPECT((int64_t)pl.splits * waves_k * kDecodeRowsPerStep * pl.steps >= K);
+                EXPECT((int64_t)(pl.splits - 1) * waves_k * kDecodeRowsPerStep * pl.steps < K);
                 EXPECT(pl.ticket_stride >= 4 && pl.ticket_stride % 4 == 0);
                 EXPECT((size_t)pl.ticket_stride * pl.n_tiles <= kTicketRegionBytes);
                 if (pl.splits > 1)

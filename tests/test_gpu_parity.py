@@ -210,8 +210,11 @@ def test_one_hot_rows_exact(name, Mmax, g, M):
 
 
 @pytest.mark.parametrize("M,K,N,g", [(1, 8192, 1280, 128), (16, 4096, 1024, 64),
-                                     (300, 1024, 640, 128), (64, 512, 256, -1)])
+                                     (5, 512, 40, 32), (300, 1024, 640, 128),
+                                     (64, 512, 256, -1)])
 def test_q_equal_z_gives_bias_exactly(M, K, N, g):
+    """q == z everywhere: every kernel subtracts z per weight in exact float16
+    integer arithmetic, so y is exactly the bias (exactly 0 without one)."""
     say(f"q==z M={M} K={K} N={N} g={g}")
     p = awq_inputs.make_inputs(M, K, N, g, seed=M + K, bias=True, scale_lo=-1, scale_hi=1)
     gg = K if g == -1 else g
