@@ -97,6 +97,6 @@ hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint3
                          hipStream_t stream);
 hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                           const _Float16* scales, const _Float16* bias, _Float16* y,
-                          int M, int K, int N, int g, int m_tiles, int n_tiles,
+                          int M, int K, int N, int group_shift, int m_tiles, int n_tiles,
                           hipStream_t stream);
 }  // namespace awq

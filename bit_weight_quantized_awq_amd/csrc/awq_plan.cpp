@@ -76,9 +76,18 @@ bool decode_supported(const Problem& p, const Alignment& al) {
          (p.N % 32 != 0 || al.qweight) && (p.g % kDecodeRowsPerStep == 0 || p.G == 1);
 }
 
+static int log2_exact(int64_t v) {
+  int s = 0;
+  while ((int64_t{1} << s) < v) ++s;
+  return (int64_t{1} << s) == v ? s : -1;
+}
+
 bool prefill_supported(const Problem& p, const Alignment& al) {
-  // Dequantisation works on 4-row blocks that must share a group.
-  return fits_32bit_offsets(p) && p.K % 8 == 0 && al.x && al.scales && p.g % 4 == 0;
+  // Dequantisation works on 4-row blocks that must share a group, and the
+  // kernel finds a row's group with a shift: a power-of-two group size of at
+  // least 4, or a single group.
+  return fits_32bit_offsets(p) && p.K % 8 == 0 && al.x && al.scales &&
+         (p.G == 1 || (p.g >= 4 && log2_exact(p.g) >= 0));
 }
 
 static int decode_steps_override() {
@@ -136,6 +145,7 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
   } else if (path == AWQ_PATH_PREFILL) {
     pl.m_tiles = static_cast<int>(ceil_div(p.M, kPrefillBM));
     pl.n_tiles = static_cast<int>(ceil_div(p.N, kPrefillBN));
+    pl.group_shift = p.G == 1 ? 31 : log2_exact(p.g);
   }
   *out = pl;
   return AWQ_SUCCESS;

@@ -41,6 +41,7 @@ struct Plan {
   size_t ws_bytes;   // workspace bytes
   int ticket_stride;  // decode: bytes between two tiles' tickets
   bool decode_lds;    // decode: LDS-streaming variant (N % 32 == 0) or register variant
+  int group_shift;    // prefill: log2(group size), or 31 for a single group
 };
 
 // Checks of the page's WQLinear construction (K % g == 0, N % 8 == 0, the -1

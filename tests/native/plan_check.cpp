@@ -48,7 +48,7 @@ int main() {
   const int64_t Ms[] = {0, 1, 2, 15, 16, 17, 255, 256, 4096};
   const int64_t Ks[] = {8, 32, 40, 96, 256, 4096, 8192, 14336};
   const int64_t Ns[] = {8, 24, 128, 1280, 7168, 12288};
-  const int64_t gs[] = {-1, 1, 4, 8, 32, 64, 128};
+  const int64_t gs[] = {-1, 1, 4, 8, 12, 32, 64, 96, 128};
   for (int64_t M : Ms)
     for (int64_t K : Ks)
       for (int64_t N : Ns)
@@ -81,6 +81,7 @@ int main() {
                 EXPECT((int64_t)pl.m_tiles * kPrefillBM >= M);
                 EXPECT((int64_t)pl.n_tiles * kPrefillBN >= N);
                 EXPECT(pl.ws_bytes == 0);
+                EXPECT(p.G == 1 ? pl.group_shift == 31 : (int64_t{1} << pl.group_shift) == p.g);
               }
             }
           }

@@ -251,6 +251,10 @@ def test_group_minus_one_bit_identical_to_K(M):
     ("prefill", 255, 72, 24, 4, False),
     ("prefill", 257, 520, 392, 8, True),
     ("prefill", 31, 40, 40, -1, True),
+    ("prefill", 300, 96, 200, 32, True),
+    ("prefill", 513, 208, 264, 16, True),
+    ("prefill", 64, 192, 128, 64, False),
+    ("prefill", 2, 8, 8, -1, True),
     ("generic", 4, 256, 128, 64, True),
     ("generic", 33, 96, 24, 3, True),
     ("generic", 2, 100, 40, -1, False),

@@ -126,6 +126,8 @@ def test_dequant_validation(kwargs, status):
     (4, 96, 64, 3, binding.AWQ_PATH_GENERIC),        # group size not a multiple of 4
     (4, 100, 64, -1, binding.AWQ_PATH_GENERIC),      # K % 8 != 0
     (4, 256, 64, 16, binding.AWQ_PATH_PREFILL),      # small groups: not decode
+    (64, 384, 64, 96, binding.AWQ_PATH_GENERIC),     # group size not a power of two
+    (64, 96, 64, -1, binding.AWQ_PATH_PREFILL),      # one group of any size
 ])
 def test_plan_selects_kernel(M, K, N, g, path):
     got, ws = awq.gemm_plan(M, K, N, g)
