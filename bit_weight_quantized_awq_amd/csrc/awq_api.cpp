@@ -91,7 +91,7 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void*
   switch (pl.path) {
     case AWQ_PATH_DECODE:
       e = awq::launch_decode(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, iG, pl.steps, pl.splits,
-                             pl.n_tiles, pl.decode_lds, workspace, pl.ticket_stride, s);
+                             pl.n_tiles, pl.decode_lds, workspace, s);
       break;
     case AWQ_PATH_PREFILL:
       e = awq::launch_prefill(xh, qw, qz, sc, bh, yh, iM, iK, iN, pl.group_shift, pl.m_tiles,

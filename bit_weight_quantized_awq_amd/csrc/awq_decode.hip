@@ -28,18 +28,99 @@
 //   differs from rounding each dequantised weight to float16 only by that
 //   rounding (relative 2^-11 per term).  A one-hot row still reproduces the
 //   float16 dequantised weight exactly.
-// * Reduction: the two K-halves of a work-group meet in LDS; work-groups write
-//   fp32 partials to the workspace, take a ticket on their column tile, and
-//   the last one sums the partials in split order (deterministic), adds the
-//   bias, rounds to float16 and resets the ticket.  Tickets sit up to 256
-//   bytes apart in a fixed region at the start of the workspace:
-//   device-scope atomics on one cache line are serialised, which costs
-//   ~0.2 us per arrival when every tile shares a line.
+// * Reduction: the K-ranges of a work-group meet in LDS; the work-groups of a
+//   column tile then meet in one 64-bit device-scope atomic per output
+//   element (see splitk_finish): each adds its partial as a 2^-24 fixed-point
+//   integer together with a contribution count, and the one whose returned
+//   sum shows every split has arrived writes y.  Integer addition makes the
+//   sum exact and independent of arrival order (deterministic), and the
+//   exchange costs one atomic round trip instead of store, acknowledge,
+//   ticket and reload.
 #include "awq_device.h"
 #include "awq_plan.h"
 
 namespace awq {
 namespace {
+
+// Split-K exchange state in the workspace (all of it zero between calls).
+struct SplitK {
+  unsigned long long* acc;   // [M][N]: fixed-point sum, contribution count
+  uint32_t* mask;            // [M][N]: splits that sent a float partial
+  float* partial;            // [splits][M][N]: those float partials
+};
+// acc layout: bits 0-52 sum of (v + 2^47) over fixed-point contributions,
+// v = rint(p * 2^24) with |p| < 2^23 (so each term is below 2^48 and up to
+// 31 of them stay below 2^53); bits 53-57 number of contributions; bits
+// 58-62 number of float contributions.  A partial outside the fixed-point
+// range (huge, infinite or NaN) is published as a float and flagged instead.
+constexpr unsigned long long kFxUnit = 1ull << 53;
+constexpr unsigned long long kFxFloat = 1ull << 58;
+constexpr long long kFxBias = 1ll << 47;
+constexpr float kFxScale = 16777216.0f;   // 2^24
+constexpr float kFxLimit = 8388608.0f;    // 2^23
+
+// Called by the thread that owns column n of this work-group, with wg_sum(m)
+// the work-group's partial for row m.  All atomics of the thread are issued
+// before any result is used.  Partials are exact multiples of 2^-24 whenever
+// the scales are (every float16 is), so a one-hot row stays exact.
+template <class F>
+__device__ __forceinline__ void splitk_finish(const F& wg_sum, const SplitK& sk,
+                                              const _Float16* __restrict__ bias,
+                                              _Float16* __restrict__ y, int M, int N, int n,
+                                              int split, int splits) {
+  unsigned long long add[kDecodeMaxM], old[kDecodeMaxM];
+  bool published = false;
+#pragma unroll
+  for (int m = 0; m < kDecodeMaxM; ++m) {
+    if (m < M) {
+      const float p = wg_sum(m);
+      if (fabsf(p) < kFxLimit) {   // false for NaN
+        const long long v = static_cast<long long>(__builtin_rintf(p * kFxScale));
+        add[m] = static_cast<unsigned long long>(v + kFxBias) + kFxUnit;
+      } else {
+        const size_t e = static_cast<size_t>(m) * N + n;
+        __hip_atomic_store(sk.partial + static_cast<size_t>(split) * M * N + e, p,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(sk.mask + e, 1u << split, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+        add[m] = kFxUnit + kFxFloat;
+        published = true;
+      }
+    }
+  }
+  // A published float partial is acknowledged before its count is added, so
+  // whoever completes the count sees it (device-coherent accesses throughout).
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (published) __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+  for (int m = 0; m < kDecodeMaxM; ++m)
+    if (m < M)
+      old[m] = __hip_atomic_fetch_add(sk.acc + static_cast<size_t>(m) * N + n, add[m],
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float b = bias ? static_cast<float>(bias[n]) : 0.f;
+#pragma unroll
+  for (int m = 0; m < kDecodeMaxM; ++m) {
+    if (m >= M) continue;
+    const unsigned long long tot = old[m] + add[m];
+    if (static_cast<int>((tot >> 53) & 31u) != splits) continue;
+    const size_t e = static_cast<size_t>(m) * N + n;
+    const int nf = static_cast<int>((tot >> 58) & 31u);
+    const long long fx = static_cast<long long>(tot & (kFxUnit - 1)) -
+                         static_cast<long long>(splits - nf) * kFxBias;
+    float r = static_cast<float>(static_cast<double>(fx) * (1.0 / 16777216.0));
+    if (nf) {
+      const uint32_t msk = __hip_atomic_load(sk.mask + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int sp = 0; sp < splits; ++sp)
+        if ((msk >> sp) & 1u)
+          r += __hip_atomic_load(sk.partial + static_cast<size_t>(sp) * M * N + e,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sk.mask + e, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    y[e] = static_cast<_Float16>(r + b);
+    __hip_atomic_store(sk.acc + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 
 // SINGLE_GROUP: every row a wave reads lies in one quantisation group (the
 // group size is a multiple of the wave's 32*STEPS rows, or there is one
@@ -50,10 +131,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
     const _Float16* __restrict__ bias, _Float16* __restrict__ y,
-    float* __restrict__ partial, uint32_t* __restrict__ tickets,
-    int M, int K, int N, int g, int G, int splits, int ticket_words) {
-  extern __shared__ float red[];  // [2][M][256] fp32
-  __shared__ int s_last;
+    SplitK sk, int M, int K, int N, int g, int G, int splits) {
+  extern __shared__ __attribute__((aligned(16))) float red[];  // [2][256][Mp] fp32
 
   const int NW = N >> 3;
   const int tid = threadIdx.x;
@@ -154,77 +233,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     for (int j = 0; j < 8; ++j) tot[j] = static_cast<float>(sv[0][j]) * acc[j];
   }
 
-  // tot[j][i] is row 4*kb + i, column 8*c + j.  Meet the other K-half in LDS.
+  // tot[j][i] is row 4*kb + i, column 8*c + j.  Meet the other K-half in LDS:
+  // red[wk][column][Mp] with Mp = M rounded up to 4, one 16-byte store per
+  // column for the lanes that hold rows below M.
+  const int Mp = (M + 3) & ~3;
   const int lcol = 8 * (wn * 16 + col16);
+  if (4 * kb < M) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * kb + i;
-      if (m < M) red[(wk * M + m) * kDecodeCols + lcol + j] = tot[j][i];
-    }
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<floatx4*>(red + (wk * kDecodeCols + lcol + j) * Mp + 4 * kb) = tot[j];
   }
   __syncthreads();
 
   const int n = n_tile * kDecodeCols + tid;
   const bool nvalid = n < N;
+  auto wg_sum = [&](int m) {
+    return red[tid * Mp + m] + red[(kDecodeCols + tid) * Mp + m];
+  };
   if (splits == 1) {
     if (nvalid) {
       const float b = bias ? static_cast<float>(bias[n]) : 0.f;
-      for (int m = 0; m < M; ++m) {
-        const float v = red[m * kDecodeCols + tid] + red[(M + m) * kDecodeCols + tid];
-        y[m * N + n] = static_cast<_Float16>(v + b);
-      }
+      for (int m = 0; m < M; ++m) y[m * N + n] = static_cast<_Float16>(wg_sum(m) + b);
     }
     return;
   }
 
-  // Split-K exchange.  Partials are written with device-coherent stores and
-  // read back with device-coherent loads (agent-scope atomic accesses: they
-  // bypass the per-XCD L2's non-coherent state instead of needing a whole-L2
-  // writeback and invalidate).  Each thread waits for its stores to be
-  // acknowledged before the barrier, so every partial of this work-group is
-  // in place before its ticket is taken; the work-group that takes the last
-  // ticket therefore sees all of them.
-  if (nvalid) {
-    for (int m = 0; m < M; ++m) {
-      const float v = red[m * kDecodeCols + tid] + red[(M + m) * kDecodeCols + tid];
-      __hip_atomic_store(partial + (split * M + m) * N + n, v, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0)
-    s_last = (__hip_atomic_fetch_add(tickets + n_tile * ticket_words, 1u, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT) ==
-              static_cast<unsigned>(splits - 1));
-  __syncthreads();
-  if (!s_last) return;
-
-  if (nvalid) {
-    const float b = bias ? static_cast<float>(bias[n]) : 0.f;
-    const int stride = M * N;
-    for (int m = 0; m < M; ++m) {
-      const float* p = partial + m * N + n;
-      float sum = 0.f;
-      int sp = 0;
-      for (; sp + 16 <= splits; sp += 16) {
-        float v[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          v[u] = __hip_atomic_load(p + (sp + u) * stride, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int u = 0; u < 16; ++u) sum += v[u];
-      }
-      for (; sp < splits; ++sp)
-        sum += __hip_atomic_load(p + sp * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      y[m * N + n] = static_cast<_Float16>(sum + b);
-    }
-  }
-  if (tid == 0) __hip_atomic_store(tickets + n_tile * ticket_words, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (nvalid) splitk_finish(wg_sum, sk, bias, y, M, N, n, split, splits);
 }
 
 // ---------------------------------------------------------------------------
@@ -253,10 +287,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
 decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
                   const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
                   const _Float16* __restrict__ bias, _Float16* __restrict__ y,
-                  float* __restrict__ partial, uint32_t* __restrict__ tickets,
-                  int M, int K, int N, int g, int G, int splits, int ticket_words) {
+                  SplitK sk, int M, int K, int N, int g, int G, int splits) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ int s_last;
   constexpr int kWaveBytes = STEPS * 4 * kLdsBlockPitch;
 
   const int NW = N >> 3;
@@ -387,6 +419,10 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
       case 1: wait_vmcnt<4>(); break;
       case 2: wait_vmcnt<8>(); break;
       case 3: wait_vmcnt<12>(); break;
+      case 4: wait_vmcnt<16>(); break;
+      case 5: wait_vmcnt<20>(); break;
+      case 6: wait_vmcnt<24>(); break;
+      case 7: wait_vmcnt<28>(); break;
       default: wait_vmcnt<0>(); break;
     }
     const int gi = SINGLE_GROUP ? 0 : s;
@@ -432,19 +468,19 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
 
   // The four K-ranges meet in LDS (the copy regions are free once every wave
   // is past its last step).  tot[h][j][i] is row 4*kb + i, local column
-  // 8*(16h + col16) + j.
+  // 8*(16h + col16) + j; red[wave][column][Mp] with Mp = M rounded up to 4,
+  // one 16-byte store per column for the lanes that hold rows below M.
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
+  const int Mp = (M + 3) & ~3;
+  if (4 * kb < M) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int lcol = 8 * (16 * h + col16);
+    for (int h = 0; h < 2; ++h) {
+      const int lcol = 8 * (16 * h + col16);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * kb + i;
-        if (m < M) red[(wave * M + m) * kDecodeCols + lcol + j] = tot[h][j][i];
-      }
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<floatx4*>(red + (wave * kDecodeCols + lcol + j) * Mp + 4 * kb) =
+            tot[h][j];
     }
   }
   __syncthreads();
@@ -452,10 +488,10 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   const int n = n_tile * kDecodeCols + tid;
   const bool nvalid = n < N;
   auto wg_sum = [&](int m) {
-    float v = red[m * kDecodeCols + tid];
-    v += red[(M + m) * kDecodeCols + tid];
-    v += red[(2 * M + m) * kDecodeCols + tid];
-    v += red[(3 * M + m) * kDecodeCols + tid];
+    float v = red[tid * Mp + m];
+    v += red[(kDecodeCols + tid) * Mp + m];
+    v += red[(2 * kDecodeCols + tid) * Mp + m];
+    v += red[(3 * kDecodeCols + tid) * Mp + m];
     return v;
   };
   if (splits == 1) {
@@ -465,65 +501,26 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
     }
     return;
   }
-  // Split-K exchange (see the register variant above for the protocol).
-  if (nvalid) {
-    for (int m = 0; m < M; ++m)
-      __hip_atomic_store(partial + (split * M + m) * N + n, wg_sum(m), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0)
-    s_last = (__hip_atomic_fetch_add(tickets + n_tile * ticket_words, 1u, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT) ==
-              static_cast<unsigned>(splits - 1));
-  __syncthreads();
-  if (!s_last) return;
-  if (nvalid) {
-    const float b = bias ? static_cast<float>(bias[n]) : 0.f;
-    const int stride = M * N;
-    for (int m = 0; m < M; ++m) {
-      const float* p = partial + m * N + n;
-      float sum = 0.f;
-      int sp = 0;
-      for (; sp + 16 <= splits; sp += 16) {
-        float v[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          v[u] = __hip_atomic_load(p + (sp + u) * stride, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int u = 0; u < 16; ++u) sum += v[u];
-      }
-      for (; sp < splits; ++sp)
-        sum += __hip_atomic_load(p + sp * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      y[m * N + n] = static_cast<_Float16>(sum + b);
-    }
-  }
-  if (tid == 0)
-    __hip_atomic_store(tickets + n_tile * ticket_words, 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  if (nvalid) splitk_finish(wg_sum, sk, bias, y, M, N, n, split, splits);
 }
 
 template <int STEPS>
 hipError_t launch_lds_steps(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                             const _Float16* scales, const _Float16* bias, _Float16* y,
                             int M, int K, int N, int g, int G, int splits, int n_tiles,
-                            float* partial, uint32_t* tickets, int ticket_words,
-                            hipStream_t stream) {
+                            SplitK sk, hipStream_t stream) {
   const size_t copy_bytes = 4 * STEPS * 4 * kLdsBlockPitch;
-  const size_t red_bytes = 4 * static_cast<size_t>(M) * kDecodeCols * sizeof(float);
+  const size_t red_bytes = 4 * static_cast<size_t>((M + 3) & ~3) * kDecodeCols * sizeof(float);
   const size_t shmem = copy_bytes > red_bytes ? copy_bytes : red_bytes;
   const bool single = (G == 1) || (g % (kDecodeRowsPerStep * STEPS) == 0);
   if (single)
     hipLaunchKernelGGL((decode_lds_kernel<STEPS, true>), dim3(n_tiles * splits), dim3(256),
-                       shmem, stream, x, qweight, qzeros, scales, bias, y, partial, tickets, M,
-                       K, N, g, G, splits, ticket_words);
+                       shmem, stream, x, qweight, qzeros, scales, bias, y, sk, M,
+                       K, N, g, G, splits);
   else
     hipLaunchKernelGGL((decode_lds_kernel<STEPS, false>), dim3(n_tiles * splits), dim3(256),
-                       shmem, stream, x, qweight, qzeros, scales, bias, y, partial, tickets, M,
-                       K, N, g, G, splits, ticket_words);
+                       shmem, stream, x, qweight, qzeros, scales, bias, y, sk, M,
+                       K, N, g, G, splits);
   return hipGetLastError();
 }
 
@@ -531,20 +528,19 @@ template <int STEPS>
 hipError_t launch_steps(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                         const _Float16* scales, const _Float16* bias, _Float16* y,
                         int M, int K, int N, int g, int G, int splits, int n_tiles,
-                        float* partial, uint32_t* tickets, int ticket_words,
-                        hipStream_t stream) {
-  const size_t shmem = 2 * static_cast<size_t>(M) * kDecodeCols * sizeof(float);
+                        SplitK sk, hipStream_t stream) {
+  const size_t shmem = 2 * static_cast<size_t>((M + 3) & ~3) * kDecodeCols * sizeof(float);
   // Work-group row ranges start at multiples of 64*STEPS, so every wave's
   // 32*STEPS rows share a group exactly when g is a multiple of 32*STEPS.
   const bool single = (G == 1) || (g % (kDecodeRowsPerStep * STEPS) == 0);
   if (single)
     hipLaunchKernelGGL((decode_kernel<STEPS, true>), dim3(n_tiles * splits), dim3(256), shmem,
-                       stream, x, qweight, qzeros, scales, bias, y, partial, tickets, M, K, N,
-                       g, G, splits, ticket_words);
+                       stream, x, qweight, qzeros, scales, bias, y, sk, M, K, N,
+                       g, G, splits);
   else
     hipLaunchKernelGGL((decode_kernel<STEPS, false>), dim3(n_tiles * splits), dim3(256), shmem,
-                       stream, x, qweight, qzeros, scales, bias, y, partial, tickets, M, K, N,
-                       g, G, splits, ticket_words);
+                       stream, x, qweight, qzeros, scales, bias, y, sk, M, K, N,
+                       g, G, splits);
   return hipGetLastError();
 }
 
@@ -553,33 +549,34 @@ hipError_t launch_steps(const _Float16* x, const uint32_t* qweight, const uint32
 hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                          const _Float16* scales, const _Float16* bias, _Float16* y,
                          int M, int K, int N, int g, int G, int steps, int splits,
-                         int n_tiles, bool lds_variant, void* workspace, int ticket_stride,
-                         hipStream_t stream) {
-  uint32_t* tickets = static_cast<uint32_t*>(workspace);
-  float* partial = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                        kTicketRegionBytes)
-                             : nullptr;
-  const int tw = ticket_stride / 4;
+                         int n_tiles, bool lds_variant, void* workspace, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  const size_t mn = static_cast<size_t>(M) * N;
+  const SplitK sk{reinterpret_cast<unsigned long long*>(ws),
+                  ws ? reinterpret_cast<uint32_t*>(ws + mn * 8) : nullptr,
+                  ws ? reinterpret_cast<float*>(ws + mn * 12) : nullptr};
   if (lds_variant) {
     switch (steps) {
       case 1: return launch_lds_steps<1>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G,
-                                         splits, n_tiles, partial, tickets, tw, stream);
+                                         splits, n_tiles, sk, stream);
       case 2: return launch_lds_steps<2>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G,
-                                         splits, n_tiles, partial, tickets, tw, stream);
+                                         splits, n_tiles, sk, stream);
       case 4: return launch_lds_steps<4>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G,
-                                         splits, n_tiles, partial, tickets, tw, stream);
+                                         splits, n_tiles, sk, stream);
+      case 8: return launch_lds_steps<8>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G,
+                                         splits, n_tiles, sk, stream);
       default: return hipErrorInvalidValue;
     }
   }
   switch (steps) {
     case 1: return launch_steps<1>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G, splits,
-                                   n_tiles, partial, tickets, tw, stream);
+                                   n_tiles, sk, stream);
     case 2: return launch_steps<2>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G, splits,
-                                   n_tiles, partial, tickets, tw, stream);
+                                   n_tiles, sk, stream);
     case 4: return launch_steps<4>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G, splits,
-                                   n_tiles, partial, tickets, tw, stream);
+                                   n_tiles, sk, stream);
     case 8: return launch_steps<8>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G, splits,
-                                   n_tiles, partial, tickets, tw, stream);
+                                   n_tiles, sk, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -66,14 +66,22 @@ static bool fits_32bit_offsets(const Problem& p) {
   return p.M * p.K <= lim && p.M * p.N <= lim && p.K * p.N / 4 <= lim;
 }
 
+// Split-K work-groups per column tile for a step count: rows per work-group
+// are 4 waves (LDS variant) or 2 waves (register variant) x 32 x steps.
+static int64_t decode_splits(const Problem& p, bool lds, int steps) {
+  const int waves_k = lds ? 4 : 2;
+  return ceil_div(p.K, static_cast<int64_t>(waves_k) * kDecodeRowsPerStep * steps);
+}
+
 bool decode_supported(const Problem& p, const Alignment& al) {
   // 16-byte x loads need K % 8 == 0; a group must not change inside a wave's
-  // 32-row step; every column tile needs a 4-byte ticket slot; the
-  // LDS-streaming variant (N % 32 == 0) copies 16-byte row segments.
-  const int64_t n_tiles = (p.N + kDecodeCols - 1) / kDecodeCols;
-  return fits_32bit_offsets(p) && n_tiles * 4 <= static_cast<int64_t>(kTicketRegionBytes) &&
-         p.M <= kDecodeMaxM && p.K % 8 == 0 && al.x && al.scales &&
-         (p.N % 32 != 0 || al.qweight) && (p.g % kDecodeRowsPerStep == 0 || p.G == 1);
+  // 32-row step; the LDS-streaming variant (N % 32 == 0) copies 16-byte row
+  // segments; the split-K exchange counts at most kDecodeMaxSplits splits
+  // (at 8 steps per wave).
+  const bool lds = p.N % 32 == 0;
+  return fits_32bit_offsets(p) && p.M <= kDecodeMaxM && p.K % 8 == 0 && al.x && al.scales &&
+         (!lds || al.qweight) && (p.g % kDecodeRowsPerStep == 0 || p.G == 1) &&
+         decode_splits(p, lds, 8) <= kDecodeMaxSplits;
 }
 
 static int log2_exact(int64_t v) {
@@ -116,32 +124,27 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
   if (path == AWQ_PATH_DECODE) {
     pl.n_tiles = static_cast<int>(ceil_div(p.N, kDecodeCols));
     pl.decode_lds = (p.N % 32 == 0);
-    // Rows per work-group: 4 waves (LDS variant) or 2 waves (register
-    // variant) along K, 32 rows per step each.
-    const int waves_k = pl.decode_lds ? 4 : 2;
     int steps = decode_steps_override();
-    if (steps == 8 && pl.decode_lds) steps = 4;
+    if (steps != 0 && decode_splits(p, pl.decode_lds, steps) > kDecodeMaxSplits) steps = 0;
     if (steps == 0) {
-      // At most 4 steps (the register variant keeps 32 word loads per lane
-      // in flight, under the 63 outstanding vector loads a wave can track);
-      // prefer step counts whose rows stay in one quantisation group, and
-      // the largest that still gives enough work-groups.
+      // Prefer step counts whose rows stay in one quantisation group, and
+      // the largest that still gives enough work-groups; 8 steps only when
+      // fewer would need more than kDecodeMaxSplits splits.
       const int64_t target = pl.decode_lds ? kDecodeLdsTargetWGs : kDecodeTargetWGs;
-      steps = 1;
+      steps = 8;
       for (int s = 4; s >= 1; s /= 2) {
         const bool single = p.G == 1 || p.g % (kDecodeRowsPerStep * s) == 0;
-        const int64_t splits = ceil_div(p.K, waves_k * kDecodeRowsPerStep * s);
-        if (single && pl.n_tiles * splits >= target) { steps = s; break; }
+        const int64_t splits = decode_splits(p, pl.decode_lds, s);
+        if (splits > kDecodeMaxSplits) break;
+        steps = s;
+        if (single && pl.n_tiles * splits >= target) break;
       }
     }
     pl.steps = steps;
-    pl.splits = static_cast<int>(ceil_div(p.K, waves_k * kDecodeRowsPerStep * steps));
-    int stride = static_cast<int>(kTicketRegionBytes / pl.n_tiles) & ~3;
-    pl.ticket_stride = stride < kTicketMaxStrideBytes ? stride : kTicketMaxStrideBytes;
-    if (pl.splits > 1) {
-      pl.ws_bytes = kTicketRegionBytes +
+    pl.splits = static_cast<int>(decode_splits(p, pl.decode_lds, steps));
+    if (pl.splits > 1)
+      pl.ws_bytes = static_cast<size_t>(p.M) * p.N * 12 +
                     static_cast<size_t>(pl.splits) * p.M * p.N * sizeof(float);
-    }
   } else if (path == AWQ_PATH_PREFILL) {
     pl.m_tiles = static_cast<int>(ceil_div(p.M, kPrefillBM));
     pl.n_tiles = static_cast<int>(ceil_div(p.N, kPrefillBN));

@@ -13,13 +13,10 @@ namespace awq {
 constexpr int kDecodeCols = 256;         // columns per work-group
 constexpr int kDecodeRowsPerStep = 32;   // rows one wave consumes per step
 constexpr int kDecodeMaxM = 16;          // rows of the 16x16 MFMA output
-// Split-K tickets live in a fixed region at the start of every workspace, so
-// the partial sums of any call (which start after it) can never overwrite
-// the tickets of a later call with a different shape sharing the workspace.
-// Device-scope atomics to one cache line serialise, so each column tile's
-// ticket gets its own slot of up to 256 bytes.
-constexpr size_t kTicketRegionBytes = 65536;
-constexpr int kTicketMaxStrideBytes = 256;
+// Split-K exchange: per output element an 8-byte fixed-point accumulator
+// with a 5-bit contribution count and a 4-byte mask of float contributions,
+// then 4 bytes per split for those float partials.  At most 31 splits.
+constexpr int kDecodeMaxSplits = 31;
 
 // Prefill kernel tile.
 constexpr int kPrefillBM = 256;
@@ -39,7 +36,6 @@ struct Plan {
   int n_tiles;       // column tiles
   int m_tiles;       // prefill: row tiles
   size_t ws_bytes;   // workspace bytes
-  int ticket_stride;  // decode: bytes between two tiles' tickets
   bool decode_lds;    // decode: LDS-streaming variant (N % 32 == 0) or register variant
   int group_shift;    // prefill: log2(group size), or 31 for a single group
 };

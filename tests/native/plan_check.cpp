@@ -71,10 +71,9 @@ int main() {
                 const int waves_k = pl.decode_lds ? 4 : 2;
                 EXPECT((int64_t)pl.splits * waves_k * kDecodeRowsPerStep * pl.steps >= K);
                 EXPECT((int64_t)(pl.splits - 1) * waves_k * kDecodeRowsPerStep * pl.steps < K);
-                EXPECT(pl.ticket_stride >= 4 && pl.ticket_stride % 4 == 0);
-                EXPECT((size_t)pl.ticket_stride * pl.n_tiles <= kTicketRegionBytes);
+                EXPECT(pl.splits <= kDecodeMaxSplits);
                 if (pl.splits > 1)
-                  EXPECT(pl.ws_bytes == kTicketRegionBytes + (size_t)pl.splits * M * N * 4);
+                  EXPECT(pl.ws_bytes == (size_t)M * N * 12 + (size_t)pl.splits * M * N * 4);
                 else
                   EXPECT(pl.ws_bytes == 0);
               } else if (pl.path == AWQ_PATH_PREFILL) {

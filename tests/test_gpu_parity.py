@@ -320,9 +320,8 @@ def test_deterministic_repeats(M):
 
 
 def test_workspace_reuse_across_shapes():
-    """One workspace serves decode calls of different shapes back to back
-    (the kernels leave every ticket at zero).  Regression: a narrow call's
-    partial sums must not land on a wider call's tickets."""
+    """One workspace serves decode calls of different shapes back to back:
+    the kernels leave every accumulator and mask they used at zero."""
     say("workspace reuse")
     ws = torch.zeros(awq.gemm_workspace_size(16, 8192, 7168, 128), dtype=torch.uint8, device=DEV)
     for (M, K, N) in [(16, 8192, 7168), (1, 8192, 1280), (4, 4096, 2048), (16, 8192, 7168)]:
@@ -331,7 +330,41 @@ def test_workspace_reuse_across_shapes():
         y = awq.gemm(d["x"], d["qweight"], d["qzeros"], d["scales"], None, 128, workspace=ws)
         ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], None, 128)
         assert_within_tol(y.cpu().numpy(), ref, f"reuse M={M} K={K} N={N}")
-    assert torch.count_nonzero(ws[:65536]).item() == 0   # every ticket slot back at zero
+    assert torch.count_nonzero(ws[:16 * 7168 * 12]).item() == 0   # accumulators and masks back at zero
+
+
+@pytest.mark.parametrize("lds", [True, False])
+def test_decode_large_partials_take_float_path(lds):
+    """A split's partial beyond the fixed-point range of the split-K exchange
+    (|p| >= 2^23) is published as a float: one activation of 60000 in a group
+    whose scales are 100 makes those outputs overflow to +-inf in float16,
+    exactly as the oracle's do, while the columns it does not reach stay
+    within tolerance.  The workspace is clean afterwards."""
+    N = 1280 if lds else 1288
+    K, g, k0 = 8192, 128, 5000
+    say(f"decode float path N={N}")
+    p = awq_inputs.make_inputs(2, K, N, g, seed=17, bias=True)
+    p["x"][0, k0] = np.float16(60000.0)
+    p["scales"][k0 // g, :] = np.float16(100.0)
+    assert awq.gemm_plan(2, K, N, g)[0] == binding.AWQ_PATH_DECODE
+    d = to_dev(p)
+    ws = torch.zeros(awq.gemm_workspace_size(2, K, N, g), dtype=torch.uint8, device=DEV)
+    y = awq.gemm(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], g,
+                 workspace=ws).cpu().numpy().astype(np.float64)
+    ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
+    with np.errstate(over="ignore"):
+        ref16 = ref.astype(np.float16).astype(np.float64)
+    big = np.isinf(ref16)
+    assert big[0].sum() > N // 2          # the float path was taken for most columns
+    assert np.array_equal(np.isinf(y), big)
+    assert np.array_equal(y[big], ref16[big])
+    assert_within_tol(y[~big], ref[~big], "finite outputs")
+    assert torch.count_nonzero(ws[:2 * N * 12]).item() == 0
+    q = awq_inputs.make_inputs(2, K, N, g, seed=18)
+    dq = to_dev(q)
+    y2 = awq.gemm(dq["x"], dq["qweight"], dq["qzeros"], dq["scales"], None, g, workspace=ws)
+    ref2 = oracle.awq_linear_ref(q["x"], q["qweight"], q["qzeros"], q["scales"], None, g)
+    assert_within_tol(y2.cpu().numpy(), ref2, "after float-path call")
 
 
 def test_wqlinear_module_forward():

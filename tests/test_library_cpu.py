@@ -160,19 +160,24 @@ def test_forced_path(monkeypatch):
 
 
 def test_decode_workspace_size_formula():
-    """A fixed 64 KiB ticket region (the same for every shape, so calls of
-    different shapes can share one workspace) plus one fp32 partial row per
-    split per batch row."""
-    M, K, N, g = 4, 8192, 7168, 128
-    path, ws = awq.gemm_plan(M, K, N, g)
-    assert path == binding.AWQ_PATH_DECODE
-    n_tiles = -(-N // 256)
-    ticket = 65536
-    assert n_tiles * 256 <= ticket
-    partial = ws - ticket
-    assert partial % (M * N * 4) == 0
-    splits = partial // (M * N * 4)
-    assert any(splits == -(-K // (64 * steps)) for steps in (1, 2, 4, 8))
+    """Per output element an 8-byte fixed-point accumulator and a 4-byte
+    float-contribution mask, then one fp32 slot per split per element; at
+    most 31 splits."""
+    for (M, K, N, g) in [(4, 8192, 7168, 128), (1, 14336, 4096, 128), (16, 8192, 1280, -1)]:
+        path, ws = awq.gemm_plan(M, K, N, g)
+        assert path == binding.AWQ_PATH_DECODE
+        assert ws == awq.gemm_workspace_size(M, K, N, g)
+        partial = ws - M * N * 12
+        assert partial % (M * N * 4) == 0
+        splits = partial // (M * N * 4)
+        assert 2 <= splits <= 31
+        assert any(splits == -(-K // (128 * steps)) for steps in (1, 2, 4, 8))
+
+
+def test_decode_split_limit():
+    """K beyond 31 splits of 8 steps cannot take the decode kernel."""
+    assert awq.gemm_plan(1, 31 * 1024, 4096, 128)[0] == binding.AWQ_PATH_DECODE
+    assert awq.gemm_plan(1, 32 * 1024, 4096, 128)[0] != binding.AWQ_PATH_DECODE
 
 
 def test_no_cpu_fallback():
