@@ -29,13 +29,16 @@
 //   rounding (relative 2^-11 per term).  A one-hot row still reproduces the
 //   float16 dequantised weight exactly.
 // * Reduction: the K-ranges of a work-group meet in LDS; the work-groups of a
-//   column tile then meet in one 64-bit device-scope atomic per output
-//   element (see splitk_finish): each adds its partial as a 2^-24 fixed-point
-//   integer together with a contribution count, and the one whose returned
-//   sum shows every split has arrived writes y.  Integer addition makes the
-//   sum exact and independent of arrival order (deterministic), and the
-//   exchange costs one atomic round trip instead of store, acknowledge,
-//   ticket and reload.
+//   column tile then meet in the workspace, deterministically in either of
+//   two ways.  For M <= 4, one 64-bit device-scope atomic per output element
+//   (splitk_atomic): each adds its partial as a 2^-24 fixed-point integer
+//   with a contribution count, and the one whose returned sum shows every
+//   split has arrived writes y -- one atomic round trip.  For larger M the
+//   atomic count grows past what the memory-side atomic units sustain, so
+//   partials are stored, each work-group takes a ticket on its column tile,
+//   and the last one sums them in split order (splitk_ticket).  Every byte
+//   the ticket and accumulator regions of the workspace is zero again when
+//   either exchange ends.
 #include "awq_device.h"
 #include "awq_plan.h"
 
@@ -44,9 +47,11 @@ namespace {
 
 // Split-K exchange state in the workspace (all of it zero between calls).
 struct SplitK {
-  unsigned long long* acc;   // [M][N]: fixed-point sum, contribution count
-  uint32_t* mask;            // [M][N]: splits that sent a float partial
-  float* partial;            // [splits][M][N]: those float partials
+  uint32_t* tickets;         // one per column tile, ticket_words apart (ticket exchange)
+  unsigned long long* acc;   // [M][N]: fixed-point sum, contribution count (atomic exchange)
+  uint32_t* mask;            // [M][N]: splits that sent a float partial (atomic exchange)
+  float* partial;            // [splits][M][N]: partials (all for ticket, float ones for atomic)
+  int ticket_words;
 };
 // acc layout: bits 0-52 sum of (v + 2^47) over fixed-point contributions,
 // v = rint(p * 2^24) with |p| < 2^23 (so each term is below 2^48 and up to
@@ -59,12 +64,44 @@ constexpr long long kFxBias = 1ll << 47;
 constexpr float kFxScale = 16777216.0f;   // 2^24
 constexpr float kFxLimit = 8388608.0f;    // 2^23
 
-// Called by the thread that owns column n of this work-group, with wg_sum(m)
-// the work-group's partial for row m.  All atomics of the thread are issued
+// Cross-wave reduction in LDS.  Layout [wave][row group of 4][column][4 rows]
+// (row groups below M only): the lane holding rows 4*kb .. 4*kb+3 of a column
+// writes them as one 16-byte store, and the thread of a column reads each
+// row group of each wave as one conflict-free 16-byte load.
+__device__ __forceinline__ void red_store(float* red, int wave, int Mq, int kb, int col,
+                                          floatx4 v) {
+  *reinterpret_cast<floatx4*>(red + ((wave * Mq + kb) * kDecodeCols + col) * 4) = v;
+}
+template <int WAVES>
+__device__ __forceinline__ void red_sum(const float* red, int Mq, int M, int col,
+                                        float (&part)[kDecodeMaxM]) {
+#pragma unroll
+  for (int c4 = 0; c4 < kDecodeMaxM / 4; ++c4) {
+    if (4 * c4 < M) {
+      floatx4 v = *reinterpret_cast<const floatx4*>(red + (c4 * kDecodeCols + col) * 4);
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w)
+        v += *reinterpret_cast<const floatx4*>(red + ((w * Mq + c4) * kDecodeCols + col) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[4 * c4 + i] = v[i];
+    }
+  }
+}
+// Output of a work-group that covers all of K (no exchange).
+__device__ __forceinline__ void store_rows(const float (&part)[kDecodeMaxM],
+                                           const _Float16* __restrict__ bias,
+                                           _Float16* __restrict__ y, int M, int N, int n) {
+  const float b = bias ? static_cast<float>(bias[n]) : 0.f;
+#pragma unroll
+  for (int m = 0; m < kDecodeMaxM; ++m)
+    if (m < M) y[m * N + n] = static_cast<_Float16>(part[m] + b);
+}
+
+// Called by the thread that owns column n of this work-group, with part[m]
+// the work-group's partial for row m < M.  All atomics of the thread are issued
 // before any result is used.  Partials are exact multiples of 2^-24 whenever
 // the scales are (every float16 is), so a one-hot row stays exact.
-template <class F>
-__device__ __forceinline__ void splitk_finish(const F& wg_sum, const SplitK& sk,
+__device__ __forceinline__ void splitk_atomic(const float (&part)[kDecodeMaxM], const SplitK& sk,
                                               const _Float16* __restrict__ bias,
                                               _Float16* __restrict__ y, int M, int N, int n,
                                               int split, int splits) {
@@ -73,7 +110,7 @@ __device__ __forceinline__ void splitk_finish(const F& wg_sum, const SplitK& sk,
 #pragma unroll
   for (int m = 0; m < kDecodeMaxM; ++m) {
     if (m < M) {
-      const float p = wg_sum(m);
+      const float p = part[m];
       if (fabsf(p) < kFxLimit) {   // false for NaN
         const long long v = static_cast<long long>(__builtin_rintf(p * kFxScale));
         add[m] = static_cast<unsigned long long>(v + kFxBias) + kFxUnit;
@@ -122,6 +159,59 @@ __device__ __forceinline__ void splitk_finish(const F& wg_sum, const SplitK& sk,
   }
 }
 
+// Ticket exchange (M > 4), called by every thread of the work-group.
+// Partials are written with device-coherent stores and read back with
+// device-coherent loads (agent-scope atomic accesses bypass the per-XCD L2's
+// non-coherent state without a whole-L2 writeback); each thread waits for
+// its stores to be acknowledged before the barrier, so every partial of the
+// work-group is in place before its ticket is taken, and the work-group that
+// takes the last ticket sees all of them.  It sums them in split order and
+// resets the ticket.
+__device__ __forceinline__ void splitk_ticket(const float (&part)[kDecodeMaxM], const SplitK& sk,
+                                              const _Float16* __restrict__ bias,
+                                              _Float16* __restrict__ y, int M, int N, int n,
+                                              bool nvalid, int split, int splits, int n_tile) {
+  __shared__ int s_last;
+  if (nvalid) {
+#pragma unroll
+    for (int m = 0; m < kDecodeMaxM; ++m)
+      if (m < M)
+        __hip_atomic_store(sk.partial + (static_cast<size_t>(split) * M + m) * N + n, part[m],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t* ticket = sk.tickets + n_tile * sk.ticket_words;
+  if (threadIdx.x == 0)
+    s_last = (__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              static_cast<unsigned>(splits - 1));
+  __syncthreads();
+  if (!s_last) return;
+  if (nvalid) {
+    const float b = bias ? static_cast<float>(bias[n]) : 0.f;
+    const size_t stride = static_cast<size_t>(M) * N;
+    for (int m = 0; m < M; ++m) {
+      float* p = sk.partial + static_cast<size_t>(m) * N + n;
+      float sum = 0.f;
+      int sp = 0;
+      for (; sp + 16 <= splits; sp += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          v[u] = __hip_atomic_load(p + (sp + u) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) sum += v[u];
+      }
+      for (; sp < splits; ++sp)
+        sum += __hip_atomic_load(p + sp * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      y[m * N + n] = static_cast<_Float16>(sum + b);
+    }
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // SINGLE_GROUP: every row a wave reads lies in one quantisation group (the
 // group size is a multiple of the wave's 32*STEPS rows, or there is one
 // group), so the scale is applied once after all steps.  Otherwise each
@@ -132,7 +222,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
     const _Float16* __restrict__ bias, _Float16* __restrict__ y,
     SplitK sk, int M, int K, int N, int g, int G, int splits) {
-  extern __shared__ __attribute__((aligned(16))) float red[];  // [2][256][Mp] fp32
+  extern __shared__ __attribute__((aligned(16))) float red[];  // see red_store
 
   const int NW = N >> 3;
   const int tid = threadIdx.x;
@@ -233,32 +323,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     for (int j = 0; j < 8; ++j) tot[j] = static_cast<float>(sv[0][j]) * acc[j];
   }
 
-  // tot[j][i] is row 4*kb + i, column 8*c + j.  Meet the other K-half in LDS:
-  // red[wk][column][Mp] with Mp = M rounded up to 4, one 16-byte store per
-  // column for the lanes that hold rows below M.
-  const int Mp = (M + 3) & ~3;
+  // tot[j][i] is row 4*kb + i, column 8*c + j.  Meet the other K-half in LDS.
+  const int Mq = (M + 3) >> 2;
   const int lcol = 8 * (wn * 16 + col16);
   if (4 * kb < M) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<floatx4*>(red + (wk * kDecodeCols + lcol + j) * Mp + 4 * kb) = tot[j];
+    for (int j = 0; j < 8; ++j) red_store(red, wk, Mq, kb, lcol + j, tot[j]);
   }
   __syncthreads();
 
   const int n = n_tile * kDecodeCols + tid;
   const bool nvalid = n < N;
-  auto wg_sum = [&](int m) {
-    return red[tid * Mp + m] + red[(kDecodeCols + tid) * Mp + m];
-  };
+  float part[kDecodeMaxM];
+  red_sum<2>(red, Mq, M, tid, part);
   if (splits == 1) {
-    if (nvalid) {
-      const float b = bias ? static_cast<float>(bias[n]) : 0.f;
-      for (int m = 0; m < M; ++m) y[m * N + n] = static_cast<_Float16>(wg_sum(m) + b);
-    }
+    if (nvalid) store_rows(part, bias, y, M, N, n);
     return;
   }
 
-  if (nvalid) splitk_finish(wg_sum, sk, bias, y, M, N, n, split, splits);
+  if (M <= kDecodeAtomicMaxM && N <= kDecodeAtomicMaxN) {
+    if (nvalid) splitk_atomic(part, sk, bias, y, M, N, n, split, splits);
+  } else {
+    splitk_ticket(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -468,40 +555,31 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
 
   // The four K-ranges meet in LDS (the copy regions are free once every wave
   // is past its last step).  tot[h][j][i] is row 4*kb + i, local column
-  // 8*(16h + col16) + j; red[wave][column][Mp] with Mp = M rounded up to 4,
-  // one 16-byte store per column for the lanes that hold rows below M.
+  // 8*(16h + col16) + j.
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
-  const int Mp = (M + 3) & ~3;
+  const int Mq = (M + 3) >> 2;
   if (4 * kb < M) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int lcol = 8 * (16 * h + col16);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<floatx4*>(red + (wave * kDecodeCols + lcol + j) * Mp + 4 * kb) =
-            tot[h][j];
-    }
+      for (int j = 0; j < 8; ++j) red_store(red, wave, Mq, kb, 8 * (16 * h + col16) + j, tot[h][j]);
   }
   __syncthreads();
 
   const int n = n_tile * kDecodeCols + tid;
   const bool nvalid = n < N;
-  auto wg_sum = [&](int m) {
-    float v = red[tid * Mp + m];
-    v += red[(kDecodeCols + tid) * Mp + m];
-    v += red[(2 * kDecodeCols + tid) * Mp + m];
-    v += red[(3 * kDecodeCols + tid) * Mp + m];
-    return v;
-  };
+  float part[kDecodeMaxM];
+  red_sum<4>(red, Mq, M, tid, part);
   if (splits == 1) {
-    if (nvalid) {
-      const float b = bias ? static_cast<float>(bias[n]) : 0.f;
-      for (int m = 0; m < M; ++m) y[m * N + n] = static_cast<_Float16>(wg_sum(m) + b);
-    }
+    if (nvalid) store_rows(part, bias, y, M, N, n);
     return;
   }
-  if (nvalid) splitk_finish(wg_sum, sk, bias, y, M, N, n, split, splits);
+  if (M <= kDecodeAtomicMaxM && N <= kDecodeAtomicMaxN) {
+    if (nvalid) splitk_atomic(part, sk, bias, y, M, N, n, split, splits);
+  } else {
+    splitk_ticket(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
+  }
 }
 
 template <int STEPS>
@@ -550,11 +628,18 @@ hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint3
                          const _Float16* scales, const _Float16* bias, _Float16* y,
                          int M, int K, int N, int g, int G, int steps, int splits,
                          int n_tiles, bool lds_variant, void* workspace, hipStream_t stream) {
+  // Workspace: ticket region, accumulator region ([M][N] accumulators, then
+  // [M][N] masks), then [splits][M][N] partials.
   char* ws = static_cast<char*>(workspace);
   const size_t mn = static_cast<size_t>(M) * N;
-  const SplitK sk{reinterpret_cast<unsigned long long*>(ws),
-                  ws ? reinterpret_cast<uint32_t*>(ws + mn * 8) : nullptr,
-                  ws ? reinterpret_cast<float*>(ws + mn * 12) : nullptr};
+  int tw = static_cast<int>(kTicketRegionBytes / 4 / n_tiles);
+  if (tw > kTicketMaxStrideBytes / 4) tw = kTicketMaxStrideBytes / 4;
+  const SplitK sk{reinterpret_cast<uint32_t*>(ws),
+                  ws ? reinterpret_cast<unsigned long long*>(ws + kTicketRegionBytes) : nullptr,
+                  ws ? reinterpret_cast<uint32_t*>(ws + kTicketRegionBytes + mn * 8) : nullptr,
+                  ws ? reinterpret_cast<float*>(ws + kTicketRegionBytes + kAtomicRegionBytes)
+                     : nullptr,
+                  tw};
   if (lds_variant) {
     switch (steps) {
       case 1: return launch_lds_steps<1>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G,

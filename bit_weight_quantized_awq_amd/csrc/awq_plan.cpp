@@ -77,11 +77,13 @@ bool decode_supported(const Problem& p, const Alignment& al) {
   // 16-byte x loads need K % 8 == 0; a group must not change inside a wave's
   // 32-row step; the LDS-streaming variant (N % 32 == 0) copies 16-byte row
   // segments; the split-K exchange counts at most kDecodeMaxSplits splits
-  // (at 8 steps per wave).
+  // (at 8 steps per wave) and every column tile has a 4-byte ticket slot.
   const bool lds = p.N % 32 == 0;
+  const int64_t n_tiles = ceil_div(p.N, kDecodeCols);
   return fits_32bit_offsets(p) && p.M <= kDecodeMaxM && p.K % 8 == 0 && al.x && al.scales &&
          (!lds || al.qweight) && (p.g % kDecodeRowsPerStep == 0 || p.G == 1) &&
-         decode_splits(p, lds, 8) <= kDecodeMaxSplits;
+         decode_splits(p, lds, 8) <= kDecodeMaxSplits &&
+         n_tiles * 4 <= static_cast<int64_t>(kTicketRegionBytes);
 }
 
 static int log2_exact(int64_t v) {
@@ -143,7 +145,7 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
     pl.steps = steps;
     pl.splits = static_cast<int>(decode_splits(p, pl.decode_lds, steps));
     if (pl.splits > 1)
-      pl.ws_bytes = static_cast<size_t>(p.M) * p.N * 12 +
+      pl.ws_bytes = kTicketRegionBytes + kAtomicRegionBytes +
                     static_cast<size_t>(pl.splits) * p.M * p.N * sizeof(float);
   } else if (path == AWQ_PATH_PREFILL) {
     pl.m_tiles = static_cast<int>(ceil_div(p.M, kPrefillBM));

@@ -13,10 +13,22 @@ namespace awq {
 constexpr int kDecodeCols = 256;         // columns per work-group
 constexpr int kDecodeRowsPerStep = 32;   // rows one wave consumes per step
 constexpr int kDecodeMaxM = 16;          // rows of the 16x16 MFMA output
-// Split-K exchange: per output element an 8-byte fixed-point accumulator
-// with a 5-bit contribution count and a 4-byte mask of float contributions,
-// then 4 bytes per split for those float partials.  At most 31 splits.
+// Split-K exchange workspace, in three parts:
+//  * a fixed ticket region: one ticket per column tile, up to 256 bytes apart
+//    (device-scope atomics on one cache line serialise);
+//  * a fixed accumulator region for the atomic exchange (M <= 4, N <= 65536):
+//    an 8-byte fixed-point accumulator per output element, then a 4-byte
+//    mask per output element;
+//  * 4 bytes per split per output element for partials.
+// The first two parts are zero between calls (each exchange resets what it
+// used) and no exchange writes partials into them, so calls of any shapes
+// can share one workspace.  The atomic exchange counts at most 31 splits.
+constexpr size_t kTicketRegionBytes = 65536;
+constexpr int kTicketMaxStrideBytes = 256;
 constexpr int kDecodeMaxSplits = 31;
+constexpr int kDecodeAtomicMaxM = 4;
+constexpr int kDecodeAtomicMaxN = 65536;
+constexpr size_t kAtomicRegionBytes = static_cast<size_t>(kDecodeAtomicMaxM) * kDecodeAtomicMaxN * 12;
 
 // Prefill kernel tile.
 constexpr int kPrefillBM = 256;

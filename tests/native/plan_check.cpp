@@ -73,7 +73,8 @@ int main() {
                 EXPECT((int64_t)(pl.splits - 1) * waves_k * kDecodeRowsPerStep * pl.steps < K);
                 EXPECT(pl.splits <= kDecodeMaxSplits);
                 if (pl.splits > 1)
-                  EXPECT(pl.ws_bytes == (size_t)M * N * 12 + (size_t)pl.splits * M * N * 4);
+                  EXPECT(pl.ws_bytes == kTicketRegionBytes + kAtomicRegionBytes +
+                                        (size_t)pl.splits * M * N * 4);
                 else
                   EXPECT(pl.ws_bytes == 0);
               } else if (pl.path == AWQ_PATH_PREFILL) {

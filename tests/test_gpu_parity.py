@@ -49,6 +49,9 @@ def to_dev(p):
     return d
 
 
+ZERO_REGION = 65536 + 4 * 65536 * 12   # ticket + accumulator regions of a decode workspace
+
+
 def assert_within_tol(gpu, ref, what):
     gpu = gpu.astype(np.float64)
     err = np.abs(gpu - ref)
@@ -320,17 +323,19 @@ def test_deterministic_repeats(M):
 
 
 def test_workspace_reuse_across_shapes():
-    """One workspace serves decode calls of different shapes back to back:
-    the kernels leave every accumulator and mask they used at zero."""
+    """One workspace serves decode calls of different shapes (both exchange
+    modes: M <= 4 atomic, M > 4 ticket) back to back: every call leaves the
+    ticket and accumulator regions zero."""
     say("workspace reuse")
     ws = torch.zeros(awq.gemm_workspace_size(16, 8192, 7168, 128), dtype=torch.uint8, device=DEV)
-    for (M, K, N) in [(16, 8192, 7168), (1, 8192, 1280), (4, 4096, 2048), (16, 8192, 7168)]:
+    for (M, K, N) in [(16, 8192, 7168), (1, 8192, 1280), (4, 4096, 2048), (8, 4096, 1280),
+                      (2, 8192, 7168), (16, 8192, 7168)]:
         p = awq_inputs.make_inputs(M, K, N, 128, seed=K + M)
         d = to_dev(p)
         y = awq.gemm(d["x"], d["qweight"], d["qzeros"], d["scales"], None, 128, workspace=ws)
         ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], None, 128)
         assert_within_tol(y.cpu().numpy(), ref, f"reuse M={M} K={K} N={N}")
-    assert torch.count_nonzero(ws[:16 * 7168 * 12]).item() == 0   # accumulators and masks back at zero
+        assert torch.count_nonzero(ws[:ZERO_REGION]).item() == 0, f"dirty after M={M} K={K} N={N}"
 
 
 @pytest.mark.parametrize("lds", [True, False])
@@ -359,7 +364,7 @@ def test_decode_large_partials_take_float_path(lds):
     assert np.array_equal(np.isinf(y), big)
     assert np.array_equal(y[big], ref16[big])
     assert_within_tol(y[~big], ref[~big], "finite outputs")
-    assert torch.count_nonzero(ws[:2 * N * 12]).item() == 0
+    assert torch.count_nonzero(ws[:ZERO_REGION]).item() == 0
     q = awq_inputs.make_inputs(2, K, N, g, seed=18)
     dq = to_dev(q)
     y2 = awq.gemm(dq["x"], dq["qweight"], dq["qzeros"], dq["scales"], None, g, workspace=ws)

@@ -160,14 +160,15 @@ def test_forced_path(monkeypatch):
 
 
 def test_decode_workspace_size_formula():
-    """Per output element an 8-byte fixed-point accumulator and a 4-byte
-    float-contribution mask, then one fp32 slot per split per element; at
-    most 31 splits."""
+    """A fixed 64 KiB ticket region, a fixed 3 MiB accumulator region (an
+    8-byte accumulator and a 4-byte mask per element, for M <= 4 and
+    N <= 65536), then one fp32 slot per split per element; at most 31
+    splits."""
     for (M, K, N, g) in [(4, 8192, 7168, 128), (1, 14336, 4096, 128), (16, 8192, 1280, -1)]:
         path, ws = awq.gemm_plan(M, K, N, g)
         assert path == binding.AWQ_PATH_DECODE
         assert ws == awq.gemm_workspace_size(M, K, N, g)
-        partial = ws - M * N * 12
+        partial = ws - 65536 - 4 * 65536 * 12
         assert partial % (M * N * 4) == 0
         splits = partial // (M * N * 4)
         assert 2 <= splits <= 31
