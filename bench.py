@@ -24,6 +24,7 @@ single-GPU share of the path.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -41,6 +42,22 @@ DECODE = dict(workload="decode_m1_k8192_n7168_g128", source="decode_sweep_k8192_
               M=1, group_size=128)
 PREFILL = dict(workload="prefill_qkv_m2048_k4096_n12288_g128",
                source="prefill_qkv_m2048_k4096_n12288", M=2048, group_size=128)
+
+
+def measured_traffic(leg):
+    """HBM-side bytes per launch of the leg's kernel from the committed PMC
+    measurement (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE, calibrated
+    on a plain copy), or None when the kernel's sources changed since."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            entry = json.load(f)[leg]
+        h = hashlib.sha256()
+        for fn in entry["sources"]:
+            with open(os.path.join(ROOT, fn), "rb") as f:
+                h.update(f.read())
+        return entry["bytes_per_launch"] if h.hexdigest() == entry["sources_sha256"] else None
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def algorithmic_bytes(M, K, N, G, bias):
@@ -216,7 +233,8 @@ def main():
                        "hbm_peak_frac_whole_job": round(gbs / HBM_PEAK_GBS, 4),
                        "eager_ms_per_step": r["eager_ms"]},
             "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode"),
                          "kernel_avg_us": round(r["ms_per_step"] * 1e3, 3),
                          "single_launch_event_us": round(r["kern_avg_ms"] * 1e3, 3)},
         })
@@ -229,7 +247,8 @@ def main():
                "M": r["M"], "K": r["K"], "N": r["N"], "group_size": r["g"], "bias": True,
                "roofline": {"bound": "mfma", "achieved": round(ktf, 1),
                             "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": round(ktf / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                            "frac": round(ktf / FP16_MFMA_PEAK_TFLOPS, 4),
+                            "traffic": measured_traffic("prefill"),
                             "kernel_avg_us": round(r["ms_per_step"] * 1e3, 3),
                             "single_launch_event_us": round(r["kern_avg_ms"] * 1e3, 3)}}
         if "decode" not in res:
