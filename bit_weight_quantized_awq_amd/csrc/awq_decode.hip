@@ -67,10 +67,15 @@ constexpr float kFxLimit = 8388608.0f;    // 2^23
 // Cross-wave reduction in LDS.  Layout [wave][row group of 4][column][4 rows]
 // (row groups below M only): the lane holding rows 4*kb .. 4*kb+3 of a column
 // writes them as one 16-byte store, and the thread of a column reads each
-// row group of each wave as one conflict-free 16-byte load.
+// row group of each wave as one 16-byte load.  Columns are XOR-swizzled
+// within groups of 16 (bits 1-3 ^= bits 4-6): the 16 lanes of one store
+// instruction (columns 8 apart) then spread over 8 bank groups instead of 2,
+// and 16 consecutive columns still cover 16 distinct bank groups for the
+// loads.
+__device__ __forceinline__ int red_col(int col) { return col ^ (((col >> 4) & 7) << 1); }
 __device__ __forceinline__ void red_store(float* red, int wave, int Mq, int kb, int col,
                                           floatx4 v) {
-  *reinterpret_cast<floatx4*>(red + ((wave * Mq + kb) * kDecodeCols + col) * 4) = v;
+  *reinterpret_cast<floatx4*>(red + ((wave * Mq + kb) * kDecodeCols + red_col(col)) * 4) = v;
 }
 template <int WAVES>
 __device__ __forceinline__ void red_sum(const float* red, int Mq, int M, int col,
@@ -78,10 +83,11 @@ __device__ __forceinline__ void red_sum(const float* red, int Mq, int M, int col
 #pragma unroll
   for (int c4 = 0; c4 < kDecodeMaxM / 4; ++c4) {
     if (4 * c4 < M) {
-      floatx4 v = *reinterpret_cast<const floatx4*>(red + (c4 * kDecodeCols + col) * 4);
+      const int pc = red_col(col);
+      floatx4 v = *reinterpret_cast<const floatx4*>(red + (c4 * kDecodeCols + pc) * 4);
 #pragma unroll
       for (int w = 1; w < WAVES; ++w)
-        v += *reinterpret_cast<const floatx4*>(red + ((w * Mq + c4) * kDecodeCols + col) * 4);
+        v += *reinterpret_cast<const floatx4*>(red + ((w * Mq + c4) * kDecodeCols + pc) * 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) part[4 * c4 + i] = v[i];
     }
@@ -223,6 +229,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     const _Float16* __restrict__ bias, _Float16* __restrict__ y,
     SplitK sk, int M, int K, int N, int g, int G, int splits) {
   extern __shared__ __attribute__((aligned(16))) float red[];  // see red_store
+  pin_arg(y);
+  pin_arg(bias);
+  pin_arg(sk.tickets);
+  pin_arg(sk.acc);
+  pin_arg(sk.mask);
+  pin_arg(sk.partial);
+  pin_arg(sk.ticket_words);
 
   const int NW = N >> 3;
   const int tid = threadIdx.x;
@@ -376,6 +389,13 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
                   const _Float16* __restrict__ bias, _Float16* __restrict__ y,
                   SplitK sk, int M, int K, int N, int g, int G, int splits) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  pin_arg(y);
+  pin_arg(bias);
+  pin_arg(sk.tickets);
+  pin_arg(sk.acc);
+  pin_arg(sk.mask);
+  pin_arg(sk.partial);
+  pin_arg(sk.ticket_words);
   constexpr int kWaveBytes = STEPS * 4 * kLdsBlockPitch;
 
   const int NW = N >> 3;

@@ -47,6 +47,15 @@ __device__ __forceinline__ uint32_t magic_pair(uint32_t paired, int shift) {
 // Buffer resource over [base, base + bytes): loads at offsets outside that
 // range return zero instead of touching memory, so tails need no branches.
 // Offsets are in bytes and must stay below 2^32.
+// Loads a kernel argument into SGPRs now.  The compiler otherwise defers
+// loads of arguments used only in an epilogue until then, where the
+// kernel-argument fetch (~1 us) lands on the critical path; an asm that
+// claims to modify the value also keeps it from being reloaded later.
+template <class T>
+__device__ __forceinline__ void pin_arg(T& v) {
+  asm volatile("" : "+s"(v));
+}
+
 constexpr uint32_t kOutOfRange = 0x80000000u;  // any offset >= the range reads 0
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

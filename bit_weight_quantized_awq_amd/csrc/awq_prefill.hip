@@ -426,6 +426,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* const a_ring = smem;
   char* const b_ring = smem + kStages * kATileBytes;
+  pin_arg(x);
+  pin_arg(qw);
+  pin_arg(qz);
+  pin_arg(sc);
+  pin_arg(bias);
+  pin_arg(y);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Tile t = tile_of(n_tiles);
