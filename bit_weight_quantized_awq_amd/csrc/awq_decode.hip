@@ -39,6 +39,8 @@
 //   and the last one sums them in split order (splitk_ticket).  Every byte
 //   the ticket and accumulator regions of the workspace is zero again when
 //   either exchange ends.
+#include <type_traits>
+
 #include "awq_device.h"
 #include "awq_plan.h"
 
@@ -77,9 +79,21 @@ __device__ __forceinline__ void red_store(float* red, int wave, int Mq, int kb, 
                                           floatx4 v) {
   *reinterpret_cast<floatx4*>(red + ((wave * Mq + kb) * kDecodeCols + red_col(col)) * 4) = v;
 }
+// M == 1: only row 0 (element 0 of the kb == 0 lanes) is stored and read.
+__device__ __forceinline__ void red_store1(float* red, int wave, int col, float v) {
+  red[(wave * kDecodeCols + red_col(col)) * 4] = v;
+}
 template <int WAVES>
 __device__ __forceinline__ void red_sum(const float* red, int Mq, int M, int col,
                                         float (&part)[kDecodeMaxM]) {
+  if (M == 1) {
+    const int pc = red_col(col);
+    float v = red[pc * 4];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) v += red[(w * kDecodeCols + pc) * 4];
+    part[0] = v;
+    return;
+  }
 #pragma unroll
   for (int c4 = 0; c4 < kDecodeMaxM / 4; ++c4) {
     if (4 * c4 < M) {
@@ -376,6 +390,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 // lanes of a transposed read (16 word columns x 4 row blocks) hit 64 distinct
 // banks.
 constexpr int kLdsBlockPitch = 1088;  // 8 rows x 128 bytes + 64-byte skew
+constexpr uint32_t kPairTwo15 = 0x78007800u;  // float16 pair (2^15, 2^15)
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -469,13 +484,17 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
 
   // Byte-pair contraction.  For byte b of a word (nibbles 2b and 2b+1,
   // columns 8c+2b and 8c+2b+1), one byte shuffle per row pair places that
-  // byte of both rows, zero-extended, in the two halves of a register; OR-ing
-  // into float16 1024.0 gives the exact 1024 + (q_even + 16*q_odd), masking
-  // the high nibble first gives 1024 + q_even.  Subtracting the group's
-  // 1024 + (z_even + 16*z_odd) and 1024 + z_even (exact small integers) feeds
-  //   acc_f[b] = sum_k x*((q_e - z_e) + 16*(q_o - z_o)),  acc_e[b] = sum_k x*(q_e - z_e)
-  // to the matrix cores; the odd column is (acc_f - acc_e) / 16.  Five VALU
-  // ops per four weights; q == z and one-hot rows stay exact.
+  // byte of both rows, zero-extended, in the two halves of a register; read
+  // as float16 that is the subnormal byte * 2^-24, and masking the high
+  // nibble gives q_e * 2^-24.  One packed fused multiply-add by 2^15 with the
+  // group's -(zero byte) * 2^-9 (or -z_e * 2^-9) turns each into the exact
+  // normal float16
+  //   f = ((q_e - z_e) + 16*(q_o - z_o)) * 2^-9,  e = (q_e - z_e) * 2^-9,
+  // so the MFMAs sum acc_f[b] = sum_k x*f and acc_e[b] = sum_k x*e, and the
+  // odd column is (acc_f - acc_e) / 16.  Four VALU ops per four weights.
+  // The operands are kept normal because the matrix cores align subnormal
+  // products without normalising them, which costs bits next to a large
+  // activation.  q == z and one-hot rows stay exact.
   floatx4 acc_e[2][4], acc_f[2][4];
   floatx4 tot[2][8];
 #pragma unroll
@@ -485,29 +504,46 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
       acc_e[h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
       acc_f[h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
+    if (!SINGLE_GROUP) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tot[h][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 8; ++j) tot[h][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
   }
 
-  // (1024 + zero byte, 1024 + low zero nibble) pairs of byte b of zero word zw.
-  auto zero_pairs = [](uint32_t zw, int b, half2_t& zf, half2_t& ze) {
+  // -(zero byte) * 2^-9 and -(low zero nibble) * 2^-9 pairs of byte b of zero
+  // word zw (exact: the subnormal byte times -2^15).
+  const half2_t up = as_h2(kPairTwo15);
+  auto zero_pairs = [up](uint32_t zw, int b, half2_t& zf, half2_t& ze) {
     const uint32_t dup = __builtin_amdgcn_perm(zw, zw, 0x0C000C00u | ((4u + b) << 16) | b);
-    zf = as_h2(dup | kMagicPair);
-    ze = as_h2(and_or(dup, kNibblePairMask, kMagicPair));
+    zf = -(as_h2(dup) * up);
+    ze = -(as_h2(dup & kNibblePairMask) * up);
   };
-  // Scale the group partials of set h and add them to the totals.
-  auto fold = [&](int h, half8_t svh) {
+  // Scale the group partials of set h into the totals, elements 0..R-1 (rows
+  // 4*kb + i): added for one group per step, assigned for one group per wave.
+  auto fold = [&](int h, half8_t svh, auto rows) {
+    constexpr int R = decltype(rows)::value;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float se = static_cast<float>(svh[2 * q]);
-      const float so = static_cast<float>(svh[2 * q + 1]) * 0.0625f;
+      const float se = static_cast<float>(svh[2 * q]) * 0x1p9f;
+      const float so = static_cast<float>(svh[2 * q + 1]) * 0x1p5f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        tot[h][2 * q][i] += se * acc_e[h][q][i];
-        tot[h][2 * q + 1][i] += so * (acc_f[h][q][i] - acc_e[h][q][i]);
+      for (int i = 0; i < R; ++i) {
+        const float ve = se * acc_e[h][q][i];
+        const float vo = so * (acc_f[h][q][i] - acc_e[h][q][i]);
+        if (SINGLE_GROUP) {
+          tot[h][2 * q][i] = ve;
+          tot[h][2 * q + 1][i] = vo;
+        } else {
+          tot[h][2 * q][i] += ve;
+          tot[h][2 * q + 1][i] += vo;
+        }
       }
     }
   };
+  using OneRow = std::integral_constant<int, 1>;
+  using FourRows = std::integral_constant<int, 4>;
+  // Only row 0 exists when M == 1 (element 0 of the kb == 0 lanes).
+  const bool one_row = M == 1;
 
   half2_t zf[NG][2][4], ze[NG][2][4];
 #pragma unroll
@@ -548,8 +584,8 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const uint32_t pb = __builtin_amdgcn_perm(w[2 * p + 1], w[2 * p], sel);
-          const half2_t f = as_h2(pb | kMagicPair) - zf[gi][h][q];
-          const half2_t e = as_h2(and_or(pb, kNibblePairMask, kMagicPair)) - ze[gi][h][q];
+          const half2_t f = __builtin_elementwise_fma(as_h2(pb), up, zf[gi][h][q]);
+          const half2_t e = __builtin_elementwise_fma(as_h2(pb & kNibblePairMask), up, ze[gi][h][q]);
           bf[2 * p] = f[0];
           bf[2 * p + 1] = f[1];
           be[2 * p] = e[0];
@@ -559,7 +595,10 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
         acc_f[h][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], bf, acc_f[h][q], 0, 0, 0);
       }
       if (!SINGLE_GROUP) {
-        fold(h, sv[s][h]);
+        if (one_row)
+          fold(h, sv[s][h], OneRow{});
+        else
+          fold(h, sv[s][h], FourRows{});
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           acc_e[h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -568,22 +607,36 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
       }
     }
   }
-  if (SINGLE_GROUP) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) fold(h, sv[0][h]);
-  }
-
   // The four K-ranges meet in LDS (the copy regions are free once every wave
   // is past its last step).  tot[h][j][i] is row 4*kb + i, local column
-  // 8*(16h + col16) + j.
-  __syncthreads();
+  // 8*(16h + col16) + j; with one row only element 0 is formed and stored.
   float* red = reinterpret_cast<float*>(smem);
   const int Mq = (M + 3) >> 2;
-  if (4 * kb < M) {
+  if (one_row) {
+    if (SINGLE_GROUP) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) fold(h, sv[0][h], OneRow{});
+    }
+    __syncthreads();
+    if (kb == 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) red_store(red, wave, Mq, kb, 8 * (16 * h + col16) + j, tot[h][j]);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) red_store1(red, wave, 8 * (16 * h + col16) + j, tot[h][j][0]);
+    }
+  } else {
+    if (SINGLE_GROUP) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) fold(h, sv[0][h], FourRows{});
+    }
+    __syncthreads();
+    if (4 * kb < M) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          red_store(red, wave, Mq, kb, 8 * (16 * h + col16) + j, tot[h][j]);
+    }
   }
   __syncthreads();
 
