@@ -417,8 +417,11 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n_tile = blockIdx.x / splits;
-  const int split = blockIdx.x - n_tile * splits;
+  // Consecutive work-groups take the same rows of neighbouring column tiles,
+  // so the 128-byte segments requested together make up whole rows.
+  const int n_tiles = gridDim.x / splits;
+  const int split = blockIdx.x / n_tiles;
+  const int n_tile = blockIdx.x - split * n_tiles;
   const int col16 = lane & 15;  // MFMA column (B) / row (A) of this lane
   const int kb = lane >> 4;     // 8-row block within a 32-row step
   const int c0 = n_tile * 32;   // first word column of the tile
