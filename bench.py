@@ -182,6 +182,35 @@ def cpu_baseline(p, g, budget_s, sample_rows=None):
     return statistics.median(times), len(times), blas_threads
 
 
+def sweep(torch, awq, dev):
+    """Every point of every named workload, timed like the headline legs."""
+    import awq_inputs
+    for name, w in awq_inputs.WORKLOADS.items():
+        if name.startswith("tiny"):
+            continue                    # launch-bound, a parity case only
+        for g in w.group_sizes:
+            for M in w.Ms:
+                spec = dict(source=name, M=M, group_size=g)
+                steps = 200 if M <= 16 else 50
+                print(f"[sweep] {name} M={M} g={g}", file=sys.stderr, flush=True)
+                r = run_leg(torch, awq, spec, steps, 10, dev)
+                sec = r["ms_per_step"] * 1e-3
+                gbs = r["nbytes"] / sec / 1e9
+                tfs = r["nflops"] / sec / 1e12
+                hbm = M <= 16
+                print(json.dumps({
+                    "workload": name, "M": M, "K": r["K"], "N": r["N"], "group_size": g,
+                    "bias": r["p"]["bias"] is not None, "kernel": r["path"],
+                    "us_per_call": round(r["ms_per_step"] * 1e3, 3),
+                    "GB_per_s": round(gbs, 1), "TFLOP_per_s": round(tfs, 2),
+                    "bound": "hbm" if hbm else "mfma",
+                    "frac": round(gbs / HBM_PEAK_GBS if hbm else tfs / FP16_MFMA_PEAK_TFLOPS, 4),
+                    "bytes": r["nbytes"], "flops": r["nflops"], "copies_rotated": r["R"]}),
+                    flush=True)
+                del r
+                torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +219,10 @@ def main():
     ap.add_argument("--legs", default="decode,prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline line, print one JSON line per point of "
+                         "every named workload (all batch sizes and group sizes), each "
+                         "against its binding roof: HBM for M <= 16, MFMA for larger M")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -206,6 +239,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     awq.lib()
+    if args.sweep:
+        sweep(torch, awq, dev)
+        return
     legs = args.legs.split(",")
     res = {}
     for name, spec in (("decode", DECODE), ("prefill", PREFILL)):

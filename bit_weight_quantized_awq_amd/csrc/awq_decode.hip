@@ -187,6 +187,38 @@ __device__ __forceinline__ void splitk_atomic(const float (&part)[kDecodeMaxM], 
 // work-group is in place before its ticket is taken, and the work-group that
 // takes the last ticket sees all of them.  It sums them in split order and
 // resets the ticket.
+// Sum over the splits, in split order, of rows 0..ROWS-1 of one column of
+// the partials (p points at column n of split 0, row 0).  Device-scope loads
+// come from memory at a latency of a microsecond or more, so each round
+// issues every row of BATCH splits before using any; indices past the last
+// split or row are clamped (the loads stay unconditional, without branches)
+// and their values dropped.
+template <int BATCH, int ROWS>
+__device__ __forceinline__ void ticket_sum(const float* p, int M, int N, int splits,
+                                           float (&sum)[kDecodeMaxM]) {
+  const size_t stride = static_cast<size_t>(M) * N;
+#pragma unroll
+  for (int m = 0; m < kDecodeMaxM; ++m) sum[m] = 0.f;
+  for (int sp = 0; sp < splits; sp += BATCH) {
+    float v[BATCH][ROWS];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int su = min(sp + u, splits - 1);
+#pragma unroll
+      for (int m = 0; m < ROWS; ++m)
+        v[u][m] = __hip_atomic_load(p + su * stride + static_cast<size_t>(min(m, M - 1)) * N,
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const bool ok = sp + u < splits;
+#pragma unroll
+      for (int m = 0; m < ROWS; ++m) sum[m] += ok ? v[u][m] : 0.f;
+    }
+  }
+}
+
+template <int BATCH>
 __device__ __forceinline__ void splitk_ticket(const float (&part)[kDecodeMaxM], const SplitK& sk,
                                               const _Float16* __restrict__ bias,
                                               _Float16* __restrict__ y, int M, int N, int n,
@@ -210,23 +242,16 @@ __device__ __forceinline__ void splitk_ticket(const float (&part)[kDecodeMaxM], 
   if (!s_last) return;
   if (nvalid) {
     const float b = bias ? static_cast<float>(bias[n]) : 0.f;
-    const size_t stride = static_cast<size_t>(M) * N;
-    for (int m = 0; m < M; ++m) {
-      float* p = sk.partial + static_cast<size_t>(m) * N + n;
-      float sum = 0.f;
-      int sp = 0;
-      for (; sp + 16 <= splits; sp += 16) {
-        float v[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          v[u] = __hip_atomic_load(p + (sp + u) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int u = 0; u < 16; ++u) sum += v[u];
-      }
-      for (; sp < splits; ++sp)
-        sum += __hip_atomic_load(p + sp * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      y[m * N + n] = static_cast<_Float16>(sum + b);
+    float sum[kDecodeMaxM];
+    switch ((M + 3) >> 2) {
+      case 1: ticket_sum<BATCH, 4>(sk.partial + n, M, N, splits, sum); break;
+      case 2: ticket_sum<BATCH, 8>(sk.partial + n, M, N, splits, sum); break;
+      case 3: ticket_sum<BATCH, 12>(sk.partial + n, M, N, splits, sum); break;
+      default: ticket_sum<BATCH, 16>(sk.partial + n, M, N, splits, sum); break;
     }
+#pragma unroll
+    for (int m = 0; m < kDecodeMaxM; ++m)
+      if (m < M) y[m * N + n] = static_cast<_Float16>(sum[m] + b);
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -371,7 +396,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   if (M <= kDecodeAtomicMaxM && N <= kDecodeAtomicMaxN) {
     if (nvalid) splitk_atomic(part, sk, bias, y, M, N, n, split, splits);
   } else {
-    splitk_ticket(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
+    splitk_ticket<2>(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
   }
 }
 
@@ -654,7 +679,7 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   if (M <= kDecodeAtomicMaxM && N <= kDecodeAtomicMaxN) {
     if (nvalid) splitk_atomic(part, sk, bias, y, M, N, n, split, splits);
   } else {
-    splitk_ticket(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
+    splitk_ticket<8>(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
   }
 }
 
