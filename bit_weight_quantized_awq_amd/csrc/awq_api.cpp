@@ -32,10 +32,14 @@ size_t awq_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_si
   Problem p;
   if (awq::validate_shape(M, K, N, group_size, &p) != AWQ_SUCCESS) return 0;
   const awq::Alignment al{true, true, true};
-  if (!awq::decode_supported(p, al)) return 0;
+  size_t need = 0;
   Plan pl;
-  if (awq::make_plan(p, al, AWQ_PATH_DECODE, &pl) != AWQ_SUCCESS) return 0;
-  return pl.ws_bytes;
+  if (awq::decode_supported(p, al) && awq::make_plan(p, al, AWQ_PATH_DECODE, &pl) == AWQ_SUCCESS)
+    need = pl.ws_bytes;
+  if (awq::prefill_supported(p, al) && awq::make_plan(p, al, AWQ_PATH_PREFILL, &pl) == AWQ_SUCCESS &&
+      pl.ws_bytes > need)
+    need = pl.ws_bytes;
+  return need;
 }
 
 int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size, const void* x,
@@ -95,7 +99,7 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void*
       break;
     case AWQ_PATH_PREFILL:
       e = awq::launch_prefill(xh, qw, qz, sc, bh, yh, iM, iK, iN, pl.group_shift, pl.m_tiles,
-                                pl.n_tiles, s);
+                              pl.n_tiles, pl.splits, pl.steps, workspace, s);
       break;
     case AWQ_PATH_GENERIC:
       e = awq::launch_generic(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, s);

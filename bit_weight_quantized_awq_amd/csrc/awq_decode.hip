@@ -188,11 +188,11 @@ __device__ __forceinline__ void splitk_atomic(const float (&part)[kDecodeMaxM], 
 // takes the last ticket sees all of them.  It sums them in split order and
 // resets the ticket.
 // Sum over the splits, in split order, of rows 0..ROWS-1 of one column of
-// the partials (p points at column n of split 0, row 0).  Device-scope loads
-// come from memory at a latency of a microsecond or more, so each round
-// issues every row of BATCH splits before using any; indices past the last
-// split or row are clamped (the loads stay unconditional, without branches)
-// and their values dropped.
+// the partials (p points at column n of split 0, row 0).  The caller has
+// invalidated this CU's caches (acquire), so plain loads see every split's
+// stores.  Each round issues every row of BATCH splits before using any;
+// indices past the last split or row are clamped (the loads stay
+// unconditional, without branches) and their values dropped.
 template <int BATCH, int ROWS>
 __device__ __forceinline__ void ticket_sum(const float* p, int M, int N, int splits,
                                            float (&sum)[kDecodeMaxM]) {
@@ -206,8 +206,7 @@ __device__ __forceinline__ void ticket_sum(const float* p, int M, int N, int spl
       const int su = min(sp + u, splits - 1);
 #pragma unroll
       for (int m = 0; m < ROWS; ++m)
-        v[u][m] = __hip_atomic_load(p + su * stride + static_cast<size_t>(min(m, M - 1)) * N,
-                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v[u][m] = p[su * stride + static_cast<size_t>(min(m, M - 1)) * N];
     }
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
@@ -240,6 +239,9 @@ __device__ __forceinline__ void splitk_ticket(const float (&part)[kDecodeMaxM], 
               static_cast<unsigned>(splits - 1));
   __syncthreads();
   if (!s_last) return;
+  // Acquire: drop this CU's and this XCD's cached copies, so the plain loads
+  // of the partials fetch what the other splits stored.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (nvalid) {
     const float b = bias ? static_cast<float>(bias[n]) : 0.f;
     float sum[kDecodeMaxM];

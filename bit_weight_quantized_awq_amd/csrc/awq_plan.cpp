@@ -100,6 +100,15 @@ bool prefill_supported(const Problem& p, const Alignment& al) {
          (p.G == 1 || (p.g >= 4 && log2_exact(p.g) >= 0));
 }
 
+// AWQ_PREFILL_SPLITS (tuning and tests): 1..kPrefillMaxSplits overrides
+// the prefill split count (each split keeps at least one K step).
+static int prefill_splits_override() {
+  const char* s = getenv("AWQ_PREFILL_SPLITS");
+  if (!s) return 0;
+  const int v = atoi(s);
+  return (v >= 1 && v <= kPrefillMaxSplits) ? v : 0;
+}
+
 static int decode_steps_override() {
   const char* s = getenv("AWQ_DECODE_STEPS");
   if (!s) return 0;
@@ -151,6 +160,24 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
     pl.m_tiles = static_cast<int>(ceil_div(p.M, kPrefillBM));
     pl.n_tiles = static_cast<int>(ceil_div(p.N, kPrefillBN));
     pl.group_shift = p.G == 1 ? 31 : log2_exact(p.g);
+    // Split K when the tiles alone leave CUs idle and K is long enough.
+    const int64_t nkt = ceil_div(p.K, kPrefillBK);
+    const int64_t tiles = static_cast<int64_t>(pl.m_tiles) * pl.n_tiles;
+    int64_t splits = 1;
+    if (tiles > 0 && tiles < kPrefillTargetWGs) {
+      splits = kPrefillTargetWGs / tiles;
+      if (splits > kPrefillMaxSplits) splits = kPrefillMaxSplits;
+      if (splits > nkt / kPrefillMinSplitSteps) splits = nkt / kPrefillMinSplitSteps;
+      if (splits < 2) splits = 1;
+    }
+    if (const int o = prefill_splits_override()) splits = o < nkt ? o : nkt;
+    const int64_t kps = ceil_div(nkt, splits);
+    splits = ceil_div(nkt, kps);   // no empty split
+    pl.splits = static_cast<int>(splits);
+    pl.steps = static_cast<int>(kps);
+    if (splits > 1)
+      pl.ws_bytes = kTicketRegionBytes + kAtomicRegionBytes +
+                    static_cast<size_t>(splits) * p.M * p.N * sizeof(float);
   }
   *out = pl;
   return AWQ_SUCCESS;

@@ -34,6 +34,15 @@ constexpr size_t kAtomicRegionBytes = static_cast<size_t>(kDecodeAtomicMaxM) * k
 constexpr int kPrefillBM = 256;
 constexpr int kPrefillBN = 128;
 constexpr int kPrefillBK = 64;
+// Prefill split K: shapes with fewer output tiles than kPrefillTargetWGs
+// (one work-group per CU) split the K steps over up to kPrefillMaxSplits
+// work-groups per tile, each with at least kPrefillMinSplitSteps steps; a
+// second kernel sums the fp32 partials.  The workspace has the decode
+// exchange's layout (so one buffer serves both): the ticket and accumulator
+// regions (unused here, left zero), then [splits][M][N] partials.
+constexpr int kPrefillTargetWGs = 256;
+constexpr int kPrefillMaxSplits = 8;
+constexpr int kPrefillMinSplitSteps = 8;
 
 struct Problem {
   int64_t M, K, N;
@@ -43,8 +52,8 @@ struct Problem {
 
 struct Plan {
   int path;          // awq_path value
-  int steps;         // decode: 32-row steps per wave
-  int splits;        // decode: work-groups along K per column tile
+  int steps;         // decode: 32-row steps per wave; prefill: K steps per split
+  int splits;        // work-groups along K per output tile (decode and prefill)
   int n_tiles;       // column tiles
   int m_tiles;       // prefill: row tiles
   size_t ws_bytes;   // workspace bytes

@@ -129,18 +129,30 @@ struct Frag {
   half8_t b[2];
 };
 
-// Tile coordinates of this work-group.  Work-group ids are remapped so that
-// each of the 8 XCDs (which receive ids round-robin) works on a contiguous
-// range of tiles that share rows of x.
+// Tile coordinates and K range of this work-group.  Work-group ids are
+// remapped so that each of the 8 XCDs (which receive ids round-robin) works
+// on a contiguous range of ids; ids run over the tiles of split 0, then of
+// split 1, ..., so an XCD's tiles share rows of x and the same K range.
 struct Tile {
-  int m0, n0;
+  int m0, n0;    // first row and column
+  int tile;      // tile index (row-tile major)
+  int sp;        // split index
+  int kt0, nks;  // first K step and number of K steps of the split
 };
-__device__ __forceinline__ Tile tile_of(int n_tiles) {
+__device__ __forceinline__ Tile tile_of(int n_tiles, int splits, int kps, int nkt) {
   int bid = blockIdx.x;
   const int nb = gridDim.x;
   if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
-  const int mt = bid / n_tiles;
-  return Tile{mt * BM, (bid - mt * n_tiles) * BN};
+  const int tiles = nb / splits;
+  Tile t;
+  t.sp = bid / tiles;
+  t.tile = bid - t.sp * tiles;
+  const int mt = t.tile / n_tiles;
+  t.m0 = mt * BM;
+  t.n0 = (t.tile - mt * n_tiles) * BN;
+  t.kt0 = t.sp * kps;
+  t.nks = min(kps, nkt - t.kt0);
+  return t;
 }
 
 // Producer waves (4 of the 8): every global load of the tile and the
@@ -164,7 +176,7 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
   const int lane = pt & 63;
   const int NW = N >> 3;
   const int G = gsh >= 31 ? 1 : (K >> gsh);
-  const int nkt = (K + BK - 1) / BK;
+  const int nks = t.nks;   // K steps of this split, from step t.kt0
   const v4i rx = raw_rsrc(x, static_cast<uint32_t>(M) * K * 2u);
   const v4i rq = raw_rsrc(qw, static_cast<uint32_t>(K) * NW * 4u);
   const v4i rz = raw_rsrc(qz, static_cast<uint32_t>(G) * NW * 4u);
@@ -209,7 +221,7 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
     uint32_t sq, sz, ss, oob;
   };
   auto step_a = [&](int k) {
-    const int kb = min(k, nkt - 1) * BK;
+    const int kb = (t.kt0 + min(k, nks - 1)) * BK;
     StepA p;
     p.soff = static_cast<uint32_t>(kb) * 2u;
     p.oob0 = (KTAIL && 8 * a_chunk0 >= K - kb) ? kOutOfRange : 0u;
@@ -217,7 +229,7 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
     return p;
   };
   auto step_b = [&](int k) {
-    const int kb = min(k, nkt - 1) * BK;
+    const int kb = (t.kt0 + min(k, nks - 1)) * BK;
     const uint32_t gb = static_cast<uint32_t>(kb >> gsh);
     StepB p;
     p.sq = static_cast<uint32_t>(kb) * q_row;
@@ -300,13 +312,13 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
     }
   };
   int kt = 0;
-  for (; kt + 2 < nkt; kt += 3) {
+  for (; kt + 2 < nks; kt += 3) {
     pstep(kt, 0);
     pstep(kt + 1, 1);
     pstep(kt + 2, 2);
   }
-  if (kt < nkt) pstep(kt, 0);
-  if (kt + 1 < nkt) pstep(kt + 1, 1);
+  if (kt < nks) pstep(kt, 0);
+  if (kt + 1 < nks) pstep(kt + 1, 1);
   // Drain the trailing prefetches.  Their destination registers are tied
   // through the wait so that none is reused while a load is still in flight.
   asm volatile("s_waitcnt vmcnt(0)"
@@ -324,11 +336,12 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
 // is multiplied after the next step's barrier, overlapping that step's first
 // reads.  Each slice runs as four sub-blocks of two LDS reads and two MFMAs.
 __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Float16* __restrict__ y,
-                                         int M, int K, int N, Tile t, const char* a_ring,
-                                         const char* b_ring, int wave, int lane) {
+                                         float* __restrict__ partial, int M, int N, int splits,
+                                         Tile t, const char* a_ring, const char* b_ring, int wave,
+                                         int lane) {
   const int wm = wave >> 1;
   const int wn = wave & 1;
-  const int nkt = (K + BK - 1) / BK;
+  const int nkt = t.nks;
   // Operand addressing.  A: lane -> row (lane % 32) of a 32-row block,
   // logical 16-byte chunk 2*ks + lane/32.  B (transposed read): 16-lane group
   // gr = lane / 16 -> columns 16*(gr % 2) .. +15, k-block gr / 2; source lane
@@ -395,18 +408,24 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[mi], cur.b[ni], acc[mi][ni], 0, 0, 0);
 
   // Epilogue: 32x32 block output, lane holds column (lane % 32) and rows
-  // 8*(r/4) + 4*(lane/32) + r%4 of register r.
+  // 8*(r/4) + 4*(lane/32) + r%4 of register r.  One split: y = acc + bias.
+  // Several: the fp32 partial of this split (summed by prefill_reduce_kernel).
+  float* const pp = partial + static_cast<size_t>(t.sp) * M * N;
 #pragma unroll
   for (int ni = 0; ni < 2; ++ni) {
     const int col = t.n0 + 64 * wn + 32 * ni + frow;
     if (col >= N) continue;
-    const float b = bias ? static_cast<float>(bias[col]) : 0.f;
+    const float b = (bias && splits == 1) ? static_cast<float>(bias[col]) : 0.f;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = t.m0 + 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < M) y[row * N + col] = static_cast<_Float16>(acc[mi][ni][r] + b);
+        if (row >= M) continue;
+        if (splits == 1)
+          y[row * N + col] = static_cast<_Float16>(acc[mi][ni][r] + b);
+        else
+          pp[static_cast<size_t>(row) * N + col] = acc[mi][ni][r];
       }
     }
   }
@@ -417,12 +436,17 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
 // each SIMD runs one of each and the producer's vector work co-issues with
 // the consumer's matrix-core work.  Both roles pass the same number of
 // barriers (one per K step).
+//
+// Split K (few tiles): work-group (tile, split) covers kps K steps and
+// stores its fp32 partial; prefill_reduce_kernel, next on the stream, sums
+// them.
 template <bool KTAIL>
 __global__ __launch_bounds__(512) void prefill_kernel(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
     const _Float16* __restrict__ bias, _Float16* __restrict__ y,
-    int M, int K, int N, int gsh, int n_tiles) {
+    int M, int K, int N, int gsh, int n_tiles, int splits, int kps,
+    float* __restrict__ partial) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* const a_ring = smem;
   char* const b_ring = smem + kStages * kATileBytes;
@@ -432,13 +456,54 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   pin_arg(sc);
   pin_arg(bias);
   pin_arg(y);
+  pin_arg(partial);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const Tile t = tile_of(n_tiles);
+  const Tile t = tile_of(n_tiles, splits, kps, (K + BK - 1) / BK);
   if (wave >= 4)
     producer<KTAIL>(x, qw, qz, sc, M, K, N, gsh, t, a_ring, b_ring, wave - 4, tid - 256);
   else
-    consumer(bias, y, M, K, N, t, a_ring, b_ring, wave, tid & 63);
+    consumer(bias, y, partial, M, N, splits, t, a_ring, b_ring, wave, tid & 63);
+}
+
+// y = sum of the split partials, in split order (deterministic), + bias.
+// Thread i takes four adjacent outputs (N % 8 == 0, so a quad never crosses
+// a row): 16-byte loads of each split's partials (the workspace is 16-byte
+// aligned), one 8-byte store when y allows it, else 2-byte ones.  SB bounds
+// the split count: loads past the last split are clamped (unconditional, so
+// all are in flight together) and their values dropped.
+template <int SB>
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(const float* __restrict__ partial,
+                                                             const _Float16* __restrict__ bias,
+                                                             _Float16* __restrict__ y, int M, int N,
+                                                             int splits) {
+  const size_t plane = static_cast<size_t>(M) * N;
+  const size_t e = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (e >= plane) return;
+  floatx4 v[SB];
+#pragma unroll
+  for (int u = 0; u < SB; ++u)
+    v[u] = *reinterpret_cast<const floatx4*>(partial + min(u, splits - 1) * plane + e);
+  floatx4 sum = v[0];
+#pragma unroll
+  for (int u = 1; u < SB; ++u) {
+    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+    sum += (u < splits) ? v[u] : zero;
+  }
+  if (bias) {
+    const _Float16* bq = bias + e % N;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sum[q] += static_cast<float>(bq[q]);
+  }
+  half4_t o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = static_cast<_Float16>(sum[q]);
+  if ((reinterpret_cast<uintptr_t>(y) & 7) == 0) {
+    *reinterpret_cast<half4_t*>(y + e) = o;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[e + q] = o[q];
+  }
 }
 
 }  // namespace
@@ -446,13 +511,35 @@ __global__ __launch_bounds__(512) void prefill_kernel(
 hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                           const _Float16* scales, const _Float16* bias, _Float16* y,
                           int M, int K, int N, int group_shift, int m_tiles, int n_tiles,
-                          hipStream_t stream) {
+                          int splits, int ksteps, void* workspace, hipStream_t stream) {
+  // Workspace (split K only), laid out like the decode exchange's so that
+  // one buffer serves both: the ticket and accumulator regions (left
+  // untouched, they must stay zero), then [splits][M][N] partials.
+  char* ws = static_cast<char*>(workspace);
+  float* partial =
+      ws ? reinterpret_cast<float*>(ws + kTicketRegionBytes + kAtomicRegionBytes) : nullptr;
+  const dim3 grid(m_tiles * n_tiles * splits);
   if (K % BK == 0)
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3(m_tiles * n_tiles), dim3(512), kLdsBytes,
-                       stream, x, qweight, qzeros, scales, bias, y, M, K, N, group_shift, n_tiles);
+    hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(512), kLdsBytes, stream, x, qweight,
+                       qzeros, scales, bias, y, M, K, N, group_shift, n_tiles, splits, ksteps,
+                       partial);
   else
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3(m_tiles * n_tiles), dim3(512), kLdsBytes,
-                       stream, x, qweight, qzeros, scales, bias, y, M, K, N, group_shift, n_tiles);
+    hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(512), kLdsBytes, stream, x, qweight,
+                       qzeros, scales, bias, y, M, K, N, group_shift, n_tiles, splits, ksteps,
+                       partial);
+  if (splits > 1) {
+    const size_t quads = static_cast<size_t>(M) * N / 4;
+    const dim3 rgrid(static_cast<unsigned>((quads + 255) / 256));
+    if (splits <= 2)
+      hipLaunchKernelGGL(prefill_reduce_kernel<2>, rgrid, dim3(256), 0, stream, partial, bias, y,
+                         M, N, splits);
+    else if (splits <= 4)
+      hipLaunchKernelGGL(prefill_reduce_kernel<4>, rgrid, dim3(256), 0, stream, partial, bias, y,
+                         M, N, splits);
+    else
+      hipLaunchKernelGGL(prefill_reduce_kernel<kPrefillMaxSplits>, rgrid, dim3(256), 0, stream,
+                         partial, bias, y, M, N, splits);
+  }
   return hipGetLastError();
 }
 

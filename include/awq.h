@@ -77,9 +77,11 @@ int awq_abi_version(void);
 /* Static, human-readable text for a status code (never NULL). */
 const char* awq_status_string(int status);
 
-/* Bytes of workspace awq_gemm needs for this problem when x and scales are
- * 16-byte aligned (the most any pointer alignment needs).  0 means none.
- * Returns 0 for invalid shapes (awq_gemm then reports the error). */
+/* Bytes of workspace awq_gemm needs for this problem whatever the pointers'
+ * alignment and whichever kernel family runs it (also one forced through
+ * AWQ_FORCE_PATH): the larger of the split-K decode and split-K prefill
+ * needs.  0 means none.  Returns 0 for invalid shapes (awq_gemm then reports
+ * the error). */
 size_t awq_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size);
 
 /* Host-only planning, no HIP call and no dereference of x, qweight or scales

@@ -80,7 +80,19 @@ int main() {
               } else if (pl.path == AWQ_PATH_PREFILL) {
                 EXPECT((int64_t)pl.m_tiles * kPrefillBM >= M);
                 EXPECT((int64_t)pl.n_tiles * kPrefillBN >= N);
-                EXPECT(pl.ws_bytes == 0);
+                const int64_t nkt = (K + kPrefillBK - 1) / kPrefillBK;
+                const int64_t tiles = (int64_t)pl.m_tiles * pl.n_tiles;
+                EXPECT(pl.splits >= 1 && pl.splits <= kPrefillMaxSplits);
+                EXPECT((int64_t)pl.splits * pl.steps >= nkt);
+                EXPECT((int64_t)(pl.splits - 1) * pl.steps < nkt);
+                EXPECT(pl.splits == 1 || (tiles * pl.splits <= kPrefillTargetWGs &&
+                                          pl.steps >= kPrefillMinSplitSteps));
+                EXPECT((tiles > 0 && tiles < kPrefillTargetWGs) || pl.splits == 1);
+                if (pl.splits > 1)
+                  EXPECT(pl.ws_bytes == kTicketRegionBytes + kAtomicRegionBytes +
+                                        (size_t)pl.splits * M * N * 4);
+                else
+                  EXPECT(pl.ws_bytes == 0);
                 EXPECT(p.G == 1 ? pl.group_shift == 31 : (int64_t{1} << pl.group_shift) == p.g);
               }
             }

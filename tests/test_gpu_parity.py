@@ -258,6 +258,9 @@ def test_group_minus_one_bit_identical_to_K(M):
     ("prefill", 513, 208, 264, 16, True),
     ("prefill", 64, 192, 128, 64, False),
     ("prefill", 2, 8, 8, -1, True),
+    ("prefill", 300, 2000, 264, 16, True),    # split K: 4 splits, K tail, ragged M and N
+    ("prefill", 64, 1536, 256, 128, False),   # split K: 3 splits
+    ("prefill", 256, 2048, 512, 128, True),   # split K: 4 splits of whole tiles
     ("generic", 4, 256, 128, 64, True),
     ("generic", 33, 96, 24, 3, True),
     ("generic", 2, 100, 40, -1, False),
@@ -309,7 +312,7 @@ def test_empty_batch_and_leading_dims():
     assert_within_tol(y3.reshape(6, 128).cpu().numpy(), ref, "leading dims")
 
 
-@pytest.mark.parametrize("M", [1, 16, 2048])
+@pytest.mark.parametrize("M", [1, 16, 256, 2048])
 def test_deterministic_repeats(M):
     """Split-K partials are summed in a fixed order: repeats are bitwise equal."""
     say(f"determinism M={M}")
@@ -324,12 +327,14 @@ def test_deterministic_repeats(M):
 
 def test_workspace_reuse_across_shapes():
     """One workspace serves decode calls of different shapes (both exchange
-    modes: M <= 4 atomic, M > 4 ticket) back to back: every call leaves the
-    ticket and accumulator regions zero."""
+    modes: M <= 4 atomic, M > 4 ticket) and split-K prefill calls back to
+    back: every call leaves the ticket and accumulator regions zero."""
     say("workspace reuse")
     ws = torch.zeros(awq.gemm_workspace_size(16, 8192, 7168, 128), dtype=torch.uint8, device=DEV)
-    for (M, K, N) in [(16, 8192, 7168), (1, 8192, 1280), (4, 4096, 2048), (8, 4096, 1280),
-                      (2, 8192, 7168), (16, 8192, 7168)]:
+    shapes = [(16, 8192, 7168), (1, 8192, 1280), (256, 2048, 512), (4, 4096, 2048),
+              (8, 4096, 1280), (64, 1536, 256), (2, 8192, 7168), (16, 8192, 7168)]
+    assert all(awq.gemm_workspace_size(M, K, N, 128) <= ws.numel() for M, K, N in shapes)
+    for (M, K, N) in shapes:
         p = awq_inputs.make_inputs(M, K, N, 128, seed=K + M)
         d = to_dev(p)
         y = awq.gemm(d["x"], d["qweight"], d["qzeros"], d["scales"], None, 128, workspace=ws)

@@ -132,10 +132,44 @@ def test_dequant_validation(kwargs, status):
 def test_plan_selects_kernel(M, K, N, g, path):
     got, ws = awq.gemm_plan(M, K, N, g)
     assert got == path
-    if path == binding.AWQ_PATH_DECODE:
-        assert ws == awq.gemm_workspace_size(M, K, N, g) or ws == 0
-    else:
+    if path == binding.AWQ_PATH_GENERIC:
         assert ws == 0
+    else:
+        assert ws <= awq.gemm_workspace_size(M, K, N, g)
+
+
+def _prefill_splits_expected(M, K, N):
+    """Split-K rule of the prefill kernel, restated: 256 x 128 tiles; when
+    there are fewer tiles than 256 CUs, up to 8 splits (no more than fill
+    the CUs), each of at least 8 K steps of 64, none empty."""
+    tiles = -(-M // 256) * -(-N // 128)
+    nkt = -(-K // 64)
+    s = 1
+    if tiles < 256:
+        s = min(8, 256 // tiles, nkt // 8)
+        s = s if s >= 2 else 1
+    kps = -(-nkt // s)
+    return -(-nkt // kps)
+
+
+@pytest.mark.parametrize("M,K,N,g,splits", [
+    (256, 14336, 4096, 128, 8),
+    (1024, 14336, 4096, 128, 2),
+    (2048, 4096, 12288, 128, 1),
+    (4096, 14336, 4096, -1, 1),
+    (300, 2000, 264, 16, 4),
+    (17, 256, 4096, 128, 1),
+    (64, 1536, 256, 128, 3),
+])
+def test_prefill_split_k_plan(M, K, N, g, splits):
+    """Workspace of a split prefill, laid out like the decode exchange's: the
+    64 KiB ticket region, the 3 MiB accumulator region, then one fp32 partial
+    per split per output element; none without a split."""
+    assert _prefill_splits_expected(M, K, N) == splits
+    path, ws = awq.gemm_plan(M, K, N, g)
+    assert path == binding.AWQ_PATH_PREFILL
+    assert ws == (0 if splits == 1 else 65536 + 4 * 65536 * 12 + splits * M * N * 4)
+    assert awq.gemm_workspace_size(M, K, N, g) == ws
 
 
 def test_plan_unaligned_x_falls_back_to_generic():
