@@ -155,6 +155,51 @@ __device__ __forceinline__ Tile tile_of(int n_tiles, int splits, int kps, int nk
   return t;
 }
 
+// Output staging (one split, y 16-byte aligned): once the K loop is done the
+// x ring is free; the consumers write float16(acc + bias) into it as a
+// row-major 256 x 128 tile (row pitch kOutPitch: the two row groups of one
+// store fall in different banks), then all 512 threads copy it to y with
+// 16-byte loads and stores: a 256-byte row segment per 16 lanes.
+constexpr int kOutPitch = BN * 2 + 16;
+static_assert(BM * kOutPitch <= kStages * kATileBytes, "output tile fits the x ring");
+
+__device__ __forceinline__ void stage_tile(const floatx16 (&acc)[4][2],
+                                           const _Float16* __restrict__ bias, char* stage, int N,
+                                           Tile t, int wave, int lane) {
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) {
+    const int lcol = 64 * wn + 32 * ni + (lane & 31);
+    const int col = t.n0 + lcol;
+    const float b = (bias && col < N) ? static_cast<float>(bias[col]) : 0.f;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lrow = 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        *reinterpret_cast<_Float16*>(stage + lrow * kOutPitch + 2 * lcol) =
+            static_cast<_Float16>(acc[mi][ni][r] + b);
+      }
+    }
+  }
+}
+// tid = 0..511: chunk c = 512*i + tid is 8 columns (16 bytes) of tile row c / 16.
+__device__ __forceinline__ void store_tile(const char* stage, _Float16* __restrict__ y, int M,
+                                           int N, Tile t, int tid) {
+#pragma unroll
+  for (int i = 0; i < BM * BN / 8 / 512; ++i) {
+    const int c = 512 * i + tid;
+    const int lrow = c >> 4;
+    const int lcol = 8 * (c & 15);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * kOutPitch + 2 * lcol);
+    const int row = t.m0 + lrow;
+    const int col = t.n0 + lcol;
+    if (row < M && col < N)
+      *reinterpret_cast<u32x4*>(y + static_cast<size_t>(row) * N + col) = v;
+  }
+}
+
 // Producer waves (4 of the 8): every global load of the tile and the
 // dequantisation of the weight slab into LDS.  pw = producer wave 0..3,
 // pt = producer thread 0..255.
@@ -171,8 +216,9 @@ __device__ __forceinline__ Tile tile_of(int n_tiles, int splits, int kps, int nk
 template <bool KTAIL>
 __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
                                          const uint32_t* __restrict__ qz,
-                                         const _Float16* __restrict__ sc, int M, int K, int N,
-                                         int gsh, Tile t, char* a_ring, char* b_ring, int pw, int pt) {
+                                         const _Float16* __restrict__ sc, _Float16* __restrict__ y,
+                                         int M, int K, int N, int gsh, Tile t, char* a_ring,
+                                         char* b_ring, int pw, int pt, bool staged) {
   const int lane = pt & 63;
   const int NW = N >> 3;
   const int G = gsh >= 31 ? 1 : (K >> gsh);
@@ -328,6 +374,10 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
                  "+v"(w3[2][3]), "+v"(z3[2]), "+v"(s3[2])
                :
                : "memory");
+  if (!staged) return;
+  __syncthreads();   // every wave is done with the ring
+  __syncthreads();   // the consumers have staged the output tile
+  store_tile(a_ring, y, M, N, t, 256 + pt);
 }
 
 // Consumer waves (4 of the 8, a 2 x 2 grid): LDS operand reads and the
@@ -337,8 +387,8 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
 // reads.  Each slice runs as four sub-blocks of two LDS reads and two MFMAs.
 __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Float16* __restrict__ y,
                                          float* __restrict__ partial, int M, int N, int splits,
-                                         Tile t, const char* a_ring, const char* b_ring, int wave,
-                                         int lane) {
+                                         Tile t, char* a_ring, const char* b_ring, int wave,
+                                         int lane, bool staged) {
   const int wm = wave >> 1;
   const int wn = wave & 1;
   const int nkt = t.nks;
@@ -408,8 +458,16 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[mi], cur.b[ni], acc[mi][ni], 0, 0, 0);
 
   // Epilogue: 32x32 block output, lane holds column (lane % 32) and rows
-  // 8*(r/4) + 4*(lane/32) + r%4 of register r.  One split: y = acc + bias.
-  // Several: the fp32 partial of this split (summed by prefill_reduce_kernel).
+  // 8*(r/4) + 4*(lane/32) + r%4 of register r.
+  if (staged) {
+    __syncthreads();   // every wave is done with the ring
+    stage_tile(acc, bias, a_ring, N, t, wave, lane);
+    __syncthreads();
+    store_tile(a_ring, y, M, N, t, 64 * wave + lane);
+    return;
+  }
+  // Otherwise one split: y = acc + bias, 2-byte stores; several: the fp32
+  // partial of this split (summed by prefill_reduce_kernel).
   float* const pp = partial + static_cast<size_t>(t.sp) * M * N;
 #pragma unroll
   for (int ni = 0; ni < 2; ++ni) {
@@ -460,10 +518,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Tile t = tile_of(n_tiles, splits, kps, (K + BK - 1) / BK);
+  const bool staged = splits == 1 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
   if (wave >= 4)
-    producer<KTAIL>(x, qw, qz, sc, M, K, N, gsh, t, a_ring, b_ring, wave - 4, tid - 256);
+    producer<KTAIL>(x, qw, qz, sc, y, M, K, N, gsh, t, a_ring, b_ring, wave - 4, tid - 256,
+                    staged);
   else
-    consumer(bias, y, partial, M, N, splits, t, a_ring, b_ring, wave, tid & 63);
+    consumer(bias, y, partial, M, N, splits, t, a_ring, b_ring, wave, tid & 63, staged);
 }
 
 // y = sum of the split partials, in split order (deterministic), + bias.
