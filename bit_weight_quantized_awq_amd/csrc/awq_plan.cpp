@@ -100,6 +100,14 @@ bool prefill_supported(const Problem& p, const Alignment& al) {
          (p.G == 1 || (p.g >= 4 && log2_exact(p.g) >= 0));
 }
 
+// AWQ_PREFILL_BN (tuning and tests): 128 or 192 forces the prefill tile width.
+static int prefill_bn_override() {
+  const char* s = getenv("AWQ_PREFILL_BN");
+  if (!s) return 0;
+  const int v = atoi(s);
+  return (v == kPrefillBN || v == kPrefillWideBN) ? v : 0;
+}
+
 // AWQ_PREFILL_SPLITS (tuning and tests): 1..kPrefillMaxSplits overrides
 // the prefill split count (each split keeps at least one K step).
 static int prefill_splits_override() {
@@ -158,7 +166,16 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
                     static_cast<size_t>(pl.splits) * p.M * p.N * sizeof(float);
   } else if (path == AWQ_PATH_PREFILL) {
     pl.m_tiles = static_cast<int>(ceil_div(p.M, kPrefillBM));
-    pl.n_tiles = static_cast<int>(ceil_div(p.N, kPrefillBN));
+    // The wide tile does 1.5x a narrow tile's work at about 1.25x its speed
+    // per flop (fewer LDS bytes per flop): take it when it needs no split and
+    // its rounds of work-groups over the CUs cost less.
+    const int64_t r_narrow = ceil_div(pl.m_tiles * ceil_div(p.N, kPrefillBN), kPrefillTargetWGs);
+    const int64_t wide_tiles = pl.m_tiles * ceil_div(p.N, kPrefillWideBN);
+    const int64_t r_wide = ceil_div(wide_tiles, kPrefillTargetWGs);
+    pl.prefill_bn =
+        (wide_tiles >= kPrefillTargetWGs && r_wide * 6 < r_narrow * 5) ? kPrefillWideBN : kPrefillBN;
+    if (const int o = prefill_bn_override()) pl.prefill_bn = o;
+    pl.n_tiles = static_cast<int>(ceil_div(p.N, pl.prefill_bn));
     pl.group_shift = p.G == 1 ? 31 : log2_exact(p.g);
     // Split K when the tiles alone leave CUs idle and K is long enough.
     const int64_t nkt = ceil_div(p.K, kPrefillBK);

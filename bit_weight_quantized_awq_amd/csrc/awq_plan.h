@@ -30,9 +30,12 @@ constexpr int kDecodeAtomicMaxM = 4;
 constexpr int kDecodeAtomicMaxN = 65536;
 constexpr size_t kAtomicRegionBytes = static_cast<size_t>(kDecodeAtomicMaxM) * kDecodeAtomicMaxN * 12;
 
-// Prefill kernel tile.
+// Prefill kernel tile: 256 rows, 128 or 192 columns (the wider tile moves
+// fewer LDS bytes per flop; it is chosen when it also takes fewer rounds of
+// work-groups over the CUs), 64 K rows per step.
 constexpr int kPrefillBM = 256;
 constexpr int kPrefillBN = 128;
+constexpr int kPrefillWideBN = 192;
 constexpr int kPrefillBK = 64;
 // Prefill split K: shapes with fewer output tiles than kPrefillTargetWGs
 // (one work-group per CU) split the K steps over up to kPrefillMaxSplits
@@ -59,6 +62,7 @@ struct Plan {
   size_t ws_bytes;   // workspace bytes
   bool decode_lds;    // decode: LDS-streaming variant (N % 32 == 0) or register variant
   int group_shift;    // prefill: log2(group size), or 31 for a single group
+  int prefill_bn;     // prefill: tile width (kPrefillBN or kPrefillWideBN)
 };
 
 // Checks of the page's WQLinear construction (K % g == 0, N % 8 == 0, the -1

@@ -42,14 +42,26 @@ namespace awq {
 namespace {
 
 constexpr int BM = kPrefillBM;   // 256
-constexpr int BN = kPrefillBN;   // 128
 constexpr int BK = kPrefillBK;   // 64
-constexpr int kStages = 3;
+constexpr int kAStages = 3;
 constexpr int kATileBytes = BM * BK * 2;        // 32 KiB, 128-byte rows
-constexpr int kBPitch = BN * 2 + 64;            // bytes per k-row of the weight tile
-constexpr int kBTileBytes = BK * kBPitch;       // 20 KiB
-constexpr int kLdsBytes = kStages * (kATileBytes + kBTileBytes);   // 156 KiB
 constexpr int kLoadsPerStep = 6 + 8;            // weight words/zeros/scales, x copies
+
+// The two tile widths.  NB: 32-column MFMA blocks per consumer wave; BST:
+// weight-tile buffers (x always has a 3-slot ring).
+template <int BN_> struct Cfg;
+template <> struct Cfg<128> {
+  static constexpr int NB = 2, BST = 3;
+};
+template <> struct Cfg<192> {
+  static constexpr int NB = 3, BST = 2;
+};
+template <int BN> constexpr int b_pitch() { return BN * 2 + 64; }   // bytes per k-row
+template <int BN> constexpr int b_tile_bytes() { return BK * b_pitch<BN>(); }
+template <int BN> constexpr int lds_bytes() {
+  return kAStages * kATileBytes + Cfg<BN>::BST * b_tile_bytes<BN>();
+}
+static_assert(lds_bytes<128>() == 156 * 1024 && lds_bytes<192>() == 152 * 1024, "LDS budget");
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -124,9 +136,10 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, uint32_t ws, int b,
   return as_u32((q2 - zp[b]) * as_h2(sv[b]));
 }
 
+template <int NB>
 struct Frag {
   half8_t a[4];
-  half8_t b[2];
+  half8_t b[NB];
 };
 
 // Tile coordinates and K range of this work-group.  Work-group ids are
@@ -139,6 +152,7 @@ struct Tile {
   int sp;        // split index
   int kt0, nks;  // first K step and number of K steps of the split
 };
+template <int BN>
 __device__ __forceinline__ Tile tile_of(int n_tiles, int splits, int kps, int nkt) {
   int bid = blockIdx.x;
   const int nb = gridDim.x;
@@ -156,21 +170,23 @@ __device__ __forceinline__ Tile tile_of(int n_tiles, int splits, int kps, int nk
 }
 
 // Output staging (one split, y 16-byte aligned): once the K loop is done the
-// x ring is free; the consumers write float16(acc + bias) into it as a
-// row-major 256 x 128 tile (row pitch kOutPitch: the two row groups of one
+// LDS is free; the consumers write float16(acc + bias) into it as a
+// row-major 256 x BN tile (row pitch out_pitch: the two row groups of one
 // store fall in different banks), then all 512 threads copy it to y with
-// 16-byte loads and stores: a 256-byte row segment per 16 lanes.
-constexpr int kOutPitch = BN * 2 + 16;
-static_assert(BM * kOutPitch <= kStages * kATileBytes, "output tile fits the x ring");
+// 16-byte loads and stores.
+template <int BN> constexpr int out_pitch() { return BN * 2 + 16; }
+static_assert(BM * out_pitch<128>() <= lds_bytes<128>() && BM * out_pitch<192>() <= lds_bytes<192>(),
+              "output tile fits the LDS");
 
-__device__ __forceinline__ void stage_tile(const floatx16 (&acc)[4][2],
+template <int BN, int NB>
+__device__ __forceinline__ void stage_tile(const floatx16 (&acc)[4][NB],
                                            const _Float16* __restrict__ bias, char* stage, int N,
                                            Tile t, int wave, int lane) {
   const int wm = wave >> 1;
   const int wn = wave & 1;
 #pragma unroll
-  for (int ni = 0; ni < 2; ++ni) {
-    const int lcol = 64 * wn + 32 * ni + (lane & 31);
+  for (int ni = 0; ni < NB; ++ni) {
+    const int lcol = (BN / 2) * wn + 32 * ni + (lane & 31);
     const int col = t.n0 + lcol;
     const float b = (bias && col < N) ? static_cast<float>(bias[col]) : 0.f;
 #pragma unroll
@@ -178,21 +194,24 @@ __device__ __forceinline__ void stage_tile(const floatx16 (&acc)[4][2],
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int lrow = 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        *reinterpret_cast<_Float16*>(stage + lrow * kOutPitch + 2 * lcol) =
+        *reinterpret_cast<_Float16*>(stage + lrow * out_pitch<BN>() + 2 * lcol) =
             static_cast<_Float16>(acc[mi][ni][r] + b);
       }
     }
   }
 }
-// tid = 0..511: chunk c = 512*i + tid is 8 columns (16 bytes) of tile row c / 16.
+// tid = 0..511: chunk c = 512*i + tid is 8 columns (16 bytes) of tile row
+// c / (BN/8).
+template <int BN>
 __device__ __forceinline__ void store_tile(const char* stage, _Float16* __restrict__ y, int M,
                                            int N, Tile t, int tid) {
+  constexpr int kChunksPerRow = BN / 8;
 #pragma unroll
   for (int i = 0; i < BM * BN / 8 / 512; ++i) {
     const int c = 512 * i + tid;
-    const int lrow = c >> 4;
-    const int lcol = 8 * (c & 15);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * kOutPitch + 2 * lcol);
+    const int lrow = c / kChunksPerRow;
+    const int lcol = 8 * (c - lrow * kChunksPerRow);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * out_pitch<BN>() + 2 * lcol);
     const int row = t.m0 + lrow;
     const int col = t.n0 + lcol;
     if (row < M && col < N)
@@ -210,15 +229,85 @@ __device__ __forceinline__ void store_tile(const char* stage, _Float16* __restri
 // step kt, group kt-2 = {weights of kt+1, x of kt} is complete once at most
 // 14 loads (group kt-1) are outstanding.  Both operands are thus fetched two
 // steps ahead.  Step kt+1's weights are dequantised during step kt into
-// weight buffer (kt+1) % 3.  Three register sets for packed weights rotate
-// (in flight twice, being dequantised once); the loop is unrolled by three
-// so that sets, ring slots and LDS addresses are static.
-template <bool KTAIL>
+// weight buffer (kt+1) % BST.  Three register sets for packed weights rotate
+// (in flight twice, being dequantised once); the loop is unrolled so that
+// sets, ring slots, buffers and LDS addresses are static.
+//
+// Weight loader, by tile width.  BN = 128: word column pt % 16 of the tile,
+// rows 4*(pt/16) .. +3 of a step (four 4-byte loads, one zero word, one
+// 16-byte scale load).  BN = 192: word columns 3*(pt%8) .. +2, rows
+// 2*(pt/8) and +1 (two 16-byte loads of which three words are used, one
+// 16-byte zero load, three 16-byte scale loads).  Either way 6 loads.  The
+// group of row k is k >> gsh (gsh = 31 for a single group); a thread's rows
+// of a step share one group (groups are at least 4 rows, aligned).  For
+// BN = 192, words and scales past the last column are read from wherever
+// they fall (the next row, or zero past the end of the buffer): they only
+// reach outputs that are never stored.
+template <int BN>
+struct WSet;
+template <>
+struct WSet<128> {
+  uint32_t w[4];
+  uint32_t z;
+  u32x4 s;
+};
+template <>
+struct WSet<192> {
+  u32x4 w[2];
+  u32x4 z;
+  u32x4 s[3];
+};
+template <int N>
+__device__ __forceinline__ void wait_set(WSet<128>& r) {
+  asm volatile("s_waitcnt vmcnt(%6)"
+               : "+v"(r.w[0]), "+v"(r.w[1]), "+v"(r.w[2]), "+v"(r.w[3]), "+v"(r.z), "+v"(r.s)
+               : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void wait_set(WSet<192>& r) {
+  asm volatile("s_waitcnt vmcnt(%6)"
+               : "+v"(r.w[0]), "+v"(r.w[1]), "+v"(r.z), "+v"(r.s[0]), "+v"(r.s[1]), "+v"(r.s[2])
+               : "n"(N));
+}
+// Wait for everything; every register set is tied so that none is reused
+// while a load into it is still in flight.
+__device__ __forceinline__ void drain_sets(WSet<128> (&r)[3]) {
+  asm volatile("s_waitcnt vmcnt(0)"
+               : "+v"(r[0].w[0]), "+v"(r[0].w[1]), "+v"(r[0].w[2]), "+v"(r[0].w[3]), "+v"(r[0].z),
+                 "+v"(r[0].s), "+v"(r[1].w[0]), "+v"(r[1].w[1]), "+v"(r[1].w[2]), "+v"(r[1].w[3]),
+                 "+v"(r[1].z), "+v"(r[1].s), "+v"(r[2].w[0]), "+v"(r[2].w[1]), "+v"(r[2].w[2]),
+                 "+v"(r[2].w[3]), "+v"(r[2].z), "+v"(r[2].s)
+               :
+               : "memory");
+}
+__device__ __forceinline__ void drain_sets(WSet<192> (&r)[3]) {
+  asm volatile("s_waitcnt vmcnt(0)"
+               : "+v"(r[0].w[0]), "+v"(r[0].w[1]), "+v"(r[0].z), "+v"(r[0].s[0]), "+v"(r[0].s[1]),
+                 "+v"(r[0].s[2]), "+v"(r[1].w[0]), "+v"(r[1].w[1]), "+v"(r[1].z), "+v"(r[1].s[0]),
+                 "+v"(r[1].s[1]), "+v"(r[1].s[2]), "+v"(r[2].w[0]), "+v"(r[2].w[1]), "+v"(r[2].z),
+                 "+v"(r[2].s[0]), "+v"(r[2].s[1]), "+v"(r[2].s[2])
+               :
+               : "memory");
+}
+
+// The dequantised halves of one packed word (8 columns of one k-row).
+__device__ __forceinline__ u32x4 dequant_word(uint32_t w, const half2_t (&zp)[4], u32x4 sv) {
+  const uint32_t ws = w >> 4;
+  u32x4 out;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) out[b] = dequant_pair(w, ws, b, zp, sv);
+  return out;
+}
+
+template <int BN, bool KTAIL>
 __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
                                          const uint32_t* __restrict__ qz,
                                          const _Float16* __restrict__ sc, _Float16* __restrict__ y,
                                          int M, int K, int N, int gsh, Tile t, char* a_ring,
                                          char* b_ring, int pw, int pt, bool staged) {
+  using C = Cfg<BN>;
+  constexpr int kBPitch = b_pitch<BN>();
+  constexpr int kBTileBytes = b_tile_bytes<BN>();
   const int lane = pt & 63;
   const int NW = N >> 3;
   const int G = gsh >= 31 ? 1 : (K >> gsh);
@@ -243,19 +332,17 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
     const int m = min(t.m0 + 64 * pw + 8 * i + a_lrow, M - 1);
     a_off[i] = static_cast<uint32_t>(m * K + 8 * ((i & 1) ? a_chunk1 : a_chunk0)) * 2u;
   }
-  // Weight loader: word column bwc of the tile, rows 4*brb .. 4*brb+3 of a
-  // step; the group of row k is k >> gsh (gsh = 31 for a single group), so
-  // rows 4*brb.. of the step at row kb lie in group (kb >> gsh) + (4*brb >> gsh).
-  const int bwc = pt & 15;
-  const int brb = pt >> 4;
-  const int bc = min((t.n0 >> 3) + bwc, NW - 1);
+  // Weight loader lane offsets (see above).
+  constexpr int WR = BN == 128 ? 4 : 2;   // k-rows per thread
+  const int wrow = BN == 128 ? 4 * (pt >> 4) : 2 * (pt >> 3);
+  const int wcol = BN == 128 ? min((t.n0 >> 3) + (pt & 15), NW - 1) : (t.n0 >> 3) + 3 * (pt & 7);
   const uint32_t q_row = static_cast<uint32_t>(NW) * 4u;
-  uint32_t q_off[4];
+  uint32_t q_off[WR];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) q_off[r] = static_cast<uint32_t>((4 * brb + r) * NW + bc) * 4u;
-  const uint32_t z_off = static_cast<uint32_t>(((4 * brb) >> gsh) * NW + bc) * 4u;
-  const uint32_t s_off = static_cast<uint32_t>(((4 * brb) >> gsh) * N + 8 * bc) * 2u;
-  char* const b_wr0 = b_ring + (4 * brb) * kBPitch + 16 * bwc;
+  for (int r = 0; r < WR; ++r) q_off[r] = static_cast<uint32_t>((wrow + r) * NW + wcol) * 4u;
+  const uint32_t z_off = static_cast<uint32_t>((wrow >> gsh) * NW + wcol) * 4u;
+  const uint32_t s_off = static_cast<uint32_t>((wrow >> gsh) * N + 8 * wcol) * 2u;
+  char* const b_wr0 = b_ring + wrow * kBPitch + (BN == 128 ? 16 * (pt & 15) : 48 * (pt & 7));
 
   // Per-step load parameters: uniform offsets of step k (clamped to the last
   // step; prefetches past the end re-read it and are never used) and, for a
@@ -281,17 +368,25 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
     p.sq = static_cast<uint32_t>(kb) * q_row;
     p.sz = gb * q_row;
     p.ss = gb * static_cast<uint32_t>(N) * 2u;
-    p.oob = (KTAIL && 4 * brb >= K - kb) ? kOutOfRange : 0u;
+    p.oob = (KTAIL && wrow >= K - kb) ? kOutOfRange : 0u;
     return p;
   };
-  uint32_t w3[3][4];
-  uint32_t z3[3];
-  u32x4 s3[3];
+  WSet<BN> ws[3];
+  // Load number u (0..5) of one step's weight group into set `set`.
+  auto load_b = [&](const StepB& p, int set, int u) {
+    if constexpr (BN == 128) {
+      if (u < 4) ws[set].w[u] = load_u32(rq, q_off[u] | p.oob, p.sq);
+      if (u == 4) ws[set].z = load_u32(rz, z_off | p.oob, p.sz);
+      if (u == 5) ws[set].s = load_u32x4(rs, s_off | p.oob, p.ss);
+    } else {
+      if (u < 2) ws[set].w[u] = load_u32x4(rq, q_off[u] | p.oob, p.sq);
+      if (u == 2) ws[set].z = load_u32x4(rz, z_off | p.oob, p.sz);
+      if (u >= 3) ws[set].s[u - 3] = load_u32x4(rs, (s_off + 16u * (u - 3)) | p.oob, p.ss);
+    }
+  };
   auto issue_b = [&](const StepB& p, int set) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) w3[set][r] = load_u32(rq, q_off[r] | p.oob, p.sq);
-    z3[set] = load_u32(rz, z_off | p.oob, p.sz);
-    s3[set] = load_u32x4(rs, s_off | p.oob, p.ss);
+    for (int u = 0; u < 6; ++u) load_b(p, set, u);
   };
   auto issue_a = [&](const StepA& p, int slot) {
     const uint32_t base = lds_addr(a_ring + slot * kATileBytes) + 64 * pw * 128;
@@ -300,17 +395,30 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
       copy_to_lds(rx, a_off[i] | ((i & 1) ? p.oob1 : p.oob0), p.soff,
                   __builtin_amdgcn_readfirstlane(base + 8 * i * 128));
   };
+  // Dequantisation unit u of a set: BN = 128: row u (0..3); BN = 192:
+  // word column u / 2, row u % 2 (0..5).  New zero pairs at each new column.
+  constexpr int kUnits = BN == 128 ? 4 : 6;
+  auto new_zero = [](int u) { return u == 0 || (BN == 192 && (u & 1) == 0); };
+  auto zero_of = [&](int set, int u) -> uint32_t {
+    if constexpr (BN == 128) return ws[set].z;
+    else return ws[set].z[u >> 1];
+  };
+  auto dequant_unit = [&](int buf, int set, int u, const half2_t (&zp)[4]) {
+    char* const dst = b_wr0 + static_cast<uint32_t>(buf) * kBTileBytes;
+    if constexpr (BN == 128) {
+      *reinterpret_cast<u32x4*>(dst + u * kBPitch) = dequant_word(ws[set].w[u], zp, ws[set].s);
+    } else {
+      const int c = u >> 1, r = u & 1;
+      *reinterpret_cast<u32x4*>(dst + r * kBPitch + 16 * c) =
+          dequant_word(ws[set].w[r][c], zp, ws[set].s[c]);
+    }
+  };
   auto dequant_to = [&](int buf, int set) {
     half2_t zp[4];
-    zero_pairs(z3[set], zp);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t w = w3[set][r];
-      const uint32_t ws = w >> 4;
-      u32x4 out;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) out[b] = dequant_pair(w, ws, b, zp, s3[set]);
-      *reinterpret_cast<u32x4*>(b_wr0 + buf * kBTileBytes + r * kBPitch) = out;
+    for (int u = 0; u < kUnits; ++u) {
+      if (new_zero(u)) zero_pairs(zero_of(set, u), zp);
+      dequant_unit(buf, set, u, zp);
     }
   };
 
@@ -320,18 +428,21 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
   issue_a(step_a(0), 0);
   issue_b(step_b(2), 2);
   issue_a(step_a(1), 1);
-  wait_regs<2 * kLoadsPerStep>(w3[0], z3[0], s3[0]);
+  wait_set<2 * kLoadsPerStep>(ws[0]);
   dequant_to(0, 0);
 
-  // j = kt % 3: set j receives step kt+3, set (j+1) % 3 holds step kt+1.
+  // Step kt: j = kt % 3.  Set j receives step kt+3; set (j+1) % 3 holds
+  // step kt+1, dequantised into buffer (kt+1) % BST (static for BST = 3,
+  // computed per step otherwise).
   auto pstep = [&](int kt, int j) {
     const int jd = (j + 1) % 3;
-    wait_regs<kLoadsPerStep>(w3[jd], z3[jd], s3[jd]);  // x of kt, weights of kt+1
+    const int bd = C::BST == 3 ? jd : (kt + 1) % C::BST;
+    wait_set<kLoadsPerStep>(ws[jd]);                    // x of kt, weights of kt+1
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // weight tile kt written
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // Loads are spread between the four dequantised words, so that the wave
-    // never stalls behind a full load queue with vector work pending.
+    // Loads are spread between the dequantised words, so that the wave never
+    // stalls behind a full load queue with vector work pending.
     const StepB pb = step_b(kt + 3);
     const StepA pa = step_a(kt + 2);
     const uint32_t abase = lds_addr(a_ring + ((j + 2) % 3) * kATileBytes) + 64 * pw * 128;
@@ -340,20 +451,25 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
                   __builtin_amdgcn_readfirstlane(abase + 8 * i * 128));
     };
     half2_t zp[4];
-    zero_pairs(z3[jd], zp);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      w3[j][r] = load_u32(rq, q_off[r] | pb.oob, pb.sq);
-      dma(2 * r);
-      if (r == 1) z3[j] = load_u32(rz, z_off | pb.oob, pb.sz);
-      if (r == 2) s3[j] = load_u32x4(rs, s_off | pb.oob, pb.ss);
-      dma(2 * r + 1);
-      const uint32_t w = w3[jd][r];
-      const uint32_t ws = w >> 4;
-      u32x4 out;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) out[b] = dequant_pair(w, ws, b, zp, s3[jd]);
-      *reinterpret_cast<u32x4*>(b_wr0 + jd * kBTileBytes + r * kBPitch) = out;
+    for (int u = 0; u < kUnits; ++u) {
+      if constexpr (BN == 128) {
+        load_b(pb, j, u);
+        dma(2 * u);
+        if (u == 1) load_b(pb, j, 4);
+        if (u == 2) load_b(pb, j, 5);
+        dma(2 * u + 1);
+      } else {
+        load_b(pb, j, u);
+        if (u < 2) {
+          dma(2 * u);
+          dma(2 * u + 1);
+        } else {
+          dma(u + 2);
+        }
+      }
+      if (new_zero(u)) zero_pairs(zero_of(jd, u), zp);
+      dequant_unit(bd, jd, u, zp);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -365,113 +481,158 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
   }
   if (kt < nks) pstep(kt, 0);
   if (kt + 1 < nks) pstep(kt + 1, 1);
-  // Drain the trailing prefetches.  Their destination registers are tied
-  // through the wait so that none is reused while a load is still in flight.
-  asm volatile("s_waitcnt vmcnt(0)"
-               : "+v"(w3[0][0]), "+v"(w3[0][1]), "+v"(w3[0][2]), "+v"(w3[0][3]), "+v"(z3[0]),
-                 "+v"(s3[0]), "+v"(w3[1][0]), "+v"(w3[1][1]), "+v"(w3[1][2]), "+v"(w3[1][3]),
-                 "+v"(z3[1]), "+v"(s3[1]), "+v"(w3[2][0]), "+v"(w3[2][1]), "+v"(w3[2][2]),
-                 "+v"(w3[2][3]), "+v"(z3[2]), "+v"(s3[2])
-               :
-               : "memory");
+  drain_sets(ws);
   if (!staged) return;
-  __syncthreads();   // every wave is done with the ring
+  __syncthreads();   // every wave is done with the LDS
   __syncthreads();   // the consumers have staged the output tile
-  store_tile(a_ring, y, M, N, t, 256 + pt);
+  store_tile<BN>(a_ring, y, M, N, t, 256 + pt);
 }
 
 // Consumer waves (4 of the 8, a 2 x 2 grid): LDS operand reads and the
-// matrix-core work for a 128 x 64 sub-tile each, then the epilogue.  LDS
-// operands are read one k slice ahead of the MFMAs; the last slice of a step
-// is multiplied after the next step's barrier, overlapping that step's first
-// reads.  Each slice runs as four sub-blocks of two LDS reads and two MFMAs.
+// matrix-core work for a 128 x (BN/2) sub-tile each (4 x NB blocks of
+// 32 x 32), then the epilogue.  LDS operands are read one k slice ahead of
+// the MFMAs; the last slice of a step is multiplied after the next step's
+// barrier, overlapping that step's first reads.  Each slice runs as four
+// sub-blocks of LDS reads (one x block, and the weight blocks spread over
+// the four) and NB MFMAs.
+template <int BN>
 __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Float16* __restrict__ y,
                                          float* __restrict__ partial, int M, int N, int splits,
                                          Tile t, char* a_ring, const char* b_ring, int wave,
                                          int lane, bool staged) {
+  using C = Cfg<BN>;
+  constexpr int NB = C::NB;
+  constexpr int kBPitch = b_pitch<BN>();
+  constexpr int kBTileBytes = b_tile_bytes<BN>();
+  // The narrow tile keeps two operand sets (reads a slice ahead into nxt);
+  // the wide one's 4 x 3 accumulator blocks (192 registers) leave room for
+  // one, replaced in place.
   const int wm = wave >> 1;
   const int wn = wave & 1;
   const int nkt = t.nks;
   // Operand addressing.  A: lane -> row (lane % 32) of a 32-row block,
   // logical 16-byte chunk 2*ks + lane/32.  B (transposed read): 16-lane group
-  // gr = lane / 16 -> columns 16*(gr % 2) .. +15, k-block gr / 2; source lane
-  // s = lane % 16 reads k-row s/4 (+4 for the second half), columns 4*(s%4)..
+  // gr = lane / 16 -> columns 16*(gr % 2) .. +15 of a 32-column block, k-block
+  // gr / 2; source lane s = lane % 16 reads k-row s/4 (+4 for the second
+  // half), columns 4*(s%4) ..
   const int frow = lane & 31;
   const int fhalf = lane >> 5;
   const int gr = lane >> 4;
   const int sl = lane & 15;
-  const int b_col = 64 * wn + 16 * (gr & 1) + 4 * (sl & 3);
+  const int b_col = (BN / 2) * wn + 16 * (gr & 1) + 4 * (sl & 3);
   const int b_krow = 8 * (gr >> 1) + (sl >> 2);
   const char* const b_rd0 = b_ring + b_krow * kBPitch + 2 * b_col;
 
-  floatx16 acc[4][2];
+  floatx16 acc[4][NB];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < NB; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-  Frag cur, nxt;
+  Frag<NB> cur, nxt;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) cur.a[mi] = half8_t{};
-  cur.b[0] = half8_t{};
-  cur.b[1] = half8_t{};
+#pragma unroll
+  for (int ni = 0; ni < NB; ++ni) cur.b[ni] = half8_t{};
 
-  auto cstep = [&](int j) {
+  // Weight read number q (0 .. 2*NB-1) of a slice: block q / 2, k-rows +4*(q%2).
+  // Step with x slot j and weight buffer jb: static for the narrow tile
+  // (loop unrolled by 3), computed per step for the wide one, whose
+  // registers leave no room for an address per slot.
+  auto cstep = [&](int j, int jb) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of step kt-1 done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const char* a_slot = a_ring + j * kATileBytes;
-    const char* b_rd = b_rd0 + j * kBTileBytes;
+    const char* a_slot = a_ring + static_cast<uint32_t>(j) * kATileBytes;
+    const char* b_rd = b_rd0 + static_cast<uint32_t>(jb) * kBTileBytes;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      short4_t raw[4];
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
+      auto a_src = [&](int sub) {
         const int row = 128 * wm + 32 * sub + frow;
         const int chunk = (2 * ks + fhalf) ^ ((row >> 1) & 7);
-        nxt.a[sub] = *reinterpret_cast<const half8_t*>(a_slot + row * 128 + 16 * chunk);
-        raw[sub] = read_tr16(b_rd + 16 * ks * kBPitch + 64 * (sub >> 1) + (sub & 1) * 4 * kBPitch);
-        acc[sub][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[sub], cur.b[0], acc[sub][0], 0, 0, 0);
-        acc[sub][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[sub], cur.b[1], acc[sub][1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+        return reinterpret_cast<const half8_t*>(a_slot + row * 128 + 16 * chunk);
+      };
+      auto b_src = [&](int q) {
+        return b_rd + 16 * ks * kBPitch + 64 * (q >> 1) + (q & 1) * 4 * kBPitch;
+      };
+      if constexpr (NB == 2) {
+        short4_t raw[4];
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        nxt.b[ni] = __builtin_bit_cast(
-            half8_t, __builtin_shufflevector(raw[2 * ni], raw[2 * ni + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-      cur = nxt;
+        for (int sub = 0; sub < 4; ++sub) {
+          nxt.a[sub] = *a_src(sub);
+          raw[sub] = read_tr16(b_src(sub));
+#pragma unroll
+          for (int ni = 0; ni < NB; ++ni)
+            acc[sub][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[sub], cur.b[ni],
+                                                                  acc[sub][ni], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int ni = 0; ni < NB; ++ni)
+          nxt.b[ni] = __builtin_bit_cast(
+              half8_t, __builtin_shufflevector(raw[2 * ni], raw[2 * ni + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+        cur = nxt;
+      } else {
+        // Weight-block major, every operand replaced in place by the next
+        // slice's as soon as its last MFMA of this slice is issued: block ni
+        // after its four MFMAs, x block sub after the last block's.
+#pragma unroll
+        for (int ni = 0; ni < NB; ++ni) {
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub) {
+            acc[sub][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[sub], cur.b[ni],
+                                                                  acc[sub][ni], 0, 0, 0);
+            if (ni == NB - 1) cur.a[sub] = *a_src(sub);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          const short4_t lo = read_tr16(b_src(2 * ni));
+          const short4_t hi = read_tr16(b_src(2 * ni + 1));
+          cur.b[ni] =
+              __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
   };
-  int kt = 0;
-  for (; kt + 2 < nkt; kt += 3) {
-    cstep(0);
-    cstep(1);
-    cstep(2);
+  if constexpr (C::BST == 3) {
+    int kt = 0;
+    for (; kt + 2 < nkt; kt += 3) {
+      cstep(0, 0);
+      cstep(1, 1);
+      cstep(2, 2);
+    }
+    if (kt < nkt) cstep(0, 0);
+    if (kt + 1 < nkt) cstep(1, 1);
+  } else {
+    int j = 0;
+#pragma unroll 1
+    for (int kt = 0; kt < nkt; ++kt) {
+      cstep(__builtin_amdgcn_readfirstlane(j), kt & 1);
+      j = j == 2 ? 0 : j + 1;
+    }
   }
-  if (kt < nkt) cstep(0);
-  if (kt + 1 < nkt) cstep(1);
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < NB; ++ni)
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[mi], cur.b[ni], acc[mi][ni], 0, 0, 0);
 
   // Epilogue: 32x32 block output, lane holds column (lane % 32) and rows
   // 8*(r/4) + 4*(lane/32) + r%4 of register r.
   if (staged) {
-    __syncthreads();   // every wave is done with the ring
-    stage_tile(acc, bias, a_ring, N, t, wave, lane);
+    __syncthreads();   // every wave is done with the LDS
+    stage_tile<BN, NB>(acc, bias, a_ring, N, t, wave, lane);
     __syncthreads();
-    store_tile(a_ring, y, M, N, t, 64 * wave + lane);
+    store_tile<BN>(a_ring, y, M, N, t, 64 * wave + lane);
     return;
   }
   // Otherwise one split: y = acc + bias, 2-byte stores; several: the fp32
   // partial of this split (summed by prefill_reduce_kernel).
   float* const pp = partial + static_cast<size_t>(t.sp) * M * N;
 #pragma unroll
-  for (int ni = 0; ni < 2; ++ni) {
-    const int col = t.n0 + 64 * wn + 32 * ni + frow;
+  for (int ni = 0; ni < NB; ++ni) {
+    const int col = t.n0 + (BN / 2) * wn + 32 * ni + frow;
     if (col >= N) continue;
     const float b = (bias && splits == 1) ? static_cast<float>(bias[col]) : 0.f;
 #pragma unroll
@@ -493,12 +654,12 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
 // and dequantisation).  Waves are spread over the 4 SIMDs round-robin, so
 // each SIMD runs one of each and the producer's vector work co-issues with
 // the consumer's matrix-core work.  Both roles pass the same number of
-// barriers (one per K step).
+// barriers (one per K step, two more when the output is staged).
 //
 // Split K (few tiles): work-group (tile, split) covers kps K steps and
 // stores its fp32 partial; prefill_reduce_kernel, next on the stream, sums
 // them.
-template <bool KTAIL>
+template <int BN, bool KTAIL>
 __global__ __launch_bounds__(512) void prefill_kernel(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
@@ -507,7 +668,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     float* __restrict__ partial) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* const a_ring = smem;
-  char* const b_ring = smem + kStages * kATileBytes;
+  char* const b_ring = smem + kAStages * kATileBytes;
   pin_arg(x);
   pin_arg(qw);
   pin_arg(qz);
@@ -517,13 +678,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   pin_arg(partial);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const Tile t = tile_of(n_tiles, splits, kps, (K + BK - 1) / BK);
+  const Tile t = tile_of<BN>(n_tiles, splits, kps, (K + BK - 1) / BK);
   const bool staged = splits == 1 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
   if (wave >= 4)
-    producer<KTAIL>(x, qw, qz, sc, y, M, K, N, gsh, t, a_ring, b_ring, wave - 4, tid - 256,
-                    staged);
+    producer<BN, KTAIL>(x, qw, qz, sc, y, M, K, N, gsh, t, a_ring, b_ring, wave - 4, tid - 256,
+                        staged);
   else
-    consumer(bias, y, partial, M, N, splits, t, a_ring, b_ring, wave, tid & 63, staged);
+    consumer<BN>(bias, y, partial, M, N, splits, t, a_ring, b_ring, wave, tid & 63, staged);
 }
 
 // y = sum of the split partials, in split order (deterministic), + bias.
@@ -570,8 +731,9 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float* __rest
 
 hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                           const _Float16* scales, const _Float16* bias, _Float16* y,
-                          int M, int K, int N, int group_shift, int m_tiles, int n_tiles,
-                          int splits, int ksteps, void* workspace, hipStream_t stream) {
+                          int M, int K, int N, int group_shift, int bn, int m_tiles,
+                          int n_tiles, int splits, int ksteps, void* workspace,
+                          hipStream_t stream) {
   // Workspace (split K only), laid out like the decode exchange's so that
   // one buffer serves both: the ticket and accumulator regions (left
   // untouched, they must stay zero), then [splits][M][N] partials.
@@ -579,14 +741,26 @@ hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint
   float* partial =
       ws ? reinterpret_cast<float*>(ws + kTicketRegionBytes + kAtomicRegionBytes) : nullptr;
   const dim3 grid(m_tiles * n_tiles * splits);
-  if (K % BK == 0)
-    hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(512), kLdsBytes, stream, x, qweight,
-                       qzeros, scales, bias, y, M, K, N, group_shift, n_tiles, splits, ksteps,
-                       partial);
-  else
-    hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(512), kLdsBytes, stream, x, qweight,
-                       qzeros, scales, bias, y, M, K, N, group_shift, n_tiles, splits, ksteps,
-                       partial);
+  const bool tail = K % BK != 0;
+  if (bn == 192) {
+    if (tail)
+      hipLaunchKernelGGL((prefill_kernel<192, true>), grid, dim3(512), lds_bytes<192>(), stream,
+                         x, qweight, qzeros, scales, bias, y, M, K, N, group_shift, n_tiles,
+                         splits, ksteps, partial);
+    else
+      hipLaunchKernelGGL((prefill_kernel<192, false>), grid, dim3(512), lds_bytes<192>(), stream,
+                         x, qweight, qzeros, scales, bias, y, M, K, N, group_shift, n_tiles,
+                         splits, ksteps, partial);
+  } else {
+    if (tail)
+      hipLaunchKernelGGL((prefill_kernel<128, true>), grid, dim3(512), lds_bytes<128>(), stream,
+                         x, qweight, qzeros, scales, bias, y, M, K, N, group_shift, n_tiles,
+                         splits, ksteps, partial);
+    else
+      hipLaunchKernelGGL((prefill_kernel<128, false>), grid, dim3(512), lds_bytes<128>(), stream,
+                         x, qweight, qzeros, scales, bias, y, M, K, N, group_shift, n_tiles,
+                         splits, ksteps, partial);
+  }
   if (splits > 1) {
     const size_t quads = static_cast<size_t>(M) * N / 4;
     const dim3 rgrid(static_cast<unsigned>((quads + 255) / 256));

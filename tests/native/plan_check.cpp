@@ -79,7 +79,9 @@ int main() {
                   EXPECT(pl.ws_bytes == 0);
               } else if (pl.path == AWQ_PATH_PREFILL) {
                 EXPECT((int64_t)pl.m_tiles * kPrefillBM >= M);
-                EXPECT((int64_t)pl.n_tiles * kPrefillBN >= N);
+                EXPECT(pl.prefill_bn == kPrefillBN || pl.prefill_bn == kPrefillWideBN);
+                EXPECT((int64_t)pl.n_tiles * pl.prefill_bn >= N);
+                EXPECT((int64_t)(pl.n_tiles - 1) * pl.prefill_bn < N);
                 const int64_t nkt = (K + kPrefillBK - 1) / kPrefillBK;
                 const int64_t tiles = (int64_t)pl.m_tiles * pl.n_tiles;
                 EXPECT(pl.splits >= 1 && pl.splits <= kPrefillMaxSplits);

@@ -64,20 +64,24 @@ def assert_within_tol(gpu, ref, what):
             f"gpu={gpu[tuple(i)]!r} ref={ref[tuple(i)]!r}; max err {err.max():.3e}")
 
 
-def run_gemm(d, path=None, M=None):
+def run_gemm(d, path=None, M=None, env=None):
+    """awq_gemm on device inputs d; path forces a kernel family, env sets
+    further planning variables for the call only."""
     x = d["x"] if M is None else d["x"][:M]
-    old = os.environ.get("AWQ_FORCE_PATH")
+    env = dict(env or {})
+    if path is not None:
+        env["AWQ_FORCE_PATH"] = path
+    old = {k: os.environ.get(k) for k in env}
     try:
-        if path is not None:
-            os.environ["AWQ_FORCE_PATH"] = path
+        os.environ.update(env)
         y = awq.gemm(x, d["qweight"], d["qzeros"], d["scales"], d["bias"], d["group_size"])
         torch.cuda.synchronize()
     finally:
-        if path is not None:
-            if old is None:
-                os.environ.pop("AWQ_FORCE_PATH", None)
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
             else:
-                os.environ["AWQ_FORCE_PATH"] = old
+                os.environ[k] = v
     return y.cpu().numpy()
 
 
@@ -273,6 +277,50 @@ def test_forced_path_and_tails(path, M, K, N, g, bias):
     y = run_gemm(d, path=path)
     ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
     assert_within_tol(y, ref, f"{path} M={M} K={K} N={N} g={g}")
+
+
+WIDE = {"AWQ_PREFILL_BN": "192"}
+
+
+@pytest.mark.parametrize("M,K,N,g,bias", [
+    (300, 2000, 264, 16, True),    # K tail, ragged M, N = 192 + 72
+    (513, 208, 392, 8, False),     # three row tiles, N = 2 * 192 + 8
+    (256, 1024, 384, 128, True),   # whole tiles
+    (64, 1536, 200, -1, True),     # one group, N = 192 + 8
+    (1024, 4096, 768, 128, True),  # split K with the wide tile
+])
+def test_prefill_wide_tile(M, K, N, g, bias):
+    """The 256 x 192 prefill tile, forced, on shapes that cut through its
+    column blocks, row blocks and K steps."""
+    say(f"wide prefill M={M} K={K} N={N} g={g}")
+    p = awq_inputs.make_inputs(M, K, N, g, seed=M + 3 * K + N, bias=bias)
+    d = to_dev(p)
+    y = run_gemm(d, path="prefill", env=WIDE)
+    ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
+    assert_within_tol(y, ref, f"wide M={M} K={K} N={N} g={g}")
+
+
+def test_prefill_wide_tile_exact_cases():
+    """One-hot rows reproduce the dequantised rows bit for bit (positive
+    scales: a weight of -0.0 would come out as +0.0, a sum that starts from
+    zero) and q == z gives the bias bit for bit (scales of both signs)
+    through the wide tile."""
+    say("wide prefill exact cases")
+    M, K, N, g = 300, 1024, 456, 64
+    p = awq_inputs.make_inputs(M, K, N, g, seed=21, bias=True)
+    w = oracle.dequant(p["qweight"], p["qzeros"], p["scales"], g)
+    ks = np.random.default_rng(5).choice(K, M)
+    x = np.zeros((M, K), dtype=np.float16)
+    x[np.arange(M), ks] = 1.0
+    d = to_dev(dict(p, x=x, bias=None))
+    y = run_gemm(d, path="prefill", env=WIDE)
+    np.testing.assert_array_equal(y.view(np.uint16), w[ks].view(np.uint16))
+    p = awq_inputs.make_inputs(M, K, N, g, seed=22, bias=True, scale_lo=-1, scale_hi=1)
+    p["qweight"] = np.repeat(p["qzeros"], g, axis=0)
+    d = to_dev(p)
+    y = run_gemm(d, path="prefill", env=WIDE)
+    np.testing.assert_array_equal(y.view(np.uint16),
+                                  np.broadcast_to(p["bias"], (M, N)).view(np.uint16))
 
 
 @pytest.mark.parametrize("M", [2, 3, 17, 31, 255])
