@@ -98,8 +98,9 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void*
                              pl.n_tiles, pl.decode_lds, workspace, s);
       break;
     case AWQ_PATH_PREFILL:
-      e = awq::launch_prefill(xh, qw, qz, sc, bh, yh, iM, iK, iN, pl.group_shift, pl.prefill_bn,
-                              pl.m_tiles, pl.n_tiles, pl.splits, pl.steps, workspace, s);
+      e = awq::launch_prefill(xh, qw, qz, sc, bh, yh, iM, iK, iN, pl.group_shift, pl.prefill_bm,
+                              pl.prefill_bn, pl.m_tiles, pl.n_tiles, pl.splits, pl.steps,
+                              workspace, s);
       break;
     case AWQ_PATH_GENERIC:
       e = awq::launch_generic(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, s);

@@ -105,7 +105,7 @@ hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint3
                          int n_tiles, bool lds_variant, void* workspace, hipStream_t stream);
 hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                           const _Float16* scales, const _Float16* bias, _Float16* y,
-                          int M, int K, int N, int group_shift, int bn, int m_tiles,
-                          int n_tiles, int splits, int ksteps, void* workspace,
+                          int M, int K, int N, int group_shift, int bm, int bn,
+                          int m_tiles, int n_tiles, int splits, int ksteps, void* workspace,
                           hipStream_t stream);
 }  // namespace awq

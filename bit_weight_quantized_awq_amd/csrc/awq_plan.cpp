@@ -108,6 +108,14 @@ static int prefill_bn_override() {
   return (v == kPrefillBN || v == kPrefillWideBN) ? v : 0;
 }
 
+// AWQ_PREFILL_BM (tuning and tests): 64, 128 or 256 forces the tile height.
+static int prefill_bm_override() {
+  const char* s = getenv("AWQ_PREFILL_BM");
+  if (!s) return 0;
+  const int v = atoi(s);
+  return (v == kPrefillMinBM || v == 2 * kPrefillMinBM || v == kPrefillBM) ? v : 0;
+}
+
 // AWQ_PREFILL_SPLITS (tuning and tests): 1..kPrefillMaxSplits overrides
 // the prefill split count (each split keeps at least one K step).
 static int prefill_splits_override() {
@@ -165,16 +173,22 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
       pl.ws_bytes = kTicketRegionBytes + kAtomicRegionBytes +
                     static_cast<size_t>(pl.splits) * p.M * p.N * sizeof(float);
   } else if (path == AWQ_PATH_PREFILL) {
-    pl.m_tiles = static_cast<int>(ceil_div(p.M, kPrefillBM));
-    // The wide tile does 1.5x a narrow tile's work at about 1.25x its speed
-    // per flop (fewer LDS bytes per flop): take it when it needs no split and
-    // its rounds of work-groups over the CUs cost less.
+    pl.prefill_bm = p.M <= kPrefillMinBM ? kPrefillMinBM
+                                         : (p.M <= 2 * kPrefillMinBM ? 2 * kPrefillMinBM : kPrefillBM);
+    if (const int o = prefill_bm_override()) pl.prefill_bm = o;
+    pl.m_tiles = static_cast<int>(ceil_div(p.M, pl.prefill_bm));
+    // The wide tile (256 rows only) does 1.5x a narrow tile's work at a
+    // little more speed per flop (fewer LDS bytes per flop): take it when it
+    // needs no split and its rounds of work-groups over the CUs cost less.
     const int64_t r_narrow = ceil_div(pl.m_tiles * ceil_div(p.N, kPrefillBN), kPrefillTargetWGs);
     const int64_t wide_tiles = pl.m_tiles * ceil_div(p.N, kPrefillWideBN);
     const int64_t r_wide = ceil_div(wide_tiles, kPrefillTargetWGs);
-    pl.prefill_bn =
-        (wide_tiles >= kPrefillTargetWGs && r_wide * 6 < r_narrow * 5) ? kPrefillWideBN : kPrefillBN;
+    pl.prefill_bn = (pl.prefill_bm == kPrefillBM && wide_tiles >= kPrefillTargetWGs &&
+                     r_wide * 6 < r_narrow * 5)
+                        ? kPrefillWideBN
+                        : kPrefillBN;
     if (const int o = prefill_bn_override()) pl.prefill_bn = o;
+    if (pl.prefill_bm != kPrefillBM) pl.prefill_bn = kPrefillBN;   // 192 needs 256 rows
     pl.n_tiles = static_cast<int>(ceil_div(p.N, pl.prefill_bn));
     pl.group_shift = p.G == 1 ? 31 : log2_exact(p.g);
     // Split K when the tiles alone leave CUs idle and K is long enough.

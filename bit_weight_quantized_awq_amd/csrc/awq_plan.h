@@ -30,10 +30,13 @@ constexpr int kDecodeAtomicMaxM = 4;
 constexpr int kDecodeAtomicMaxN = 65536;
 constexpr size_t kAtomicRegionBytes = static_cast<size_t>(kDecodeAtomicMaxM) * kDecodeAtomicMaxN * 12;
 
-// Prefill kernel tile: 256 rows, 128 or 192 columns (the wider tile moves
-// fewer LDS bytes per flop; it is chosen when it also takes fewer rounds of
+// Prefill kernel tile: 64, 128 or 256 rows (the smallest that covers the
+// batch, so small batches waste no matrix-core work on padding rows), 128
+// or 192 columns (192 only with 256 rows: the wider tile moves fewer LDS
+// bytes per flop; it is chosen when it also takes fewer rounds of
 // work-groups over the CUs), 64 K rows per step.
 constexpr int kPrefillBM = 256;
+constexpr int kPrefillMinBM = 64;
 constexpr int kPrefillBN = 128;
 constexpr int kPrefillWideBN = 192;
 constexpr int kPrefillBK = 64;
@@ -63,6 +66,7 @@ struct Plan {
   bool decode_lds;    // decode: LDS-streaming variant (N % 32 == 0) or register variant
   int group_shift;    // prefill: log2(group size), or 31 for a single group
   int prefill_bn;     // prefill: tile width (kPrefillBN or kPrefillWideBN)
+  int prefill_bm;     // prefill: tile height (64, 128 or kPrefillBM)
 };
 
 // Checks of the page's WQLinear construction (K % g == 0, N % 8 == 0, the -1

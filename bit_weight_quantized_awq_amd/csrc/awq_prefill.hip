@@ -41,27 +41,30 @@
 namespace awq {
 namespace {
 
-constexpr int BM = kPrefillBM;   // 256
 constexpr int BK = kPrefillBK;   // 64
 constexpr int kAStages = 3;
-constexpr int kATileBytes = BM * BK * 2;        // 32 KiB, 128-byte rows
-constexpr int kLoadsPerStep = 6 + 8;            // weight words/zeros/scales, x copies
 
-// The two tile widths.  NB: 32-column MFMA blocks per consumer wave; BST:
-// weight-tile buffers (x always has a 3-slot ring).
-template <int BN_> struct Cfg;
-template <> struct Cfg<128> {
-  static constexpr int NB = 2, BST = 3;
-};
-template <> struct Cfg<192> {
-  static constexpr int NB = 3, BST = 2;
+// Tile shapes BM x BN: BM = 64, 128 or 256 rows (the smallest covering the
+// batch, up to 256), BN = 128 or 192 columns (192 with 256 rows only).
+//   MI: 32-row MFMA blocks per consumer wave (its sub-tile is BM/2 x BN/2)
+//   NB: 32-column MFMA blocks per consumer wave
+//   BST: weight-tile buffers (x always has a 3-slot ring)
+//   NDMA: x copies per producer thread per step (8 rows of 128 bytes each)
+template <int BM, int BN>
+struct Cfg {
+  static_assert((BM == 64 || BM == 128 || BM == 256) && (BN == 128 || (BN == 192 && BM == 256)),
+                "tile shape");
+  static constexpr int MI = BM / 64, NB = BN / 64, BST = BN == 192 ? 2 : 3, NDMA = BM / 32;
+  static constexpr int kATileBytes = BM * BK * 2;
+  static constexpr int kLoadsPerStep = 6 + NDMA;   // weight words/zeros/scales, x copies
 };
 template <int BN> constexpr int b_pitch() { return BN * 2 + 64; }   // bytes per k-row
 template <int BN> constexpr int b_tile_bytes() { return BK * b_pitch<BN>(); }
-template <int BN> constexpr int lds_bytes() {
-  return kAStages * kATileBytes + Cfg<BN>::BST * b_tile_bytes<BN>();
+template <int BM, int BN> constexpr int lds_bytes() {
+  return kAStages * Cfg<BM, BN>::kATileBytes + Cfg<BM, BN>::BST * b_tile_bytes<BN>();
 }
-static_assert(lds_bytes<128>() == 156 * 1024 && lds_bytes<192>() == 152 * 1024, "LDS budget");
+static_assert(lds_bytes<256, 128>() == 156 * 1024 && lds_bytes<256, 192>() == 152 * 1024,
+              "LDS budget");
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -136,9 +139,9 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, uint32_t ws, int b,
   return as_u32((q2 - zp[b]) * as_h2(sv[b]));
 }
 
-template <int NB>
+template <int MI, int NB>
 struct Frag {
-  half8_t a[4];
+  half8_t a[MI];
   half8_t b[NB];
 };
 
@@ -152,7 +155,7 @@ struct Tile {
   int sp;        // split index
   int kt0, nks;  // first K step and number of K steps of the split
 };
-template <int BN>
+template <int BM, int BN>
 __device__ __forceinline__ Tile tile_of(int n_tiles, int splits, int kps, int nkt) {
   int bid = blockIdx.x;
   const int nb = gridDim.x;
@@ -175,11 +178,14 @@ __device__ __forceinline__ Tile tile_of(int n_tiles, int splits, int kps, int nk
 // store fall in different banks), then all 512 threads copy it to y with
 // 16-byte loads and stores.
 template <int BN> constexpr int out_pitch() { return BN * 2 + 16; }
-static_assert(BM * out_pitch<128>() <= lds_bytes<128>() && BM * out_pitch<192>() <= lds_bytes<192>(),
+static_assert(256 * out_pitch<128>() <= lds_bytes<256, 128>() &&
+                  256 * out_pitch<192>() <= lds_bytes<256, 192>() &&
+                  128 * out_pitch<128>() <= lds_bytes<128, 128>() &&
+                  64 * out_pitch<128>() <= lds_bytes<64, 128>(),
               "output tile fits the LDS");
 
-template <int BN, int NB>
-__device__ __forceinline__ void stage_tile(const floatx16 (&acc)[4][NB],
+template <int BM, int BN, int MI, int NB>
+__device__ __forceinline__ void stage_tile(const floatx16 (&acc)[MI][NB],
                                            const _Float16* __restrict__ bias, char* stage, int N,
                                            Tile t, int wave, int lane) {
   const int wm = wave >> 1;
@@ -190,10 +196,10 @@ __device__ __forceinline__ void stage_tile(const floatx16 (&acc)[4][NB],
     const int col = t.n0 + lcol;
     const float b = (bias && col < N) ? static_cast<float>(bias[col]) : 0.f;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int lrow = 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int lrow = (BM / 2) * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         *reinterpret_cast<_Float16*>(stage + lrow * out_pitch<BN>() + 2 * lcol) =
             static_cast<_Float16>(acc[mi][ni][r] + b);
       }
@@ -202,10 +208,11 @@ __device__ __forceinline__ void stage_tile(const floatx16 (&acc)[4][NB],
 }
 // tid = 0..511: chunk c = 512*i + tid is 8 columns (16 bytes) of tile row
 // c / (BN/8).
-template <int BN>
+template <int BM, int BN>
 __device__ __forceinline__ void store_tile(const char* stage, _Float16* __restrict__ y, int M,
                                            int N, Tile t, int tid) {
   constexpr int kChunksPerRow = BN / 8;
+  static_assert(BM * BN / 8 % 512 == 0, "whole chunks per thread");
 #pragma unroll
   for (int i = 0; i < BM * BN / 8 / 512; ++i) {
     const int c = 512 * i + tid;
@@ -223,11 +230,12 @@ __device__ __forceinline__ void store_tile(const char* stage, _Float16* __restri
 // dequantisation of the weight slab into LDS.  pw = producer wave 0..3,
 // pt = producer thread 0..255.
 //
-// Step s issues one group of 14 loads per thread: packed weights/zeros/
-// scales of step s+3 (6 loads) and the x copies of step s+2 (8 loads).
-// Every group has 14 loads, so one wait count serves: before the barrier of
-// step kt, group kt-2 = {weights of kt+1, x of kt} is complete once at most
-// 14 loads (group kt-1) are outstanding.  Both operands are thus fetched two
+// Step s issues one group of 6 + NDMA loads per thread: packed weights/
+// zeros/scales of step s+3 (6 loads) and the x copies of step s+2 (NDMA =
+// BM/32: each producer wave copies BM/4 rows).  Every group has the same
+// count, so one wait count serves: before the barrier of step kt, group
+// kt-2 = {weights of kt+1, x of kt} is complete once at most one group
+// (kt-1) is outstanding.  Both operands are thus fetched two
 // steps ahead.  Step kt+1's weights are dequantised during step kt into
 // weight buffer (kt+1) % BST.  Three register sets for packed weights rotate
 // (in flight twice, being dequantised once); the loop is unrolled so that
@@ -299,15 +307,18 @@ __device__ __forceinline__ u32x4 dequant_word(uint32_t w, const half2_t (&zp)[4]
   return out;
 }
 
-template <int BN, bool KTAIL>
+template <int BM, int BN, bool KTAIL>
 __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
                                          const uint32_t* __restrict__ qz,
                                          const _Float16* __restrict__ sc, _Float16* __restrict__ y,
                                          int M, int K, int N, int gsh, Tile t, char* a_ring,
                                          char* b_ring, int pw, int pt, bool staged) {
-  using C = Cfg<BN>;
+  using C = Cfg<BM, BN>;
   constexpr int kBPitch = b_pitch<BN>();
   constexpr int kBTileBytes = b_tile_bytes<BN>();
+  constexpr int kATileBytes = C::kATileBytes;
+  constexpr int kLoadsPerStep = C::kLoadsPerStep;
+  constexpr int NDMA = C::NDMA;
   const int lane = pt & 63;
   const int NW = N >> 3;
   const int G = gsh >= 31 ? 1 : (K >> gsh);
@@ -320,16 +331,17 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
   // Lane offsets.  Rows of x past M and columns past N only reach outputs
   // that are never stored, so they are clamped to in-range data, not masked.
   //
-  // x copy: instruction i of producer wave pw covers tile rows 64*pw + 8*i ..
-  // +7; lane -> (row, physical chunk lane % 8), logical chunk = physical ^
-  // swz(row) with swz(row) = (row / 2) % 8 = (4*i + lane/16) % 8: two values.
+  // x copy: instruction i of producer wave pw covers tile rows
+  // (BM/4)*pw + 8*i .. +7; lane -> (row, physical chunk lane % 8), logical
+  // chunk = physical ^ swz(row) with swz(row) = (row / 2) % 8 =
+  // (4*i + lane/16) % 8 (BM/8 is a multiple of 8): two values.
   const int a_lrow = lane >> 3;
   const int a_chunk0 = (lane & 7) ^ ((lane >> 4) & 7);   // even i
   const int a_chunk1 = a_chunk0 ^ 4;                     // odd i
-  uint32_t a_off[8];
+  uint32_t a_off[NDMA];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = min(t.m0 + 64 * pw + 8 * i + a_lrow, M - 1);
+  for (int i = 0; i < NDMA; ++i) {
+    const int m = min(t.m0 + (BM / 4) * pw + 8 * i + a_lrow, M - 1);
     a_off[i] = static_cast<uint32_t>(m * K + 8 * ((i & 1) ? a_chunk1 : a_chunk0)) * 2u;
   }
   // Weight loader lane offsets (see above).
@@ -389,9 +401,9 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
     for (int u = 0; u < 6; ++u) load_b(p, set, u);
   };
   auto issue_a = [&](const StepA& p, int slot) {
-    const uint32_t base = lds_addr(a_ring + slot * kATileBytes) + 64 * pw * 128;
+    const uint32_t base = lds_addr(a_ring + slot * kATileBytes) + (BM / 4) * pw * 128;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NDMA; ++i)
       copy_to_lds(rx, a_off[i] | ((i & 1) ? p.oob1 : p.oob0), p.soff,
                   __builtin_amdgcn_readfirstlane(base + 8 * i * 128));
   };
@@ -445,7 +457,8 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
     // stalls behind a full load queue with vector work pending.
     const StepB pb = step_b(kt + 3);
     const StepA pa = step_a(kt + 2);
-    const uint32_t abase = lds_addr(a_ring + ((j + 2) % 3) * kATileBytes) + 64 * pw * 128;
+    const uint32_t abase =
+        lds_addr(a_ring + ((j + 2) % 3) * kATileBytes) + (BM / 4) * pw * 128;
     auto dma = [&](int i) {
       copy_to_lds(rx, a_off[i] | ((i & 1) ? pa.oob1 : pa.oob0), pa.soff,
                   __builtin_amdgcn_readfirstlane(abase + 8 * i * 128));
@@ -454,11 +467,16 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) {
       if constexpr (BN == 128) {
+        // x copies [u*NDMA/4, (u+1)*NDMA/4) with this unit.
+        constexpr int kPer = NDMA / 4;
         load_b(pb, j, u);
-        dma(2 * u);
+        if constexpr (kPer >= 1) dma(kPer * u);
         if (u == 1) load_b(pb, j, 4);
         if (u == 2) load_b(pb, j, 5);
-        dma(2 * u + 1);
+        if constexpr (kPer >= 2) dma(kPer * u + 1);
+        if constexpr (kPer == 0) {
+          if (u & 1) dma(u >> 1);
+        }
       } else {
         load_b(pb, j, u);
         if (u < 2) {
@@ -485,25 +503,27 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
   if (!staged) return;
   __syncthreads();   // every wave is done with the LDS
   __syncthreads();   // the consumers have staged the output tile
-  store_tile<BN>(a_ring, y, M, N, t, 256 + pt);
+  store_tile<BM, BN>(a_ring, y, M, N, t, 256 + pt);
 }
 
 // Consumer waves (4 of the 8, a 2 x 2 grid): LDS operand reads and the
-// matrix-core work for a 128 x (BN/2) sub-tile each (4 x NB blocks of
+// matrix-core work for a (BM/2) x (BN/2) sub-tile each (MI x NB blocks of
 // 32 x 32), then the epilogue.  LDS operands are read one k slice ahead of
 // the MFMAs; the last slice of a step is multiplied after the next step's
 // barrier, overlapping that step's first reads.  Each slice runs as four
 // sub-blocks of LDS reads (one x block, and the weight blocks spread over
 // the four) and NB MFMAs.
-template <int BN>
+template <int BM, int BN>
 __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Float16* __restrict__ y,
                                          float* __restrict__ partial, int M, int N, int splits,
                                          Tile t, char* a_ring, const char* b_ring, int wave,
                                          int lane, bool staged) {
-  using C = Cfg<BN>;
+  using C = Cfg<BM, BN>;
+  constexpr int MI = C::MI;
   constexpr int NB = C::NB;
   constexpr int kBPitch = b_pitch<BN>();
   constexpr int kBTileBytes = b_tile_bytes<BN>();
+  constexpr int kATileBytes = C::kATileBytes;
   // The narrow tile keeps two operand sets (reads a slice ahead into nxt);
   // the wide one's 4 x 3 accumulator blocks (192 registers) leave room for
   // one, replaced in place.
@@ -523,16 +543,16 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
   const int b_krow = 8 * (gr >> 1) + (sl >> 2);
   const char* const b_rd0 = b_ring + b_krow * kBPitch + 2 * b_col;
 
-  floatx16 acc[4][NB];
+  floatx16 acc[MI][NB];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NB; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-  Frag<NB> cur, nxt;
+  Frag<MI, NB> cur, nxt;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) cur.a[mi] = half8_t{};
+  for (int mi = 0; mi < MI; ++mi) cur.a[mi] = half8_t{};
 #pragma unroll
   for (int ni = 0; ni < NB; ++ni) cur.b[ni] = half8_t{};
 
@@ -549,7 +569,7 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       auto a_src = [&](int sub) {
-        const int row = 128 * wm + 32 * sub + frow;
+        const int row = (BM / 2) * wm + 32 * sub + frow;
         const int chunk = (2 * ks + fhalf) ^ ((row >> 1) & 7);
         return reinterpret_cast<const half8_t*>(a_slot + row * 128 + 16 * chunk);
       };
@@ -557,11 +577,13 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
         return b_rd + 16 * ks * kBPitch + 64 * (q >> 1) + (q & 1) * 4 * kBPitch;
       };
       if constexpr (NB == 2) {
+        // The four weight reads of a slice spread over the MI sub-blocks.
         short4_t raw[4];
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
+        for (int sub = 0; sub < MI; ++sub) {
           nxt.a[sub] = *a_src(sub);
-          raw[sub] = read_tr16(b_src(sub));
+#pragma unroll
+          for (int q = sub * 4 / MI; q < (sub + 1) * 4 / MI; ++q) raw[q] = read_tr16(b_src(q));
 #pragma unroll
           for (int ni = 0; ni < NB; ++ni)
             acc[sub][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[sub], cur.b[ni],
@@ -580,7 +602,7 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
 #pragma unroll
         for (int ni = 0; ni < NB; ++ni) {
 #pragma unroll
-          for (int sub = 0; sub < 4; ++sub) {
+          for (int sub = 0; sub < MI; ++sub) {
             acc[sub][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[sub], cur.b[ni],
                                                                   acc[sub][ni], 0, 0, 0);
             if (ni == NB - 1) cur.a[sub] = *a_src(sub);
@@ -613,7 +635,7 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
     }
   }
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NB; ++ni)
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[mi], cur.b[ni], acc[mi][ni], 0, 0, 0);
@@ -622,9 +644,9 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
   // 8*(r/4) + 4*(lane/32) + r%4 of register r.
   if (staged) {
     __syncthreads();   // every wave is done with the LDS
-    stage_tile<BN, NB>(acc, bias, a_ring, N, t, wave, lane);
+    stage_tile<BM, BN, MI, NB>(acc, bias, a_ring, N, t, wave, lane);
     __syncthreads();
-    store_tile<BN>(a_ring, y, M, N, t, 64 * wave + lane);
+    store_tile<BM, BN>(a_ring, y, M, N, t, 64 * wave + lane);
     return;
   }
   // Otherwise one split: y = acc + bias, 2-byte stores; several: the fp32
@@ -636,10 +658,10 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
     if (col >= N) continue;
     const float b = (bias && splits == 1) ? static_cast<float>(bias[col]) : 0.f;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = t.m0 + 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int row = t.m0 + (BM / 2) * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row >= M) continue;
         if (splits == 1)
           y[row * N + col] = static_cast<_Float16>(acc[mi][ni][r] + b);
@@ -659,7 +681,7 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
 // Split K (few tiles): work-group (tile, split) covers kps K steps and
 // stores its fp32 partial; prefill_reduce_kernel, next on the stream, sums
 // them.
-template <int BN, bool KTAIL>
+template <int BM, int BN, bool KTAIL>
 __global__ __launch_bounds__(512) void prefill_kernel(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
@@ -668,7 +690,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     float* __restrict__ partial) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* const a_ring = smem;
-  char* const b_ring = smem + kAStages * kATileBytes;
+  char* const b_ring = smem + kAStages * Cfg<BM, BN>::kATileBytes;
   pin_arg(x);
   pin_arg(qw);
   pin_arg(qz);
@@ -678,13 +700,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   pin_arg(partial);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const Tile t = tile_of<BN>(n_tiles, splits, kps, (K + BK - 1) / BK);
+  const Tile t = tile_of<BM, BN>(n_tiles, splits, kps, (K + BK - 1) / BK);
   const bool staged = splits == 1 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
   if (wave >= 4)
-    producer<BN, KTAIL>(x, qw, qz, sc, y, M, K, N, gsh, t, a_ring, b_ring, wave - 4, tid - 256,
-                        staged);
+    producer<BM, BN, KTAIL>(x, qw, qz, sc, y, M, K, N, gsh, t, a_ring, b_ring, wave - 4,
+                            tid - 256, staged);
   else
-    consumer<BN>(bias, y, partial, M, N, splits, t, a_ring, b_ring, wave, tid & 63, staged);
+    consumer<BM, BN>(bias, y, partial, M, N, splits, t, a_ring, b_ring, wave, tid & 63, staged);
 }
 
 // y = sum of the split partials, in split order (deterministic), + bias.
@@ -731,8 +753,8 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float* __rest
 
 hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                           const _Float16* scales, const _Float16* bias, _Float16* y,
-                          int M, int K, int N, int group_shift, int bn, int m_tiles,
-                          int n_tiles, int splits, int ksteps, void* workspace,
+                          int M, int K, int N, int group_shift, int bm, int bn,
+                          int m_tiles, int n_tiles, int splits, int ksteps, void* workspace,
                           hipStream_t stream) {
   // Workspace (split K only), laid out like the decode exchange's so that
   // one buffer serves both: the ticket and accumulator regions (left
@@ -742,25 +764,22 @@ hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint
       ws ? reinterpret_cast<float*>(ws + kTicketRegionBytes + kAtomicRegionBytes) : nullptr;
   const dim3 grid(m_tiles * n_tiles * splits);
   const bool tail = K % BK != 0;
-  if (bn == 192) {
-    if (tail)
-      hipLaunchKernelGGL((prefill_kernel<192, true>), grid, dim3(512), lds_bytes<192>(), stream,
-                         x, qweight, qzeros, scales, bias, y, M, K, N, group_shift, n_tiles,
-                         splits, ksteps, partial);
-    else
-      hipLaunchKernelGGL((prefill_kernel<192, false>), grid, dim3(512), lds_bytes<192>(), stream,
-                         x, qweight, qzeros, scales, bias, y, M, K, N, group_shift, n_tiles,
-                         splits, ksteps, partial);
-  } else {
-    if (tail)
-      hipLaunchKernelGGL((prefill_kernel<128, true>), grid, dim3(512), lds_bytes<128>(), stream,
-                         x, qweight, qzeros, scales, bias, y, M, K, N, group_shift, n_tiles,
-                         splits, ksteps, partial);
-    else
-      hipLaunchKernelGGL((prefill_kernel<128, false>), grid, dim3(512), lds_bytes<128>(), stream,
-                         x, qweight, qzeros, scales, bias, y, M, K, N, group_shift, n_tiles,
-                         splits, ksteps, partial);
-  }
+  auto go = [&](auto kernel, int lds) {
+    hipLaunchKernelGGL(kernel, grid, dim3(512), lds, stream, x, qweight, qzeros, scales, bias, y,
+                       M, K, N, group_shift, n_tiles, splits, ksteps, partial);
+  };
+  if (bm == 256 && bn == 192)
+    tail ? go(prefill_kernel<256, 192, true>, lds_bytes<256, 192>())
+         : go(prefill_kernel<256, 192, false>, lds_bytes<256, 192>());
+  else if (bm == 256)
+    tail ? go(prefill_kernel<256, 128, true>, lds_bytes<256, 128>())
+         : go(prefill_kernel<256, 128, false>, lds_bytes<256, 128>());
+  else if (bm == 128)
+    tail ? go(prefill_kernel<128, 128, true>, lds_bytes<128, 128>())
+         : go(prefill_kernel<128, 128, false>, lds_bytes<128, 128>());
+  else
+    tail ? go(prefill_kernel<64, 128, true>, lds_bytes<64, 128>())
+         : go(prefill_kernel<64, 128, false>, lds_bytes<64, 128>());
   if (splits > 1) {
     const size_t quads = static_cast<size_t>(M) * N / 4;
     const dim3 rgrid(static_cast<unsigned>((quads + 255) / 256));

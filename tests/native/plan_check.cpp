@@ -78,7 +78,10 @@ int main() {
                 else
                   EXPECT(pl.ws_bytes == 0);
               } else if (pl.path == AWQ_PATH_PREFILL) {
-                EXPECT((int64_t)pl.m_tiles * kPrefillBM >= M);
+                EXPECT(pl.prefill_bm == 64 || pl.prefill_bm == 128 || pl.prefill_bm == kPrefillBM);
+                EXPECT(pl.prefill_bn == kPrefillBN || pl.prefill_bm == kPrefillBM);
+                EXPECT((int64_t)pl.m_tiles * pl.prefill_bm >= M);
+                EXPECT(M <= 64 ? pl.prefill_bm == 64 : (M <= 128 ? pl.prefill_bm == 128 : pl.prefill_bm == 256));
                 EXPECT(pl.prefill_bn == kPrefillBN || pl.prefill_bn == kPrefillWideBN);
                 EXPECT((int64_t)pl.n_tiles * pl.prefill_bn >= N);
                 EXPECT((int64_t)(pl.n_tiles - 1) * pl.prefill_bn < N);

@@ -323,6 +323,46 @@ def test_prefill_wide_tile_exact_cases():
                                   np.broadcast_to(p["bias"], (M, N)).view(np.uint16))
 
 
+@pytest.mark.parametrize("bm,M,K,N,g,bias", [
+    (64, 17, 4096, 1024, 128, True),    # split K, one row tile mostly padding
+    (64, 64, 2000, 264, 16, False),     # K tail, N = 2 * 128 + 8
+    (64, 200, 512, 384, 64, True),      # four row tiles, the last ragged
+    (128, 65, 8192, 1280, 128, True),   # split K
+    (128, 300, 1032, 136, -1, False),   # one group, K tail, N = 128 + 8
+    (128, 128, 256, 512, 8, True),      # whole tiles, short K (no split)
+])
+def test_prefill_short_tiles(bm, M, K, N, g, bias):
+    """The 64- and 128-row prefill tiles (forced), on shapes that cut through
+    their row blocks, column blocks and K steps."""
+    say(f"prefill BM={bm} M={M} K={K} N={N} g={g}")
+    p = awq_inputs.make_inputs(M, K, N, g, seed=bm + M + K + N, bias=bias)
+    d = to_dev(p)
+    y = run_gemm(d, path="prefill", env={"AWQ_PREFILL_BM": str(bm)})
+    ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
+    assert_within_tol(y, ref, f"BM={bm} M={M} K={K} N={N} g={g}")
+
+
+@pytest.mark.parametrize("bm", [64, 128])
+def test_prefill_short_tiles_exact(bm):
+    """One-hot rows and q == z stay exact with the short tiles (split K
+    included: the reduction adds exact zeros)."""
+    say(f"prefill BM={bm} exact cases")
+    M, K, N, g = bm - 3, 2048, 520, 64
+    env = {"AWQ_PREFILL_BM": str(bm)}
+    p = awq_inputs.make_inputs(M, K, N, g, seed=bm)
+    w = oracle.dequant(p["qweight"], p["qzeros"], p["scales"], g)
+    ks = np.random.default_rng(bm).choice(K, M)
+    x = np.zeros((M, K), dtype=np.float16)
+    x[np.arange(M), ks] = 1.0
+    y = run_gemm(to_dev(dict(p, x=x, bias=None)), path="prefill", env=env)
+    np.testing.assert_array_equal(y.view(np.uint16), w[ks].view(np.uint16))
+    q = awq_inputs.make_inputs(M, K, N, g, seed=bm + 1, bias=True, scale_lo=-1, scale_hi=1)
+    q["qweight"] = np.repeat(q["qzeros"], g, axis=0)
+    y = run_gemm(to_dev(q), path="prefill", env=env)
+    np.testing.assert_array_equal(y.view(np.uint16),
+                                  np.broadcast_to(q["bias"], (M, N)).view(np.uint16))
+
+
 @pytest.mark.parametrize("M", [2, 3, 17, 31, 255])
 def test_mid_batch_tails(M):
     say(f"batch tail M={M}")

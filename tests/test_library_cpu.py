@@ -139,10 +139,13 @@ def test_plan_selects_kernel(M, K, N, g, path):
 
 
 def _prefill_splits_expected(M, K, N):
-    """Split-K rule of the prefill kernel, restated: 256 x 128 tiles; when
-    there are fewer tiles than 256 CUs, up to 8 splits (no more than fill
-    the CUs), each of at least 8 K steps of 64, none empty."""
-    tiles = -(-M // 256) * -(-N // 128)
+    """Split-K rule of the prefill kernel, restated: tiles of 64, 128 or 256
+    rows (the smallest covering M, up to 256) by 128 columns; when there are
+    fewer tiles than 256 CUs, up to 8 splits (no more than fill the CUs),
+    each of at least 8 K steps of 64, none empty.  (Shapes that take the
+    256 x 192 tile have enough tiles not to split.)"""
+    bm = 64 if M <= 64 else (128 if M <= 128 else 256)
+    tiles = -(-M // bm) * -(-N // 128)
     nkt = -(-K // 64)
     s = 1
     if tiles < 256:
@@ -160,6 +163,8 @@ def _prefill_splits_expected(M, K, N):
     (300, 2000, 264, 16, 4),
     (17, 256, 4096, 128, 1),
     (64, 1536, 256, 128, 3),
+    (17, 8192, 7168, 128, 4),     # 64-row tiles: 56 tiles
+    (100, 4096, 1024, 128, 8),    # 128-row tiles: 8 tiles
 ])
 def test_prefill_split_k_plan(M, K, N, g, splits):
     """Workspace of a split prefill, laid out like the decode exchange's: the
