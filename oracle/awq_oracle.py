@@ -32,6 +32,14 @@ Functions:
     awq_linear_ref(...)    -- float64 forward, (*, K) -> (*, N)
     awq_linear_ref_rows    -- the same for a chosen subset of input rows
     awq_linear_loops(...)  -- pure-Python triple loop, for tiny inputs only
+    dense_linear_ref(...)  -- the unquantised float16 linear (baseline), float64
+    dense_linear_loops     -- its pure-Python triple loop, for tiny inputs only
+
+The unquantised linear follows the page "Predibase Lorax Linear Layer
+Factory" (Description: FastLinear, a float16 F.linear whose weight is
+(out_features, in_features); its ROCm variant sends single-token products at
+in_features 8192 and out_features 1280 or 7168 to a custom skinny kernel):
+y = x . w^T (+ bias).
 """
 from __future__ import annotations
 
@@ -176,4 +184,37 @@ def awq_linear_loops(x, qweight, qzeros, scales, bias, group_size):
         for m in range(M):
             for n in range(N):
                 y[m][n] += float(bias[n])
+    return np.array(y, dtype=np.float64)
+
+
+def dense_linear_ref(x, w, bias):
+    """The unquantised FastLinear forward (page "Predibase Lorax Linear Layer
+    Factory", Description): F.linear(x, w, bias) = x . w^T + bias with w of
+    shape (out_features, in_features), evaluated in float64 (exact products of
+    float16 values).  Returns float64 of shape (*x.shape[:-1], N)."""
+    x = np.asarray(x)
+    w = np.asarray(w)
+    N, K = w.shape
+    if x.shape[-1] != K:
+        raise ValueError(f"input feature size {x.shape[-1]} != in_features {K}")
+    lead = x.shape[:-1]
+    y = x.reshape(-1, K).astype(np.float64) @ w.astype(np.float64).T
+    if bias is not None:
+        b = np.asarray(bias)
+        if b.shape != (N,):
+            raise ValueError("bias must have shape (out_features,)")
+        y = y + b.astype(np.float64)[None, :]
+    return y.reshape(*lead, N)
+
+
+def dense_linear_loops(x, w, bias):
+    """Pure-Python restatement of dense_linear_ref for tiny inputs."""
+    M, K, N = len(x), len(x[0]), len(w)
+    y = [[0.0] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += float(x[m][k]) * float(w[n][k])
+            y[m][n] = acc + (float(bias[n]) if bias is not None else 0.0)
     return np.array(y, dtype=np.float64)

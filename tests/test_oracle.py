@@ -326,3 +326,40 @@ def test_input_generator_shapes_and_prefix():
     nib = oracle.unpack_int4(t["qweight"])
     counts = np.bincount(nib.ravel(), minlength=16) / nib.size
     assert np.all(np.abs(counts - 1 / 16) < 0.01)
+
+
+# ----------------------------------------------- the unquantised baseline
+def test_dense_linear_pins():
+    """F.linear(x, w, b) = x . w^T + b (page "Predibase Lorax Linear Layer
+    Factory", Description: FastLinear).  Pinned by: the pure-Python loop on a
+    tiny case; an identity weight returning x exactly; one-hot rows selecting
+    the columns of w^T bit for bit; and the identity F.linear(x, W^T) = x . W
+    against the independently pinned quantised forward, whose dequantised
+    weight is (K, N) where F.linear's is (N, K) -- a transposed operand fails
+    here."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((3, 5)).astype(np.float16)
+    w = rng.standard_normal((4, 5)).astype(np.float16)
+    b = rng.standard_normal(4).astype(np.float16)
+    np.testing.assert_allclose(oracle.dense_linear_ref(x, w, b),
+                               oracle.dense_linear_loops(x, w, b), rtol=1e-12, atol=1e-12)
+    eye = np.eye(6, dtype=np.float16)
+    xs = rng.standard_normal((2, 6)).astype(np.float16)
+    np.testing.assert_array_equal(oracle.dense_linear_ref(xs, eye, None), xs.astype(np.float64))
+    w2 = rng.standard_normal((7, 9)).astype(np.float16)
+    onehot = np.zeros((3, 9), dtype=np.float16)
+    ks = [0, 4, 8]
+    onehot[np.arange(3), ks] = 1.0
+    np.testing.assert_array_equal(oracle.dense_linear_ref(onehot, w2, None),
+                                  w2.T[ks].astype(np.float64))
+    p = awq_inputs.make_inputs(2, 64, 24, 32, seed=9, bias=True)
+    wq = oracle.dequant(p["qweight"], p["qzeros"], p["scales"], 32)      # (K, N)
+    np.testing.assert_allclose(oracle.dense_linear_ref(p["x"], wq.T, p["bias"]),
+                               oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"],
+                                                     p["scales"], p["bias"], 32),
+                               rtol=1e-12, atol=1e-12)
+    with pytest.raises(AssertionError):
+        # a transposed weight (read as (K, N)) must not pass the same check
+        np.testing.assert_allclose(oracle.dense_linear_loops(p["x"][:, :24], wq[:24, :24], None),
+                                   oracle.dense_linear_ref(p["x"][:, :24], wq[:24, :24].T, None),
+                                   rtol=1e-6, atol=1e-6)
