@@ -209,6 +209,51 @@ def sweep(torch, awq, dev):
                     flush=True)
                 del r
                 torch.cuda.empty_cache()
+    # The unquantised float16 baseline at the single-token shapes the pages
+    # name (FastLinear / FastLinearROCm: K = 8192, N = 1280 or 7168), timed
+    # the same way; the W4A16 time at the same shape gives the speed-up.
+    import awq_inputs
+    for (K, N) in ((8192, 1280), (8192, 7168)):
+        d_us = dense_time_us(torch, awq, 1, K, N, dev)
+        name = "decode_k8192_n1280" if N == 1280 else "decode_sweep_k8192_n7168"
+        r = run_leg(torch, awq, dict(source=name, M=1, group_size=128), 200, 10, dev)
+        w4_us = r["ms_per_step"] * 1e3
+        nbytes = K * N * 2 + K * 2 + N * 2
+        print(json.dumps({
+            "workload": f"dense_fp16_baseline_m1_k{K}_n{N}", "M": 1, "K": K, "N": N,
+            "kernel": "dense_gemv", "us_per_call": round(d_us, 3),
+            "GB_per_s": round(nbytes / (d_us * 1e-6) / 1e9, 1), "bound": "hbm",
+            "frac": round(nbytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes,
+            "w4a16_us_per_call": round(w4_us, 3), "w4a16_speedup": round(d_us / w4_us, 2)}),
+            flush=True)
+
+
+def dense_time_us(torch, awq, M, K, N, dev, calls=200):
+    """awq_dense_gemv per-call time, weights rotated through >= 512 MiB."""
+    gen = torch.Generator(device="cpu").manual_seed(K + N)
+    nbytes = K * N * 2
+    R = max(2, -(-ROTATE_BYTES // nbytes))
+    ws = [(torch.randn((N, K), generator=gen) * 0.02).to(torch.float16).to(dev) for _ in range(R)]
+    x = torch.randn((M, K), generator=gen).to(torch.float16).to(dev)
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(stream):
+        for i in range(10):
+            awq.dense_gemv(x, ws[i % R], None, out=y)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(calls):
+            awq.dense_gemv(x, ws[i % R], None, out=y)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    with torch.cuda.stream(stream):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / calls
 
 
 def main():

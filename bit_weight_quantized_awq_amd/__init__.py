@@ -9,7 +9,7 @@ from __future__ import annotations
 
 from .binding import (  # noqa: F401
     AWQ_PATH_DECODE, AWQ_PATH_GENERIC, AWQ_PATH_PREFILL, AwqError, PATH_NAMES, abi_version,
-    dequant, gemm, gemm_plan, gemm_workspace_size, lib, status_string,
+    dense_gemv, dequant, gemm, gemm_plan, gemm_workspace_size, lib, status_string,
 )
 
 

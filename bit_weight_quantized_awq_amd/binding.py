@@ -40,6 +40,7 @@ SIGNATURES = {
     "awq_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                 _vp, ctypes.c_size_t, _vp]),
     "awq_dequant": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "awq_dense_gemv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
 }
 
 _lib = None
@@ -197,6 +198,43 @@ def gemm(x, qweight, qzeros, scales, bias=None, group_size: int = 128, out=None,
                         stream)
     if st != AWQ_SUCCESS:
         raise AwqError(st, "awq_gemm")
+    return y.reshape(*lead, N)
+
+
+def dense_gemv(x, w, bias=None, out=None):
+    """Unquantised baseline through awq_dense_gemv: F.linear(x, w, bias) for
+    float16 x (*, K) with at most 4 rows and w (N, K).  Returns float16
+    (*, N) on x's device, enqueued on the current stream."""
+    torch = _torch()
+    device = w.device
+    _check_device("x", x, device)
+    if bias is not None:
+        _check_device("bias", bias, device)
+    for name, t in (("x", x), ("w", w), ("bias", bias)):
+        if t is not None and t.dtype != torch.float16:
+            raise TypeError(f"{name} must be float16")
+    N, K = w.shape
+    if x.shape[-1] != K:
+        raise ValueError(f"x has {x.shape[-1]} features, w has {K}")
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, K).contiguous()
+    w = w.contiguous()
+    if bias is not None:
+        if tuple(bias.shape) != (N,):
+            raise ValueError(f"bias shape {tuple(bias.shape)} != ({N},)")
+        bias = bias.contiguous()
+    M = x2.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=device)
+    if out is not None:
+        _check_device("out", out, device)
+        if out.shape != (M, N) or out.dtype != torch.float16 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float16 (M, N) tensor")
+    stream = torch.cuda.current_stream(device).cuda_stream
+    st = lib().awq_dense_gemv(x2.data_ptr() if M else None, w.data_ptr(),
+                              bias.data_ptr() if bias is not None else None,
+                              y.data_ptr() if M else None, M, K, N, stream)
+    if st != AWQ_SUCCESS:
+        raise AwqError(st, "awq_dense_gemv")
     return y.reshape(*lead, N)
 
 

@@ -28,6 +28,7 @@ SOURCES = [
     "awq_generic.hip",
     "awq_decode.hip",
     "awq_prefill.hip",
+    "awq_dense.hip",
 ]
 
 COMMON_FLAGS = [

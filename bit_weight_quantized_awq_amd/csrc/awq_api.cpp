@@ -111,6 +111,18 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void*
   return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP;
 }
 
+int awq_dense_gemv(const void* x, const void* w, const void* bias, void* y, int64_t M, int64_t K,
+                   int64_t N, void* stream) {
+  const int st = awq::validate_dense(x, w, bias, y, M, K, N);
+  if (st != AWQ_SUCCESS) return st;
+  if (M == 0) return AWQ_SUCCESS;
+  const hipError_t e = awq::launch_dense_gemv(
+      static_cast<const _Float16*>(x), static_cast<const _Float16*>(w),
+      static_cast<const _Float16*>(bias), static_cast<_Float16*>(y), static_cast<int>(M),
+      static_cast<int>(K), static_cast<int>(N), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP;
+}
+
 int awq_dequant(const void* qweight, const void* qzeros, const void* scales, void* w,
                 int64_t K, int64_t N, int64_t group_size, void* stream) {
   Problem p;

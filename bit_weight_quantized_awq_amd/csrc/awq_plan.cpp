@@ -59,6 +59,19 @@ int validate_dequant_pointers(const void* qweight, const void* qzeros,
   return AWQ_SUCCESS;
 }
 
+int validate_dense(const void* x, const void* w, const void* bias, const void* y, int64_t M,
+                   int64_t K, int64_t N) {
+  if (M < 0 || K <= 0 || N <= 0) return AWQ_ERROR_INVALID_VALUE;
+  if (!w) return AWQ_ERROR_INVALID_VALUE;
+  if (M > 0 && (!x || !y)) return AWQ_ERROR_INVALID_VALUE;
+  if (M > kDenseMaxM || K % 8 != 0 || M * K > kDenseMaxMK) return AWQ_ERROR_SHAPE;
+  if (K > kMaxElems || N > kMaxElems || K * N > kMaxElems || M * N > kMaxElems)
+    return AWQ_ERROR_SHAPE;
+  if (!aligned(w, 16) || (x && !aligned(x, 16))) return AWQ_ERROR_MISALIGNED;
+  if ((y && !aligned(y, 2)) || (bias && !aligned(bias, 2))) return AWQ_ERROR_MISALIGNED;
+  return AWQ_SUCCESS;
+}
+
 // The fast kernels address every operand with 32-bit byte offsets (buffer
 // loads whose out-of-range offsets read zero): keep each operand below 1 GiB.
 static bool fits_32bit_offsets(const Problem& p) {

@@ -79,6 +79,14 @@ int validate_gemm_pointers(const void* x, const void* qweight, const void* qzero
 int validate_dequant_pointers(const void* qweight, const void* qzeros,
                               const void* scales, const void* w);
 
+// The unquantised baseline (awq_dense_gemv): 1 <= M <= kDenseMaxM (M == 0 is
+// a no-op), K % 8 == 0, M * K <= kDenseMaxMK (x is staged in LDS), x and w
+// 16-byte aligned, bias and y 2-byte aligned.  Returns an awq_status value.
+constexpr int kDenseMaxM = 4;
+constexpr int64_t kDenseMaxMK = 65536;
+int validate_dense(const void* x, const void* w, const void* bias, const void* y, int64_t M,
+                   int64_t K, int64_t N);
+
 // Alignment flags: whether x, scales and qweight start on a 16-byte boundary.
 struct Alignment {
   bool x, scales, qweight;

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define AWQ_ABI_VERSION 1
+#define AWQ_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 enum awq_status {
@@ -115,6 +115,22 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros,
  * (the page's "per-group dequantization", Description). */
 int awq_dequant(const void* qweight, const void* qzeros, const void* scales,
                 void* w, int64_t K, int64_t N, int64_t group_size, void* stream);
+
+/* The unquantised float16 linear, as a baseline for the W4A16 decode: the
+ * FastLinear of the page "Predibase Lorax Linear Layer Factory"
+ * (Description), F.linear(x, w, bias):
+ *   y[m, n] = float16_RNE(fp32 sum_k x[m, k] * w[n, k] + bias[n]).
+ * Its ROCm variant sends single-token products at K = 8192, N = 1280 or
+ * 7168 to a custom skinny kernel; this one covers 1 <= M <= 4.
+ *
+ * x: float16 (M, K) row-major, 16-byte aligned.  w: float16 (N, K)
+ * row-major (out_features x in_features), 16-byte aligned.  bias: float16
+ * (N) or NULL.  y: float16 (M, N), written.  All device pointers owned by
+ * the caller; no workspace; deterministic.  K % 8 == 0 and M * K <= 65536
+ * (x is staged in LDS), else AWQ_ERROR_SHAPE; M > 4 is AWQ_ERROR_SHAPE;
+ * M == 0 is a no-op.  Enqueued on `stream`, nothing synchronises. */
+int awq_dense_gemv(const void* x, const void* w, const void* bias, void* y,
+                   int64_t M, int64_t K, int64_t N, void* stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

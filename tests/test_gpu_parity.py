@@ -474,3 +474,43 @@ def test_wqlinear_module_forward():
     assert y.shape == (2, 4, 512)
     ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], p["bias"], 128)
     assert_within_tol(y.reshape(8, 512).cpu().numpy(), ref, "WQLinear")
+
+
+# ------------------------------------------------ the unquantised baseline
+@pytest.mark.parametrize("M,K,N,bias", [
+    (1, 8192, 1280, False),    # the pages' single-token shapes
+    (1, 8192, 7168, True),
+    (4, 8192, 7168, False),
+    (3, 1000, 200, True),      # K not a multiple of 512: partial last chunk
+    (2, 8, 9, True),           # one chunk, N not a multiple of 8 rows
+])
+def test_dense_gemv_parity(M, K, N, bias):
+    """awq_dense_gemv (F.linear, weight (N, K)) against the float64 oracle."""
+    say(f"dense M={M} K={K} N={N}")
+    rng = np.random.default_rng(M + K + N)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    b = (rng.standard_normal(N) * 0.1).astype(np.float16) if bias else None
+    xd, wd = torch.from_numpy(x).to(DEV), torch.from_numpy(w).to(DEV)
+    bd = torch.from_numpy(b).to(DEV) if bias else None
+    y = awq.dense_gemv(xd, wd, bd)
+    ref = oracle.dense_linear_ref(x, w, b)
+    assert_within_tol(y.cpu().numpy(), ref, f"dense M={M} K={K} N={N}")
+    y2 = awq.dense_gemv(xd, wd, bd)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))   # fixed summation order
+
+
+def test_dense_gemv_exact_cases():
+    """One-hot rows return the selected weight column exactly; an empty
+    batch launches nothing."""
+    say("dense exact cases")
+    K, N = 4096, 3000
+    w = (np.random.default_rng(1).standard_normal((N, K))).astype(np.float16)
+    ks = [0, 1234, K - 1]
+    x = np.zeros((3, K), dtype=np.float16)
+    x[np.arange(3), ks] = 1.0
+    y = awq.dense_gemv(torch.from_numpy(x).to(DEV), torch.from_numpy(w).to(DEV)).cpu().numpy()
+    np.testing.assert_array_equal(y.view(np.uint16), w.T[ks].view(np.uint16))
+    y0 = awq.dense_gemv(torch.zeros((0, K), dtype=torch.float16, device=DEV),
+                        torch.from_numpy(w).to(DEV))
+    assert y0.shape == (0, N)

@@ -62,6 +62,30 @@ def _dequant(qw=A, qz=A, sc=A, w=A, K=256, N=128, g=64):
     return awq.lib().awq_dequant(qw, qz, sc, w, K, N, g, None)
 
 
+def _dense(x=A, w=A, bias=None, y=A, M=1, K=8192, N=1280):
+    return awq.lib().awq_dense_gemv(x, w, bias, y, M, K, N, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(w=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(x=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(M=-1), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(K=0), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(N=0), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(M=5), binding.AWQ_ERROR_SHAPE),            # at most 4 rows
+    (dict(K=100), binding.AWQ_ERROR_SHAPE),          # K % 8 != 0
+    (dict(M=4, K=16392), binding.AWQ_ERROR_SHAPE),   # x does not fit the LDS stage
+    (dict(x=A + 8), binding.AWQ_ERROR_MISALIGNED),
+    (dict(w=A + 4), binding.AWQ_ERROR_MISALIGNED),
+    (dict(y=A + 1), binding.AWQ_ERROR_MISALIGNED),
+    (dict(bias=A + 1), binding.AWQ_ERROR_MISALIGNED),
+    (dict(M=0, x=None, y=None), binding.AWQ_SUCCESS),  # empty batch: no launch
+])
+def test_dense_validation(kwargs, status):
+    """The unquantised baseline rejects every invalid argument on the host."""
+    assert _dense(**kwargs) == status
+
+
 @pytest.mark.parametrize("kwargs,status", [
     (dict(qw=None), binding.AWQ_ERROR_INVALID_VALUE),
     (dict(qz=None), binding.AWQ_ERROR_INVALID_VALUE),
@@ -98,6 +122,30 @@ def test_gemm_workspace_checked_before_launch():
     assert _gemm(M=M, K=K, N=N, g=g) == binding.AWQ_ERROR_WORKSPACE
     assert _gemm(M=M, K=K, N=N, g=g, ws=A, wsb=need - 1) == binding.AWQ_ERROR_WORKSPACE
     assert _gemm(M=M, K=K, N=N, g=g, ws=A + 8, wsb=need) == binding.AWQ_ERROR_MISALIGNED
+
+
+def _dense(x=A, w=A, bias=None, y=A, M=1, K=8192, N=1280):
+    return awq.lib().awq_dense_gemv(x, w, bias, y, M, K, N, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(w=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(x=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(M=-1), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(K=0), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(N=0), binding.AWQ_ERROR_INVALID_VALUE),
+    (dict(M=5), binding.AWQ_ERROR_SHAPE),            # at most 4 rows
+    (dict(K=100), binding.AWQ_ERROR_SHAPE),          # K % 8 != 0
+    (dict(M=4, K=16392), binding.AWQ_ERROR_SHAPE),   # x does not fit the LDS stage
+    (dict(x=A + 8), binding.AWQ_ERROR_MISALIGNED),
+    (dict(w=A + 4), binding.AWQ_ERROR_MISALIGNED),
+    (dict(y=A + 1), binding.AWQ_ERROR_MISALIGNED),
+    (dict(bias=A + 1), binding.AWQ_ERROR_MISALIGNED),
+    (dict(M=0, x=None, y=None), binding.AWQ_SUCCESS),  # empty batch: no launch
+])
+def test_dense_validation(kwargs, status):
+    """The unquantised baseline rejects every invalid argument on the host."""
+    assert _dense(**kwargs) == status
 
 
 @pytest.mark.parametrize("kwargs,status", [
