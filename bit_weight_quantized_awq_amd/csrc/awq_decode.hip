@@ -51,20 +51,21 @@ namespace {
 struct SplitK {
   uint32_t* tickets;         // one per column tile, ticket_words apart (ticket exchange)
   unsigned long long* acc;   // [M][N]: fixed-point sum, contribution count (atomic exchange)
-  uint32_t* mask;            // [M][N]: splits that sent a float partial (atomic exchange)
+  unsigned long long* mask;  // [M][N]: splits that sent a float partial (atomic exchange)
   float* partial;            // [splits][M][N]: partials (all for ticket, float ones for atomic)
   int ticket_words;
 };
-// acc layout: bits 0-52 sum of (v + 2^47) over fixed-point contributions,
-// v = rint(p * 2^24) with |p| < 2^23 (so each term is below 2^48 and up to
-// 31 of them stay below 2^53); bits 53-57 number of contributions; bits
+// acc layout: bits 0-51 sum of (v + 2^45) over fixed-point contributions,
+// v = rint(p * 2^24) with |p| < 2^21 (so each term is below 2^46 and up to
+// 63 of them stay below 2^52); bits 52-57 number of contributions; bits
 // 58-62 number of float contributions.  A partial outside the fixed-point
 // range (huge, infinite or NaN) is published as a float and flagged instead.
-constexpr unsigned long long kFxUnit = 1ull << 53;
+constexpr unsigned long long kFxUnit = 1ull << 52;
 constexpr unsigned long long kFxFloat = 1ull << 58;
-constexpr long long kFxBias = 1ll << 47;
+constexpr long long kFxBias = 1ll << 45;
 constexpr float kFxScale = 16777216.0f;   // 2^24
-constexpr float kFxLimit = 8388608.0f;    // 2^23
+constexpr float kFxLimit = 2097152.0f;    // 2^21
+static_assert(kDecodeMaxSplits <= 63, "six-bit contribution counts");
 
 // Cross-wave reduction in LDS.  Layout [wave][row group of 4][column][4 rows]
 // (row groups below M only): the lane holding rows 4*kb .. 4*kb+3 of a column
@@ -138,7 +139,7 @@ __device__ __forceinline__ void splitk_atomic(const float (&part)[kDecodeMaxM], 
         const size_t e = static_cast<size_t>(m) * N + n;
         __hip_atomic_store(sk.partial + static_cast<size_t>(split) * M * N + e, p,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_or(sk.mask + e, 1u << split, __ATOMIC_RELAXED,
+        __hip_atomic_fetch_or(sk.mask + e, 1ull << split, __ATOMIC_RELAXED,
                               __HIP_MEMORY_SCOPE_AGENT);
         add[m] = kFxUnit + kFxFloat;
         published = true;
@@ -160,19 +161,20 @@ __device__ __forceinline__ void splitk_atomic(const float (&part)[kDecodeMaxM], 
   for (int m = 0; m < kDecodeMaxM; ++m) {
     if (m >= M) continue;
     const unsigned long long tot = old[m] + add[m];
-    if (static_cast<int>((tot >> 53) & 31u) != splits) continue;
+    if (static_cast<int>((tot >> 52) & 63u) != splits) continue;
     const size_t e = static_cast<size_t>(m) * N + n;
-    const int nf = static_cast<int>((tot >> 58) & 31u);
+    const int nf = static_cast<int>((tot >> 58) & 63u);
     const long long fx = static_cast<long long>(tot & (kFxUnit - 1)) -
                          static_cast<long long>(splits - nf) * kFxBias;
     float r = static_cast<float>(static_cast<double>(fx) * (1.0 / 16777216.0));
     if (nf) {
-      const uint32_t msk = __hip_atomic_load(sk.mask + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long msk =
+          __hip_atomic_load(sk.mask + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (int sp = 0; sp < splits; ++sp)
-        if ((msk >> sp) & 1u)
+        if ((msk >> sp) & 1ull)
           r += __hip_atomic_load(sk.partial + static_cast<size_t>(sp) * M * N + e,
                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(sk.mask + e, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sk.mask + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     y[e] = static_cast<_Float16>(r + b);
     __hip_atomic_store(sk.acc + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -739,7 +741,8 @@ hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint3
   if (tw > kTicketMaxStrideBytes / 4) tw = kTicketMaxStrideBytes / 4;
   const SplitK sk{reinterpret_cast<uint32_t*>(ws),
                   ws ? reinterpret_cast<unsigned long long*>(ws + kTicketRegionBytes) : nullptr,
-                  ws ? reinterpret_cast<uint32_t*>(ws + kTicketRegionBytes + mn * 8) : nullptr,
+                  ws ? reinterpret_cast<unsigned long long*>(ws + kTicketRegionBytes + mn * 8)
+                     : nullptr,
                   ws ? reinterpret_cast<float*>(ws + kTicketRegionBytes + kAtomicRegionBytes)
                      : nullptr,
                   tw};

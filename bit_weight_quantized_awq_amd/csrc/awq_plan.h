@@ -17,18 +17,18 @@ constexpr int kDecodeMaxM = 16;          // rows of the 16x16 MFMA output
 //  * a fixed ticket region: one ticket per column tile, up to 256 bytes apart
 //    (device-scope atomics on one cache line serialise);
 //  * a fixed accumulator region for the atomic exchange (M <= 4, N <= 65536):
-//    an 8-byte fixed-point accumulator per output element, then a 4-byte
-//    mask per output element;
+//    an 8-byte fixed-point accumulator per output element, then an 8-byte
+//    mask (one bit per split) per output element;
 //  * 4 bytes per split per output element for partials.
 // The first two parts are zero between calls (each exchange resets what it
 // used) and no exchange writes partials into them, so calls of any shapes
-// can share one workspace.  The atomic exchange counts at most 31 splits.
+// can share one workspace.  The atomic exchange counts at most 63 splits.
 constexpr size_t kTicketRegionBytes = 65536;
 constexpr int kTicketMaxStrideBytes = 256;
-constexpr int kDecodeMaxSplits = 31;
+constexpr int kDecodeMaxSplits = 63;
 constexpr int kDecodeAtomicMaxM = 4;
 constexpr int kDecodeAtomicMaxN = 65536;
-constexpr size_t kAtomicRegionBytes = static_cast<size_t>(kDecodeAtomicMaxM) * kDecodeAtomicMaxN * 12;
+constexpr size_t kAtomicRegionBytes = static_cast<size_t>(kDecodeAtomicMaxM) * kDecodeAtomicMaxN * 16;
 
 // Prefill kernel tile: 64, 128 or 256 rows (the smallest that covers the
 // batch, so small batches waste no matrix-core work on padding rows), 128

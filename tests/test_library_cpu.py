@@ -216,12 +216,12 @@ def _prefill_splits_expected(M, K, N):
 ])
 def test_prefill_split_k_plan(M, K, N, g, splits):
     """Workspace of a split prefill, laid out like the decode exchange's: the
-    64 KiB ticket region, the 3 MiB accumulator region, then one fp32 partial
+    64 KiB ticket region, the 4 MiB accumulator region, then one fp32 partial
     per split per output element; none without a split."""
     assert _prefill_splits_expected(M, K, N) == splits
     path, ws = awq.gemm_plan(M, K, N, g)
     assert path == binding.AWQ_PATH_PREFILL
-    assert ws == (0 if splits == 1 else 65536 + 4 * 65536 * 12 + splits * M * N * 4)
+    assert ws == (0 if splits == 1 else 65536 + 4 * 65536 * 16 + splits * M * N * 4)
     assert awq.gemm_workspace_size(M, K, N, g) == ws
 
 
@@ -247,25 +247,25 @@ def test_forced_path(monkeypatch):
 
 
 def test_decode_workspace_size_formula():
-    """A fixed 64 KiB ticket region, a fixed 3 MiB accumulator region (an
-    8-byte accumulator and a 4-byte mask per element, for M <= 4 and
-    N <= 65536), then one fp32 slot per split per element; at most 31
+    """A fixed 64 KiB ticket region, a fixed 4 MiB accumulator region (an
+    8-byte accumulator and an 8-byte mask per element, for M <= 4 and
+    N <= 65536), then one fp32 slot per split per element; at most 63
     splits."""
     for (M, K, N, g) in [(4, 8192, 7168, 128), (1, 14336, 4096, 128), (16, 8192, 1280, -1)]:
         path, ws = awq.gemm_plan(M, K, N, g)
         assert path == binding.AWQ_PATH_DECODE
         assert ws == awq.gemm_workspace_size(M, K, N, g)
-        partial = ws - 65536 - 4 * 65536 * 12
+        partial = ws - 65536 - 4 * 65536 * 16
         assert partial % (M * N * 4) == 0
         splits = partial // (M * N * 4)
-        assert 2 <= splits <= 31
+        assert 2 <= splits <= 63
         assert any(splits == -(-K // (128 * steps)) for steps in (1, 2, 4, 8))
 
 
 def test_decode_split_limit():
-    """K beyond 31 splits of 8 steps cannot take the decode kernel."""
-    assert awq.gemm_plan(1, 31 * 1024, 4096, 128)[0] == binding.AWQ_PATH_DECODE
-    assert awq.gemm_plan(1, 32 * 1024, 4096, 128)[0] != binding.AWQ_PATH_DECODE
+    """K beyond 63 splits of 8 steps cannot take the decode kernel."""
+    assert awq.gemm_plan(1, 63 * 1024, 4096, 128)[0] == binding.AWQ_PATH_DECODE
+    assert awq.gemm_plan(1, 64 * 1024, 4096, 128)[0] != binding.AWQ_PATH_DECODE
 
 
 def test_no_cpu_fallback():
