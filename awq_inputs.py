@@ -88,3 +88,24 @@ def workload_inputs(name, M, group_size=None):
     if g not in w.group_sizes:
         raise ValueError(f"group_size={g} is not a point of {name}")
     return make_inputs(M, w.K, w.N, g, w.seed, w.scale_lo, w.scale_hi, w.bias)
+
+
+def act_order_g_idx(K, group_size, seed):
+    """Row-to-group map of an activation-ordered quantisation: the K input
+    rows are visited in a seeded random order and each run of group_size
+    consecutive visited rows forms one group, so every group holds exactly
+    group_size rows scattered over the input.  int32 (K,)."""
+    if group_size <= 0 or K % group_size:
+        raise ValueError("K must be a positive multiple of group_size")
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(K)
+    g_idx = np.empty(K, dtype=np.int32)
+    g_idx[order] = np.arange(K, dtype=np.int64) // group_size
+    return g_idx
+
+
+def random_g_idx(K, G, seed):
+    """Row-to-group map with independent uniform entries in [0, G): groups
+    of unequal sizes, some possibly empty.  int32 (K,)."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, G, size=K, dtype=np.int64).astype(np.int32)

@@ -185,6 +185,7 @@ def cpu_baseline(p, g, budget_s, sample_rows=None):
 def sweep(torch, awq, dev):
     """Every point of every named workload, timed like the headline legs."""
     import awq_inputs
+    fused = {}
     for name, w in awq_inputs.WORKLOADS.items():
         if name.startswith("tiny"):
             continue                    # launch-bound, a parity case only
@@ -194,6 +195,8 @@ def sweep(torch, awq, dev):
                 steps = 200 if M <= 16 else 50
                 print(f"[sweep] {name} M={M} g={g}", file=sys.stderr, flush=True)
                 r = run_leg(torch, awq, spec, steps, 10, dev)
+                if M >= 256 and g == 128:
+                    fused[(name, M, r["K"], r["N"], r["p"]["bias"] is not None)] = r["ms_per_step"]
                 sec = r["ms_per_step"] * 1e-3
                 gbs = r["nbytes"] / sec / 1e9
                 tfs = r["nflops"] / sec / 1e12
@@ -226,6 +229,59 @@ def sweep(torch, awq, dev):
             "frac": round(nbytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes,
             "w4a16_us_per_call": round(w4_us, 3), "w4a16_speedup": round(d_us / w4_us, 2)}),
             flush=True)
+    # Context at the matrix-core-bound points: torch's float16 linear (the
+    # vendor GEMM library) on an unquantised weight of the same shape, and
+    # the unfused route (awq_dequant into a float16 weight, then that GEMM).
+    for (name, M, K, N, bias), ms in fused.items():
+        print(f"[sweep] vendor float16 GEMM M={M} K={K} N={N}", file=sys.stderr, flush=True)
+        lin_us, unfused_us = vendor_gemm_times_us(torch, awq, M, K, N, bias, dev)
+        flops = 2 * M * N * K
+        print(json.dumps({
+            "workload": f"vendor_fp16_gemm_{name}", "M": M, "K": K, "N": N, "bias": bias,
+            "kernel": "torch.nn.functional.linear (float16 weight (N, K))",
+            "us_per_call": round(lin_us, 3), "TFLOP_per_s": round(flops / lin_us / 1e6, 2),
+            "bound": "mfma", "frac": round(flops / lin_us / 1e6 / FP16_MFMA_PEAK_TFLOPS, 4),
+            "unfused_dequant_then_gemm_us": round(unfused_us, 3),
+            "w4a16_fused_us_per_call": round(ms * 1e3, 3)}), flush=True)
+
+
+def vendor_gemm_times_us(torch, awq, M, K, N, bias, dev, calls=30):
+    """Median per-call times of torch's float16 linear on a random (N, K)
+    weight, and of awq_dequant (g=128) followed by a float16 matmul."""
+    gen = torch.Generator(device="cpu").manual_seed(M + K + N)
+    x = torch.randn((M, K), generator=gen).to(torch.float16).to(dev)
+    ws = [(torch.randn((N, K), generator=gen) * 0.02).to(torch.float16).to(dev) for _ in range(2)]
+    b = (torch.randn((N,), generator=gen) * 0.1).to(torch.float16).to(dev) if bias else None
+    G = K // 128
+    qw = torch.randint(-2**31, 2**31 - 1, (K, N // 8), generator=gen, dtype=torch.int32).to(dev)
+    qz = torch.randint(-2**31, 2**31 - 1, (G, N // 8), generator=gen, dtype=torch.int32).to(dev)
+    sc = (torch.rand((G, N), generator=gen) * 0.009 + 0.001).to(torch.float16).to(dev)
+    wkn = torch.empty((K, N), dtype=torch.float16, device=dev)
+
+    def linear(i):
+        return torch.nn.functional.linear(x, ws[i % 2], b)
+
+    def unfused(i):
+        awq.dequant(qw, qz, sc, 128, out=wkn)
+        y = torch.matmul(x, wkn)
+        return y + b if b is not None else y
+
+    out = []
+    for fn in (linear, unfused):
+        for i in range(5):
+            fn(i)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for i in range(calls):
+                fn(i)
+            t1.record()
+            torch.cuda.synchronize()
+            ts.append(t0.elapsed_time(t1) * 1e3 / calls)
+        out.append(sorted(ts)[1])
+    return out[0], out[1]
 
 
 def dense_time_us(torch, awq, M, K, N, dev, calls=200):

@@ -35,6 +35,22 @@ Functions:
     dense_linear_ref(...)  -- the unquantised float16 linear (baseline), float64
     dense_linear_loops     -- its pure-Python triple loop, for tiny inputs only
 
+Row-to-group map (g_idx): the page "Predibase Lorax Linear Layer Factory"
+(Description, the get_linear bullets) lists g_idx among the quantised
+weight's components (the GPTQ tuple) and says no more about it.  Read here as
+the plainest generalisation of the contiguous groups above: g_idx is an
+integer vector of length in_features whose entry k names the scale/zero row
+of input row k, so w[k, n] = float16_RNE((q[k, n] - z[g_idx[k], n]) *
+s[g_idx[k], n]); g_idx[k] = k // group_size is the contiguous case.  The
+packing of qweight and qzeros stays the one above.
+
+    validate_gidx(...)     -- shape and range checks of a row-to-group map
+    dequant_gidx(...)      -- float16 (K, N) dequantised weight under a map
+    awq_linear_gidx_ref    -- float64 forward under a map
+    awq_linear_gidx_loops  -- its pure-Python triple loop, for tiny inputs
+    gidx_order(...)        -- stable sort of the rows by group (rows of each
+                              group contiguous, ties in input order)
+
 The unquantised linear follows the page "Predibase Lorax Linear Layer
 Factory" (Description: FastLinear, a float16 F.linear whose weight is
 (out_features, in_features); its ROCm variant sends single-token products at
@@ -218,3 +234,94 @@ def dense_linear_loops(x, w, bias):
                 acc += float(x[m][k]) * float(w[n][k])
             y[m][n] = acc + (float(bias[n]) if bias is not None else 0.0)
     return np.array(y, dtype=np.float64)
+
+
+def validate_gidx(g_idx, K, G):
+    """A row-to-group map for K input rows and G scale/zero rows: integer
+    vector of shape (K,) with every entry in [0, G).  Returns it as int64."""
+    g_idx = np.asarray(g_idx)
+    if g_idx.shape != (K,):
+        raise ValueError(f"g_idx shape {g_idx.shape} != {(K,)}")
+    if g_idx.size and not np.issubdtype(g_idx.dtype, np.integer):
+        raise ValueError("g_idx must hold integers")
+    g_idx = g_idx.astype(np.int64)
+    if G <= 0:
+        raise ValueError("need at least one group")
+    if g_idx.size and (g_idx.min() < 0 or g_idx.max() >= G):
+        raise ValueError("g_idx entries must lie in [0, G)")
+    return g_idx
+
+
+def dequant_gidx(qweight, qzeros, scales, g_idx):
+    """Dequantisation with a row-to-group map: input row k takes zero row
+    g_idx[k] of qzeros and scale row g_idx[k] of scales; each weight is
+    (q - z) * s formed exactly in float64 and rounded once to float16."""
+    scales = np.asarray(scales)
+    qzeros = np.asarray(qzeros)
+    if scales.ndim != 2:
+        raise ValueError("scales must be 2-D")
+    G = scales.shape[0]
+    K = int(qweight.shape[0])
+    N = int(qweight.shape[1]) * PACK
+    if K <= 0 or N <= 0:
+        raise ValueError("empty weight")
+    if tuple(qzeros.shape) != (G, N // PACK) or tuple(scales.shape) != (G, N):
+        raise ValueError("qzeros must be (G, N/8) and scales (G, N)")
+    grp = validate_gidx(g_idx, K, G)
+    q = unpack_int4(qweight)                       # (K, N)
+    z = unpack_int4(qzeros)                        # (G, N)
+    diff = (q - z[grp, :]).astype(np.float64)      # exact integer in [-15, 15]
+    s = scales.astype(np.float64)[grp, :]
+    with np.errstate(over="ignore"):
+        return (diff * s).astype(np.float16)       # one rounding
+
+
+def awq_linear_gidx_ref(x, qweight, qzeros, scales, g_idx, bias):
+    """Forward under a row-to-group map: y = x . dequant_gidx(...) (+ bias)
+    in float64, (*, K) -> (*, N)."""
+    x = np.asarray(x)
+    w = dequant_gidx(qweight, qzeros, scales, g_idx)
+    K, N = w.shape
+    if x.shape[-1] != K:
+        raise ValueError(f"input feature size {x.shape[-1]} != in_features {K}")
+    lead = x.shape[:-1]
+    y = x.reshape(-1, K).astype(np.float64) @ w.astype(np.float64)
+    if bias is not None:
+        b = np.asarray(bias)
+        if b.shape != (N,):
+            raise ValueError("bias must have shape (out_features,)")
+        y = y + b.astype(np.float64)[None, :]
+    return y.reshape(*lead, N)
+
+
+def awq_linear_gidx_loops(x, qweight, qzeros, scales, g_idx, bias):
+    """Pure-Python restatement of awq_linear_gidx_ref for tiny inputs: the
+    group of row k is looked up in g_idx, nibbles are taken with shifts."""
+    M = len(x)
+    K = len(qweight)
+    N = len(qweight[0]) * PACK
+    y = [[0.0] * N for _ in range(M)]
+    for n in range(N):
+        c, j = divmod(n, PACK)
+        for k in range(K):
+            gk = int(g_idx[k])
+            q = ((int(qweight[k][c]) & 0xFFFFFFFF) >> (4 * j)) & 0xF
+            z = ((int(qzeros[gk][c]) & 0xFFFFFFFF) >> (4 * j)) & 0xF
+            w = float(np.float16((q - z) * float(scales[gk][n])))
+            for m in range(M):
+                y[m][n] += float(x[m][k]) * w
+    if bias is not None:
+        for m in range(M):
+            for n in range(N):
+                y[m][n] += float(bias[n])
+    return np.array(y, dtype=np.float64)
+
+
+def gidx_order(g_idx, G):
+    """Rows sorted by group, stably: perm[j] is the input row placed j-th,
+    so the rows of group 0 come first in increasing input order, then those
+    of group 1, and so on.  Also returns the number of rows of each group."""
+    grp = validate_gidx(g_idx, len(np.asarray(g_idx)), G)
+    perm = np.argsort(grp, kind="stable")
+    counts = np.bincount(grp, minlength=G)
+    return perm.astype(np.int64), counts.astype(np.int64)

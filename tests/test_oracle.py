@@ -363,3 +363,131 @@ def test_dense_linear_pins():
         np.testing.assert_allclose(oracle.dense_linear_loops(p["x"][:, :24], wq[:24, :24], None),
                                    oracle.dense_linear_ref(p["x"][:, :24], wq[:24, :24].T, None),
                                    rtol=1e-6, atol=1e-6)
+
+
+# ------------------------------------------------ row-to-group map (g_idx)
+def test_gidx_contiguous_map_is_the_grouped_dequant():
+    """g_idx[k] = k // g is the contiguous grouping: bit-identical to the
+    independently pinned grouped dequantisation, and the worked examples'
+    weights come out bit for bit through the map."""
+    for g in (1, 4, 32, 64):
+        p = awq_inputs.make_inputs(1, 64, 24, g, seed=20 + g)
+        gi = np.arange(64) // g
+        np.testing.assert_array_equal(
+            oracle.dequant_gidx(p["qweight"], p["qzeros"], p["scales"], gi).view(np.uint16),
+            oracle.dequant(p["qweight"], p["qzeros"], p["scales"], g).view(np.uint16))
+    for ex in GOLDEN_CASES:
+        K = ex["K"]
+        g = K if ex["g"] == -1 else ex["g"]
+        w = oracle.dequant_gidx(ex["qweight"], ex["qzeros"], ex["scales"], np.arange(K) // g)
+        np.testing.assert_array_equal(w.view(np.uint16), ex["w_bits"])
+
+
+def test_gidx_constant_map_is_one_group():
+    p = awq_inputs.make_inputs(2, 48, 16, -1, seed=31)
+    np.testing.assert_array_equal(
+        oracle.dequant_gidx(p["qweight"], p["qzeros"], p["scales"], np.zeros(48, np.int32)),
+        oracle.dequant(p["qweight"], p["qzeros"], p["scales"], -1))
+
+
+def test_gidx_act_order_is_a_row_permutation_of_grouped():
+    """An activation-ordered weight is a grouped weight whose input rows were
+    shuffled: with perm a permutation of the rows, qweight_p = qweight[perm]
+    and g_idx = perm // g, every dequantised row k equals the grouped row
+    perm[k] bit for bit, and x[:, perm] through the map gives the grouped
+    forward of x (the same terms summed in another order)."""
+    K, N, g = 96, 32, 16
+    p = awq_inputs.make_inputs(3, K, N, g, seed=41, bias=True)
+    perm = np.random.default_rng(42).permutation(K)
+    qw_p = p["qweight"][perm]
+    gi = perm // g
+    w_grouped = oracle.dequant(p["qweight"], p["qzeros"], p["scales"], g)
+    w_map = oracle.dequant_gidx(qw_p, p["qzeros"], p["scales"], gi)
+    np.testing.assert_array_equal(w_map.view(np.uint16), w_grouped[perm].view(np.uint16))
+    y_map = oracle.awq_linear_gidx_ref(p["x"][:, perm], qw_p, p["qzeros"], p["scales"], gi,
+                                       p["bias"])
+    y_grp = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
+    np.testing.assert_allclose(y_map, y_grp, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("M,K,N,G,bias", [(2, 16, 8, 3, True), (1, 24, 16, 5, False)])
+def test_gidx_tiny_bruteforce_loops(M, K, N, G, bias):
+    """Arbitrary maps (unequal, possibly empty groups) against the
+    pure-Python loop."""
+    p = awq_inputs.make_inputs(M, K, N, -1, seed=K + G, bias=bias)
+    rng = np.random.default_rng(K * G)
+    qz = rng.integers(0, 2 ** 32, size=(G, N // 8), dtype=np.uint32).view(np.int32)
+    sc = rng.uniform(0.001, 0.01, size=(G, N)).astype(np.float16)
+    gi = awq_inputs.random_g_idx(K, G, seed=G)
+    ref = oracle.awq_linear_gidx_ref(p["x"], p["qweight"], qz, sc, gi, p["bias"])
+    loops = oracle.awq_linear_gidx_loops(p["x"].tolist(), p["qweight"].tolist(), qz.tolist(),
+                                         sc.tolist(), gi.tolist(),
+                                         None if p["bias"] is None else p["bias"].tolist())
+    np.testing.assert_allclose(ref, loops, rtol=1e-12, atol=1e-12)
+
+
+def test_gidx_validation():
+    with pytest.raises(ValueError):
+        oracle.validate_gidx(np.array([0, 1, 3]), 3, 3)        # entry >= G
+    with pytest.raises(ValueError):
+        oracle.validate_gidx(np.array([0, -1, 1]), 3, 3)       # negative entry
+    with pytest.raises(ValueError):
+        oracle.validate_gidx(np.array([0, 1]), 3, 3)           # wrong length
+    with pytest.raises(ValueError):
+        oracle.validate_gidx(np.array([0.0, 1.0, 2.0]), 3, 3)  # not integers
+    p = awq_inputs.make_inputs(1, 16, 8, 4, seed=1)
+    with pytest.raises(ValueError):                            # scales rows != zero rows
+        oracle.dequant_gidx(p["qweight"], p["qzeros"], p["scales"][:3], np.zeros(16, np.int32))
+
+
+def test_gidx_order_is_a_stable_sort_by_group():
+    """gidx_order: a permutation of the rows under which the map is
+    non-decreasing, rows of one group kept in input order, and group sizes
+    that count the rows; on an activation-ordered map every group holds g
+    rows, so the sorted map is exactly j // g."""
+    gi = awq_inputs.random_g_idx(200, 7, seed=3)
+    perm, counts = oracle.gidx_order(gi, 7)
+    assert sorted(perm.tolist()) == list(range(200))
+    s = gi[perm]
+    assert np.all(np.diff(s) >= 0)
+    for grp in range(7):
+        rows = perm[s == grp]
+        assert np.all(np.diff(rows) > 0)
+        assert counts[grp] == np.count_nonzero(gi == grp)
+    ao = awq_inputs.act_order_g_idx(256, 32, seed=5)
+    perm, counts = oracle.gidx_order(ao, 8)
+    np.testing.assert_array_equal(ao[perm], np.arange(256) // 32)
+    assert np.all(counts == 32)
+
+
+def test_gidx_planted_mistakes_are_caught():
+    """Copies of dequant_gidx with one slip each fail the permutation pin:
+    ignoring the map (contiguous groups), indexing the packed weight rows
+    through the map, or taking the zero row from the map but the scale row
+    from k // g."""
+    K, N, g = 64, 16, 16
+    p = awq_inputs.make_inputs(1, K, N, g, seed=7)
+    perm = np.random.default_rng(8).permutation(K)
+    qw_p, gi = p["qweight"][perm], perm // g
+    want = oracle.dequant(p["qweight"], p["qzeros"], p["scales"], g)[perm].view(np.uint16)
+
+    def make(slip):
+        def dq(qweight, qzeros, scales, g_idx):
+            q = oracle.unpack_int4(qweight)
+            z = oracle.unpack_int4(qzeros)
+            kk = np.arange(qweight.shape[0])
+            zr, sr = g_idx, g_idx
+            if slip == "ignore":
+                zr = sr = kk // g
+            elif slip == "scale_contiguous":
+                sr = kk // g
+            elif slip == "weight_rows":
+                q = q[g_idx]
+            d = (q - z[zr]).astype(np.float64) * scales.astype(np.float64)[sr]
+            return d.astype(np.float16)
+        return dq
+
+    assert np.array_equal(make(None)(qw_p, p["qzeros"], p["scales"], gi).view(np.uint16), want)
+    for slip in ("ignore", "scale_contiguous", "weight_rows"):
+        got = make(slip)(qw_p, p["qzeros"], p["scales"], gi).view(np.uint16)
+        assert not np.array_equal(got, want), slip
