@@ -41,6 +41,14 @@ SIGNATURES = {
                                 _vp, ctypes.c_size_t, _vp]),
     "awq_dequant": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "awq_dense_gemv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "awq_dequant_gidx": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "awq_gemm_gidx": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                     _i64, _vp]),
+    "awq_gidx_order": (ctypes.c_int, [_vp, _i64, _i64, _vp, ctypes.POINTER(ctypes.c_int64)]),
+    "awq_permute_rows": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
+    "awq_gemm_act_order_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64, _i64]),
+    "awq_gemm_act_order": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                          _i64, _vp, ctypes.c_size_t, _vp]),
 }
 
 _lib = None
@@ -95,6 +103,30 @@ def gemm_plan(M: int, K: int, N: int, group_size: int, x_ptr: int = 0,
     if st != AWQ_SUCCESS:
         raise AwqError(st, "awq_gemm_plan")
     return path.value, ws.value
+
+
+def gidx_order(g_idx, num_groups: int):
+    """Host-only awq_gidx_order: (perm, group_size) for a row-to-group map
+    given as a sequence or numpy array of K integers.  perm is an int32 numpy
+    array (perm[j] = row placed j-th, rows stably sorted by group);
+    group_size is K / num_groups when every group holds that many rows,
+    else 0."""
+    import numpy as np
+    g = np.ascontiguousarray(np.asarray(g_idx), dtype=np.int32)
+    if g.ndim != 1:
+        raise ValueError("g_idx must be 1-D")
+    K = g.shape[0]
+    perm = np.empty(K, dtype=np.int32)
+    gs = ctypes.c_int64(0)
+    st = lib().awq_gidx_order(g.ctypes.data if K else None, K, num_groups,
+                              perm.ctypes.data if K else None, ctypes.byref(gs))
+    if st != AWQ_SUCCESS:
+        raise AwqError(st, "awq_gidx_order")
+    return perm, gs.value
+
+
+def act_order_workspace_size(M: int, K: int, N: int, group_size: int) -> int:
+    return lib().awq_gemm_act_order_workspace_size(M, K, N, group_size)
 
 
 # --------------------------------------------------------------------- torch
@@ -263,3 +295,192 @@ def dequant(qweight, qzeros, scales, group_size: int = 128, out=None):
     if st != AWQ_SUCCESS:
         raise AwqError(st, "awq_dequant")
     return w
+
+
+def _check_map(g_idx, K, device):
+    torch = _torch()
+    _check_device("g_idx", g_idx, device)
+    if g_idx.dtype != torch.int32 or tuple(g_idx.shape) != (K,):
+        raise ValueError(f"g_idx must be int32 of shape ({K},)")
+    return g_idx.contiguous()
+
+
+def _check_map_groups(N, qzeros, scales):
+    G = scales.shape[0]
+    if scales.dim() != 2 or tuple(scales.shape) != (G, N) or tuple(qzeros.shape) != (G, N // 8):
+        raise ValueError(f"qzeros {tuple(qzeros.shape)} / scales {tuple(scales.shape)} must be "
+                         f"(G, {N // 8}) / (G, {N})")
+    return G
+
+
+def dequant_gidx(qweight, qzeros, scales, g_idx, out=None):
+    """float16 (K, N) weight dequantised under a row-to-group map through
+    awq_dequant_gidx (bit-exact); g_idx int32 (K,) on the device, G = rows
+    of scales."""
+    torch = _torch()
+    device = qweight.device
+    for name, t in (("qweight", qweight), ("qzeros", qzeros), ("scales", scales)):
+        _check_device(name, t, device)
+    if qweight.dtype != torch.int32 or qzeros.dtype != torch.int32:
+        raise TypeError("qweight and qzeros must be int32")
+    if scales.dtype != torch.float16:
+        raise TypeError("scales must be float16")
+    K = qweight.shape[0]
+    N = qweight.shape[1] * 8
+    G = _check_map_groups(N, qzeros, scales)
+    g_idx = _check_map(g_idx, K, device)
+    qweight, qzeros, scales = qweight.contiguous(), qzeros.contiguous(), scales.contiguous()
+    if out is not None:
+        _check_device("out", out, device)
+        if out.shape != (K, N) or out.dtype != torch.float16 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float16 (K, N) tensor")
+    w = out if out is not None else torch.empty((K, N), dtype=torch.float16, device=device)
+    stream = torch.cuda.current_stream(device).cuda_stream
+    st = lib().awq_dequant_gidx(qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
+                                g_idx.data_ptr(), w.data_ptr(), K, N, G, stream)
+    if st != AWQ_SUCCESS:
+        raise AwqError(st, "awq_dequant_gidx")
+    return w
+
+
+def _prep_x(x, K):
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, K)
+    if not x2.is_contiguous():
+        x2 = x2.contiguous()
+    return lead, x2
+
+
+def _prep_out(out, M, N, device):
+    torch = _torch()
+    if out is None:
+        return torch.empty((M, N), dtype=torch.float16, device=device)
+    _check_device("out", out, device)
+    if out.shape != (M, N) or out.dtype != torch.float16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float16 (M, N) tensor")
+    return out
+
+
+def gemm_gidx(x, qweight, qzeros, scales, g_idx, bias=None, out=None):
+    """y = x . W + bias under any row-to-group map, through awq_gemm_gidx
+    (the general kernel).  Returns float16 (*, N)."""
+    torch = _torch()
+    device = qweight.device
+    for name, t in (("x", x), ("qweight", qweight), ("qzeros", qzeros), ("scales", scales)):
+        _check_device(name, t, device)
+    if x.dtype != torch.float16 or scales.dtype != torch.float16:
+        raise TypeError("x and scales must be float16")
+    if qweight.dtype != torch.int32 or qzeros.dtype != torch.int32:
+        raise TypeError("qweight and qzeros must be int32")
+    K = qweight.shape[0]
+    N = qweight.shape[1] * 8
+    if x.shape[-1] != K:
+        raise ValueError(f"x has {x.shape[-1]} features, qweight has {K}")
+    G = _check_map_groups(N, qzeros, scales)
+    g_idx = _check_map(g_idx, K, device)
+    bias = _check_bias(bias, N, device)
+    lead, x2 = _prep_x(x, K)
+    M = x2.shape[0]
+    y = _prep_out(out, M, N, device)
+    qweight, qzeros, scales = qweight.contiguous(), qzeros.contiguous(), scales.contiguous()
+    stream = torch.cuda.current_stream(device).cuda_stream
+    st = lib().awq_gemm_gidx(x2.data_ptr() if M else None, qweight.data_ptr(),
+                             qzeros.data_ptr(), scales.data_ptr(), g_idx.data_ptr(),
+                             bias.data_ptr() if bias is not None else None,
+                             y.data_ptr() if M else None, M, K, N, G, stream)
+    if st != AWQ_SUCCESS:
+        raise AwqError(st, "awq_gemm_gidx")
+    return y.reshape(*lead, N)
+
+
+def _check_bias(bias, N, device):
+    torch = _torch()
+    if bias is None:
+        return None
+    _check_device("bias", bias, device)
+    if bias.dtype != torch.float16:
+        raise TypeError("bias must be float16")
+    if tuple(bias.shape) != (N,):
+        raise ValueError(f"bias shape {tuple(bias.shape)} != ({N},)")
+    return bias.contiguous()
+
+
+def permute_rows(qweight, perm, out=None):
+    """qweight[perm] for a packed int32 (K, N/8) weight through
+    awq_permute_rows; perm int32 (K,) on the device."""
+    torch = _torch()
+    device = qweight.device
+    _check_device("qweight", qweight, device)
+    if qweight.dtype != torch.int32:
+        raise TypeError("qweight must be int32")
+    K = qweight.shape[0]
+    N = qweight.shape[1] * 8
+    perm = _check_map(perm, K, device)
+    qweight = qweight.contiguous()
+    if out is None:
+        out = torch.empty_like(qweight)
+    else:
+        _check_device("out", out, device)
+        if out.shape != qweight.shape or out.dtype != torch.int32 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous int32 tensor shaped like qweight")
+    stream = torch.cuda.current_stream(device).cuda_stream
+    st = lib().awq_permute_rows(qweight.data_ptr(), perm.data_ptr(), out.data_ptr(), K, N, stream)
+    if st != AWQ_SUCCESS:
+        raise AwqError(st, "awq_permute_rows")
+    return out
+
+
+def prepare_act_order(qweight, g_idx, num_groups: int):
+    """Load-time reorder of an activation-order weight: (qweight_sorted,
+    perm on the device, group_size).  g_idx may be a host sequence, a numpy
+    array or a tensor; every group must hold the same number of rows (else
+    ValueError: such maps take gemm_gidx)."""
+    torch = _torch()
+    if hasattr(g_idx, "detach"):
+        g_idx = g_idx.detach().cpu().numpy()
+    perm, group_size = gidx_order(g_idx, num_groups)
+    if group_size == 0:
+        raise ValueError("the groups of this map differ in size; use gemm_gidx")
+    perm_dev = torch.from_numpy(perm).to(qweight.device)
+    return permute_rows(qweight, perm_dev), perm_dev, group_size
+
+
+def gemm_act_order(x, perm, qweight_sorted, qzeros, scales, bias=None, group_size: int = 128,
+                   out=None, workspace=None):
+    """y = x[:, perm] . W_sorted + bias through awq_gemm_act_order (equal to
+    the forward of the original activation-order weight).  Returns float16
+    (*, N)."""
+    torch = _torch()
+    device = qweight_sorted.device
+    for name, t in (("x", x), ("qweight_sorted", qweight_sorted), ("qzeros", qzeros),
+                    ("scales", scales)):
+        _check_device(name, t, device)
+    if x.dtype != torch.float16 or scales.dtype != torch.float16:
+        raise TypeError("x and scales must be float16")
+    if qweight_sorted.dtype != torch.int32 or qzeros.dtype != torch.int32:
+        raise TypeError("qweight_sorted and qzeros must be int32")
+    K = qweight_sorted.shape[0]
+    N = qweight_sorted.shape[1] * 8
+    if x.shape[-1] != K:
+        raise ValueError(f"x has {x.shape[-1]} features, qweight has {K}")
+    _check_group_shapes(K, N, group_size, qzeros, scales)
+    perm = _check_map(perm, K, device)
+    bias = _check_bias(bias, N, device)
+    lead, x2 = _prep_x(x, K)
+    M = x2.shape[0]
+    y = _prep_out(out, M, N, device)
+    qweight_sorted = qweight_sorted.contiguous()
+    qzeros, scales = qzeros.contiguous(), scales.contiguous()
+    stream = torch.cuda.current_stream(device).cuda_stream
+    need = act_order_workspace_size(M, K, N, group_size) if M > 0 else 0
+    ws = _workspace(device, stream, need) if workspace is None else workspace
+    ws_ptr = ws.data_ptr() if ws is not None else None
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    st = lib().awq_gemm_act_order(x2.data_ptr() if M else None, perm.data_ptr(),
+                                  qweight_sorted.data_ptr(), qzeros.data_ptr(),
+                                  scales.data_ptr(), bias.data_ptr() if bias is not None else None,
+                                  y.data_ptr() if M else None, M, K, N, group_size, ws_ptr,
+                                  ws_bytes, stream)
+    if st != AWQ_SUCCESS:
+        raise AwqError(st, "awq_gemm_act_order")
+    return y.reshape(*lead, N)

@@ -29,6 +29,7 @@ SOURCES = [
     "awq_decode.hip",
     "awq_prefill.hip",
     "awq_dense.hip",
+    "awq_gidx.hip",
 ]
 
 COMMON_FLAGS = [

@@ -29,17 +29,7 @@ const char* awq_status_string(int status) {
 }
 
 size_t awq_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size) {
-  Problem p;
-  if (awq::validate_shape(M, K, N, group_size, &p) != AWQ_SUCCESS) return 0;
-  const awq::Alignment al{true, true, true};
-  size_t need = 0;
-  Plan pl;
-  if (awq::decode_supported(p, al) && awq::make_plan(p, al, AWQ_PATH_DECODE, &pl) == AWQ_SUCCESS)
-    need = pl.ws_bytes;
-  if (awq::prefill_supported(p, al) && awq::make_plan(p, al, AWQ_PATH_PREFILL, &pl) == AWQ_SUCCESS &&
-      pl.ws_bytes > need)
-    need = pl.ws_bytes;
-  return need;
+  return awq::gemm_workspace_size(M, K, N, group_size);
 }
 
 int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size, const void* x,
@@ -60,21 +50,21 @@ int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size, const voi
   return AWQ_SUCCESS;
 }
 
-int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void* scales,
-             const void* bias, void* y, int64_t M, int64_t K, int64_t N, int64_t group_size,
-             void* workspace, size_t workspace_bytes, void* stream) {
-  Problem p;
-  int st = awq::validate_shape(M, K, N, group_size, &p);
-  if (st != AWQ_SUCCESS) return st;
-  st = awq::validate_gemm_pointers(x, qweight, qzeros, scales, bias, y, M);
-  if (st != AWQ_SUCCESS) return st;
-  if (M == 0) return AWQ_SUCCESS;
+}  // extern "C"
+
+namespace {
+
+// Plans and launches the grouped forward for a validated problem p (x, y
+// non-NULL and M > 0).  Shared by awq_gemm and awq_gemm_act_order.
+int run_gemm(const Problem& p, const void* x, const void* qweight, const void* qzeros,
+             const void* scales, const void* bias, void* y, void* workspace,
+             size_t workspace_bytes, hipStream_t s) {
   const int force = awq::force_path_from_env();
   if (force < 0) return AWQ_ERROR_INVALID_VALUE;
   Plan pl;
   const awq::Alignment al{awq::aligned(x, 16), awq::aligned(scales, 16),
                           awq::aligned(qweight, 16)};
-  st = awq::make_plan(p, al, force, &pl);
+  int st = awq::make_plan(p, al, force, &pl);
   if (st != AWQ_SUCCESS) return st;
   if (pl.ws_bytes > 0) {
     if (!workspace || workspace_bytes < pl.ws_bytes) return AWQ_ERROR_WORKSPACE;
@@ -89,7 +79,6 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void*
   auto* yh = static_cast<_Float16*>(y);
   const int iM = static_cast<int>(p.M), iK = static_cast<int>(p.K), iN = static_cast<int>(p.N);
   const int ig = static_cast<int>(p.g), iG = static_cast<int>(p.G);
-  hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipError_t e = hipErrorInvalidValue;
   switch (pl.path) {
@@ -103,12 +92,29 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void*
                               workspace, s);
       break;
     case AWQ_PATH_GENERIC:
-      e = awq::launch_generic(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, s);
+      e = awq::launch_generic(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, nullptr, iG, s);
       break;
     default:
       return AWQ_ERROR_INVALID_VALUE;
   }
   return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void* scales,
+             const void* bias, void* y, int64_t M, int64_t K, int64_t N, int64_t group_size,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  Problem p;
+  int st = awq::validate_shape(M, K, N, group_size, &p);
+  if (st != AWQ_SUCCESS) return st;
+  st = awq::validate_gemm_pointers(x, qweight, qzeros, scales, bias, y, M);
+  if (st != AWQ_SUCCESS) return st;
+  if (M == 0) return AWQ_SUCCESS;
+  return run_gemm(p, x, qweight, qzeros, scales, bias, y, workspace, workspace_bytes,
+                  static_cast<hipStream_t>(stream));
 }
 
 int awq_dense_gemv(const void* x, const void* w, const void* bias, void* y, int64_t M, int64_t K,
@@ -134,9 +140,96 @@ int awq_dequant(const void* qweight, const void* qzeros, const void* scales, voi
                                      static_cast<const uint32_t*>(qzeros),
                                      static_cast<const _Float16*>(scales),
                                      static_cast<_Float16*>(w), static_cast<int>(p.K),
-                                     static_cast<int>(p.N), static_cast<int>(p.g),
-                                     static_cast<hipStream_t>(stream));
+                                     static_cast<int>(p.N), static_cast<int>(p.g), nullptr,
+                                     static_cast<int>(p.G), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP;
+}
+
+int awq_dequant_gidx(const void* qweight, const void* qzeros, const void* scales,
+                     const void* g_idx, void* w, int64_t K, int64_t N, int64_t num_groups,
+                     void* stream) {
+  Problem p;
+  int st = awq::validate_gidx_shape(0, K, N, num_groups, &p);
+  if (st != AWQ_SUCCESS) return st;
+  st = awq::validate_dequant_pointers(qweight, qzeros, scales, w);
+  if (st != AWQ_SUCCESS) return st;
+  if (!g_idx) return AWQ_ERROR_INVALID_VALUE;
+  if (!awq::aligned(g_idx, 4)) return AWQ_ERROR_MISALIGNED;
+  const hipError_t e = awq::launch_dequant(
+      static_cast<const uint32_t*>(qweight), static_cast<const uint32_t*>(qzeros),
+      static_cast<const _Float16*>(scales), static_cast<_Float16*>(w), static_cast<int>(p.K),
+      static_cast<int>(p.N), 1, static_cast<const int32_t*>(g_idx), static_cast<int>(p.G),
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP;
+}
+
+int awq_gemm_gidx(const void* x, const void* qweight, const void* qzeros, const void* scales,
+                  const void* g_idx, const void* bias, void* y, int64_t M, int64_t K, int64_t N,
+                  int64_t num_groups, void* stream) {
+  Problem p;
+  int st = awq::validate_gidx_shape(M, K, N, num_groups, &p);
+  if (st != AWQ_SUCCESS) return st;
+  st = awq::validate_gemm_pointers(x, qweight, qzeros, scales, bias, y, M);
+  if (st != AWQ_SUCCESS) return st;
+  if (!g_idx) return AWQ_ERROR_INVALID_VALUE;
+  if (!awq::aligned(g_idx, 4)) return AWQ_ERROR_MISALIGNED;
+  if (M == 0) return AWQ_SUCCESS;
+  const hipError_t e = awq::launch_generic(
+      static_cast<const _Float16*>(x), static_cast<const uint32_t*>(qweight),
+      static_cast<const uint32_t*>(qzeros), static_cast<const _Float16*>(scales),
+      static_cast<const _Float16*>(bias), static_cast<_Float16*>(y), static_cast<int>(p.M),
+      static_cast<int>(p.K), static_cast<int>(p.N), 1, static_cast<const int32_t*>(g_idx),
+      static_cast<int>(p.G), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP;
+}
+
+int awq_gidx_order(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* perm,
+                   int64_t* group_size) {
+  return awq::gidx_order(g_idx, K, num_groups, perm, group_size);
+}
+
+int awq_permute_rows(const void* qweight, const void* perm, void* qweight_out, int64_t K,
+                     int64_t N, void* stream) {
+  Problem p;
+  int st = awq::validate_shape(0, K, N, -1, &p);
+  if (st != AWQ_SUCCESS) return st;
+  if (!qweight || !perm || !qweight_out) return AWQ_ERROR_INVALID_VALUE;
+  if (!awq::aligned(qweight, 4) || !awq::aligned(perm, 4) || !awq::aligned(qweight_out, 4))
+    return AWQ_ERROR_MISALIGNED;
+  const hipError_t e = awq::launch_permute_rows(
+      static_cast<const uint32_t*>(qweight), static_cast<const int32_t*>(perm),
+      static_cast<uint32_t*>(qweight_out), static_cast<int>(K), static_cast<int>(N / 8),
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP;
+}
+
+size_t awq_gemm_act_order_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size) {
+  return awq::act_order_workspace_size(M, K, N, group_size);
+}
+
+int awq_gemm_act_order(const void* x, const void* perm, const void* qweight_sorted,
+                       const void* qzeros, const void* scales, const void* bias, void* y,
+                       int64_t M, int64_t K, int64_t N, int64_t group_size, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  Problem p;
+  int st = awq::validate_shape(M, K, N, group_size, &p);
+  if (st != AWQ_SUCCESS) return st;
+  st = awq::validate_gemm_pointers(x, qweight_sorted, qzeros, scales, bias, y, M);
+  if (st != AWQ_SUCCESS) return st;
+  if (!perm) return AWQ_ERROR_INVALID_VALUE;
+  if (!awq::aligned(perm, 4)) return AWQ_ERROR_MISALIGNED;
+  if (M == 0) return AWQ_SUCCESS;
+  const size_t need = awq::act_order_workspace_size(M, K, N, group_size);
+  if (!workspace || workspace_bytes < need) return AWQ_ERROR_WORKSPACE;
+  if (!awq::aligned(workspace, 256)) return AWQ_ERROR_MISALIGNED;
+  const size_t xoff = awq::act_order_x_offset(M, K, N, group_size);
+  auto* xp = reinterpret_cast<_Float16*>(static_cast<char*>(workspace) + xoff);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = awq::launch_gather_cols(static_cast<const _Float16*>(x),
+                                               static_cast<const int32_t*>(perm), xp,
+                                               static_cast<int>(M), static_cast<int>(K), s);
+  if (e != hipSuccess) return AWQ_ERROR_HIP;
+  return run_gemm(p, xp, qweight_sorted, qzeros, scales, bias, y, workspace, xoff, s);
 }
 
 }  // extern "C"

@@ -2,6 +2,10 @@
 // a multiple of 8, unaligned x or scales).  Plain fp32 FMA, no matrix cores:
 // this is the correctness fallback, not a fast path.
 //
+// It also runs the forward under an arbitrary row-to-group map (awq_gemm_gidx:
+// the g_idx of the GPTQ tuple on the page "Predibase Lorax Linear Layer
+// Factory", Description), looking row k's group up instead of k / g.
+//
 // Work-group tile: 16 rows x 256 columns, one output column per thread.  A
 // 16 x 64 slab of x is staged in LDS as fp32; each thread dequantises its
 // column's weights exactly (float16_RNE((q - z) * s)) and accumulates the 16
@@ -18,7 +22,7 @@ __global__ __launch_bounds__(256) void generic_kernel(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
     const _Float16* __restrict__ bias, _Float16* __restrict__ y,
-    int M, int K, int N, int g, int n_tiles) {
+    int M, int K, int N, int g, const int32_t* __restrict__ gidx, int G, int n_tiles) {
   __shared__ float xs[kRows][kKChunk];
   const int NW = N / 8;
   const int mt = blockIdx.x / n_tiles;
@@ -41,10 +45,12 @@ __global__ __launch_bounds__(256) void generic_kernel(
       const int kend = min(kKChunk, K - k0);
       for (int kk = 0; kk < kend; ++kk) {
         const int k = k0 + kk;
-        const int grp = k / g;
+        // An entry of the map outside [0, G) reads zero point 0 and scale 0.
+        const int grp = gidx ? gidx[k] : k / g;
+        const bool gok = grp >= 0 && grp < G;
         const int q = (qw[k * NW + c] >> shift) & 0xF;
-        const int z = (qz[grp * NW + c] >> shift) & 0xF;
-        const float s = static_cast<float>(sc[grp * N + n]);
+        const int z = gok ? (qz[grp * NW + c] >> shift) & 0xF : 0;
+        const float s = gok ? static_cast<float>(sc[grp * N + n]) : 0.f;
         const float w = static_cast<float>(static_cast<_Float16>(static_cast<float>(q - z) * s));
 #pragma unroll
         for (int r = 0; r < kRows; ++r) acc[r] = fmaf(xs[r][kk], w, acc[r]);
@@ -66,11 +72,12 @@ __global__ __launch_bounds__(256) void generic_kernel(
 
 hipError_t launch_generic(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                           const _Float16* scales, const _Float16* bias, _Float16* y,
-                          int M, int K, int N, int g, hipStream_t stream) {
+                          int M, int K, int N, int g, const int32_t* gidx, int G,
+                          hipStream_t stream) {
   const int n_tiles = (N + 255) / 256;
   const int m_tiles = (M + kRows - 1) / kRows;
   hipLaunchKernelGGL(generic_kernel, dim3(n_tiles * m_tiles), dim3(256), 0, stream,
-                     x, qweight, qzeros, scales, bias, y, M, K, N, g, n_tiles);
+                     x, qweight, qzeros, scales, bias, y, M, K, N, g, gidx, G, n_tiles);
   return hipGetLastError();
 }
 

@@ -4,6 +4,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <vector>
+
 #include "awq.h"
 
 namespace awq {
@@ -225,6 +227,73 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
   }
   *out = pl;
   return AWQ_SUCCESS;
+}
+
+size_t gemm_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size) {
+  Problem p;
+  if (validate_shape(M, K, N, group_size, &p) != AWQ_SUCCESS) return 0;
+  const Alignment al{true, true, true};
+  size_t need = 0;
+  Plan pl;
+  if (decode_supported(p, al) && make_plan(p, al, AWQ_PATH_DECODE, &pl) == AWQ_SUCCESS)
+    need = pl.ws_bytes;
+  if (prefill_supported(p, al) && make_plan(p, al, AWQ_PATH_PREFILL, &pl) == AWQ_SUCCESS &&
+      pl.ws_bytes > need)
+    need = pl.ws_bytes;
+  return need;
+}
+
+int validate_gidx_shape(int64_t M, int64_t K, int64_t N, int64_t num_groups, Problem* out) {
+  if (M < 0 || K <= 0 || N <= 0 || num_groups <= 0) return AWQ_ERROR_INVALID_VALUE;
+  if (N % 8 != 0) return AWQ_ERROR_SHAPE;
+  if (K > kMaxElems || N > kMaxElems || M > kMaxElems || num_groups > kMaxElems)
+    return AWQ_ERROR_SHAPE;
+  if (K * N > kMaxElems || M * K > kMaxElems || M * N > kMaxElems || num_groups * N > kMaxElems)
+    return AWQ_ERROR_SHAPE;
+  if (out) {
+    out->M = M;
+    out->K = K;
+    out->N = N;
+    out->g = 0;
+    out->G = num_groups;
+  }
+  return AWQ_SUCCESS;
+}
+
+int gidx_order(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* perm,
+               int64_t* group_size) {
+  if (!g_idx || !perm || K <= 0 || num_groups <= 0) return AWQ_ERROR_INVALID_VALUE;
+  if (K > kMaxElems || num_groups > kMaxElems) return AWQ_ERROR_SHAPE;
+  std::vector<int64_t> start(static_cast<size_t>(num_groups) + 1, 0);
+  for (int64_t k = 0; k < K; ++k) {
+    const int32_t gk = g_idx[k];
+    if (gk < 0 || gk >= num_groups) return AWQ_ERROR_INVALID_VALUE;
+    ++start[static_cast<size_t>(gk) + 1];
+  }
+  bool uniform = K % num_groups == 0;
+  for (int64_t j = 0; j < num_groups; ++j) {
+    if (start[j + 1] != K / num_groups) uniform = false;
+    start[j + 1] += start[j];
+  }
+  for (int64_t k = 0; k < K; ++k) perm[start[g_idx[k]]++] = static_cast<int32_t>(k);
+  if (group_size) *group_size = uniform ? K / num_groups : 0;
+  return AWQ_SUCCESS;
+}
+
+size_t act_order_x_offset(int64_t M, int64_t K, int64_t N, int64_t group_size) {
+  // Never inside the regions that must stay zero between calls, whatever
+  // this problem's own plan needs: the workspace may also serve awq_gemm
+  // calls of other shapes.
+  size_t base = gemm_workspace_size(M, K, N, group_size);
+  const size_t fixed = kTicketRegionBytes + kAtomicRegionBytes;
+  if (base < fixed) base = fixed;
+  return round_up(base, 256);
+}
+
+size_t act_order_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size) {
+  if (M <= 0 || validate_shape(M, K, N, group_size, nullptr) != AWQ_SUCCESS) return 0;
+  return act_order_x_offset(M, K, N, group_size) +
+         round_up(static_cast<size_t>(M) * static_cast<size_t>(K) * 2, 256);
 }
 
 int force_path_from_env() {

@@ -95,12 +95,37 @@ struct Alignment {
 bool decode_supported(const Problem& p, const Alignment& al);
 bool prefill_supported(const Problem& p, const Alignment& al);
 
+// awq_gemm_workspace_size: the larger of the decode and prefill plans' needs
+// (0 for invalid shapes).
+size_t gemm_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size);
+
 // force: 0 = automatic, otherwise an awq_path value.  Returns an awq_status.
 int make_plan(const Problem& p, const Alignment& al, int force, Plan* out);
 
 // Parses AWQ_FORCE_PATH.  Returns 0 (unset/automatic), an awq_path value, or
 // -1 for an unrecognised value.
 int force_path_from_env();
+
+// Row-to-group map problems (awq_dequant_gidx, awq_gemm_gidx): M >= 0,
+// K > 0, N > 0 with N % 8 == 0, num_groups >= 1, every operand (including
+// scales, num_groups x N) below 2^31 elements.  Fills p with g = 0 (no
+// contiguous grouping) and G = num_groups.  Returns an awq_status value.
+int validate_gidx_shape(int64_t M, int64_t K, int64_t N, int64_t num_groups, Problem* out);
+
+// Stable order of the K rows by group (counting sort): perm[j] is the row
+// placed j-th.  Entries of g_idx outside [0, num_groups) give
+// AWQ_ERROR_INVALID_VALUE (perm untouched).  *group_size receives K /
+// num_groups when every group holds exactly that many rows, else 0.
+int gidx_order(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* perm,
+               int64_t* group_size);
+
+// Workspace of awq_gemm_act_order: the awq_gemm workspace of the problem
+// (at least the fixed ticket and accumulator regions), rounded up to 256
+// bytes, then room for x with its columns reordered (M x K float16, rounded
+// up to 256 bytes).  0 for M == 0 or invalid shapes.
+size_t act_order_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size);
+// Byte offset of the reordered x inside that workspace.
+size_t act_order_x_offset(int64_t M, int64_t K, int64_t N, int64_t group_size);
 
 inline bool aligned(const void* p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;

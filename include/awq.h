@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define AWQ_ABI_VERSION 2
+#define AWQ_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 enum awq_status {
@@ -131,6 +131,87 @@ int awq_dequant(const void* qweight, const void* qzeros, const void* scales,
  * M == 0 is a no-op.  Enqueued on `stream`, nothing synchronises. */
 int awq_dense_gemv(const void* x, const void* w, const void* bias, void* y,
                    int64_t M, int64_t K, int64_t N, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Row-to-group map (g_idx).  The page "Predibase Lorax Linear Layer Factory"
+ * (Description, the get_linear bullets) lists g_idx among the components of
+ * a GPTQ-quantised weight and says nothing more.  This library reads it as
+ * the per-row generalisation of the contiguous groups above: g_idx is int32
+ * (K) and input row k takes zero row and scale row g_idx[k],
+ *
+ *     W[k, n] = float16_RNE((q[k, n] - z[g_idx[k], n]) * s[g_idx[k], n]),
+ *
+ * with qweight/qzeros packed as above, qzeros (G, N/8) and scales (G, N),
+ * G = num_groups >= 1.  g_idx[k] = k / g is the contiguous case.
+ *
+ * Two routes.  Any map: awq_dequant_gidx, awq_gemm_gidx (general kernel,
+ * slow).  A map that gives every group the same number of rows (activation
+ * order, where the rows of each group are scattered over the input): sort
+ * the rows by group once at load time (awq_gidx_order on the host, then
+ * awq_permute_rows on the device), after which awq_gemm_act_order runs the
+ * fast grouped kernels.
+ * ------------------------------------------------------------------------ */
+
+/* w[K, N] float16 dequantised under a row-to-group map, bit-exact.
+ * g_idx: DEVICE int32 (K), 4-byte aligned.  The map lives in device memory,
+ * so its entries are not checked on the host: an entry outside
+ * [0, num_groups) is read as zero point 0 and scale 0 (that row of w is
+ * zero); no access goes outside the operands.  Other arguments, errors and
+ * stream behaviour as awq_dequant; num_groups <= 0 is AWQ_ERROR_INVALID_VALUE. */
+int awq_dequant_gidx(const void* qweight, const void* qzeros, const void* scales,
+                     const void* g_idx, void* w, int64_t K, int64_t N, int64_t num_groups,
+                     void* stream);
+
+/* y[M, N] = float16_RNE(fp32 accumulation of x . W + bias) under any
+ * row-to-group map (W as above).  The general kernel (plain fp32 FMA): a
+ * correctness route for maps with groups of unequal size; activation-order
+ * maps should take awq_gemm_act_order.  g_idx as in awq_dequant_gidx.  No
+ * workspace.  Other arguments, errors and stream behaviour as awq_gemm. */
+int awq_gemm_gidx(const void* x, const void* qweight, const void* qzeros, const void* scales,
+                  const void* g_idx, const void* bias, void* y, int64_t M, int64_t K, int64_t N,
+                  int64_t num_groups, void* stream);
+
+/* Host-only, no HIP call.  Stable order of the K input rows by group:
+ * perm[j] (HOST int32 (K), written) is the row placed j-th, so the rows of
+ * group 0 come first in increasing row order, then those of group 1, ...
+ * g_idx: HOST int32 (K).  *group_size (may be NULL) receives K / num_groups
+ * when every group holds exactly that many rows (the reordered weight is then
+ * a grouped weight of that group size), else 0.  An entry outside
+ * [0, num_groups), NULL pointers, K <= 0 or num_groups <= 0 give
+ * AWQ_ERROR_INVALID_VALUE and leave perm untouched. */
+int awq_gidx_order(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* perm,
+                   int64_t* group_size);
+
+/* Reorders the rows of a packed weight: qweight_out[j, :] = qweight[perm[j], :]
+ * for int32 (K, N/8) matrices (DEVICE pointers, 4-byte aligned; must not
+ * overlap).  perm: DEVICE int32 (K), e.g. awq_gidx_order's output copied to
+ * the device; an entry outside [0, K) writes a row of zeros.  N % 8 != 0 is
+ * AWQ_ERROR_SHAPE.  Enqueued on `stream`; a load-time step. */
+int awq_permute_rows(const void* qweight, const void* perm, void* qweight_out, int64_t K,
+                     int64_t N, void* stream);
+
+/* Workspace bytes of awq_gemm_act_order: the awq_gemm workspace of the same
+ * problem (at least its fixed zero-filled regions), then M x K float16 for x
+ * with its columns reordered.  0 for M == 0 or invalid shapes. */
+size_t awq_gemm_act_order_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size);
+
+/* Forward of an activation-order weight after the load-time reorder:
+ *   y = float16_RNE(fp32 accumulation of x[:, perm] . W_sorted + bias),
+ * W_sorted the grouped weight (group_size) of qweight_sorted, qzeros and
+ * scales.  With perm and group_size from awq_gidx_order and qweight_sorted =
+ * awq_permute_rows(qweight, perm), this equals x . W (+ bias) for the
+ * original (qweight, g_idx): the same products summed in another order.
+ * perm: DEVICE int32 (K), 4-byte aligned (entries outside [0, K) read x as 0).
+ * workspace: at least awq_gemm_act_order_workspace_size(...) bytes, 256-byte
+ * aligned, zero-filled once like awq_gemm's (the same buffer may serve both);
+ * the reordered x is written into it, so concurrent calls must not share it.
+ * Two launches on `stream`: the column reorder of x, then the awq_gemm kernel
+ * family for the problem.  Other arguments, errors and stream behaviour as
+ * awq_gemm. */
+int awq_gemm_act_order(const void* x, const void* perm, const void* qweight_sorted,
+                       const void* qzeros, const void* scales, const void* bias, void* y,
+                       int64_t M, int64_t K, int64_t N, int64_t group_size, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

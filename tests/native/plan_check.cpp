@@ -103,6 +103,43 @@ int main() {
             }
           }
         }
+  // Row-to-group maps: validation, the stable counting sort and its group
+  // size report, bad entries, and the act-order workspace rule.
+  EXPECT(validate_gidx_shape(4, 256, 128, 4, &p) == AWQ_SUCCESS && p.G == 4 && p.g == 0);
+  EXPECT(validate_gidx_shape(4, 256, 128, 0, &p) == AWQ_ERROR_INVALID_VALUE);
+  EXPECT(validate_gidx_shape(4, 256, 121, 4, &p) == AWQ_ERROR_SHAPE);
+  EXPECT(validate_gidx_shape(1, 8, 8, INT64_MAX, &p) == AWQ_ERROR_SHAPE);
+  EXPECT(validate_gidx_shape(1, 8, (int64_t)1 << 20, (int64_t)1 << 12, &p) == AWQ_ERROR_SHAPE);
+  {
+    const int32_t gi[6] = {2, 0, 1, 0, 2, 1};
+    int32_t perm[6] = {-1, -1, -1, -1, -1, -1};
+    int64_t gs = -1;
+    EXPECT(gidx_order(gi, 6, 3, perm, &gs) == AWQ_SUCCESS && gs == 2);
+    const int32_t want[6] = {1, 3, 2, 5, 0, 4};
+    for (int i = 0; i < 6; ++i) EXPECT(perm[i] == want[i]);
+    const int32_t uneven[5] = {0, 0, 1, 0, 1};
+    EXPECT(gidx_order(uneven, 5, 2, perm, &gs) == AWQ_SUCCESS && gs == 0);
+    EXPECT(gidx_order(uneven, 5, 3, perm, nullptr) == AWQ_SUCCESS);   // an empty group
+    const int32_t bad[3] = {0, 3, 1};
+    int32_t keep[3] = {7, 7, 7};
+    EXPECT(gidx_order(bad, 3, 3, keep, &gs) == AWQ_ERROR_INVALID_VALUE);
+    EXPECT(keep[0] == 7 && keep[1] == 7 && keep[2] == 7);
+    const int32_t neg[2] = {0, -1};
+    EXPECT(gidx_order(neg, 2, 2, keep, &gs) == AWQ_ERROR_INVALID_VALUE);
+    EXPECT(gidx_order(nullptr, 2, 2, keep, &gs) == AWQ_ERROR_INVALID_VALUE);
+    EXPECT(gidx_order(gi, 6, 0, perm, &gs) == AWQ_ERROR_INVALID_VALUE);
+  }
+  {
+    const size_t fixed = kTicketRegionBytes + kAtomicRegionBytes;
+    EXPECT(act_order_workspace_size(0, 256, 128, 64) == 0);
+    EXPECT(act_order_workspace_size(4, 256, 128, 48) == 0);
+    EXPECT(act_order_x_offset(4, 256, 128, 64) >= fixed);
+    EXPECT(act_order_x_offset(16, 8192, 7168, 128) >= gemm_workspace_size(16, 8192, 7168, 128));
+    EXPECT(act_order_x_offset(16, 8192, 7168, 128) % 256 == 0);
+    EXPECT(act_order_workspace_size(16, 8192, 7168, 128) ==
+           act_order_x_offset(16, 8192, 7168, 128) + 16 * 8192 * 2);
+  }
+
   if (failures) {
     fprintf(stderr, "%d failures\n", failures);
     return 1;

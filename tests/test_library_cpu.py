@@ -124,30 +124,6 @@ def test_gemm_workspace_checked_before_launch():
     assert _gemm(M=M, K=K, N=N, g=g, ws=A + 8, wsb=need) == binding.AWQ_ERROR_MISALIGNED
 
 
-def _dense(x=A, w=A, bias=None, y=A, M=1, K=8192, N=1280):
-    return awq.lib().awq_dense_gemv(x, w, bias, y, M, K, N, None)
-
-
-@pytest.mark.parametrize("kwargs,status", [
-    (dict(w=None), binding.AWQ_ERROR_INVALID_VALUE),
-    (dict(x=None), binding.AWQ_ERROR_INVALID_VALUE),
-    (dict(M=-1), binding.AWQ_ERROR_INVALID_VALUE),
-    (dict(K=0), binding.AWQ_ERROR_INVALID_VALUE),
-    (dict(N=0), binding.AWQ_ERROR_INVALID_VALUE),
-    (dict(M=5), binding.AWQ_ERROR_SHAPE),            # at most 4 rows
-    (dict(K=100), binding.AWQ_ERROR_SHAPE),          # K % 8 != 0
-    (dict(M=4, K=16392), binding.AWQ_ERROR_SHAPE),   # x does not fit the LDS stage
-    (dict(x=A + 8), binding.AWQ_ERROR_MISALIGNED),
-    (dict(w=A + 4), binding.AWQ_ERROR_MISALIGNED),
-    (dict(y=A + 1), binding.AWQ_ERROR_MISALIGNED),
-    (dict(bias=A + 1), binding.AWQ_ERROR_MISALIGNED),
-    (dict(M=0, x=None, y=None), binding.AWQ_SUCCESS),  # empty batch: no launch
-])
-def test_dense_validation(kwargs, status):
-    """The unquantised baseline rejects every invalid argument on the host."""
-    assert _dense(**kwargs) == status
-
-
 @pytest.mark.parametrize("kwargs,status", [
     (dict(qw=None), binding.AWQ_ERROR_INVALID_VALUE),
     (dict(w=None), binding.AWQ_ERROR_INVALID_VALUE),
@@ -311,3 +287,96 @@ def test_validation_under_sanitizers(tmp_path):
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stdout + res.stderr
     assert "plan_check ok" in res.stdout
+
+
+# ------------------------------------------------- row-to-group map (g_idx)
+def _dq_gidx(qw=A, qz=A, sc=A, gi=A, w=A, K=256, N=128, G=4):
+    return awq.lib().awq_dequant_gidx(qw, qz, sc, gi, w, K, N, G, None)
+
+
+def _gemm_gidx(x=A, qw=A, qz=A, sc=A, gi=A, bias=None, y=A, M=4, K=256, N=128, G=4):
+    return awq.lib().awq_gemm_gidx(x, qw, qz, sc, gi, bias, y, M, K, N, G, None)
+
+
+def _act(x=A, perm=A, qw=A, qz=A, sc=A, bias=None, y=A, M=4, K=256, N=128, g=64, ws=None,
+         wsb=0):
+    return awq.lib().awq_gemm_act_order(x, perm, qw, qz, sc, bias, y, M, K, N, g, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn,kwargs,status", [
+    (_dq_gidx, dict(gi=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (_dq_gidx, dict(G=0), binding.AWQ_ERROR_INVALID_VALUE),
+    (_dq_gidx, dict(N=12), binding.AWQ_ERROR_SHAPE),
+    (_dq_gidx, dict(K=65536, N=65536), binding.AWQ_ERROR_SHAPE),
+    (_dq_gidx, dict(G=1 << 20, N=4096), binding.AWQ_ERROR_SHAPE),   # scales >= 2^31 elements
+    (_dq_gidx, dict(gi=A + 2), binding.AWQ_ERROR_MISALIGNED),
+    (_dq_gidx, dict(w=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (_gemm_gidx, dict(gi=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (_gemm_gidx, dict(G=-1), binding.AWQ_ERROR_INVALID_VALUE),
+    (_gemm_gidx, dict(x=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (_gemm_gidx, dict(N=100), binding.AWQ_ERROR_SHAPE),
+    (_gemm_gidx, dict(gi=A + 1), binding.AWQ_ERROR_MISALIGNED),
+    (_gemm_gidx, dict(x=A + 1), binding.AWQ_ERROR_MISALIGNED),
+    (_gemm_gidx, dict(M=0, x=None, y=None), binding.AWQ_SUCCESS),
+    (_act, dict(perm=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (_act, dict(perm=A + 2), binding.AWQ_ERROR_MISALIGNED),
+    (_act, dict(g=96), binding.AWQ_ERROR_SHAPE),
+    (_act, dict(), binding.AWQ_ERROR_WORKSPACE),                    # the reordered x needs room
+    (_act, dict(M=0, x=None, y=None), binding.AWQ_SUCCESS),
+])
+def test_gidx_validation(fn, kwargs, status):
+    assert fn(**kwargs) == status
+
+
+def test_act_order_workspace_rules():
+    """The reordered x sits after the awq_gemm workspace of the same problem
+    and never inside the fixed zero-filled regions (64 KiB tickets + 4 MiB
+    accumulators); the call checks size and 256-byte alignment first."""
+    fixed = 65536 + 4 * 65536 * 16
+    for M, K, N, g in [(1, 8192, 7168, 128), (16, 8192, 7168, 128), (2048, 4096, 12288, 128),
+                       (4, 256, 128, 64), (3, 996, 64, 4)]:
+        need = awq.act_order_workspace_size(M, K, N, g)
+        base = max(awq.gemm_workspace_size(M, K, N, g), fixed)
+        xoff = -(-base // 256) * 256
+        assert need == xoff + -(-(M * K * 2) // 256) * 256
+    assert awq.act_order_workspace_size(0, 256, 128, 64) == 0
+    assert awq.act_order_workspace_size(4, 256, 128, 96) == 0
+    need = awq.act_order_workspace_size(4, 256, 128, 64)
+    assert _act(ws=A, wsb=need - 1) == binding.AWQ_ERROR_WORKSPACE
+    assert _act(ws=A + 16, wsb=need) == binding.AWQ_ERROR_MISALIGNED
+
+
+def test_gidx_order_matches_oracle():
+    """awq_gidx_order (host) is index work: its perm must equal the oracle's
+    stable sort exactly, and it reports the common group size only when
+    every group holds K / G rows."""
+    import awq_inputs
+    import numpy as np
+    import oracle
+    for K, G, seed in [(1, 1, 0), (7, 3, 1), (200, 7, 2), (4096, 50, 3)]:
+        gi = awq_inputs.random_g_idx(K, G, seed)
+        perm, gs = awq.gidx_order(gi, G)
+        want, counts = oracle.gidx_order(gi, G)
+        np.testing.assert_array_equal(perm, want)
+        assert gs == (K // G if np.all(counts == K // G) and K % G == 0 else 0)
+    for K, g in [(256, 32), (8192, 128), (14336, 128), (96, 1)]:
+        gi = awq_inputs.act_order_g_idx(K, g, seed=K)
+        perm, gs = awq.gidx_order(gi, K // g)
+        want, _ = oracle.gidx_order(gi, K // g)
+        np.testing.assert_array_equal(perm, want)
+        assert gs == g
+
+
+@pytest.mark.parametrize("gi,G", [([0, 1, 3], 3), ([0, -1], 2), ([0, 0], 0)])
+def test_gidx_order_rejects_bad_maps(gi, G):
+    with pytest.raises(binding.AwqError) as e:
+        awq.gidx_order(gi, G)
+    assert e.value.status == binding.AWQ_ERROR_INVALID_VALUE
+
+
+def test_permute_rows_validation():
+    lib = awq.lib()
+    assert lib.awq_permute_rows(A, None, A, 256, 128, None) == binding.AWQ_ERROR_INVALID_VALUE
+    assert lib.awq_permute_rows(A, A, A, 0, 128, None) == binding.AWQ_ERROR_INVALID_VALUE
+    assert lib.awq_permute_rows(A, A, A, 256, 100, None) == binding.AWQ_ERROR_SHAPE
+    assert lib.awq_permute_rows(A, A + 2, A, 256, 128, None) == binding.AWQ_ERROR_MISALIGNED
