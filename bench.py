@@ -95,18 +95,33 @@ def run_leg(torch, awq, spec, steps, warmup, dev):
     K, N, G = problem_dims(p)
     nbytes = algorithmic_bytes(M, K, N, G, p["bias"] is not None)
     nflops = 2 * M * N * K
+    act = spec.get("act_order", False)
+    if act:
+        # The same weight under an activation-order map: g_idx (K int32) is
+        # read by the method too; the load-time reorder is not timed.
+        nbytes += 4 * K
     R = max(2, -(-ROTATE_BYTES // nbytes))
     copies = make_copies(torch, p, R, dev)
     ws_bytes = awq.gemm_workspace_size(M, K, N, g)
-    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     path, need = awq.gemm_plan(M, K, N, g, copies[0]["x"].data_ptr(),
                                copies[0]["scales"].data_ptr())
     assert need <= ws_bytes
+    if act:
+        g_idx = awq_inputs.act_order_g_idx(K, g, seed=K + N)
+        for c in copies:
+            c["qweight"], c["perm"], gs = awq.prepare_act_order(c["qweight"], g_idx, G)
+            assert gs == g
+        ws_bytes = awq.act_order_workspace_size(M, K, N, g)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def step(i):
         c = copies[i % R]
-        awq.gemm(c["x"], c["qweight"], c["qzeros"], c["scales"], c["bias"], g, out=c["y"],
-                 workspace=ws)
+        if act:
+            awq.gemm_act_order(c["x"], c["perm"], c["qweight"], c["qzeros"], c["scales"],
+                               c["bias"], g, out=c["y"], workspace=ws)
+        else:
+            awq.gemm(c["x"], c["qweight"], c["qzeros"], c["scales"], c["bias"], g, out=c["y"],
+                     workspace=ws)
 
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
@@ -195,7 +210,7 @@ def sweep(torch, awq, dev):
                 steps = 200 if M <= 16 else 50
                 print(f"[sweep] {name} M={M} g={g}", file=sys.stderr, flush=True)
                 r = run_leg(torch, awq, spec, steps, 10, dev)
-                if M >= 256 and g == 128:
+                if g == 128:
                     fused[(name, M, r["K"], r["N"], r["p"]["bias"] is not None)] = r["ms_per_step"]
                 sec = r["ms_per_step"] * 1e-3
                 gbs = r["nbytes"] / sec / 1e9
@@ -229,10 +244,34 @@ def sweep(torch, awq, dev):
             "frac": round(nbytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes,
             "w4a16_us_per_call": round(w4_us, 3), "w4a16_speedup": round(d_us / w4_us, 2)}),
             flush=True)
+    # Activation-order weights (row-to-group map): the load-time reorder is
+    # done once; each step reorders x's columns and runs the grouped kernels.
+    for name, M in (("decode_sweep_k8192_n7168", 1), ("decode_sweep_k8192_n7168", 16),
+                    ("prefill_qkv_m2048_k4096_n12288", 2048)):
+        print(f"[sweep] act order {name} M={M}", file=sys.stderr, flush=True)
+        spec = dict(source=name, M=M, group_size=128, act_order=True)
+        r = run_leg(torch, awq, spec, 200 if M <= 16 else 50, 10, dev)
+        sec = r["ms_per_step"] * 1e-3
+        gbs = r["nbytes"] / sec / 1e9
+        tfs = r["nflops"] / sec / 1e12
+        hbm = M <= 16
+        plain = fused.get((name, M, r["K"], r["N"], r["p"]["bias"] is not None))
+        print(json.dumps({
+            "workload": f"act_order_{name}", "M": M, "K": r["K"], "N": r["N"], "group_size": 128,
+            "kernel": f"gather_cols + {r['path']}", "us_per_call": round(sec * 1e6, 3),
+            "GB_per_s": round(gbs, 1), "TFLOP_per_s": round(tfs, 2),
+            "bound": "hbm" if hbm else "mfma",
+            "frac": round(gbs / HBM_PEAK_GBS if hbm else tfs / FP16_MFMA_PEAK_TFLOPS, 4),
+            "bytes": r["nbytes"], "copies_rotated": r["R"],
+            "grouped_us_per_call": round(plain * 1e3, 3) if plain else None}), flush=True)
+        del r
+        torch.cuda.empty_cache()
     # Context at the matrix-core-bound points: torch's float16 linear (the
     # vendor GEMM library) on an unquantised weight of the same shape, and
     # the unfused route (awq_dequant into a float16 weight, then that GEMM).
     for (name, M, K, N, bias), ms in fused.items():
+        if M < 256:
+            continue
         print(f"[sweep] vendor float16 GEMM M={M} K={K} N={N}", file=sys.stderr, flush=True)
         lin_us, unfused_us = vendor_gemm_times_us(torch, awq, M, K, N, bias, dev)
         flops = 2 * M * N * K

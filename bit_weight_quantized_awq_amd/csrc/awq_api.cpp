@@ -55,20 +55,32 @@ int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size, const voi
 namespace {
 
 // Plans and launches the grouped forward for a validated problem p (x, y
-// non-NULL and M > 0).  Shared by awq_gemm and awq_gemm_act_order.
+// non-NULL and M > 0).  Shared by awq_gemm and awq_gemm_act_order.  With a
+// column order perm (act order), x is read as x[:, perm]: the LDS decode
+// kernel gathers it itself (up to 4 steps); every other kernel reads a copy
+// reordered into xp first (M x K float16, 16-byte aligned).
 int run_gemm(const Problem& p, const void* x, const void* qweight, const void* qzeros,
              const void* scales, const void* bias, void* y, void* workspace,
-             size_t workspace_bytes, hipStream_t s) {
+             size_t workspace_bytes, const int32_t* perm, _Float16* xp, hipStream_t s) {
   const int force = awq::force_path_from_env();
   if (force < 0) return AWQ_ERROR_INVALID_VALUE;
   Plan pl;
-  const awq::Alignment al{awq::aligned(x, 16), awq::aligned(scales, 16),
+  // A reordered x is 16-byte aligned wherever it is read from.
+  const awq::Alignment al{perm ? true : awq::aligned(x, 16), awq::aligned(scales, 16),
                           awq::aligned(qweight, 16)};
   int st = awq::make_plan(p, al, force, &pl);
   if (st != AWQ_SUCCESS) return st;
   if (pl.ws_bytes > 0) {
     if (!workspace || workspace_bytes < pl.ws_bytes) return AWQ_ERROR_WORKSPACE;
     if (!awq::aligned(workspace, 16)) return AWQ_ERROR_MISALIGNED;
+  }
+  const bool fused_gather = perm && pl.path == AWQ_PATH_DECODE && pl.decode_lds &&
+                            pl.steps <= 4 && p.M <= awq::decode_gather_max_m();
+  if (perm && !fused_gather) {
+    const hipError_t e = awq::launch_gather_cols(static_cast<const _Float16*>(x), perm, xp,
+                                                 static_cast<int>(p.M), static_cast<int>(p.K), s);
+    if (e != hipSuccess) return AWQ_ERROR_HIP;
+    x = xp;
   }
 
   const auto* xh = static_cast<const _Float16*>(x);
@@ -84,7 +96,8 @@ int run_gemm(const Problem& p, const void* x, const void* qweight, const void* q
   switch (pl.path) {
     case AWQ_PATH_DECODE:
       e = awq::launch_decode(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, iG, pl.steps, pl.splits,
-                             pl.n_tiles, pl.decode_lds, workspace, s);
+                             pl.n_tiles, pl.decode_lds, workspace,
+                             fused_gather ? perm : nullptr, s);
       break;
     case AWQ_PATH_PREFILL:
       e = awq::launch_prefill(xh, qw, qz, sc, bh, yh, iM, iK, iN, pl.group_shift, pl.prefill_bm,
@@ -113,8 +126,8 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void*
   st = awq::validate_gemm_pointers(x, qweight, qzeros, scales, bias, y, M);
   if (st != AWQ_SUCCESS) return st;
   if (M == 0) return AWQ_SUCCESS;
-  return run_gemm(p, x, qweight, qzeros, scales, bias, y, workspace, workspace_bytes,
-                  static_cast<hipStream_t>(stream));
+  return run_gemm(p, x, qweight, qzeros, scales, bias, y, workspace, workspace_bytes, nullptr,
+                  nullptr, static_cast<hipStream_t>(stream));
 }
 
 int awq_dense_gemv(const void* x, const void* w, const void* bias, void* y, int64_t M, int64_t K,
@@ -224,12 +237,8 @@ int awq_gemm_act_order(const void* x, const void* perm, const void* qweight_sort
   if (!awq::aligned(workspace, 256)) return AWQ_ERROR_MISALIGNED;
   const size_t xoff = awq::act_order_x_offset(M, K, N, group_size);
   auto* xp = reinterpret_cast<_Float16*>(static_cast<char*>(workspace) + xoff);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = awq::launch_gather_cols(static_cast<const _Float16*>(x),
-                                               static_cast<const int32_t*>(perm), xp,
-                                               static_cast<int>(M), static_cast<int>(K), s);
-  if (e != hipSuccess) return AWQ_ERROR_HIP;
-  return run_gemm(p, xp, qweight_sorted, qzeros, scales, bias, y, workspace, xoff, s);
+  return run_gemm(p, x, qweight_sorted, qzeros, scales, bias, y, workspace, xoff,
+                  static_cast<const int32_t*>(perm), xp, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -36,9 +36,13 @@
 //   split has arrived writes y -- one atomic round trip.  For larger M the
 //   atomic count grows past what the memory-side atomic units sustain, so
 //   partials are stored, each work-group takes a ticket on its column tile,
-//   and the last one sums them in split order (splitk_ticket).  Every byte
+//   and the last one sums them in split order (splitk_ticket).  Every byte of
 //   the ticket and accumulator regions of the workspace is zero again when
 //   either exchange ends.
+// * Activation order (a row-to-group map whose groups were made contiguous
+//   by reordering the packed rows at load time): the LDS variant reads x
+//   through the same row order, gathering x[m, perm[k]] itself, so the
+//   forward stays one launch.
 #include <type_traits>
 
 #include "awq_device.h"
@@ -426,12 +430,44 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int STEPS, bool SINGLE_GROUP>
+// Waits until at most n (a multiple of 4 below 64) vector-memory loads are
+// outstanding.
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  switch (n >> 2) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<4>(); break;
+    case 2: wait_vmcnt<8>(); break;
+    case 3: wait_vmcnt<12>(); break;
+    case 4: wait_vmcnt<16>(); break;
+    case 5: wait_vmcnt<20>(); break;
+    case 6: wait_vmcnt<24>(); break;
+    case 7: wait_vmcnt<28>(); break;
+    case 8: wait_vmcnt<32>(); break;
+    case 9: wait_vmcnt<36>(); break;
+    case 10: wait_vmcnt<40>(); break;
+    case 11: wait_vmcnt<44>(); break;
+    case 12: wait_vmcnt<48>(); break;
+    case 13: wait_vmcnt<52>(); break;
+    case 14: wait_vmcnt<56>(); break;
+    case 15: wait_vmcnt<60>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+// GATHER: x is read through a column order, x[m, perm[k]] in place of
+// x[m, k] (the activation-order forward).  Each lane then gathers its eight
+// values per step one by one; the perm entries are loaded first and the
+// packed-word copies are split in two halves around the gathers, so the
+// dependent perm -> x round trip overlaps the first half of the weight
+// stream instead of delaying all of it.
+template <int STEPS, bool SINGLE_GROUP, bool GATHER>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
                   const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
                   const _Float16* __restrict__ bias, _Float16* __restrict__ y,
-                  SplitK sk, int M, int K, int N, int g, int G, int splits) {
+                  SplitK sk, int M, int K, int N, int g, int G, int splits,
+                  const int32_t* __restrict__ perm) {
+  static_assert(!GATHER || STEPS <= 4, "gather loads must fit the load counter");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   pin_arg(y);
   pin_arg(bias);
@@ -479,28 +515,17 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
           half8_t, buf_load_u32x4(rs, offset_or_oob(ok, static_cast<uint32_t>(grp * N + 8 * c) * 2u)));
     }
   }
-  half8_t xa[STEPS];
-#pragma unroll
-  for (int s = 0; s < STEPS; ++s) {
-    const int kr = kw0 + 32 * s + 8 * kb;
-    const uint32_t xoff =
-        offset_or_oob(col16 < M && kr < K, static_cast<uint32_t>(col16 * K + kr) * 2u);
-    xa[s] = __builtin_bit_cast(half8_t, buf_load_u32x4(rx, xoff));
-  }
-  // Nothing may be scheduled between here and the waits below except the
-  // LDS copies: the waits count outstanding copies.
-  __builtin_amdgcn_sched_barrier(0);
-
   // Packed words: HBM -> LDS, 4 instructions (4 x 8 rows) per step, issued
-  // last so that waiting for step s leaves later steps in flight.
+  // after the x loads so that waiting for step s leaves later steps in flight.
   char* wlds = smem + wave * kWaveBytes;
-  {
-    const int lrow = lane >> 3;   // row within an 8-row block
-    const int lword = c0 + 4 * (lane & 7);
-    const uint32_t row_bytes = static_cast<uint32_t>(NW) * 4u;
-    const bool cok = lword < NW;
+  const int lrow = lane >> 3;   // row within an 8-row block
+  const int lword = c0 + 4 * (lane & 7);
+  const uint32_t row_bytes = static_cast<uint32_t>(NW) * 4u;
+  const bool cok = lword < NW;
+  auto copy_steps = [&](int s_begin, int s_end) {
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
+      if (s < s_begin || s >= s_end) continue;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int row = kw0 + 32 * s + 8 * b + lrow;
@@ -511,8 +536,71 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
             16, off, 0, 0, 0);
       }
     }
+  };
+  // Steps whose copies precede the x gathers (GATHER only).
+  constexpr int kEarly = GATHER ? (STEPS + 1) / 2 : 0;
+
+  half8_t xa[STEPS];
+  if (!GATHER) {
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      const int kr = kw0 + 32 * s + 8 * kb;
+      const uint32_t xoff =
+          offset_or_oob(col16 < M && kr < K, static_cast<uint32_t>(col16 * K + kr) * 2u);
+      xa[s] = __builtin_bit_cast(half8_t, buf_load_u32x4(rx, xoff));
+    }
+    // Nothing may be scheduled between here and the waits below except the
+    // LDS copies: the waits count outstanding copies.
+    __builtin_amdgcn_sched_barrier(0);
+    copy_steps(0, STEPS);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    // perm entries of the lane's eight rows per step (rows past K read 0 and
+    // are never used), then the first half of the copies, then the gathers
+    // (each needs its perm entry: the compiler waits for the perm loads
+    // only), then the rest of the copies.
+    // Only the lanes of rows below M load (the others' operands are zero),
+    // so a gather instruction touches M x 4 addresses, not 64.
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(perm, static_cast<uint32_t>(K) * 4u);
+    const bool row_lane = col16 < M;
+    u32x4 pv[STEPS][2];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      pv[s][0] = u32x4{0u, 0u, 0u, 0u};
+      pv[s][1] = u32x4{0u, 0u, 0u, 0u};
+      xa[s] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    if (row_lane) {
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) {
+        const int kr = kw0 + 32 * s + 8 * kb;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          pv[s][h] = buf_load_u32x4(rp, offset_or_oob(kr < K, static_cast<uint32_t>(kr + 4 * h) * 4u));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    copy_steps(0, kEarly);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t kmax = static_cast<uint32_t>(K);
+    if (row_lane) {
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) {
+        const int kr = kw0 + 32 * s + 8 * kb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t src = pv[s][i >> 2][i & 3];
+          const uint32_t off = offset_or_oob(kr < K && src < kmax,
+                                             static_cast<uint32_t>(col16) * kmax * 2u + src * 2u);
+          xa[s][i] =
+              __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rx, off, 0, 0));
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    copy_steps(kEarly, STEPS);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
 
   // Byte-pair contraction.  For byte b of a word (nibbles 2b and 2b+1,
   // columns 8c+2b and 8c+2b+1), one byte shuffle per row pair places that
@@ -588,18 +676,10 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     // Step s's four LDS copies are done once at most 4*(STEPS-1-s) loads
-    // (the later steps' copies) are outstanding.
-    switch (STEPS - 1 - s) {
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<4>(); break;
-      case 2: wait_vmcnt<8>(); break;
-      case 3: wait_vmcnt<12>(); break;
-      case 4: wait_vmcnt<16>(); break;
-      case 5: wait_vmcnt<20>(); break;
-      case 6: wait_vmcnt<24>(); break;
-      case 7: wait_vmcnt<28>(); break;
-      default: wait_vmcnt<0>(); break;
-    }
+    // (the later steps' copies) are outstanding; with GATHER the early
+    // steps' copies precede the gathers and the late copies, so they are
+    // done once only the late copies remain.
+    wait_vmcnt_upto(s < kEarly ? 4 * (STEPS - kEarly) : 4 * (STEPS - 1 - s));
     const int gi = SINGLE_GROUP ? 0 : s;
     const char* blk = wlds + (4 * s + kb) * kLdsBlockPitch;
 #pragma unroll
@@ -687,23 +767,23 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   }
 }
 
-template <int STEPS>
+template <int STEPS, bool GATHER>
 hipError_t launch_lds_steps(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                             const _Float16* scales, const _Float16* bias, _Float16* y,
                             int M, int K, int N, int g, int G, int splits, int n_tiles,
-                            SplitK sk, hipStream_t stream) {
+                            SplitK sk, const int32_t* perm, hipStream_t stream) {
   const size_t copy_bytes = 4 * STEPS * 4 * kLdsBlockPitch;
   const size_t red_bytes = 4 * static_cast<size_t>((M + 3) & ~3) * kDecodeCols * sizeof(float);
   const size_t shmem = copy_bytes > red_bytes ? copy_bytes : red_bytes;
   const bool single = (G == 1) || (g % (kDecodeRowsPerStep * STEPS) == 0);
   if (single)
-    hipLaunchKernelGGL((decode_lds_kernel<STEPS, true>), dim3(n_tiles * splits), dim3(256),
-                       shmem, stream, x, qweight, qzeros, scales, bias, y, sk, M,
-                       K, N, g, G, splits);
+    hipLaunchKernelGGL((decode_lds_kernel<STEPS, true, GATHER>), dim3(n_tiles * splits),
+                       dim3(256), shmem, stream, x, qweight, qzeros, scales, bias, y, sk, M,
+                       K, N, g, G, splits, perm);
   else
-    hipLaunchKernelGGL((decode_lds_kernel<STEPS, false>), dim3(n_tiles * splits), dim3(256),
-                       shmem, stream, x, qweight, qzeros, scales, bias, y, sk, M,
-                       K, N, g, G, splits);
+    hipLaunchKernelGGL((decode_lds_kernel<STEPS, false, GATHER>), dim3(n_tiles * splits),
+                       dim3(256), shmem, stream, x, qweight, qzeros, scales, bias, y, sk, M,
+                       K, N, g, G, splits, perm);
   return hipGetLastError();
 }
 
@@ -732,7 +812,8 @@ hipError_t launch_steps(const _Float16* x, const uint32_t* qweight, const uint32
 hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                          const _Float16* scales, const _Float16* bias, _Float16* y,
                          int M, int K, int N, int g, int G, int steps, int splits,
-                         int n_tiles, bool lds_variant, void* workspace, hipStream_t stream) {
+                         int n_tiles, bool lds_variant, void* workspace,
+                         const int32_t* perm, hipStream_t stream) {
   // Workspace: ticket region, accumulator region ([M][N] accumulators, then
   // [M][N] masks), then [splits][M][N] partials.
   char* ws = static_cast<char*>(workspace);
@@ -746,16 +827,28 @@ hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint3
                   ws ? reinterpret_cast<float*>(ws + kTicketRegionBytes + kAtomicRegionBytes)
                      : nullptr,
                   tw};
+  if (lds_variant && perm) {
+    switch (steps) {
+      case 1: return launch_lds_steps<1, true>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
+                                               G, splits, n_tiles, sk, perm, stream);
+      case 2: return launch_lds_steps<2, true>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
+                                               G, splits, n_tiles, sk, perm, stream);
+      case 4: return launch_lds_steps<4, true>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
+                                               G, splits, n_tiles, sk, perm, stream);
+      default: return hipErrorInvalidValue;   // decode_gathers() is false for 8 steps
+    }
+  }
+  if (perm) return hipErrorInvalidValue;
   if (lds_variant) {
     switch (steps) {
-      case 1: return launch_lds_steps<1>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G,
-                                         splits, n_tiles, sk, stream);
-      case 2: return launch_lds_steps<2>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G,
-                                         splits, n_tiles, sk, stream);
-      case 4: return launch_lds_steps<4>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G,
-                                         splits, n_tiles, sk, stream);
-      case 8: return launch_lds_steps<8>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G,
-                                         splits, n_tiles, sk, stream);
+      case 1: return launch_lds_steps<1, false>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
+                                                G, splits, n_tiles, sk, nullptr, stream);
+      case 2: return launch_lds_steps<2, false>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
+                                                G, splits, n_tiles, sk, nullptr, stream);
+      case 4: return launch_lds_steps<4, false>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
+                                                G, splits, n_tiles, sk, nullptr, stream);
+      case 8: return launch_lds_steps<8, false>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
+                                                G, splits, n_tiles, sk, nullptr, stream);
       default: return hipErrorInvalidValue;
     }
   }

@@ -68,6 +68,75 @@ __global__ __launch_bounds__(256) void gather_cols_kernel(const _Float16* __rest
   }
 }
 
+// The same reorder for many rows.  ROWS consecutive rows of x and all of
+// perm are copied into LDS with asynchronous 16-byte direct-to-LDS loads
+// (all in flight at once, one wait), then every thread forms 8 consecutive
+// outputs of each row from LDS.  Scattered 2-byte reads from global memory
+// cost one cache-line lookup per lane; from LDS a few bank cycles per
+// instruction.  Needs K % 8 == 0, x, perm and xp 16-byte aligned and
+// lds_gather_bytes(ROWS, K) bytes of LDS.
+constexpr uint32_t kDmaChunk = 1024;   // bytes one wave's direct-to-LDS load moves
+__host__ __device__ constexpr uint32_t round_chunk(uint32_t b) {
+  return (b + kDmaChunk - 1) / kDmaChunk * kDmaChunk;
+}
+__host__ __device__ constexpr uint32_t lds_gather_bytes(int rows, int K) {
+  return round_chunk(static_cast<uint32_t>(rows) * K * 2u) + round_chunk(static_cast<uint32_t>(K) * 4u);
+}
+
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t bytes,
+                                            int wave, int lane) {
+  for (uint32_t off = static_cast<uint32_t>(wave) * kDmaChunk; off < bytes; off += 4 * kDmaChunk)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(lds + off), 16,
+        off + static_cast<uint32_t>(lane) * 16u, 0, 0, 0);
+}
+
+template <int ROWS>
+__global__ __launch_bounds__(256) void gather_cols_lds_kernel(const _Float16* __restrict__ x,
+                                                              const int32_t* __restrict__ perm,
+                                                              _Float16* __restrict__ xp, int M,
+                                                              int K) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int m0 = blockIdx.x * ROWS;
+  const int rows = min(ROWS, M - m0);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t xbytes = static_cast<uint32_t>(rows) * K * 2u;
+  const uint32_t pbytes = static_cast<uint32_t>(K) * 4u;
+  const uint32_t xregion = round_chunk(static_cast<uint32_t>(ROWS) * K * 2u);
+  // Loads past each range read zero (the LDS regions are whole chunks).
+  copy_to_lds(make_rsrc(x + static_cast<size_t>(m0) * K, xbytes), smem, xbytes, wave, lane);
+  copy_to_lds(make_rsrc(perm, pbytes), smem + xregion, pbytes, wave, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const _Float16* xs = reinterpret_cast<const _Float16*>(smem);
+  const u32x4* ps = reinterpret_cast<const u32x4*>(smem + xregion);
+  const int chunks = K / 8;
+  for (int c = threadIdx.x; c < chunks; c += 256) {
+    const u32x4 p0 = ps[2 * c];
+    const u32x4 p1 = ps[2 * c + 1];
+    int src[8];
+    bool ok[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      src[i] = static_cast<int>(i < 4 ? p0[i] : p1[i - 4]);
+      ok[i] = src[i] >= 0 && src[i] < K;
+      if (!ok[i]) src[i] = 0;
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      if (r < rows) {
+        half8_t v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = ok[i] ? xs[r * K + src[i]] : static_cast<_Float16>(0.f);
+        *reinterpret_cast<half8_t*>(xp + static_cast<size_t>(m0 + r) * K + 8 * c) = v;
+      }
+    }
+  }
+}
+
+constexpr uint32_t kLdsMax = 160 * 1024;
+constexpr int kGatherLdsMinRows = 32;   // below this the direct form is as fast
+
 int blocks_for(long long items) { return static_cast<int>((items + 255) / 256); }
 
 }  // namespace
@@ -90,6 +159,31 @@ hipError_t launch_gather_cols(const _Float16* x, const int32_t* perm, _Float16* 
                               hipStream_t stream) {
   const bool vec = K % 8 == 0 && reinterpret_cast<uintptr_t>(perm) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(xp) % 16 == 0;
+  // Rows per work-group: 4 while the stage leaves room for a second
+  // work-group per CU, else fewer; rows past the LDS size take the direct form.
+  int rows = 0;
+  if (lds_gather_bytes(4, K) <= 96 * 1024) rows = 4;
+  else if (lds_gather_bytes(2, K) <= 128 * 1024) rows = 2;
+  else if (lds_gather_bytes(1, K) <= kLdsMax) rows = 1;
+  if (vec && reinterpret_cast<uintptr_t>(x) % 16 == 0 && M >= kGatherLdsMinRows && rows > 0) {
+    const size_t lds = lds_gather_bytes(rows, K);
+    const dim3 grid((M + rows - 1) / rows);
+    switch (rows) {
+      case 4:
+        hipLaunchKernelGGL(gather_cols_lds_kernel<4>, grid, dim3(256), lds, stream, x, perm, xp,
+                           M, K);
+        break;
+      case 2:
+        hipLaunchKernelGGL(gather_cols_lds_kernel<2>, grid, dim3(256), lds, stream, x, perm, xp,
+                           M, K);
+        break;
+      default:
+        hipLaunchKernelGGL(gather_cols_lds_kernel<1>, grid, dim3(256), lds, stream, x, perm, xp,
+                           M, K);
+        break;
+    }
+    return hipGetLastError();
+  }
   const long long items = static_cast<long long>(M) * (vec ? K / 8 : K);
   if (vec)
     hipLaunchKernelGGL(gather_cols_kernel<true>, dim3(blocks_for(items)), dim3(256), 0, stream,

@@ -296,6 +296,15 @@ size_t act_order_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_s
          round_up(static_cast<size_t>(M) * static_cast<size_t>(K) * 2, 256);
 }
 
+int decode_gather_max_m() {
+  const char* s = getenv("AWQ_DECODE_GATHER_MAX_M");
+  if (s && *s) {
+    const int v = atoi(s);
+    if (v >= 0 && v <= kDecodeMaxM) return v;
+  }
+  return kDecodeGatherMaxM;
+}
+
 int force_path_from_env() {
   const char* s = getenv("AWQ_FORCE_PATH");
   if (!s || !*s) return 0;

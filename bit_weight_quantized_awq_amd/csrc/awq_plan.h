@@ -27,6 +27,7 @@ constexpr size_t kTicketRegionBytes = 65536;
 constexpr int kTicketMaxStrideBytes = 256;
 constexpr int kDecodeMaxSplits = 63;
 constexpr int kDecodeAtomicMaxM = 4;
+constexpr int kDecodeGatherMaxM = 4;
 constexpr int kDecodeAtomicMaxN = 65536;
 constexpr size_t kAtomicRegionBytes = static_cast<size_t>(kDecodeAtomicMaxM) * kDecodeAtomicMaxN * 16;
 
@@ -101,6 +102,12 @@ size_t gemm_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size);
 
 // force: 0 = automatic, otherwise an awq_path value.  Returns an awq_status.
 int make_plan(const Problem& p, const Alignment& al, int force, Plan* out);
+
+// Largest batch for which the LDS decode kernel gathers an act-order x
+// itself (each column tile gathers its K range again, so the scattered loads
+// grow with M x N / 256; beyond this a separate reorder pass is cheaper).
+// AWQ_DECODE_GATHER_MAX_M overrides it (tuning and tests; 0 disables).
+int decode_gather_max_m();
 
 // Parses AWQ_FORCE_PATH.  Returns 0 (unset/automatic), an awq_path value, or
 // -1 for an unrecognised value.

@@ -159,7 +159,9 @@ def run_act_order(p, M=None, workspace=None):
 @pytest.mark.parametrize("M,K,N,g,bias", [
     (1, 4096, 1024, 128, False), (4, 4096, 1024, 128, True), (16, 2048, 512, 64, False),
     (3, 1024, 520, 128, True),                       # register decode variant (N % 32 != 0)
-    (64, 2048, 768, 128, False), (256, 1024, 1024, 128, True), (300, 1024, 520, 32, False),
+    (64, 2048, 768, 128, False), (256, 1024, 1024, 128, True), (301, 1024, 520, 32, False),
+    (66, 14336, 256, 128, True),                      # x rows staged two per work-group
+    (40, 20480, 128, 128, False),                     # one row per work-group
     (2, 996, 64, 4, False),                           # K % 8 != 0: general kernel, scalar gather
 ])
 def test_act_order_parity(M, K, N, g, bias):
@@ -172,6 +174,22 @@ def test_act_order_parity(M, K, N, g, bias):
     ref = oracle.awq_linear_gidx_ref(p["x"], p["qweight"], p["qzeros"], p["scales"],
                                      p["g_idx"], p["bias"])
     assert_within_tol(y, ref, f"act order M={M}")
+
+
+@pytest.mark.parametrize("steps", [1, 2, 4, 8])
+@pytest.mark.parametrize("M", [1, 5])
+def test_act_order_decode_every_step_count(steps, M, monkeypatch):
+    """The LDS decode kernel gathers x through perm itself for 1, 2 and 4
+    steps per wave (the load order differs with the step count); 8 steps
+    take the separate reorder.  Forced through AWQ_DECODE_STEPS."""
+    say(f"act order decode steps={steps} M={M}")
+    monkeypatch.setenv("AWQ_DECODE_STEPS", str(steps))
+    p = act_problem(M, 8192, 1024, 128, seed=steps * 10 + M, bias=True)
+    assert awq.gemm_plan(M, 8192, 1024, 128)[0] == binding.AWQ_PATH_DECODE
+    y = run_act_order(p)
+    ref = oracle.awq_linear_gidx_ref(p["x"], p["qweight"], p["qzeros"], p["scales"],
+                                     p["g_idx"], p["bias"])
+    assert_within_tol(y, ref, f"act order decode steps={steps}")
 
 
 @pytest.mark.parametrize("M,K,N,g", [(8, 4096, 1024, 128), (256, 2048, 768, 64)])
