@@ -192,6 +192,20 @@ def test_act_order_decode_every_step_count(steps, M, monkeypatch):
     assert_within_tol(y, ref, f"act order decode steps={steps}")
 
 
+@pytest.mark.parametrize("M", [1, 4, 8, 16])
+def test_act_order_fused_and_separate_reorder(M, monkeypatch):
+    """Both forms of the decode's x reorder (gathered inside the decode
+    kernel, or a separate pass first), forced through
+    AWQ_DECODE_GATHER_MAX_M, match the oracle at every decode batch."""
+    p = act_problem(M, 8192, 1280, 128, seed=70 + M, bias=True)
+    ref = oracle.awq_linear_gidx_ref(p["x"], p["qweight"], p["qzeros"], p["scales"],
+                                     p["g_idx"], p["bias"])
+    for limit in ("16", "0"):
+        say(f"act order decode M={M} gather limit {limit}")
+        monkeypatch.setenv("AWQ_DECODE_GATHER_MAX_M", limit)
+        assert_within_tol(run_act_order(p), ref, f"act order M={M} limit {limit}")
+
+
 @pytest.mark.parametrize("M,K,N,g", [(8, 4096, 1024, 128), (256, 2048, 768, 64)])
 def test_act_order_one_hot_rows_exact(M, K, N, g):
     """x[i] = e_{k_i} selects row k_i of the dequantised map weight bit for
