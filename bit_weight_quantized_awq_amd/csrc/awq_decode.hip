@@ -193,37 +193,62 @@ __device__ __forceinline__ void splitk_atomic(const float (&part)[kDecodeMaxM], 
 // work-group is in place before its ticket is taken, and the work-group that
 // takes the last ticket sees all of them.  It sums them in split order and
 // resets the ticket.
-// Sum over the splits, in split order, of rows 0..ROWS-1 of one column of
-// the partials (p points at column n of split 0, row 0).  The caller has
-// invalidated this CU's caches (acquire), so plain loads see every split's
-// stores.  Each round issues every row of BATCH splits before using any;
-// indices past the last split or row are clamped (the loads stay
-// unconditional, without branches) and their values dropped.
-template <int BATCH, int ROWS>
-__device__ __forceinline__ void ticket_sum(const float* p, int M, int N, int splits,
-                                           float (&sum)[kDecodeMaxM]) {
+// Final sum of a column tile's partials by the work-group holding the last
+// ticket: thread t covers the four columns 4*(t % 64) .. +3 of the tile and
+// the rows t / 64 + 4*i (i < MQ), reading each (split, row) as one 16-byte
+// load, so a round of BATCH splits moves 16 * BATCH * MQ bytes per thread
+// (the partials of a 16-row tile are 256 KiB: with one float per load the
+// load counter would cap a round at 63 x 4 bytes).  Sums run in split
+// order from zero.  The caller has invalidated this CU's caches (acquire),
+// so plain loads see every split's stores.  Indices past the last split
+// or row are clamped (the loads stay unconditional) and their values dropped.
+template <int BATCH, int MQ>
+__device__ __forceinline__ void ticket_sum_store(const float* __restrict__ partial,
+                                                 const _Float16* __restrict__ bias,
+                                                 _Float16* __restrict__ y, int M, int N,
+                                                 int splits, int n0, int rq) {
   const size_t stride = static_cast<size_t>(M) * N;
+  floatx4 sum[MQ];
 #pragma unroll
-  for (int m = 0; m < kDecodeMaxM; ++m) sum[m] = 0.f;
+  for (int i = 0; i < MQ; ++i) sum[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   for (int sp = 0; sp < splits; sp += BATCH) {
-    float v[BATCH][ROWS];
+    floatx4 v[BATCH][MQ];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int su = min(sp + u, splits - 1);
 #pragma unroll
-      for (int m = 0; m < ROWS; ++m)
-        v[u][m] = p[su * stride + static_cast<size_t>(min(m, M - 1)) * N];
+      for (int i = 0; i < MQ; ++i) {
+        const int m = min(rq + 4 * i, M - 1);
+        v[u][i] = *reinterpret_cast<const floatx4*>(partial + su * stride +
+                                                    static_cast<size_t>(m) * N + n0);
+      }
     }
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const bool ok = sp + u < splits;
 #pragma unroll
-      for (int m = 0; m < ROWS; ++m) sum[m] += ok ? v[u][m] : 0.f;
+      for (int i = 0; i < MQ; ++i) sum[i] += ok ? v[u][i] : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  floatx4 b = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (bias) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = static_cast<float>(bias[n0 + j]);
+  }
+#pragma unroll
+  for (int i = 0; i < MQ; ++i) {
+    const int m = rq + 4 * i;
+    if (m < M) {
+      half4_t o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = static_cast<_Float16>(sum[i][j] + b[j]);
+      *reinterpret_cast<half4_t*>(y + static_cast<size_t>(m) * N + n0) = o;
     }
   }
 }
 
-template <int BATCH>
+// VREGS: 16-byte registers the final sum may hold in flight per thread.
+template <int VREGS>
 __device__ __forceinline__ void splitk_ticket(const float (&part)[kDecodeMaxM], const SplitK& sk,
                                               const _Float16* __restrict__ bias,
                                               _Float16* __restrict__ y, int M, int N, int n,
@@ -248,18 +273,18 @@ __device__ __forceinline__ void splitk_ticket(const float (&part)[kDecodeMaxM], 
   // Acquire: drop this CU's and this XCD's cached copies, so the plain loads
   // of the partials fetch what the other splits stored.
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (nvalid) {
-    const float b = bias ? static_cast<float>(bias[n]) : 0.f;
-    float sum[kDecodeMaxM];
-    switch ((M + 3) >> 2) {
-      case 1: ticket_sum<BATCH, 4>(sk.partial + n, M, N, splits, sum); break;
-      case 2: ticket_sum<BATCH, 8>(sk.partial + n, M, N, splits, sum); break;
-      case 3: ticket_sum<BATCH, 12>(sk.partial + n, M, N, splits, sum); break;
-      default: ticket_sum<BATCH, 16>(sk.partial + n, M, N, splits, sum); break;
+  {
+    // N % 8 == 0, so a group of four columns is all inside or all outside.
+    const int n0 = n_tile * kDecodeCols + 4 * (threadIdx.x & 63);
+    const int rq = threadIdx.x >> 6;
+    if (n0 < N) {
+      switch ((M + 3) >> 2) {
+        case 1: ticket_sum_store<VREGS, 1>(sk.partial, bias, y, M, N, splits, n0, rq); break;
+        case 2: ticket_sum_store<VREGS / 2, 2>(sk.partial, bias, y, M, N, splits, n0, rq); break;
+        case 3: ticket_sum_store<VREGS / 3, 3>(sk.partial, bias, y, M, N, splits, n0, rq); break;
+        default: ticket_sum_store<VREGS / 4, 4>(sk.partial, bias, y, M, N, splits, n0, rq); break;
+      }
     }
-#pragma unroll
-    for (int m = 0; m < kDecodeMaxM; ++m)
-      if (m < M) y[m * N + n] = static_cast<_Float16>(sum[m] + b);
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -404,7 +429,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   if (M <= kDecodeAtomicMaxM && N <= kDecodeAtomicMaxN) {
     if (nvalid) splitk_atomic(part, sk, bias, y, M, N, n, split, splits);
   } else {
-    splitk_ticket<2>(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
+    splitk_ticket<8>(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
   }
 }
 
@@ -763,7 +788,7 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   if (M <= kDecodeAtomicMaxM && N <= kDecodeAtomicMaxN) {
     if (nvalid) splitk_atomic(part, sk, bias, y, M, N, n, split, splits);
   } else {
-    splitk_ticket<8>(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
+    splitk_ticket<32>(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
   }
 }
 
