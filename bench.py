@@ -258,7 +258,10 @@ def sweep(torch, awq, dev):
         plain = fused.get((name, M, r["K"], r["N"], r["p"]["bias"] is not None))
         print(json.dumps({
             "workload": f"act_order_{name}", "M": M, "K": r["K"], "N": r["N"], "group_size": 128,
-            "kernel": f"gather_cols + {r['path']}", "us_per_call": round(sec * 1e6, 3),
+            "kernel": (f"{r['path']} (gathers x through the order itself)"
+                       if r["path"] == "decode" and M <= 4 and r["N"] % 32 == 0
+                       else f"x reorder pass + {r['path']}"),
+            "us_per_call": round(sec * 1e6, 3),
             "GB_per_s": round(gbs, 1), "TFLOP_per_s": round(tfs, 2),
             "bound": "hbm" if hbm else "mfma",
             "frac": round(gbs / HBM_PEAK_GBS if hbm else tfs / FP16_MFMA_PEAK_TFLOPS, 4),
