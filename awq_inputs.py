@@ -35,9 +35,10 @@ class Workload:
     note: str = field(default="", compare=False)
 
 
-# The five seeded workloads: a tiny case, the two decode shapes of the
-# ROCm skinny-GEMM dispatch (K=8192, N in {1280, 7168}), a fused-QKV prefill
-# projection and an MLP down-projection.
+# The seeded workloads: a tiny case, the two decode shapes of the ROCm
+# skinny-GEMM dispatch (K=8192, N in {1280, 7168}), a fused-QKV prefill
+# projection, an MLP down-projection, and batches between decode and prefill
+# at the larger decode shape.
 WORKLOADS = {
     "tiny_m4_k256_n128": Workload(
         "tiny_m4_k256_n128", (4,), 256, 128, (64,), 0, 0.002, 0.02, True,
@@ -54,6 +55,9 @@ WORKLOADS = {
     "mlp_down_k14336_n4096": Workload(
         "mlp_down_k14336_n4096", (1, 16, 256, 1024, 4096), 14336, 4096,
         (128, -1), 4, 0.001, 0.01, False, "MLP down-projection M sweep"),
+    "midm_k8192_n7168": Workload(
+        "midm_k8192_n7168", (32, 64, 128), 8192, 7168, (128,), 5, 0.001, 0.01, False,
+        "batches between decode and prefill"),
 }
 
 

@@ -226,6 +226,59 @@ __device__ __forceinline__ void store_tile(const char* stage, _Float16* __restri
   }
 }
 
+// Split K: the fp32 partial of a split goes out the same way, staged as a
+// row-major BM x BN fp32 tile (row pitch part_pitch) and copied with 16-byte
+// loads and stores (64 per row of 128 columns), instead of 4-byte stores
+// scattered over 2 rows per instruction.  Used when the tile fits the LDS.
+template <int BN> constexpr int part_pitch() { return BN * 4 + 16; }
+template <int BM, int BN> constexpr bool partial_stages() {
+  return BM * part_pitch<BN>() <= lds_bytes<BM, BN>();
+}
+static_assert(partial_stages<256, 128>() && partial_stages<128, 128>() &&
+                  partial_stages<64, 128>(),
+              "split partials of the narrow tiles are staged");
+template <int BM, int BN, int MI, int NB>
+__device__ __forceinline__ void stage_partial(const floatx16 (&acc)[MI][NB], char* stage,
+                                              int wave, int lane) {
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+#pragma unroll
+  for (int ni = 0; ni < NB; ++ni) {
+    const int lcol = (BN / 2) * wn + 32 * ni + (lane & 31);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lrow = (BM / 2) * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        *reinterpret_cast<float*>(stage + lrow * part_pitch<BN>() + 4 * lcol) = acc[mi][ni][r];
+      }
+    }
+  }
+}
+// tid = 0..511: chunk c = 512*i + tid is 4 columns (16 bytes) of tile row
+// c / (BN/4); pp is this split's [M][N] partial plane.
+template <int BM, int BN>
+__device__ __forceinline__ void store_partial(const char* stage, float* __restrict__ pp, int M,
+                                              int N, Tile t, int tid) {
+  constexpr int kChunksPerRow = BN / 4;
+  static_assert(BM * BN / 4 % 512 == 0, "whole chunks per thread");
+#pragma unroll
+  for (int i = 0; i < BM * BN / 4 / 512; ++i) {
+    const int c = 512 * i + tid;
+    const int lrow = c / kChunksPerRow;
+    const int lcol = 4 * (c - lrow * kChunksPerRow);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * part_pitch<BN>() + 4 * lcol);
+    const int row = t.m0 + lrow;
+    const int col = t.n0 + lcol;
+    if (row < M && col < N)
+      *reinterpret_cast<u32x4*>(pp + static_cast<size_t>(row) * N + col) = v;
+  }
+}
+
+// Output modes of a work-group: direct per-lane stores, the staged float16
+// y tile (one split), or the staged fp32 partial (split K).
+enum : int { kOutDirect = 0, kOutStagedY = 1, kOutStagedPartial = 2 };
+
 // Producer waves (4 of the 8): every global load of the tile and the
 // dequantisation of the weight slab into LDS.  pw = producer wave 0..3,
 // pt = producer thread 0..255.
@@ -312,7 +365,8 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
                                          const uint32_t* __restrict__ qz,
                                          const _Float16* __restrict__ sc, _Float16* __restrict__ y,
                                          int M, int K, int N, int gsh, Tile t, char* a_ring,
-                                         char* b_ring, int pw, int pt, bool staged) {
+                                         char* b_ring, int pw, int pt, int out_mode,
+                                         float* __restrict__ partial) {
   using C = Cfg<BM, BN>;
   constexpr int kBPitch = b_pitch<BN>();
   constexpr int kBTileBytes = b_tile_bytes<BN>();
@@ -500,10 +554,13 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
   if (kt < nks) pstep(kt, 0);
   if (kt + 1 < nks) pstep(kt + 1, 1);
   drain_sets(ws);
-  if (!staged) return;
+  if (out_mode == kOutDirect) return;
   __syncthreads();   // every wave is done with the LDS
   __syncthreads();   // the consumers have staged the output tile
-  store_tile<BM, BN>(a_ring, y, M, N, t, 256 + pt);
+  if (out_mode == kOutStagedY)
+    store_tile<BM, BN>(a_ring, y, M, N, t, 256 + pt);
+  else if constexpr (partial_stages<BM, BN>())
+    store_partial<BM, BN>(a_ring, partial + static_cast<size_t>(t.sp) * M * N, M, N, t, 256 + pt);
 }
 
 // Consumer waves (4 of the 8, a 2 x 2 grid): LDS operand reads and the
@@ -517,7 +574,7 @@ template <int BM, int BN>
 __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Float16* __restrict__ y,
                                          float* __restrict__ partial, int M, int N, int splits,
                                          Tile t, char* a_ring, const char* b_ring, int wave,
-                                         int lane, bool staged) {
+                                         int lane, int out_mode) {
   using C = Cfg<BM, BN>;
   constexpr int MI = C::MI;
   constexpr int NB = C::NB;
@@ -642,12 +699,22 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
 
   // Epilogue: 32x32 block output, lane holds column (lane % 32) and rows
   // 8*(r/4) + 4*(lane/32) + r%4 of register r.
-  if (staged) {
+  if (out_mode == kOutStagedY) {
     __syncthreads();   // every wave is done with the LDS
     stage_tile<BM, BN, MI, NB>(acc, bias, a_ring, N, t, wave, lane);
     __syncthreads();
     store_tile<BM, BN>(a_ring, y, M, N, t, 64 * wave + lane);
     return;
+  }
+  if constexpr (partial_stages<BM, BN>()) {
+    if (out_mode == kOutStagedPartial) {
+      __syncthreads();   // every wave is done with the LDS
+      stage_partial<BM, BN, MI, NB>(acc, a_ring, wave, lane);
+      __syncthreads();
+      store_partial<BM, BN>(a_ring, partial + static_cast<size_t>(t.sp) * M * N, M, N, t,
+                            64 * wave + lane);
+      return;
+    }
   }
   // Otherwise one split: y = acc + bias, 2-byte stores; several: the fp32
   // partial of this split (summed by prefill_reduce_kernel).
@@ -676,7 +743,7 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
 // and dequantisation).  Waves are spread over the 4 SIMDs round-robin, so
 // each SIMD runs one of each and the producer's vector work co-issues with
 // the consumer's matrix-core work.  Both roles pass the same number of
-// barriers (one per K step, two more when the output is staged).
+// barriers (one per K step, two more when the output or partial is staged).
 //
 // Split K (few tiles): work-group (tile, split) covers kps K steps and
 // stores its fp32 partial; prefill_reduce_kernel, next on the stream, sums
@@ -701,12 +768,15 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Tile t = tile_of<BM, BN>(n_tiles, splits, kps, (K + BK - 1) / BK);
-  const bool staged = splits == 1 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+  // The partial plane is 16-byte aligned (workspace layout, N % 8 == 0).
+  const int out_mode = splits == 1
+                           ? ((reinterpret_cast<uintptr_t>(y) & 15) == 0 ? kOutStagedY : kOutDirect)
+                           : (partial_stages<BM, BN>() ? kOutStagedPartial : kOutDirect);
   if (wave >= 4)
     producer<BM, BN, KTAIL>(x, qw, qz, sc, y, M, K, N, gsh, t, a_ring, b_ring, wave - 4,
-                            tid - 256, staged);
+                            tid - 256, out_mode, partial);
   else
-    consumer<BM, BN>(bias, y, partial, M, N, splits, t, a_ring, b_ring, wave, tid & 63, staged);
+    consumer<BM, BN>(bias, y, partial, M, N, splits, t, a_ring, b_ring, wave, tid & 63, out_mode);
 }
 
 // y = sum of the split partials, in split order (deterministic), + bias.

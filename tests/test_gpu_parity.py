@@ -169,6 +169,9 @@ GEMM_CASES = [
     ("mlp_down_k14336_n4096", 4096, 1024, -1, 96),
     ("mlp_down_k14336_n4096", 4096, 4096, -1, 96),
     ("prefill_qkv_m2048_k4096_n12288", 2048, 2048, 128, 96),
+    ("midm_k8192_n7168", 128, 32, 128, None),
+    ("midm_k8192_n7168", 128, 64, 128, None),
+    ("midm_k8192_n7168", 128, 128, 128, None),
 ]
 
 
