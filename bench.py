@@ -175,26 +175,35 @@ def run_leg(torch, awq, spec, steps, warmup, dev):
                 kern_min_ms=min(kern_ms), eager_ms=eager_ms, ws_bytes=ws_bytes)
 
 
-def cpu_baseline(p, g, budget_s, sample_rows=None):
-    """The oracle, as it stands, on the host cores (rank 0 only)."""
-    import numpy as np
-    import oracle
+def blas_thread_count():
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        blas_threads = os.cpu_count() or 1
-    x = p["x"] if sample_rows is None else p["x"][:sample_rows]
+        return os.cpu_count() or 1
+
+
+def time_oracle(fn, budget_s):
+    """Median wall time of fn() over repeated runs within about budget_s."""
     times = []
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        oracle.awq_linear_ref(x, p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
+        fn()
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > budget_s or len(times) >= 20:
             break
-    del np
-    return statistics.median(times), len(times), blas_threads
+    return statistics.median(times), len(times)
+
+
+def cpu_baseline(p, g, budget_s, sample_rows=None):
+    """The oracle, as it stands, on the host cores (rank 0 only)."""
+    import oracle
+    x = p["x"] if sample_rows is None else p["x"][:sample_rows]
+    t, n = time_oracle(
+        lambda: oracle.awq_linear_ref(x, p["qweight"], p["qzeros"], p["scales"], p["bias"], g),
+        budget_s)
+    return t, n, blas_thread_count()
 
 
 def sweep(torch, awq, dev):
@@ -215,7 +224,8 @@ def sweep(torch, awq, dev):
                 sec = r["ms_per_step"] * 1e-3
                 gbs = r["nbytes"] / sec / 1e9
                 tfs = r["nflops"] / sec / 1e12
-                hbm = M <= 16
+                # The binding roof: whichever takes longer at peak.
+                hbm = r["nbytes"] / HBM_PEAK_GBS >= r["nflops"] / FP16_MFMA_PEAK_TFLOPS / 1e3
                 print(json.dumps({
                     "workload": name, "M": M, "K": r["K"], "N": r["N"], "group_size": g,
                     "bias": r["p"]["bias"] is not None, "kernel": r["path"],
@@ -237,12 +247,17 @@ def sweep(torch, awq, dev):
         r = run_leg(torch, awq, dict(source=name, M=1, group_size=128), 200, 10, dev)
         w4_us = r["ms_per_step"] * 1e3
         nbytes = K * N * 2 + K * 2 + N * 2
+        t_cpu, n_cpu = dense_oracle_time(K, N)
         print(json.dumps({
             "workload": f"dense_fp16_baseline_m1_k{K}_n{N}", "M": 1, "K": K, "N": N,
             "kernel": "dense_gemv", "us_per_call": round(d_us, 3),
             "GB_per_s": round(nbytes / (d_us * 1e-6) / 1e9, 1), "bound": "hbm",
             "frac": round(nbytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes,
-            "w4a16_us_per_call": round(w4_us, 3), "w4a16_speedup": round(d_us / w4_us, 2)}),
+            "w4a16_us_per_call": round(w4_us, 3), "w4a16_speedup": round(d_us / w4_us, 2),
+            "cpu_baseline": {"value": round(nbytes / t_cpu / 1e9, 3), "unit": "GB/s",
+                             "cores": blas_thread_count(), "kind": "oracle",
+                             "sample": f"the same product through oracle.dense_linear_ref "
+                                       f"(float64), median of {n_cpu} runs of {t_cpu:.3f} s"}}),
             flush=True)
     # Activation-order weights (row-to-group map): the load-time reorder is
     # done once; each step reorders x's columns and runs the grouped kernels.
@@ -254,8 +269,14 @@ def sweep(torch, awq, dev):
         sec = r["ms_per_step"] * 1e-3
         gbs = r["nbytes"] / sec / 1e9
         tfs = r["nflops"] / sec / 1e12
-        hbm = M <= 16
+        hbm = r["nbytes"] / HBM_PEAK_GBS >= r["nflops"] / FP16_MFMA_PEAK_TFLOPS / 1e3
         plain = fused.get((name, M, r["K"], r["N"], r["p"]["bias"] is not None))
+        t_cpu, n_cpu, rows = act_order_oracle_time(r["p"], r["K"], min(M, 16))
+        cpu = {"value": round(r["nbytes"] * rows / M / t_cpu / 1e9, 3), "unit": "GB/s",
+               "cores": blas_thread_count(), "kind": "oracle",
+               "sample": f"first {rows} of the {M} rows through oracle.awq_linear_gidx_ref "
+                         f"(map lookup, float16 dequant, float64 matmul), median of {n_cpu} runs "
+                         f"of {t_cpu:.2f} s; GB/s scaled to the rows computed"}
         print(json.dumps({
             "workload": f"act_order_{name}", "M": M, "K": r["K"], "N": r["N"], "group_size": 128,
             "kernel": (f"{r['path']} (gathers x through the order itself)"
@@ -266,14 +287,15 @@ def sweep(torch, awq, dev):
             "bound": "hbm" if hbm else "mfma",
             "frac": round(gbs / HBM_PEAK_GBS if hbm else tfs / FP16_MFMA_PEAK_TFLOPS, 4),
             "bytes": r["nbytes"], "copies_rotated": r["R"],
-            "grouped_us_per_call": round(plain * 1e3, 3) if plain else None}), flush=True)
+            "grouped_us_per_call": round(plain * 1e3, 3) if plain else None,
+            "cpu_baseline": cpu}), flush=True)
         del r
         torch.cuda.empty_cache()
-    # Context at the matrix-core-bound points: torch's float16 linear (the
+    # Context at the batches of 32 rows and more: torch's float16 linear (the
     # vendor GEMM library) on an unquantised weight of the same shape, and
     # the unfused route (awq_dequant into a float16 weight, then that GEMM).
     for (name, M, K, N, bias), ms in fused.items():
-        if M < 256:
+        if M < 32:
             continue
         print(f"[sweep] vendor float16 GEMM M={M} K={K} N={N}", file=sys.stderr, flush=True)
         lin_us, unfused_us = vendor_gemm_times_us(torch, awq, M, K, N, bias, dev)
@@ -285,6 +307,29 @@ def sweep(torch, awq, dev):
             "bound": "mfma", "frac": round(flops / lin_us / 1e6 / FP16_MFMA_PEAK_TFLOPS, 4),
             "unfused_dequant_then_gemm_us": round(unfused_us, 3),
             "w4a16_fused_us_per_call": round(ms * 1e3, 3)}), flush=True)
+
+
+def dense_oracle_time(K, N):
+    """Oracle time of the unquantised single-token product (float64)."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(K + N)
+    x = rng.standard_normal((1, K)).astype(np.float16)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    return time_oracle(lambda: oracle.dense_linear_ref(x, w, None), 3.0)
+
+
+def act_order_oracle_time(p, K, rows):
+    """Oracle time of the act-order forward on the first `rows` rows."""
+    import awq_inputs
+    import oracle
+    g_idx = awq_inputs.act_order_g_idx(K, 128, seed=K + p["scales"].shape[1])
+    x = p["x"][:rows]
+    run = lambda: oracle.awq_linear_gidx_ref(x, p["qweight"], p["qzeros"], p["scales"], g_idx,  # noqa: E731
+                                             p["bias"])
+    run()   # the first run pays for page faults of its large temporaries
+    t, n = time_oracle(run, 4.0)
+    return t, n, rows
 
 
 def vendor_gemm_times_us(torch, awq, M, K, N, bias, dev, calls=30):
