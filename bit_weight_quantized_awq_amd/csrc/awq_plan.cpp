@@ -4,6 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "awq.h"
@@ -264,19 +265,27 @@ int gidx_order(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* per
                int64_t* group_size) {
   if (!g_idx || !perm || K <= 0 || num_groups <= 0) return AWQ_ERROR_INVALID_VALUE;
   if (K > kMaxElems || num_groups > kMaxElems) return AWQ_ERROR_SHAPE;
-  std::vector<int64_t> start(static_cast<size_t>(num_groups) + 1, 0);
-  for (int64_t k = 0; k < K; ++k) {
-    const int32_t gk = g_idx[k];
-    if (gk < 0 || gk >= num_groups) return AWQ_ERROR_INVALID_VALUE;
-    ++start[static_cast<size_t>(gk) + 1];
+  for (int64_t k = 0; k < K; ++k)
+    if (g_idx[k] < 0 || g_idx[k] >= num_groups) return AWQ_ERROR_INVALID_VALUE;
+  // Stable sort of the row indices by group (memory O(K), independent of
+  // num_groups); host allocation failure is reported, never thrown across
+  // the C ABI.
+  try {
+    std::vector<int32_t> order(static_cast<size_t>(K));
+    for (int64_t k = 0; k < K; ++k) order[static_cast<size_t>(k)] = static_cast<int32_t>(k);
+    std::stable_sort(order.begin(), order.end(),
+                     [g_idx](int32_t a, int32_t b) { return g_idx[a] < g_idx[b]; });
+    // Every group holds K / num_groups rows exactly when the sorted map is
+    // j / (K / num_groups) for every position j.
+    bool uniform = K % num_groups == 0;
+    const int64_t per = uniform ? K / num_groups : 0;
+    for (int64_t j = 0; j < K && uniform; ++j)
+      if (g_idx[order[static_cast<size_t>(j)]] != j / per) uniform = false;
+    for (int64_t j = 0; j < K; ++j) perm[j] = order[static_cast<size_t>(j)];
+    if (group_size) *group_size = uniform ? per : 0;
+  } catch (...) {
+    return AWQ_ERROR_INVALID_VALUE;
   }
-  bool uniform = K % num_groups == 0;
-  for (int64_t j = 0; j < num_groups; ++j) {
-    if (start[j + 1] != K / num_groups) uniform = false;
-    start[j + 1] += start[j];
-  }
-  for (int64_t k = 0; k < K; ++k) perm[start[g_idx[k]]++] = static_cast<int32_t>(k);
-  if (group_size) *group_size = uniform ? K / num_groups : 0;
   return AWQ_SUCCESS;
 }
 

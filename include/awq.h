@@ -178,7 +178,8 @@ int awq_gemm_gidx(const void* x, const void* qweight, const void* qzeros, const 
  * when every group holds exactly that many rows (the reordered weight is then
  * a grouped weight of that group size), else 0.  An entry outside
  * [0, num_groups), NULL pointers, K <= 0 or num_groups <= 0 give
- * AWQ_ERROR_INVALID_VALUE and leave perm untouched. */
+ * AWQ_ERROR_INVALID_VALUE and leave perm untouched (as does a failed host
+ * allocation of K indices). */
 int awq_gidx_order(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* perm,
                    int64_t* group_size);
 

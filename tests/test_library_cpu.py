@@ -367,6 +367,13 @@ def test_gidx_order_matches_oracle():
         assert gs == g
 
 
+def test_gidx_order_memory_does_not_depend_on_group_count():
+    """A map over a huge group range (most groups empty) sorts in O(K)
+    memory; it is not an act-order map, so no group size is reported."""
+    perm, gs = awq.gidx_order([3, 0, (1 << 30) - 1, 0], 1 << 30)
+    assert perm.tolist() == [1, 3, 0, 2] and gs == 0
+
+
 @pytest.mark.parametrize("gi,G", [([0, 1, 3], 3), ([0, -1], 2), ([0, 0], 0)])
 def test_gidx_order_rejects_bad_maps(gi, G):
     with pytest.raises(binding.AwqError) as e:
