@@ -95,10 +95,10 @@ def run_leg(torch, awq, spec, steps, warmup, dev):
     K, N, G = problem_dims(p)
     nbytes = algorithmic_bytes(M, K, N, G, p["bias"] is not None)
     nflops = 2 * M * N * K
-    act = spec.get("act_order", False)
+    act = spec.get("gidx")   # None, "act_order" or "uneven"
     if act:
-        # The same weight under an activation-order map: g_idx (K int32) is
-        # read by the method too; the load-time reorder is not timed.
+        # The same weight under a row-to-group map: g_idx (K int32) is read
+        # by the method too; the load-time rebuild is not timed.
         nbytes += 4 * K
     R = max(2, -(-ROTATE_BYTES // nbytes))
     copies = make_copies(torch, p, R, dev)
@@ -107,18 +107,21 @@ def run_leg(torch, awq, spec, steps, warmup, dev):
                                copies[0]["scales"].data_ptr())
     assert need <= ws_bytes
     if act:
-        g_idx = awq_inputs.act_order_g_idx(K, g, seed=K + N)
+        g_idx = (awq_inputs.act_order_g_idx(K, g, seed=K + N) if act == "act_order"
+                 else awq_inputs.random_g_idx(K, G, seed=K + N))
         for c in copies:
-            c["qweight"], c["perm"], gs = awq.prepare_act_order(c["qweight"], g_idx, G)
-            assert gs == g
-        ws_bytes = awq.act_order_workspace_size(M, K, N, g)
+            c["w"] = awq.prepare_gidx(c["qweight"], c["qzeros"], c["scales"], g_idx)
+            del c["qweight"], c["qzeros"], c["scales"]
+        w0 = copies[0]["w"]
+        ws_bytes = awq.sorted_workspace_size(M, w0.rows, N, w0.block_rows)
+        path, _ = awq.gemm_plan(M, w0.rows, N, w0.block_rows)
+        p = dict(p, g_idx=g_idx)
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def step(i):
         c = copies[i % R]
         if act:
-            awq.gemm_act_order(c["x"], c["perm"], c["qweight"], c["qzeros"], c["scales"],
-                               c["bias"], g, out=c["y"], workspace=ws)
+            awq.gemm_sorted(c["x"], c["w"], c["bias"], out=c["y"], workspace=ws)
         else:
             awq.gemm(c["x"], c["qweight"], c["qzeros"], c["scales"], c["bias"], g, out=c["y"],
                      workspace=ws)
@@ -170,7 +173,9 @@ def run_leg(torch, awq, spec, steps, warmup, dev):
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - e0) * 1e3 / steps
 
+    sorted_rows = copies[0]["w"].rows if act else K
     return dict(p=p, M=M, K=K, N=N, G=G, g=g, nbytes=nbytes, nflops=nflops, R=R,
+                sorted_rows=sorted_rows,
                 path=awq.PATH_NAMES[path], ms_per_step=ms_per_step, kern_avg_ms=kern_avg_ms,
                 kern_min_ms=min(kern_ms), eager_ms=eager_ms, ws_bytes=ws_bytes)
 
@@ -259,26 +264,31 @@ def sweep(torch, awq, dev):
                              "sample": f"the same product through oracle.dense_linear_ref "
                                        f"(float64), median of {n_cpu} runs of {t_cpu:.3f} s"}}),
             flush=True)
-    # Activation-order weights (row-to-group map): the load-time reorder is
-    # done once; each step reorders x's columns and runs the grouped kernels.
-    for name, M in (("decode_sweep_k8192_n7168", 1), ("decode_sweep_k8192_n7168", 16),
-                    ("prefill_qkv_m2048_k4096_n12288", 2048)):
-        print(f"[sweep] act order {name} M={M}", file=sys.stderr, flush=True)
-        spec = dict(source=name, M=M, group_size=128, act_order=True)
+    # Weights under a row-to-group map, rebuilt once as grouped weights:
+    # activation order (whole groups) and an uneven map (32-row blocks,
+    # padded); each step reorders x's columns and runs the grouped kernels.
+    for name, M, kind in (("decode_sweep_k8192_n7168", 1, "act_order"),
+                          ("decode_sweep_k8192_n7168", 16, "act_order"),
+                          ("prefill_qkv_m2048_k4096_n12288", 2048, "act_order"),
+                          ("decode_sweep_k8192_n7168", 1, "uneven"),
+                          ("prefill_qkv_m2048_k4096_n12288", 2048, "uneven")):
+        print(f"[sweep] {kind} map {name} M={M}", file=sys.stderr, flush=True)
+        spec = dict(source=name, M=M, group_size=128, gidx=kind)
         r = run_leg(torch, awq, spec, 200 if M <= 16 else 50, 10, dev)
         sec = r["ms_per_step"] * 1e-3
         gbs = r["nbytes"] / sec / 1e9
         tfs = r["nflops"] / sec / 1e12
         hbm = r["nbytes"] / HBM_PEAK_GBS >= r["nflops"] / FP16_MFMA_PEAK_TFLOPS / 1e3
         plain = fused.get((name, M, r["K"], r["N"], r["p"]["bias"] is not None))
-        t_cpu, n_cpu, rows = act_order_oracle_time(r["p"], r["K"], min(M, 16))
+        t_cpu, n_cpu, rows = gidx_oracle_time(r["p"], min(M, 16))
         cpu = {"value": round(r["nbytes"] * rows / M / t_cpu / 1e9, 3), "unit": "GB/s",
                "cores": blas_thread_count(), "kind": "oracle",
                "sample": f"first {rows} of the {M} rows through oracle.awq_linear_gidx_ref "
                          f"(map lookup, float16 dequant, float64 matmul), median of {n_cpu} runs "
                          f"of {t_cpu:.2f} s; GB/s scaled to the rows computed"}
         print(json.dumps({
-            "workload": f"act_order_{name}", "M": M, "K": r["K"], "N": r["N"], "group_size": 128,
+            "workload": f"{kind}_map_{name}", "M": M, "K": r["K"], "N": r["N"],
+            "group_size": 128, "map": kind, "sorted_rows": r["sorted_rows"],
             "kernel": (f"{r['path']} (gathers x through the order itself)"
                        if r["path"] == "decode" and M <= 4 and r["N"] % 32 == 0
                        else f"x reorder pass + {r['path']}"),
@@ -319,14 +329,13 @@ def dense_oracle_time(K, N):
     return time_oracle(lambda: oracle.dense_linear_ref(x, w, None), 3.0)
 
 
-def act_order_oracle_time(p, K, rows):
-    """Oracle time of the act-order forward on the first `rows` rows."""
-    import awq_inputs
+def gidx_oracle_time(p, rows):
+    """Oracle time of the forward under p's row-to-group map on the first
+    `rows` rows."""
     import oracle
-    g_idx = awq_inputs.act_order_g_idx(K, 128, seed=K + p["scales"].shape[1])
     x = p["x"][:rows]
-    run = lambda: oracle.awq_linear_gidx_ref(x, p["qweight"], p["qzeros"], p["scales"], g_idx,  # noqa: E731
-                                             p["bias"])
+    run = lambda: oracle.awq_linear_gidx_ref(x, p["qweight"], p["qzeros"], p["scales"],  # noqa: E731
+                                             p["g_idx"], p["bias"])
     run()   # the first run pays for page faults of its large temporaries
     t, n = time_oracle(run, 4.0)
     return t, n, rows

@@ -10,8 +10,8 @@ from __future__ import annotations
 from .binding import (  # noqa: F401
     AWQ_PATH_DECODE, AWQ_PATH_GENERIC, AWQ_PATH_PREFILL, AwqError, PATH_NAMES, abi_version,
     dense_gemv, dequant, gemm, gemm_plan, gemm_workspace_size, lib, status_string,
-    act_order_workspace_size, dequant_gidx, gemm_act_order, gemm_gidx, gidx_order,
-    permute_rows, prepare_act_order,
+    SortedWeight, dequant_gidx, gather_rows, gemm_gidx, gemm_sorted, gidx_layout, prepare_gidx,
+    sorted_workspace_size,
 )
 
 

@@ -44,11 +44,14 @@ SIGNATURES = {
     "awq_dequant_gidx": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "awq_gemm_gidx": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                      _i64, _vp]),
-    "awq_gidx_order": (ctypes.c_int, [_vp, _i64, _i64, _vp, ctypes.POINTER(ctypes.c_int64)]),
-    "awq_permute_rows": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
-    "awq_gemm_act_order_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64, _i64]),
-    "awq_gemm_act_order": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
-                                          _i64, _vp, ctypes.c_size_t, _vp]),
+    "awq_gidx_layout": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64,
+                                       ctypes.POINTER(ctypes.c_int64),
+                                       ctypes.POINTER(ctypes.c_int64),
+                                       ctypes.POINTER(ctypes.c_int64)]),
+    "awq_gather_rows": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp]),
+    "awq_gemm_sorted_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64, _i64]),
+    "awq_gemm_sorted": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                       _i64, _vp, ctypes.c_size_t, _vp]),
 }
 
 _lib = None
@@ -105,28 +108,34 @@ def gemm_plan(M: int, K: int, N: int, group_size: int, x_ptr: int = 0,
     return path.value, ws.value
 
 
-def gidx_order(g_idx, num_groups: int):
-    """Host-only awq_gidx_order: (perm, group_size) for a row-to-group map
-    given as a sequence or numpy array of K integers.  perm is an int32 numpy
-    array (perm[j] = row placed j-th, rows stably sorted by group);
-    group_size is K / num_groups when every group holds that many rows,
-    else 0."""
+def gidx_layout(g_idx, num_groups: int):
+    """Host-only awq_gidx_layout: (perm, block_group, block_rows) for a
+    row-to-group map given as a sequence or numpy array of K integers.
+    perm (int32, rows of the sorted weight) is the input row placed j-th or
+    -1 for a null row; block_group (int32) is the group of each block of
+    block_rows rows."""
     import numpy as np
     g = np.ascontiguousarray(np.asarray(g_idx), dtype=np.int32)
-    if g.ndim != 1:
-        raise ValueError("g_idx must be 1-D")
+    if g.ndim != 1 or g.shape[0] == 0:
+        raise ValueError("g_idx must be a non-empty 1-D sequence")
     K = g.shape[0]
-    perm = np.empty(K, dtype=np.int32)
-    gs = ctypes.c_int64(0)
-    st = lib().awq_gidx_order(g.ctypes.data if K else None, K, num_groups,
-                              perm.ctypes.data if K else None, ctypes.byref(gs))
+    rows, brows, blocks = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    st = lib().awq_gidx_layout(g.ctypes.data, K, num_groups, None, 0, None, 0,
+                               ctypes.byref(rows), ctypes.byref(brows), ctypes.byref(blocks))
     if st != AWQ_SUCCESS:
-        raise AwqError(st, "awq_gidx_order")
-    return perm, gs.value
+        raise AwqError(st, "awq_gidx_layout")
+    perm = np.empty(rows.value, dtype=np.int32)
+    block_group = np.empty(blocks.value, dtype=np.int32)
+    st = lib().awq_gidx_layout(g.ctypes.data, K, num_groups, perm.ctypes.data, perm.size,
+                               block_group.ctypes.data, block_group.size, ctypes.byref(rows),
+                               ctypes.byref(brows), ctypes.byref(blocks))
+    if st != AWQ_SUCCESS:
+        raise AwqError(st, "awq_gidx_layout")
+    return perm, block_group, brows.value
 
 
-def act_order_workspace_size(M: int, K: int, N: int, group_size: int) -> int:
-    return lib().awq_gemm_act_order_workspace_size(M, K, N, group_size)
+def sorted_workspace_size(M: int, rows: int, N: int, block_rows: int) -> int:
+    return lib().awq_gemm_sorted_workspace_size(M, rows, N, block_rows)
 
 
 # --------------------------------------------------------------------- torch
@@ -405,82 +414,108 @@ def _check_bias(bias, N, device):
     return bias.contiguous()
 
 
-def permute_rows(qweight, perm, out=None):
-    """qweight[perm] for a packed int32 (K, N/8) weight through
-    awq_permute_rows; perm int32 (K,) on the device."""
+def gather_rows(src, idx, out=None):
+    """out[j] = src[idx[j]] (zero rows for indices out of range) through
+    awq_gather_rows, for a 2-D tensor whose rows are whole 4-byte words;
+    idx int32 on the device."""
     torch = _torch()
-    device = qweight.device
-    _check_device("qweight", qweight, device)
-    if qweight.dtype != torch.int32:
-        raise TypeError("qweight must be int32")
-    K = qweight.shape[0]
-    N = qweight.shape[1] * 8
-    perm = _check_map(perm, K, device)
-    qweight = qweight.contiguous()
+    device = src.device
+    _check_device("src", src, device)
+    _check_device("idx", idx, device)
+    if src.dim() != 2 or idx.dim() != 1 or idx.dtype != torch.int32:
+        raise ValueError("src must be 2-D and idx a 1-D int32 tensor")
+    src = src.contiguous()
+    idx = idx.contiguous()
+    rows = idx.shape[0]
+    row_bytes = src.shape[1] * src.element_size()
     if out is None:
-        out = torch.empty_like(qweight)
+        out = torch.empty((rows, src.shape[1]), dtype=src.dtype, device=device)
     else:
         _check_device("out", out, device)
-        if out.shape != qweight.shape or out.dtype != torch.int32 or not out.is_contiguous():
-            raise ValueError("out must be a contiguous int32 tensor shaped like qweight")
+        if out.shape != (rows, src.shape[1]) or out.dtype != src.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor of shape (len(idx), src.shape[1])")
     stream = torch.cuda.current_stream(device).cuda_stream
-    st = lib().awq_permute_rows(qweight.data_ptr(), perm.data_ptr(), out.data_ptr(), K, N, stream)
+    st = lib().awq_gather_rows(src.data_ptr(), src.shape[0], idx.data_ptr(), out.data_ptr(),
+                               rows, row_bytes, stream)
     if st != AWQ_SUCCESS:
-        raise AwqError(st, "awq_permute_rows")
+        raise AwqError(st, "awq_gather_rows")
     return out
 
 
-def prepare_act_order(qweight, g_idx, num_groups: int):
-    """Load-time reorder of an activation-order weight: (qweight_sorted,
-    perm on the device, group_size).  g_idx may be a host sequence, a numpy
-    array or a tensor; every group must hold the same number of rows (else
-    ValueError: such maps take gemm_gidx)."""
+class SortedWeight:
+    """A weight under a row-to-group map, rebuilt as a grouped weight:
+    qweight (rows, N/8), qzeros and scales (rows / block_rows, ...), perm
+    (rows, int32 on the device: input row of each sorted row, -1 for null
+    rows) and in_features (K of x)."""
+
+    def __init__(self, qweight, qzeros, scales, perm, block_rows, in_features):
+        self.qweight = qweight
+        self.qzeros = qzeros
+        self.scales = scales
+        self.perm = perm
+        self.block_rows = block_rows
+        self.in_features = in_features
+
+    @property
+    def rows(self):
+        return self.qweight.shape[0]
+
+
+def prepare_gidx(qweight, qzeros, scales, g_idx):
+    """Load-time rebuild of (qweight, qzeros, scales) under a row-to-group
+    map g_idx (K integers: host sequence, numpy array or tensor) into a
+    SortedWeight: awq_gidx_layout on the host, awq_gather_rows on the
+    device."""
     torch = _torch()
+    device = qweight.device
+    for name, t in (("qweight", qweight), ("qzeros", qzeros), ("scales", scales)):
+        _check_device(name, t, device)
+    if qweight.dtype != torch.int32 or qzeros.dtype != torch.int32:
+        raise TypeError("qweight and qzeros must be int32")
+    if scales.dtype != torch.float16:
+        raise TypeError("scales must be float16")
+    K = qweight.shape[0]
+    N = qweight.shape[1] * 8
+    G = _check_map_groups(N, qzeros, scales)
     if hasattr(g_idx, "detach"):
         g_idx = g_idx.detach().cpu().numpy()
-    perm, group_size = gidx_order(g_idx, num_groups)
-    if group_size == 0:
-        raise ValueError("the groups of this map differ in size; use gemm_gidx")
-    perm_dev = torch.from_numpy(perm).to(qweight.device)
-    return permute_rows(qweight, perm_dev), perm_dev, group_size
+    if len(g_idx) != K:
+        raise ValueError(f"g_idx has {len(g_idx)} entries, qweight has {K} rows")
+    perm, block_group, block_rows = gidx_layout(g_idx, G)
+    perm_dev = torch.from_numpy(perm).to(device)
+    bg_dev = torch.from_numpy(block_group).to(device)
+    return SortedWeight(gather_rows(qweight, perm_dev), gather_rows(qzeros, bg_dev),
+                        gather_rows(scales, bg_dev), perm_dev, block_rows, K)
 
 
-def gemm_act_order(x, perm, qweight_sorted, qzeros, scales, bias=None, group_size: int = 128,
-                   out=None, workspace=None):
-    """y = x[:, perm] . W_sorted + bias through awq_gemm_act_order (equal to
-    the forward of the original activation-order weight).  Returns float16
-    (*, N)."""
+def gemm_sorted(x, w, bias=None, out=None, workspace=None):
+    """y = x[:, perm] . W_sorted + bias through awq_gemm_sorted, for a
+    SortedWeight w (equal to the forward of the original weight under its
+    map).  Returns float16 (*, N)."""
     torch = _torch()
-    device = qweight_sorted.device
-    for name, t in (("x", x), ("qweight_sorted", qweight_sorted), ("qzeros", qzeros),
-                    ("scales", scales)):
-        _check_device(name, t, device)
-    if x.dtype != torch.float16 or scales.dtype != torch.float16:
-        raise TypeError("x and scales must be float16")
-    if qweight_sorted.dtype != torch.int32 or qzeros.dtype != torch.int32:
-        raise TypeError("qweight_sorted and qzeros must be int32")
-    K = qweight_sorted.shape[0]
-    N = qweight_sorted.shape[1] * 8
-    if x.shape[-1] != K:
-        raise ValueError(f"x has {x.shape[-1]} features, qweight has {K}")
-    _check_group_shapes(K, N, group_size, qzeros, scales)
-    perm = _check_map(perm, K, device)
+    device = w.qweight.device
+    _check_device("x", x, device)
+    if x.dtype != torch.float16:
+        raise TypeError("x must be float16")
+    K_in = w.in_features
+    rows = w.rows
+    N = w.qweight.shape[1] * 8
+    if x.shape[-1] != K_in:
+        raise ValueError(f"x has {x.shape[-1]} features, the weight has {K_in}")
     bias = _check_bias(bias, N, device)
-    lead, x2 = _prep_x(x, K)
+    lead, x2 = _prep_x(x, K_in)
     M = x2.shape[0]
     y = _prep_out(out, M, N, device)
-    qweight_sorted = qweight_sorted.contiguous()
-    qzeros, scales = qzeros.contiguous(), scales.contiguous()
     stream = torch.cuda.current_stream(device).cuda_stream
-    need = act_order_workspace_size(M, K, N, group_size) if M > 0 else 0
+    need = sorted_workspace_size(M, rows, N, w.block_rows) if M > 0 else 0
     ws = _workspace(device, stream, need) if workspace is None else workspace
     ws_ptr = ws.data_ptr() if ws is not None else None
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    st = lib().awq_gemm_act_order(x2.data_ptr() if M else None, perm.data_ptr(),
-                                  qweight_sorted.data_ptr(), qzeros.data_ptr(),
-                                  scales.data_ptr(), bias.data_ptr() if bias is not None else None,
-                                  y.data_ptr() if M else None, M, K, N, group_size, ws_ptr,
-                                  ws_bytes, stream)
+    st = lib().awq_gemm_sorted(x2.data_ptr() if M else None, w.perm.data_ptr(),
+                               w.qweight.data_ptr(), w.qzeros.data_ptr(), w.scales.data_ptr(),
+                               bias.data_ptr() if bias is not None else None,
+                               y.data_ptr() if M else None, M, K_in, rows, N, w.block_rows,
+                               ws_ptr, ws_bytes, stream)
     if st != AWQ_SUCCESS:
-        raise AwqError(st, "awq_gemm_act_order")
+        raise AwqError(st, "awq_gemm_sorted")
     return y.reshape(*lead, N)

@@ -55,13 +55,15 @@ int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size, const voi
 namespace {
 
 // Plans and launches the grouped forward for a validated problem p (x, y
-// non-NULL and M > 0).  Shared by awq_gemm and awq_gemm_act_order.  With a
-// column order perm (act order), x is read as x[:, perm]: the LDS decode
-// kernel gathers it itself (up to 4 steps); every other kernel reads a copy
-// reordered into xp first (M x K float16, 16-byte aligned).
+// non-NULL and M > 0).  Shared by awq_gemm and awq_gemm_sorted.  With a
+// column order perm (sorted weight), x (M x Kx) is read as x[:, perm] with
+// 0 where perm is outside [0, Kx): the LDS decode kernel gathers it itself
+// (small batches); every other kernel reads a copy reordered into xp first
+// (M x K float16, 16-byte aligned).
 int run_gemm(const Problem& p, const void* x, const void* qweight, const void* qzeros,
              const void* scales, const void* bias, void* y, void* workspace,
-             size_t workspace_bytes, const int32_t* perm, _Float16* xp, hipStream_t s) {
+             size_t workspace_bytes, const int32_t* perm, int64_t Kx, _Float16* xp,
+             hipStream_t s) {
   const int force = awq::force_path_from_env();
   if (force < 0) return AWQ_ERROR_INVALID_VALUE;
   Plan pl;
@@ -78,7 +80,8 @@ int run_gemm(const Problem& p, const void* x, const void* qweight, const void* q
                             pl.steps <= 4 && p.M <= awq::decode_gather_max_m();
   if (perm && !fused_gather) {
     const hipError_t e = awq::launch_gather_cols(static_cast<const _Float16*>(x), perm, xp,
-                                                 static_cast<int>(p.M), static_cast<int>(p.K), s);
+                                                 static_cast<int>(p.M), static_cast<int>(Kx),
+                                                 static_cast<int>(p.K), s);
     if (e != hipSuccess) return AWQ_ERROR_HIP;
     x = xp;
   }
@@ -97,7 +100,8 @@ int run_gemm(const Problem& p, const void* x, const void* qweight, const void* q
     case AWQ_PATH_DECODE:
       e = awq::launch_decode(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, iG, pl.steps, pl.splits,
                              pl.n_tiles, pl.decode_lds, workspace,
-                             fused_gather ? perm : nullptr, s);
+                             fused_gather ? perm : nullptr,
+                             fused_gather ? static_cast<int>(Kx) : iK, s);
       break;
     case AWQ_PATH_PREFILL:
       e = awq::launch_prefill(xh, qw, qz, sc, bh, yh, iM, iK, iN, pl.group_shift, pl.prefill_bm,
@@ -127,7 +131,7 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void*
   if (st != AWQ_SUCCESS) return st;
   if (M == 0) return AWQ_SUCCESS;
   return run_gemm(p, x, qweight, qzeros, scales, bias, y, workspace, workspace_bytes, nullptr,
-                  nullptr, static_cast<hipStream_t>(stream));
+                  K, nullptr, static_cast<hipStream_t>(stream));
 }
 
 int awq_dense_gemv(const void* x, const void* w, const void* bias, void* y, int64_t M, int64_t K,
@@ -196,49 +200,55 @@ int awq_gemm_gidx(const void* x, const void* qweight, const void* qzeros, const 
   return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP;
 }
 
-int awq_gidx_order(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* perm,
-                   int64_t* group_size) {
-  return awq::gidx_order(g_idx, K, num_groups, perm, group_size);
+int awq_gidx_layout(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* perm,
+                    int64_t perm_capacity, int32_t* block_group, int64_t block_capacity,
+                    int64_t* rows, int64_t* block_rows, int64_t* blocks) {
+  return awq::gidx_layout(g_idx, K, num_groups, perm, perm_capacity, block_group,
+                          block_capacity, rows, block_rows, blocks);
 }
 
-int awq_permute_rows(const void* qweight, const void* perm, void* qweight_out, int64_t K,
-                     int64_t N, void* stream) {
-  Problem p;
-  int st = awq::validate_shape(0, K, N, -1, &p);
-  if (st != AWQ_SUCCESS) return st;
-  if (!qweight || !perm || !qweight_out) return AWQ_ERROR_INVALID_VALUE;
-  if (!awq::aligned(qweight, 4) || !awq::aligned(perm, 4) || !awq::aligned(qweight_out, 4))
+int awq_gather_rows(const void* src, int64_t src_rows, const void* idx, void* dst,
+                    int64_t dst_rows, int64_t row_bytes, void* stream) {
+  if (!src || !idx || !dst || src_rows <= 0 || dst_rows <= 0 || row_bytes <= 0)
+    return AWQ_ERROR_INVALID_VALUE;
+  if (row_bytes % 4 != 0) return AWQ_ERROR_SHAPE;
+  const int64_t lim = (int64_t{1} << 31) - 1;
+  const int64_t words = row_bytes / 4;
+  if (src_rows > lim || dst_rows > lim || src_rows * words > lim || dst_rows * words > lim)
+    return AWQ_ERROR_SHAPE;
+  if (!awq::aligned(src, 4) || !awq::aligned(idx, 4) || !awq::aligned(dst, 4))
     return AWQ_ERROR_MISALIGNED;
-  const hipError_t e = awq::launch_permute_rows(
-      static_cast<const uint32_t*>(qweight), static_cast<const int32_t*>(perm),
-      static_cast<uint32_t*>(qweight_out), static_cast<int>(K), static_cast<int>(N / 8),
-      static_cast<hipStream_t>(stream));
+  const hipError_t e = awq::launch_gather_rows(
+      static_cast<const uint32_t*>(src), static_cast<int>(src_rows),
+      static_cast<const int32_t*>(idx), static_cast<uint32_t*>(dst), static_cast<int>(dst_rows),
+      static_cast<int>(words), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP;
 }
 
-size_t awq_gemm_act_order_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size) {
-  return awq::act_order_workspace_size(M, K, N, group_size);
+size_t awq_gemm_sorted_workspace_size(int64_t M, int64_t rows, int64_t N, int64_t block_rows) {
+  return awq::sorted_workspace_size(M, rows, N, block_rows);
 }
 
-int awq_gemm_act_order(const void* x, const void* perm, const void* qweight_sorted,
-                       const void* qzeros, const void* scales, const void* bias, void* y,
-                       int64_t M, int64_t K, int64_t N, int64_t group_size, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+int awq_gemm_sorted(const void* x, const void* perm, const void* qweight_sorted,
+                    const void* qzeros_sorted, const void* scales_sorted, const void* bias,
+                    void* y, int64_t M, int64_t K_in, int64_t rows, int64_t N, int64_t block_rows,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   Problem p;
-  int st = awq::validate_shape(M, K, N, group_size, &p);
+  int st = awq::validate_shape(M, rows, N, block_rows, &p);
   if (st != AWQ_SUCCESS) return st;
-  st = awq::validate_gemm_pointers(x, qweight_sorted, qzeros, scales, bias, y, M);
+  st = awq::validate_gemm_pointers(x, qweight_sorted, qzeros_sorted, scales_sorted, bias, y, M);
   if (st != AWQ_SUCCESS) return st;
-  if (!perm) return AWQ_ERROR_INVALID_VALUE;
+  if (!perm || K_in <= 0) return AWQ_ERROR_INVALID_VALUE;
+  if (K_in > (int64_t{1} << 31) - 1 || M * K_in > (int64_t{1} << 31) - 1) return AWQ_ERROR_SHAPE;
   if (!awq::aligned(perm, 4)) return AWQ_ERROR_MISALIGNED;
   if (M == 0) return AWQ_SUCCESS;
-  const size_t need = awq::act_order_workspace_size(M, K, N, group_size);
+  const size_t need = awq::sorted_workspace_size(M, rows, N, block_rows);
   if (!workspace || workspace_bytes < need) return AWQ_ERROR_WORKSPACE;
   if (!awq::aligned(workspace, 256)) return AWQ_ERROR_MISALIGNED;
-  const size_t xoff = awq::act_order_x_offset(M, K, N, group_size);
+  const size_t xoff = awq::sorted_x_offset(M, rows, N, block_rows);
   auto* xp = reinterpret_cast<_Float16*>(static_cast<char*>(workspace) + xoff);
-  return run_gemm(p, x, qweight_sorted, qzeros, scales, bias, y, workspace, xoff,
-                  static_cast<const int32_t*>(perm), xp, static_cast<hipStream_t>(stream));
+  return run_gemm(p, x, qweight_sorted, qzeros_sorted, scales_sorted, bias, y, workspace, xoff,
+                  static_cast<const int32_t*>(perm), K_in, xp, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

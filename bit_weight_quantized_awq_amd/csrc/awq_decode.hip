@@ -479,8 +479,9 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
   }
 }
 
-// GATHER: x is read through a column order, x[m, perm[k]] in place of
-// x[m, k] (the activation-order forward).  Each lane then gathers its eight
+// GATHER: x (M rows of Kx columns) is read through a column order,
+// x[m, perm[k]] in place of x[m, k], and as 0 where perm[k] is outside
+// [0, Kx) (the sorted-weight forward; its null rows have perm -1).  Each lane then gathers its eight
 // values per step one by one; the perm entries are loaded first and the
 // packed-word copies are split in two halves around the gathers, so the
 // dependent perm -> x round trip overlaps the first half of the weight
@@ -491,7 +492,7 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
                   const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
                   const _Float16* __restrict__ bias, _Float16* __restrict__ y,
                   SplitK sk, int M, int K, int N, int g, int G, int splits,
-                  const int32_t* __restrict__ perm) {
+                  const int32_t* __restrict__ perm, int Kx) {
   static_assert(!GATHER || STEPS <= 4, "gather loads must fit the load counter");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   pin_arg(y);
@@ -607,7 +608,8 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
     __builtin_amdgcn_sched_barrier(0);
     copy_steps(0, kEarly);
     __builtin_amdgcn_sched_barrier(0);
-    const uint32_t kmax = static_cast<uint32_t>(K);
+    const uint32_t kmax = static_cast<uint32_t>(Kx);
+    const __amdgpu_buffer_rsrc_t rxg = make_rsrc(x, static_cast<uint32_t>(M) * Kx * 2u);
     if (row_lane) {
 #pragma unroll
       for (int s = 0; s < STEPS; ++s) {
@@ -618,7 +620,7 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
           const uint32_t off = offset_or_oob(kr < K && src < kmax,
                                              static_cast<uint32_t>(col16) * kmax * 2u + src * 2u);
           xa[s][i] =
-              __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rx, off, 0, 0));
+              __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rxg, off, 0, 0));
         }
       }
     }
@@ -796,7 +798,7 @@ template <int STEPS, bool GATHER>
 hipError_t launch_lds_steps(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                             const _Float16* scales, const _Float16* bias, _Float16* y,
                             int M, int K, int N, int g, int G, int splits, int n_tiles,
-                            SplitK sk, const int32_t* perm, hipStream_t stream) {
+                            SplitK sk, const int32_t* perm, int Kx, hipStream_t stream) {
   const size_t copy_bytes = 4 * STEPS * 4 * kLdsBlockPitch;
   const size_t red_bytes = 4 * static_cast<size_t>((M + 3) & ~3) * kDecodeCols * sizeof(float);
   const size_t shmem = copy_bytes > red_bytes ? copy_bytes : red_bytes;
@@ -804,11 +806,11 @@ hipError_t launch_lds_steps(const _Float16* x, const uint32_t* qweight, const ui
   if (single)
     hipLaunchKernelGGL((decode_lds_kernel<STEPS, true, GATHER>), dim3(n_tiles * splits),
                        dim3(256), shmem, stream, x, qweight, qzeros, scales, bias, y, sk, M,
-                       K, N, g, G, splits, perm);
+                       K, N, g, G, splits, perm, Kx);
   else
     hipLaunchKernelGGL((decode_lds_kernel<STEPS, false, GATHER>), dim3(n_tiles * splits),
                        dim3(256), shmem, stream, x, qweight, qzeros, scales, bias, y, sk, M,
-                       K, N, g, G, splits, perm);
+                       K, N, g, G, splits, perm, Kx);
   return hipGetLastError();
 }
 
@@ -838,7 +840,7 @@ hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint3
                          const _Float16* scales, const _Float16* bias, _Float16* y,
                          int M, int K, int N, int g, int G, int steps, int splits,
                          int n_tiles, bool lds_variant, void* workspace,
-                         const int32_t* perm, hipStream_t stream) {
+                         const int32_t* perm, int Kx, hipStream_t stream) {
   // Workspace: ticket region, accumulator region ([M][N] accumulators, then
   // [M][N] masks), then [splits][M][N] partials.
   char* ws = static_cast<char*>(workspace);
@@ -855,11 +857,11 @@ hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint3
   if (lds_variant && perm) {
     switch (steps) {
       case 1: return launch_lds_steps<1, true>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
-                                               G, splits, n_tiles, sk, perm, stream);
+                                               G, splits, n_tiles, sk, perm, Kx, stream);
       case 2: return launch_lds_steps<2, true>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
-                                               G, splits, n_tiles, sk, perm, stream);
+                                               G, splits, n_tiles, sk, perm, Kx, stream);
       case 4: return launch_lds_steps<4, true>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
-                                               G, splits, n_tiles, sk, perm, stream);
+                                               G, splits, n_tiles, sk, perm, Kx, stream);
       default: return hipErrorInvalidValue;   // decode_gathers() is false for 8 steps
     }
   }
@@ -867,13 +869,13 @@ hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint3
   if (lds_variant) {
     switch (steps) {
       case 1: return launch_lds_steps<1, false>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
-                                                G, splits, n_tiles, sk, nullptr, stream);
+                                                G, splits, n_tiles, sk, nullptr, K, stream);
       case 2: return launch_lds_steps<2, false>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
-                                                G, splits, n_tiles, sk, nullptr, stream);
+                                                G, splits, n_tiles, sk, nullptr, K, stream);
       case 4: return launch_lds_steps<4, false>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
-                                                G, splits, n_tiles, sk, nullptr, stream);
+                                                G, splits, n_tiles, sk, nullptr, K, stream);
       case 8: return launch_lds_steps<8, false>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
-                                                G, splits, n_tiles, sk, nullptr, stream);
+                                                G, splits, n_tiles, sk, nullptr, K, stream);
       default: return hipErrorInvalidValue;
     }
   }

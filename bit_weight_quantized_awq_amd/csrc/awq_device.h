@@ -100,17 +100,17 @@ hipError_t launch_generic(const _Float16* x, const uint32_t* qweight, const uint
                           const _Float16* scales, const _Float16* bias, _Float16* y,
                           int M, int K, int N, int g, const int32_t* gidx, int G,
                           hipStream_t stream);
-// Row reorder of a packed (K, NW) word matrix: dst[j] = src[perm[j]].
-hipError_t launch_permute_rows(const uint32_t* src, const int32_t* perm, uint32_t* dst, int K,
-                               int NW, hipStream_t stream);
-// Column reorder of x (M, K): xp[m, j] = x[m, perm[j]].
-hipError_t launch_gather_cols(const _Float16* x, const int32_t* perm, _Float16* xp, int M, int K,
-                              hipStream_t stream);
+// Row gather of a word matrix: dst[j] = src[idx[j]] (zeros out of range).
+hipError_t launch_gather_rows(const uint32_t* src, int src_rows, const int32_t* idx,
+                              uint32_t* dst, int dst_rows, int row_words, hipStream_t stream);
+// Column reorder of x (M, Kin) into xp (M, Kout): xp[m, j] = x[m, perm[j]].
+hipError_t launch_gather_cols(const _Float16* x, const int32_t* perm, _Float16* xp, int M,
+                              int Kin, int Kout, hipStream_t stream);
 hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                          const _Float16* scales, const _Float16* bias, _Float16* y,
                          int M, int K, int N, int g, int G, int steps, int splits,
                          int n_tiles, bool lds_variant, void* workspace,
-                         const int32_t* perm, hipStream_t stream);
+                         const int32_t* perm, int Kx, hipStream_t stream);
 hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                           const _Float16* scales, const _Float16* bias, _Float16* y,
                           int M, int K, int N, int group_shift, int bm, int bn,

@@ -261,9 +261,11 @@ int validate_gidx_shape(int64_t M, int64_t K, int64_t N, int64_t num_groups, Pro
   return AWQ_SUCCESS;
 }
 
-int gidx_order(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* perm,
-               int64_t* group_size) {
-  if (!g_idx || !perm || K <= 0 || num_groups <= 0) return AWQ_ERROR_INVALID_VALUE;
+int gidx_layout(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* perm,
+                int64_t perm_capacity, int32_t* block_group, int64_t block_capacity,
+                int64_t* rows, int64_t* block_rows, int64_t* blocks) {
+  if (!g_idx || !rows || !block_rows || !blocks || K <= 0 || num_groups <= 0)
+    return AWQ_ERROR_INVALID_VALUE;
   if (K > kMaxElems || num_groups > kMaxElems) return AWQ_ERROR_SHAPE;
   for (int64_t k = 0; k < K; ++k)
     if (g_idx[k] < 0 || g_idx[k] >= num_groups) return AWQ_ERROR_INVALID_VALUE;
@@ -275,34 +277,69 @@ int gidx_order(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* per
     for (int64_t k = 0; k < K; ++k) order[static_cast<size_t>(k)] = static_cast<int32_t>(k);
     std::stable_sort(order.begin(), order.end(),
                      [g_idx](int32_t a, int32_t b) { return g_idx[a] < g_idx[b]; });
-    // Every group holds K / num_groups rows exactly when the sorted map is
-    // j / (K / num_groups) for every position j.
-    bool uniform = K % num_groups == 0;
-    const int64_t per = uniform ? K / num_groups : 0;
-    for (int64_t j = 0; j < K && uniform; ++j)
-      if (g_idx[order[static_cast<size_t>(j)]] != j / per) uniform = false;
-    for (int64_t j = 0; j < K; ++j) perm[j] = order[static_cast<size_t>(j)];
-    if (group_size) *group_size = uniform ? per : 0;
+    // Activation order: every group holds K / num_groups rows, i.e. the
+    // sorted map is j / (K / num_groups) at every position j.
+    bool whole = K % num_groups == 0;
+    const int64_t per = whole ? K / num_groups : 0;
+    whole = whole && per >= kGidxBlockRows && (per & (per - 1)) == 0;
+    for (int64_t j = 0; j < K && whole; ++j)
+      if (g_idx[order[static_cast<size_t>(j)]] != j / per) whole = false;
+    if (whole) {
+      *rows = K;
+      *block_rows = per;
+      *blocks = num_groups;
+    } else {
+      int64_t nb = 0;
+      for (int64_t j = 0; j < K;) {
+        int64_t e = j;
+        while (e < K && g_idx[order[static_cast<size_t>(e)]] == g_idx[order[static_cast<size_t>(j)]]) ++e;
+        nb += (e - j + kGidxBlockRows - 1) / kGidxBlockRows;
+        j = e;
+      }
+      *rows = nb * kGidxBlockRows;
+      *block_rows = kGidxBlockRows;
+      *blocks = nb;
+    }
+    if (*rows > kMaxElems) return AWQ_ERROR_SHAPE;
+    if (!perm && !block_group) return AWQ_SUCCESS;   // size query
+    if (!perm || !block_group || perm_capacity < *rows || block_capacity < *blocks)
+      return AWQ_ERROR_SHAPE;
+    if (whole) {
+      for (int64_t j = 0; j < K; ++j) perm[j] = order[static_cast<size_t>(j)];
+      for (int64_t b = 0; b < num_groups; ++b) block_group[b] = static_cast<int32_t>(b);
+    } else {
+      int64_t out = 0, b = 0;
+      for (int64_t j = 0; j < K;) {
+        const int32_t grp = g_idx[order[static_cast<size_t>(j)]];
+        int64_t e = j;
+        while (e < K && g_idx[order[static_cast<size_t>(e)]] == grp) ++e;
+        const int64_t nblk = (e - j + kGidxBlockRows - 1) / kGidxBlockRows;
+        for (int64_t t = 0; t < nblk * kGidxBlockRows; ++t)
+          perm[out++] = j + t < e ? order[static_cast<size_t>(j + t)] : -1;
+        for (int64_t t = 0; t < nblk; ++t) block_group[b++] = grp;
+        j = e;
+      }
+    }
   } catch (...) {
     return AWQ_ERROR_INVALID_VALUE;
   }
   return AWQ_SUCCESS;
 }
 
-size_t act_order_x_offset(int64_t M, int64_t K, int64_t N, int64_t group_size) {
+size_t sorted_x_offset(int64_t M, int64_t rows, int64_t N, int64_t block_rows) {
   // Never inside the regions that must stay zero between calls, whatever
   // this problem's own plan needs: the workspace may also serve awq_gemm
   // calls of other shapes.
-  size_t base = gemm_workspace_size(M, K, N, group_size);
+  size_t base = gemm_workspace_size(M, rows, N, block_rows);
   const size_t fixed = kTicketRegionBytes + kAtomicRegionBytes;
   if (base < fixed) base = fixed;
   return round_up(base, 256);
 }
 
-size_t act_order_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size) {
-  if (M <= 0 || validate_shape(M, K, N, group_size, nullptr) != AWQ_SUCCESS) return 0;
-  return act_order_x_offset(M, K, N, group_size) +
-         round_up(static_cast<size_t>(M) * static_cast<size_t>(K) * 2, 256);
+size_t sorted_workspace_size(int64_t M, int64_t rows, int64_t N, int64_t block_rows) {
+  if (M <= 0 || validate_shape(M, rows, N, block_rows, nullptr) != AWQ_SUCCESS) return 0;
+  return sorted_x_offset(M, rows, N, block_rows) +
+         round_up(static_cast<size_t>(M) * static_cast<size_t>(rows) * 2, 256);
 }
 
 int decode_gather_max_m() {

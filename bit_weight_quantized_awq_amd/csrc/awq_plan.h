@@ -119,20 +119,30 @@ int force_path_from_env();
 // contiguous grouping) and G = num_groups.  Returns an awq_status value.
 int validate_gidx_shape(int64_t M, int64_t K, int64_t N, int64_t num_groups, Problem* out);
 
-// Stable order of the K rows by group (counting sort): perm[j] is the row
-// placed j-th.  Entries of g_idx outside [0, num_groups) give
-// AWQ_ERROR_INVALID_VALUE (perm untouched).  *group_size receives K /
-// num_groups when every group holds exactly that many rows, else 0.
-int gidx_order(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* perm,
-               int64_t* group_size);
+// Sorted layout of a row-to-group map (awq_gidx_layout): rows stably sorted
+// by group, then cut into blocks that each lie in one group.  When every
+// group holds K / num_groups rows and that count is a power of two of at
+// least kGidxBlockRows (activation order), a block is a whole group and no
+// row is added; otherwise blocks are kGidxBlockRows rows and the last block
+// of each group is padded with null rows (perm entry -1).  Writes *rows
+// (rows of the sorted weight), *block_rows and *blocks always (on success
+// or AWQ_ERROR_SHAPE); perm (rows entries) and block_group (blocks entries:
+// the map's group of each block) when non-NULL and their capacities
+// suffice, else AWQ_ERROR_SHAPE.  Entries of g_idx outside [0, num_groups)
+// give AWQ_ERROR_INVALID_VALUE.
+constexpr int64_t kGidxBlockRows = 32;
+int gidx_layout(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* perm,
+                int64_t perm_capacity, int32_t* block_group, int64_t block_capacity,
+                int64_t* rows, int64_t* block_rows, int64_t* blocks);
 
-// Workspace of awq_gemm_act_order: the awq_gemm workspace of the problem
-// (at least the fixed ticket and accumulator regions), rounded up to 256
-// bytes, then room for x with its columns reordered (M x K float16, rounded
-// up to 256 bytes).  0 for M == 0 or invalid shapes.
-size_t act_order_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size);
+// Workspace of awq_gemm_sorted: the awq_gemm workspace of the sorted problem
+// (M, rows, N, block_rows), at least the fixed ticket and accumulator
+// regions, rounded up to 256 bytes, then room for x with its columns
+// reordered (M x rows float16, rounded up to 256 bytes).  0 for M == 0 or
+// invalid shapes.
+size_t sorted_workspace_size(int64_t M, int64_t rows, int64_t N, int64_t block_rows);
 // Byte offset of the reordered x inside that workspace.
-size_t act_order_x_offset(int64_t M, int64_t K, int64_t N, int64_t group_size);
+size_t sorted_x_offset(int64_t M, int64_t rows, int64_t N, int64_t block_rows);
 
 inline bool aligned(const void* p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define AWQ_ABI_VERSION 3
+#define AWQ_ABI_VERSION 4
 
 /* Status codes returned by every entry point. */
 enum awq_status {
@@ -144,12 +144,13 @@ int awq_dense_gemv(const void* x, const void* w, const void* bias, void* y,
  * with qweight/qzeros packed as above, qzeros (G, N/8) and scales (G, N),
  * G = num_groups >= 1.  g_idx[k] = k / g is the contiguous case.
  *
- * Two routes.  Any map: awq_dequant_gidx, awq_gemm_gidx (general kernel,
- * slow).  A map that gives every group the same number of rows (activation
- * order, where the rows of each group are scattered over the input): sort
- * the rows by group once at load time (awq_gidx_order on the host, then
- * awq_permute_rows on the device), after which awq_gemm_act_order runs the
- * fast grouped kernels.
+ * Two routes.  Directly: awq_dequant_gidx and awq_gemm_gidx look the group
+ * up per row (the latter in the general kernel: correct, slow).  Fast: at
+ * load time, awq_gidx_layout (host) sorts the rows by group and cuts them
+ * into blocks that each lie in one group, and awq_gather_rows (device)
+ * builds the sorted weight and each block's zero and scale rows; the result
+ * is an ordinary grouped weight, and awq_gemm_sorted runs it on the grouped
+ * kernels with x's columns brought into the same order.
  * ------------------------------------------------------------------------ */
 
 /* w[K, N] float16 dequantised under a row-to-group map, bit-exact.
@@ -163,56 +164,70 @@ int awq_dequant_gidx(const void* qweight, const void* qzeros, const void* scales
                      void* stream);
 
 /* y[M, N] = float16_RNE(fp32 accumulation of x . W + bias) under any
- * row-to-group map (W as above).  The general kernel (plain fp32 FMA): a
- * correctness route for maps with groups of unequal size; activation-order
- * maps should take awq_gemm_act_order.  g_idx as in awq_dequant_gidx.  No
- * workspace.  Other arguments, errors and stream behaviour as awq_gemm. */
+ * row-to-group map (W as above), looking the group up per row in the
+ * general kernel (plain fp32 FMA): the direct form of the definition, slow;
+ * awq_gemm_sorted is the fast route for every map.  g_idx as in
+ * awq_dequant_gidx.  No workspace.  Other arguments, errors and stream
+ * behaviour as awq_gemm. */
 int awq_gemm_gidx(const void* x, const void* qweight, const void* qzeros, const void* scales,
                   const void* g_idx, const void* bias, void* y, int64_t M, int64_t K, int64_t N,
                   int64_t num_groups, void* stream);
 
-/* Host-only, no HIP call.  Stable order of the K input rows by group:
- * perm[j] (HOST int32 (K), written) is the row placed j-th, so the rows of
- * group 0 come first in increasing row order, then those of group 1, ...
- * g_idx: HOST int32 (K).  *group_size (may be NULL) receives K / num_groups
- * when every group holds exactly that many rows (the reordered weight is then
- * a grouped weight of that group size), else 0.  An entry outside
- * [0, num_groups), NULL pointers, K <= 0 or num_groups <= 0 give
- * AWQ_ERROR_INVALID_VALUE and leave perm untouched (as does a failed host
- * allocation of K indices). */
-int awq_gidx_order(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* perm,
-                   int64_t* group_size);
+/* Host-only, no HIP call.  Sorted layout of a row-to-group map.
+ * g_idx: HOST int32 (K), entries in [0, num_groups).  The rows are sorted
+ * stably by group (ties in increasing row order), then cut into blocks:
+ *   - when every group holds exactly K / num_groups rows and that count is a
+ *     power of two >= 32 (activation order), one block per group, no rows
+ *     added: *rows = K, *block_rows = K / num_groups, *blocks = num_groups;
+ *   - otherwise blocks of 32 rows, each group's last block padded with null
+ *     rows: *block_rows = 32, *rows = 32 * *blocks.
+ * perm (HOST int32, *rows entries): the input row placed j-th, or -1 for a
+ * null row.  block_group (HOST int32, *blocks entries): the map's group of
+ * each block.  Call with perm and block_group NULL to get the sizes; with
+ * both non-NULL, capacities (entries) below *rows / *blocks give
+ * AWQ_ERROR_SHAPE (sizes still written).  rows, block_rows and blocks must be
+ * non-NULL.  An entry outside [0, num_groups), K <= 0 or num_groups <= 0 is
+ * AWQ_ERROR_INVALID_VALUE (as is a failed host allocation of K indices). */
+int awq_gidx_layout(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* perm,
+                    int64_t perm_capacity, int32_t* block_group, int64_t block_capacity,
+                    int64_t* rows, int64_t* block_rows, int64_t* blocks);
 
-/* Reorders the rows of a packed weight: qweight_out[j, :] = qweight[perm[j], :]
- * for int32 (K, N/8) matrices (DEVICE pointers, 4-byte aligned; must not
- * overlap).  perm: DEVICE int32 (K), e.g. awq_gidx_order's output copied to
- * the device; an entry outside [0, K) writes a row of zeros.  N % 8 != 0 is
- * AWQ_ERROR_SHAPE.  Enqueued on `stream`; a load-time step. */
-int awq_permute_rows(const void* qweight, const void* perm, void* qweight_out, int64_t K,
-                     int64_t N, void* stream);
+/* Device row gather: dst row j = src row idx[j] for j < dst_rows, rows of
+ * row_bytes bytes (row_bytes % 4 == 0, else AWQ_ERROR_SHAPE); an index
+ * outside [0, src_rows) writes a row of zeros.  src, dst (must not overlap)
+ * and idx (DEVICE int32, dst_rows entries) 4-byte aligned.  Builds a sorted
+ * weight from awq_gidx_layout's output: qweight_sorted = rows of qweight by
+ * perm (row_bytes = N / 2), qzeros_sorted and scales_sorted = rows of qzeros
+ * and scales by block_group (row_bytes N / 2 and 2 N).  Enqueued on
+ * `stream`; a load-time step. */
+int awq_gather_rows(const void* src, int64_t src_rows, const void* idx, void* dst,
+                    int64_t dst_rows, int64_t row_bytes, void* stream);
 
-/* Workspace bytes of awq_gemm_act_order: the awq_gemm workspace of the same
- * problem (at least its fixed zero-filled regions), then M x K float16 for x
- * with its columns reordered.  0 for M == 0 or invalid shapes. */
-size_t awq_gemm_act_order_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size);
+/* Workspace bytes of awq_gemm_sorted: the awq_gemm workspace of the sorted
+ * problem (M, rows, N, block_rows), at least its fixed zero-filled regions,
+ * then M x rows float16 for x with its columns reordered.  0 for M == 0 or
+ * invalid shapes. */
+size_t awq_gemm_sorted_workspace_size(int64_t M, int64_t rows, int64_t N, int64_t block_rows);
 
-/* Forward of an activation-order weight after the load-time reorder:
+/* Forward of a sorted weight:
  *   y = float16_RNE(fp32 accumulation of x[:, perm] . W_sorted + bias),
- * W_sorted the grouped weight (group_size) of qweight_sorted, qzeros and
- * scales.  With perm and group_size from awq_gidx_order and qweight_sorted =
- * awq_permute_rows(qweight, perm), this equals x . W (+ bias) for the
- * original (qweight, g_idx): the same products summed in another order.
- * perm: DEVICE int32 (K), 4-byte aligned (entries outside [0, K) read x as 0).
- * workspace: at least awq_gemm_act_order_workspace_size(...) bytes, 256-byte
- * aligned, zero-filled once like awq_gemm's (the same buffer may serve both);
- * the reordered x is written into it, so concurrent calls must not share it.
- * Two launches on `stream`: the column reorder of x, then the awq_gemm kernel
- * family for the problem.  Other arguments, errors and stream behaviour as
- * awq_gemm. */
-int awq_gemm_act_order(const void* x, const void* perm, const void* qweight_sorted,
-                       const void* qzeros, const void* scales, const void* bias, void* y,
-                       int64_t M, int64_t K, int64_t N, int64_t group_size, void* workspace,
-                       size_t workspace_bytes, void* stream);
+ * x float16 (M, K_in); perm DEVICE int32 (rows), 4-byte aligned, an entry
+ * outside [0, K_in) reading x as 0; W_sorted the grouped weight (group size
+ * block_rows) of qweight_sorted (rows, N/8), qzeros_sorted (rows/block_rows,
+ * N/8) and scales_sorted (rows/block_rows, N).  With those built by
+ * awq_gidx_layout and awq_gather_rows this equals x . W (+ bias) for the
+ * original (qweight, qzeros, scales, g_idx): the same products summed in
+ * another order, null rows adding exact zeros.  workspace: at least
+ * awq_gemm_sorted_workspace_size(...) bytes, 256-byte aligned, zero-filled
+ * once like awq_gemm's (the same buffer may serve both); the reordered x is
+ * written into it, so concurrent calls must not share it.  One or two
+ * launches on `stream` (small batches gather x inside the decode kernel).
+ * Other arguments, errors and stream behaviour as awq_gemm with K = rows and
+ * group_size = block_rows. */
+int awq_gemm_sorted(const void* x, const void* perm, const void* qweight_sorted,
+                    const void* qzeros_sorted, const void* scales_sorted, const void* bias,
+                    void* y, int64_t M, int64_t K_in, int64_t rows, int64_t N, int64_t block_rows,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

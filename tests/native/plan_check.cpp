@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <vector>
+
 #include "awq.h"
 #include "awq_plan.h"
 
@@ -111,33 +113,51 @@ int main() {
   EXPECT(validate_gidx_shape(1, 8, 8, INT64_MAX, &p) == AWQ_ERROR_SHAPE);
   EXPECT(validate_gidx_shape(1, 8, (int64_t)1 << 20, (int64_t)1 << 12, &p) == AWQ_ERROR_SHAPE);
   {
+    // Uneven map: blocks of 32 rows padded with -1, in group order.
     const int32_t gi[6] = {2, 0, 1, 0, 2, 1};
-    int32_t perm[6] = {-1, -1, -1, -1, -1, -1};
-    int64_t gs = -1;
-    EXPECT(gidx_order(gi, 6, 3, perm, &gs) == AWQ_SUCCESS && gs == 2);
-    const int32_t want[6] = {1, 3, 2, 5, 0, 4};
-    for (int i = 0; i < 6; ++i) EXPECT(perm[i] == want[i]);
-    const int32_t uneven[5] = {0, 0, 1, 0, 1};
-    EXPECT(gidx_order(uneven, 5, 2, perm, &gs) == AWQ_SUCCESS && gs == 0);
-    EXPECT(gidx_order(uneven, 5, 3, perm, nullptr) == AWQ_SUCCESS);   // an empty group
+    int64_t rows = 0, brows = 0, nblk = 0;
+    EXPECT(gidx_layout(gi, 6, 3, nullptr, 0, nullptr, 0, &rows, &brows, &nblk) == AWQ_SUCCESS);
+    EXPECT(rows == 96 && brows == 32 && nblk == 3);
+    std::vector<int32_t> perm(96, 7), blk(3, 7);
+    EXPECT(gidx_layout(gi, 6, 3, perm.data(), 96, blk.data(), 3, &rows, &brows, &nblk) ==
+           AWQ_SUCCESS);
+    EXPECT(perm[0] == 1 && perm[1] == 3 && perm[2] == -1 && perm[31] == -1);
+    EXPECT(perm[32] == 2 && perm[33] == 5 && perm[64] == 0 && perm[65] == 4 && perm[95] == -1);
+    EXPECT(blk[0] == 0 && blk[1] == 1 && blk[2] == 2);
+    EXPECT(gidx_layout(gi, 6, 3, perm.data(), 95, blk.data(), 3, &rows, &brows, &nblk) ==
+           AWQ_ERROR_SHAPE);
+    // Activation order with 32-row groups: whole groups, no padding.
+    std::vector<int32_t> ao(128);
+    for (int k = 0; k < 128; ++k) ao[k] = (k * 37) % 128 / 32;
+    EXPECT(gidx_layout(ao.data(), 128, 4, perm.data(), 96, blk.data(), 3, &rows, &brows, &nblk) ==
+           AWQ_ERROR_SHAPE);
+    EXPECT(rows == 128 && brows == 32 && nblk == 4);
+    std::vector<int32_t> perm2(128), blk2(4);
+    EXPECT(gidx_layout(ao.data(), 128, 4, perm2.data(), 128, blk2.data(), 4, &rows, &brows,
+                       &nblk) == AWQ_SUCCESS);
+    for (int j = 0; j < 128; ++j) EXPECT(ao[perm2[j]] == j / 32);
     const int32_t bad[3] = {0, 3, 1};
-    int32_t keep[3] = {7, 7, 7};
-    EXPECT(gidx_order(bad, 3, 3, keep, &gs) == AWQ_ERROR_INVALID_VALUE);
-    EXPECT(keep[0] == 7 && keep[1] == 7 && keep[2] == 7);
+    EXPECT(gidx_layout(bad, 3, 3, nullptr, 0, nullptr, 0, &rows, &brows, &nblk) ==
+           AWQ_ERROR_INVALID_VALUE);
     const int32_t neg[2] = {0, -1};
-    EXPECT(gidx_order(neg, 2, 2, keep, &gs) == AWQ_ERROR_INVALID_VALUE);
-    EXPECT(gidx_order(nullptr, 2, 2, keep, &gs) == AWQ_ERROR_INVALID_VALUE);
-    EXPECT(gidx_order(gi, 6, 0, perm, &gs) == AWQ_ERROR_INVALID_VALUE);
+    EXPECT(gidx_layout(neg, 2, 2, nullptr, 0, nullptr, 0, &rows, &brows, &nblk) ==
+           AWQ_ERROR_INVALID_VALUE);
+    EXPECT(gidx_layout(nullptr, 2, 2, nullptr, 0, nullptr, 0, &rows, &brows, &nblk) ==
+           AWQ_ERROR_INVALID_VALUE);
+    EXPECT(gidx_layout(gi, 6, 0, nullptr, 0, nullptr, 0, &rows, &brows, &nblk) ==
+           AWQ_ERROR_INVALID_VALUE);
+    EXPECT(gidx_layout(gi, 6, 3, nullptr, 0, nullptr, 0, nullptr, &brows, &nblk) ==
+           AWQ_ERROR_INVALID_VALUE);
   }
   {
     const size_t fixed = kTicketRegionBytes + kAtomicRegionBytes;
-    EXPECT(act_order_workspace_size(0, 256, 128, 64) == 0);
-    EXPECT(act_order_workspace_size(4, 256, 128, 48) == 0);
-    EXPECT(act_order_x_offset(4, 256, 128, 64) >= fixed);
-    EXPECT(act_order_x_offset(16, 8192, 7168, 128) >= gemm_workspace_size(16, 8192, 7168, 128));
-    EXPECT(act_order_x_offset(16, 8192, 7168, 128) % 256 == 0);
-    EXPECT(act_order_workspace_size(16, 8192, 7168, 128) ==
-           act_order_x_offset(16, 8192, 7168, 128) + 16 * 8192 * 2);
+    EXPECT(sorted_workspace_size(0, 256, 128, 64) == 0);
+    EXPECT(sorted_workspace_size(4, 256, 128, 48) == 0);
+    EXPECT(sorted_x_offset(4, 256, 128, 64) >= fixed);
+    EXPECT(sorted_x_offset(16, 8192, 7168, 128) >= gemm_workspace_size(16, 8192, 7168, 128));
+    EXPECT(sorted_x_offset(16, 8192, 7168, 128) % 256 == 0);
+    EXPECT(sorted_workspace_size(16, 8192, 7168, 128) ==
+           sorted_x_offset(16, 8192, 7168, 128) + 16 * 8192 * 2);
   }
 
   if (failures) {

@@ -1,10 +1,10 @@
 """Parity of the row-to-group map (g_idx) entry points against the CPU oracle.
 
-Bar: awq_dequant_gidx and awq_permute_rows bit-exact; awq_gemm_gidx and
-awq_gemm_act_order within |gpu - ref| <= 1e-2 + 1e-2*|ref| elementwise
-against the float64 oracle (oracle.awq_linear_gidx_ref on the ORIGINAL
-weight and map, never the reordered one); exact where the arithmetic is
-exact (one-hot rows).  Maps come from the seeded generators in awq_inputs.
+Bar: awq_dequant_gidx and awq_gather_rows bit-exact; awq_gemm_gidx and
+awq_gemm_sorted within |gpu - ref| <= 1e-2 + 1e-2*|ref| elementwise against
+the float64 oracle (oracle.awq_linear_gidx_ref on the ORIGINAL weight and
+map, never the rebuilt one); exact where the arithmetic is exact (one-hot
+rows).  Maps come from the seeded generators in awq_inputs.
 """
 import sys
 
@@ -97,26 +97,22 @@ def test_dequant_gidx_out_of_range_entries_give_zero_rows():
     np.testing.assert_array_equal(w[keep].view(np.uint16), ref[keep].view(np.uint16))
 
 
-# ------------------------------------------------------------ permute_rows
-@pytest.mark.parametrize("K,N", [(1000, 520), (1024, 512), (8192, 7168)])
-def test_permute_rows_bit_exact(K, N):
-    say(f"permute_rows K={K} N={N}")
+# ------------------------------------------------------------- gather_rows
+@pytest.mark.parametrize("K,N,rows", [(1000, 520, 1000), (1024, 512, 1536), (8192, 7168, 8192)])
+def test_gather_rows_bit_exact(K, N, rows):
+    """Any index vector, repeats and out-of-range entries (zero rows)
+    included."""
+    say(f"gather_rows K={K} N={N} rows={rows}")
     p = awq_inputs.make_inputs(1, K, N, -1, seed=K)
-    perm = np.random.default_rng(K).permutation(K).astype(np.int32)
-    out = awq.permute_rows(dev(p["qweight"]), dev(perm)).cpu().numpy()
-    np.testing.assert_array_equal(out, p["qweight"][perm])
-
-
-def test_permute_rows_out_of_range_entry_writes_zeros():
-    say("permute_rows out-of-range entry")
-    K, N = 64, 64
-    p = awq_inputs.make_inputs(1, K, N, -1, seed=3)
-    perm = np.arange(K, dtype=np.int32)[::-1].copy()
-    perm[7] = K
-    out = awq.permute_rows(dev(p["qweight"]), dev(perm)).cpu().numpy()
-    assert np.all(out[7] == 0)
-    keep = np.setdiff1d(np.arange(K), [7])
-    np.testing.assert_array_equal(out[keep], p["qweight"][perm[keep]])
+    rng = np.random.default_rng(K)
+    idx = rng.integers(-3, K + 3, size=rows).astype(np.int32)
+    out = awq.gather_rows(dev(p["qweight"]), dev(idx)).cpu().numpy()
+    ok = (idx >= 0) & (idx < K)
+    np.testing.assert_array_equal(out[ok], p["qweight"][idx[ok]])
+    assert np.all(out[~ok] == 0)
+    sc = p["scales"]
+    out_s = awq.gather_rows(dev(sc), dev(np.array([0, 0], dtype=np.int32))).cpu().numpy()
+    np.testing.assert_array_equal(out_s.view(np.uint16), sc[[0, 0]].view(np.uint16))
 
 
 # --------------------------------------------------------------- gemm_gidx
@@ -135,25 +131,31 @@ def test_gemm_gidx_any_map(M, K, N, G, bias):
     assert_within_tol(y.cpu().numpy(), ref, "gemm_gidx")
 
 
-# --------------------------------------------------------------- act order
+# ------------------------------------------------------- sorted weights
 def act_problem(M, K, N, g, seed, bias=False):
     p = awq_inputs.make_inputs(M, K, N, g, seed=seed, bias=bias)
     p["g_idx"] = awq_inputs.act_order_g_idx(K, g, seed=seed + 7)
     return p
 
 
-def run_act_order(p, M=None, workspace=None):
-    K = p["qweight"].shape[0]
-    G = p["scales"].shape[0]
-    qs, perm, gs = awq.prepare_act_order(dev(p["qweight"]), p["g_idx"], G)
-    assert gs == K // G
-    x = p["x"] if M is None else p["x"][:M]
-    d = dict(qzeros=dev(p["qzeros"]), scales=dev(p["scales"]),
-             bias=dev(p["bias"]) if p["bias"] is not None else None)
-    y = awq.gemm_act_order(dev(x), perm, qs, d["qzeros"], d["scales"], d["bias"], gs,
-                           workspace=workspace)
+def map_problem(M, K, N, G, seed, bias=False):
+    """An arbitrary map: unequal, possibly empty or one-row groups."""
+    p = problem(M, K, N, G, seed=seed, bias=bias)
+    p["g_idx"] = awq_inputs.random_g_idx(K, G, seed=seed + 11)
+    return p
+
+
+def run_sorted(p, workspace=None):
+    w = awq.prepare_gidx(dev(p["qweight"]), dev(p["qzeros"]), dev(p["scales"]), p["g_idx"])
+    y = awq.gemm_sorted(dev(p["x"]), w, dev(p["bias"]) if p["bias"] is not None else None,
+                        workspace=workspace)
     torch.cuda.synchronize()
-    return y.cpu().numpy()
+    return y.cpu().numpy(), w
+
+
+def ref_of(p):
+    return oracle.awq_linear_gidx_ref(p["x"], p["qweight"], p["qzeros"], p["scales"],
+                                      p["g_idx"], p["bias"])
 
 
 @pytest.mark.parametrize("M,K,N,g,bias", [
@@ -162,97 +164,110 @@ def run_act_order(p, M=None, workspace=None):
     (64, 2048, 768, 128, False), (256, 1024, 1024, 128, True), (301, 1024, 520, 32, False),
     (66, 14336, 256, 128, True),                      # x rows staged two per work-group
     (40, 20480, 128, 128, False),                     # one row per work-group
-    (2, 996, 64, 4, False),                           # K % 8 != 0: general kernel, scalar gather
+    (2, 996, 64, 4, False),                           # 4-row groups: 32-row blocks, padded
+    (5, 4800, 256, 96, True),                         # 96-row groups: three blocks each
 ])
-def test_act_order_parity(M, K, N, g, bias):
-    """prepare_act_order + gemm_act_order against the oracle's forward of the
-    original weight under its activation-order map."""
-    path = binding.PATH_NAMES[awq.gemm_plan(M, K, N, g)[0]]
-    say(f"act order M={M} K={K} N={N} g={g} ({path})")
+def test_sorted_act_order_parity(M, K, N, g, bias):
+    """Activation-order maps: prepare_gidx + gemm_sorted against the
+    oracle's forward of the original weight under its map."""
+    say(f"sorted act order M={M} K={K} N={N} g={g}")
     p = act_problem(M, K, N, g, seed=M * 3 + K, bias=bias)
-    y = run_act_order(p)
-    ref = oracle.awq_linear_gidx_ref(p["x"], p["qweight"], p["qzeros"], p["scales"],
-                                     p["g_idx"], p["bias"])
-    assert_within_tol(y, ref, f"act order M={M}")
+    y, w = run_sorted(p)
+    whole = g >= 32 and g & (g - 1) == 0
+    assert w.block_rows == (g if whole else 32)
+    assert w.rows == (K if whole else 32 * (K // g) * -(-g // 32))
+    assert_within_tol(y, ref_of(p), f"sorted act order M={M}")
+
+
+@pytest.mark.parametrize("M,K,N,G,bias", [
+    (1, 8192, 1024, 64, False), (4, 4096, 512, 37, True), (16, 2048, 256, 200, False),
+    (33, 1024, 520, 5, True), (256, 4096, 768, 100, False), (7, 300, 64, 1000, True),
+])
+def test_sorted_any_map_parity(M, K, N, G, bias):
+    """Arbitrary maps (unequal, empty and one-row groups) run on the grouped
+    kernels after the blocked rebuild, against the oracle."""
+    say(f"sorted any map M={M} K={K} N={N} G={G}")
+    p = map_problem(M, K, N, G, seed=M + K + G, bias=bias)
+    y, w = run_sorted(p)
+    assert w.block_rows == 32 and w.rows % 32 == 0 and w.rows >= K
+    assert_within_tol(y, ref_of(p), f"sorted any map M={M} G={G}")
 
 
 @pytest.mark.parametrize("steps", [1, 2, 4, 8])
 @pytest.mark.parametrize("M", [1, 5])
-def test_act_order_decode_every_step_count(steps, M, monkeypatch):
+def test_sorted_decode_every_step_count(steps, M, monkeypatch):
     """The LDS decode kernel gathers x through perm itself for 1, 2 and 4
     steps per wave (the load order differs with the step count); 8 steps
-    take the separate reorder.  Forced through AWQ_DECODE_STEPS."""
-    say(f"act order decode steps={steps} M={M}")
+    take the separate reorder.  Forced through AWQ_DECODE_STEPS; whole
+    groups and padded blocks."""
     monkeypatch.setenv("AWQ_DECODE_STEPS", str(steps))
-    p = act_problem(M, 8192, 1024, 128, seed=steps * 10 + M, bias=True)
-    assert awq.gemm_plan(M, 8192, 1024, 128)[0] == binding.AWQ_PATH_DECODE
-    y = run_act_order(p)
-    ref = oracle.awq_linear_gidx_ref(p["x"], p["qweight"], p["qzeros"], p["scales"],
-                                     p["g_idx"], p["bias"])
-    assert_within_tol(y, ref, f"act order decode steps={steps}")
+    for p in (act_problem(M, 8192, 1024, 128, seed=steps * 10 + M, bias=True),
+              map_problem(M, 8192, 1024, 50, seed=steps * 10 + M, bias=True)):
+        say(f"sorted decode steps={steps} M={M} G={p['scales'].shape[0]}")
+        y, _ = run_sorted(p)
+        assert_within_tol(y, ref_of(p), f"sorted decode steps={steps}")
 
 
 @pytest.mark.parametrize("M", [1, 4, 8, 16])
-def test_act_order_fused_and_separate_reorder(M, monkeypatch):
+def test_sorted_fused_and_separate_reorder(M, monkeypatch):
     """Both forms of the decode's x reorder (gathered inside the decode
     kernel, or a separate pass first), forced through
-    AWQ_DECODE_GATHER_MAX_M, match the oracle at every decode batch."""
-    p = act_problem(M, 8192, 1280, 128, seed=70 + M, bias=True)
-    ref = oracle.awq_linear_gidx_ref(p["x"], p["qweight"], p["qzeros"], p["scales"],
-                                     p["g_idx"], p["bias"])
-    for limit in ("16", "0"):
-        say(f"act order decode M={M} gather limit {limit}")
-        monkeypatch.setenv("AWQ_DECODE_GATHER_MAX_M", limit)
-        assert_within_tol(run_act_order(p), ref, f"act order M={M} limit {limit}")
+    AWQ_DECODE_GATHER_MAX_M, match the oracle at every decode batch, for a
+    whole-group and a padded layout."""
+    for p in (act_problem(M, 8192, 1280, 128, seed=70 + M, bias=True),
+              map_problem(M, 8192, 1280, 70, seed=70 + M, bias=True)):
+        ref = ref_of(p)
+        for limit in ("16", "0"):
+            say(f"sorted decode M={M} G={p['scales'].shape[0]} gather limit {limit}")
+            monkeypatch.setenv("AWQ_DECODE_GATHER_MAX_M", limit)
+            assert_within_tol(run_sorted(p)[0], ref, f"sorted M={M} limit {limit}")
 
 
 @pytest.mark.parametrize("M,K,N,g", [(8, 4096, 1024, 128), (256, 2048, 768, 64)])
-def test_act_order_one_hot_rows_exact(M, K, N, g):
+def test_sorted_one_hot_rows_exact(M, K, N, g):
     """x[i] = e_{k_i} selects row k_i of the dequantised map weight bit for
-    bit: after the reorder the single nonzero product is the same float16
-    weight (decode and prefill kernels)."""
-    say(f"act order one-hot M={M}")
-    p = act_problem(M, K, N, g, seed=11 + M)
-    ks = np.random.default_rng(M).choice(K, size=M, replace=False)
-    x = np.zeros((M, K), dtype=np.float16)
-    x[np.arange(M), ks] = 1.0
-    p["x"] = x
-    y = run_act_order(p)
-    w = oracle.dequant_gidx(p["qweight"], p["qzeros"], p["scales"], p["g_idx"])
-    np.testing.assert_array_equal(y.view(np.uint16), w[ks].view(np.uint16))
+    bit: after the rebuild the single nonzero product is the same float16
+    weight (decode and prefill kernels); also for a padded layout."""
+    for p in (act_problem(M, K, N, g, seed=11 + M), map_problem(M, K, N, 45, seed=11 + M)):
+        say(f"sorted one-hot M={M} G={p['scales'].shape[0]}")
+        ks = np.random.default_rng(M).choice(K, size=M, replace=False)
+        x = np.zeros((M, K), dtype=np.float16)
+        x[np.arange(M), ks] = 1.0
+        p["x"] = x
+        y, _ = run_sorted(p)
+        w = oracle.dequant_gidx(p["qweight"], p["qzeros"], p["scales"], p["g_idx"])
+        np.testing.assert_array_equal(y.view(np.uint16), w[ks].view(np.uint16))
 
 
 @pytest.mark.parametrize("M,K,N,g,rows", [(1, 8192, 7168, 128, [0]),
                                           (16, 8192, 7168, 128, [0, 7, 15]),
                                           (2048, 4096, 12288, 128, [0, 1023, 2047])])
-def test_act_order_full_size_sampled(M, K, N, g, rows):
+def test_sorted_full_size_sampled(M, K, N, g, rows):
     """The decode and prefill sizes in the launch configuration the
-    benchmark times, checked on sampled rows."""
-    say(f"act order full size M={M} K={K} N={N}")
+    benchmark times, checked on sampled rows (activation order)."""
+    say(f"sorted full size M={M} K={K} N={N}")
     p = act_problem(M, K, N, g, seed=M + 1, bias=(M == 2048))
-    y = run_act_order(p)
+    y, _ = run_sorted(p)
     w = oracle.dequant_gidx(p["qweight"], p["qzeros"], p["scales"], p["g_idx"])
     ref = p["x"][rows].astype(np.float64) @ w.astype(np.float64)
     if p["bias"] is not None:
         ref = ref + p["bias"].astype(np.float64)
-    assert_within_tol(y[rows], ref, f"act order full size M={M}")
+    assert_within_tol(y[rows], ref, f"sorted full size M={M}")
 
 
-def test_act_order_shares_workspace_with_gemm():
+def test_sorted_shares_workspace_with_gemm():
     """The reordered x sits after the regions that must stay zero, so one
-    workspace serves act-order and plain calls (atomic and ticket decode
+    workspace serves sorted and plain calls (atomic and ticket decode
     exchanges, split prefill) back to back."""
-    say("act order workspace sharing")
+    say("sorted workspace sharing")
     shapes = [(1, 8192, 7168), (16, 8192, 7168), (256, 2048, 512), (2, 4096, 1024)]
-    need = max(max(awq.act_order_workspace_size(M, K, N, 128),
+    need = max(max(awq.sorted_workspace_size(M, K, N, 128),
                    awq.gemm_workspace_size(M, K, N, 128)) for M, K, N in shapes)
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     for M, K, N in shapes:
         p = act_problem(M, K, N, 128, seed=K + M)
-        y = run_act_order(p, workspace=ws)
-        ref = oracle.awq_linear_gidx_ref(p["x"], p["qweight"], p["qzeros"], p["scales"],
-                                         p["g_idx"], None)
-        assert_within_tol(y, ref, f"act order M={M} K={K} N={N}")
+        y, _ = run_sorted(p, workspace=ws)
+        assert_within_tol(y, ref_of(p), f"sorted M={M} K={K} N={N}")
         assert torch.count_nonzero(ws[:ZERO_REGION]).item() == 0
         d = {k: dev(p[k]) for k in ("x", "qweight", "qzeros", "scales")}
         y2 = awq.gemm(d["x"], d["qweight"], d["qzeros"], d["scales"], None, 128, workspace=ws)
@@ -261,14 +276,9 @@ def test_act_order_shares_workspace_with_gemm():
         assert torch.count_nonzero(ws[:ZERO_REGION]).item() == 0
 
 
-def test_act_order_rejects_unequal_groups_and_empty_batch():
-    say("act order: unequal groups, empty batch")
-    gi = awq_inputs.random_g_idx(256, 5, seed=1)
-    q = dev(awq_inputs.make_inputs(1, 256, 64, -1, seed=1)["qweight"])
-    with pytest.raises(ValueError):
-        awq.prepare_act_order(q, gi, 5)
+def test_sorted_empty_batch():
+    say("sorted: empty batch")
     p = act_problem(1, 256, 64, 64, seed=2)
-    qs, perm, gs = awq.prepare_act_order(dev(p["qweight"]), p["g_idx"], 4)
-    y = awq.gemm_act_order(torch.empty((0, 256), dtype=torch.float16, device=DEV), perm, qs,
-                           dev(p["qzeros"]), dev(p["scales"]), None, gs)
+    w = awq.prepare_gidx(dev(p["qweight"]), dev(p["qzeros"]), dev(p["scales"]), p["g_idx"])
+    y = awq.gemm_sorted(torch.empty((0, 256), dtype=torch.float16, device=DEV), w)
     assert tuple(y.shape) == (0, 64)

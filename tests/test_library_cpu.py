@@ -298,9 +298,10 @@ def _gemm_gidx(x=A, qw=A, qz=A, sc=A, gi=A, bias=None, y=A, M=4, K=256, N=128, G
     return awq.lib().awq_gemm_gidx(x, qw, qz, sc, gi, bias, y, M, K, N, G, None)
 
 
-def _act(x=A, perm=A, qw=A, qz=A, sc=A, bias=None, y=A, M=4, K=256, N=128, g=64, ws=None,
-         wsb=0):
-    return awq.lib().awq_gemm_act_order(x, perm, qw, qz, sc, bias, y, M, K, N, g, ws, wsb, None)
+def _sorted(x=A, perm=A, qw=A, qz=A, sc=A, bias=None, y=A, M=4, Kin=256, rows=256, N=128,
+            b=64, ws=None, wsb=0):
+    return awq.lib().awq_gemm_sorted(x, perm, qw, qz, sc, bias, y, M, Kin, rows, N, b, ws, wsb,
+                                     None)
 
 
 @pytest.mark.parametrize("fn,kwargs,status", [
@@ -318,72 +319,115 @@ def _act(x=A, perm=A, qw=A, qz=A, sc=A, bias=None, y=A, M=4, K=256, N=128, g=64,
     (_gemm_gidx, dict(gi=A + 1), binding.AWQ_ERROR_MISALIGNED),
     (_gemm_gidx, dict(x=A + 1), binding.AWQ_ERROR_MISALIGNED),
     (_gemm_gidx, dict(M=0, x=None, y=None), binding.AWQ_SUCCESS),
-    (_act, dict(perm=None), binding.AWQ_ERROR_INVALID_VALUE),
-    (_act, dict(perm=A + 2), binding.AWQ_ERROR_MISALIGNED),
-    (_act, dict(g=96), binding.AWQ_ERROR_SHAPE),
-    (_act, dict(), binding.AWQ_ERROR_WORKSPACE),                    # the reordered x needs room
-    (_act, dict(M=0, x=None, y=None), binding.AWQ_SUCCESS),
+    (_sorted, dict(perm=None), binding.AWQ_ERROR_INVALID_VALUE),
+    (_sorted, dict(Kin=0), binding.AWQ_ERROR_INVALID_VALUE),
+    (_sorted, dict(perm=A + 2), binding.AWQ_ERROR_MISALIGNED),
+    (_sorted, dict(b=96), binding.AWQ_ERROR_SHAPE),                 # rows % block_rows
+    (_sorted, dict(M=1 << 20, Kin=4096), binding.AWQ_ERROR_SHAPE),  # M * K_in >= 2^31
+    (_sorted, dict(), binding.AWQ_ERROR_WORKSPACE),                 # the reordered x needs room
+    (_sorted, dict(M=0, x=None, y=None), binding.AWQ_SUCCESS),
 ])
 def test_gidx_validation(fn, kwargs, status):
     assert fn(**kwargs) == status
 
 
-def test_act_order_workspace_rules():
-    """The reordered x sits after the awq_gemm workspace of the same problem
-    and never inside the fixed zero-filled regions (64 KiB tickets + 4 MiB
-    accumulators); the call checks size and 256-byte alignment first."""
+def test_sorted_workspace_rules():
+    """The reordered x (M x rows float16) sits after the awq_gemm workspace
+    of the sorted problem and never inside the fixed zero-filled regions
+    (64 KiB tickets + 4 MiB accumulators); the call checks size and 256-byte
+    alignment first."""
     fixed = 65536 + 4 * 65536 * 16
-    for M, K, N, g in [(1, 8192, 7168, 128), (16, 8192, 7168, 128), (2048, 4096, 12288, 128),
-                       (4, 256, 128, 64), (3, 996, 64, 4)]:
-        need = awq.act_order_workspace_size(M, K, N, g)
-        base = max(awq.gemm_workspace_size(M, K, N, g), fixed)
+    for M, rows, N, b in [(1, 8192, 7168, 128), (16, 8192, 7168, 128), (2048, 4096, 12288, 128),
+                          (4, 256, 128, 64), (3, 7968, 64, 32)]:
+        need = awq.sorted_workspace_size(M, rows, N, b)
+        base = max(awq.gemm_workspace_size(M, rows, N, b), fixed)
         xoff = -(-base // 256) * 256
-        assert need == xoff + -(-(M * K * 2) // 256) * 256
-    assert awq.act_order_workspace_size(0, 256, 128, 64) == 0
-    assert awq.act_order_workspace_size(4, 256, 128, 96) == 0
-    need = awq.act_order_workspace_size(4, 256, 128, 64)
-    assert _act(ws=A, wsb=need - 1) == binding.AWQ_ERROR_WORKSPACE
-    assert _act(ws=A + 16, wsb=need) == binding.AWQ_ERROR_MISALIGNED
+        assert need == xoff + -(-(M * rows * 2) // 256) * 256
+    assert awq.sorted_workspace_size(0, 256, 128, 64) == 0
+    assert awq.sorted_workspace_size(4, 256, 128, 96) == 0
+    need = awq.sorted_workspace_size(4, 256, 128, 64)
+    assert _sorted(ws=A, wsb=need - 1) == binding.AWQ_ERROR_WORKSPACE
+    assert _sorted(ws=A + 16, wsb=need) == binding.AWQ_ERROR_MISALIGNED
 
 
-def test_gidx_order_matches_oracle():
-    """awq_gidx_order (host) is index work: its perm must equal the oracle's
-    stable sort exactly, and it reports the common group size only when
-    every group holds K / G rows."""
+def _layout_reference(g_idx, G):
+    """The sorted layout restated independently: stable sort by group, then
+    either whole groups (all of one power-of-two size >= 32) or 32-row
+    blocks padded with -1."""
+    import numpy as np
+    g_idx = [int(v) for v in g_idx]
+    K = len(g_idx)
+    by_group = {}
+    for k, v in enumerate(g_idx):
+        by_group.setdefault(v, []).append(k)
+    sizes = [len(by_group.get(v, [])) for v in range(G)]
+    per = K // G if K % G == 0 else 0
+    if per >= 32 and per & (per - 1) == 0 and all(c == per for c in sizes):
+        perm = [k for v in range(G) for k in by_group[v]]
+        return np.array(perm), np.arange(G), per
+    perm, blocks = [], []
+    for v in sorted(by_group):
+        rows = by_group[v]
+        nb = -(-len(rows) // 32)
+        perm += rows + [-1] * (32 * nb - len(rows))
+        blocks += [v] * nb
+    return np.array(perm), np.array(blocks), 32
+
+
+def test_gidx_layout_matches_reference():
+    """awq_gidx_layout (host) is index work: bit-exact against the
+    restatement above for uneven, empty and one-row groups, activation-order
+    maps (whole groups) and activation-order maps whose group size is not a
+    power of two >= 32 (blocked).  Its row order within a group is the
+    oracle's stable sort."""
     import awq_inputs
     import numpy as np
     import oracle
-    for K, G, seed in [(1, 1, 0), (7, 3, 1), (200, 7, 2), (4096, 50, 3)]:
-        gi = awq_inputs.random_g_idx(K, G, seed)
-        perm, gs = awq.gidx_order(gi, G)
-        want, counts = oracle.gidx_order(gi, G)
-        np.testing.assert_array_equal(perm, want)
-        assert gs == (K // G if np.all(counts == K // G) and K % G == 0 else 0)
-    for K, g in [(256, 32), (8192, 128), (14336, 128), (96, 1)]:
-        gi = awq_inputs.act_order_g_idx(K, g, seed=K)
-        perm, gs = awq.gidx_order(gi, K // g)
-        want, _ = oracle.gidx_order(gi, K // g)
-        np.testing.assert_array_equal(perm, want)
-        assert gs == g
+    cases = [(awq_inputs.random_g_idx(K, G, seed), G) for K, G, seed in
+             [(1, 1, 0), (7, 3, 1), (200, 7, 2), (4096, 50, 3), (300, 400, 4)]]
+    cases += [(awq_inputs.act_order_g_idx(K, g, seed=K), K // g) for K, g in
+              [(256, 32), (8192, 128), (14336, 128), (96, 1), (1000, 8), (4800, 96)]]
+    for gi, G in cases:
+        perm, blocks, b = awq.gidx_layout(gi, G)
+        want_perm, want_blocks, want_b = _layout_reference(gi, G)
+        np.testing.assert_array_equal(perm, want_perm)
+        np.testing.assert_array_equal(blocks, want_blocks)
+        assert b == want_b and len(perm) == b * len(blocks)
+        order, _ = oracle.gidx_order(gi, G)
+        np.testing.assert_array_equal(perm[perm >= 0], order)
 
 
-def test_gidx_order_memory_does_not_depend_on_group_count():
+def test_gidx_layout_memory_does_not_depend_on_group_count():
     """A map over a huge group range (most groups empty) sorts in O(K)
-    memory; it is not an act-order map, so no group size is reported."""
-    perm, gs = awq.gidx_order([3, 0, (1 << 30) - 1, 0], 1 << 30)
-    assert perm.tolist() == [1, 3, 0, 2] and gs == 0
+    memory and comes out blocked."""
+    perm, blocks, b = awq.gidx_layout([3, 0, (1 << 30) - 1, 0], 1 << 30)
+    assert b == 32 and blocks.tolist() == [0, 3, (1 << 30) - 1]
+    assert perm[:3].tolist() == [1, 3, -1] and perm[32] == 0 and perm[64] == 2
 
 
 @pytest.mark.parametrize("gi,G", [([0, 1, 3], 3), ([0, -1], 2), ([0, 0], 0)])
-def test_gidx_order_rejects_bad_maps(gi, G):
+def test_gidx_layout_rejects_bad_maps(gi, G):
     with pytest.raises(binding.AwqError) as e:
-        awq.gidx_order(gi, G)
+        awq.gidx_layout(gi, G)
     assert e.value.status == binding.AWQ_ERROR_INVALID_VALUE
 
 
-def test_permute_rows_validation():
+def test_gidx_layout_capacity_checked():
+    import numpy as np
+    g = np.array([0, 1, 0], dtype=np.int32)
+    rows, b, nb = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    perm = np.zeros(63, dtype=np.int32)
+    blocks = np.zeros(2, dtype=np.int32)
+    st = awq.lib().awq_gidx_layout(g.ctypes.data, 3, 2, perm.ctypes.data, 63,
+                                   blocks.ctypes.data, 2, ctypes.byref(rows), ctypes.byref(b),
+                                   ctypes.byref(nb))
+    assert st == binding.AWQ_ERROR_SHAPE and rows.value == 64 and nb.value == 2
+
+
+def test_gather_rows_validation():
     lib = awq.lib()
-    assert lib.awq_permute_rows(A, None, A, 256, 128, None) == binding.AWQ_ERROR_INVALID_VALUE
-    assert lib.awq_permute_rows(A, A, A, 0, 128, None) == binding.AWQ_ERROR_INVALID_VALUE
-    assert lib.awq_permute_rows(A, A, A, 256, 100, None) == binding.AWQ_ERROR_SHAPE
-    assert lib.awq_permute_rows(A, A + 2, A, 256, 128, None) == binding.AWQ_ERROR_MISALIGNED
+    assert lib.awq_gather_rows(A, 256, None, A, 256, 64, None) == binding.AWQ_ERROR_INVALID_VALUE
+    assert lib.awq_gather_rows(A, 0, A, A, 256, 64, None) == binding.AWQ_ERROR_INVALID_VALUE
+    assert lib.awq_gather_rows(A, 256, A, A, 256, 6, None) == binding.AWQ_ERROR_SHAPE
+    assert lib.awq_gather_rows(A, 256, A + 2, A, 256, 64, None) == binding.AWQ_ERROR_MISALIGNED
+    assert lib.awq_gather_rows(A, 256, A, A, 1 << 30, 64, None) == binding.AWQ_ERROR_SHAPE
