@@ -170,18 +170,25 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
     int steps = decode_steps_override();
     if (steps != 0 && decode_splits(p, pl.decode_lds, steps) > kDecodeMaxSplits) steps = 0;
     if (steps == 0) {
-      // Prefer step counts whose rows stay in one quantisation group, and
-      // the largest that still gives enough work-groups; 8 steps only when
-      // fewer would need more than kDecodeMaxSplits splits.
+      // The largest step count whose rows stay in one quantisation group and
+      // that still gives enough work-groups; failing that, the largest that
+      // gives enough work-groups (a wave whose rows span groups scales each
+      // step on its own whatever the count, and fewer splits mean less to
+      // exchange); failing that, the one with the most work-groups.  8 steps
+      // only when fewer would need more than kDecodeMaxSplits splits.
       const int64_t target = pl.decode_lds ? kDecodeLdsTargetWGs : kDecodeTargetWGs;
-      steps = 8;
+      int single_enough = 0, enough = 0, most = 0;
       for (int s = 4; s >= 1; s /= 2) {
         const bool single = p.G == 1 || p.g % (kDecodeRowsPerStep * s) == 0;
         const int64_t splits = decode_splits(p, pl.decode_lds, s);
         if (splits > kDecodeMaxSplits) break;
-        steps = s;
-        if (single && pl.n_tiles * splits >= target) break;
+        most = s;
+        if (pl.n_tiles * splits >= target) {
+          if (single && single_enough == 0) single_enough = s;
+          if (enough == 0) enough = s;
+        }
       }
+      steps = single_enough ? single_enough : (enough ? enough : (most ? most : 8));
     }
     pl.steps = steps;
     pl.splits = static_cast<int>(decode_splits(p, pl.decode_lds, steps));

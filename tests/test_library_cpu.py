@@ -238,6 +238,21 @@ def test_decode_workspace_size_formula():
         assert any(splits == -(-K // (128 * steps)) for steps in (1, 2, 4, 8))
 
 
+@pytest.mark.parametrize("M,K,N,g,splits", [
+    (1, 8192, 7168, 128, 16),   # 4 steps keep a wave in one 128-row group, 448 work-groups
+    (16, 8192, 7168, 32, 16),   # no step count >= 2 keeps 32-row groups whole: largest with
+    (1, 14336, 4096, 32, 28),   # enough work-groups (4 steps), not the most splits
+    (1, 8192, 1280, 128, 32),   # too few work-groups anywhere: the most (2 steps)
+])
+def test_decode_step_choice(M, K, N, g, splits):
+    """Decode step counts: the largest that keeps each wave in one group and
+    gives enough work-groups; else the largest that gives enough; else the
+    one with the most work-groups (fewer splits, less to exchange)."""
+    path, ws = awq.gemm_plan(M, K, N, g)
+    assert path == binding.AWQ_PATH_DECODE
+    assert (ws - 65536 - 4 * 65536 * 16) // (M * N * 4) == splits
+
+
 def test_decode_split_limit():
     """K beyond 63 splits of 8 steps cannot take the decode kernel."""
     assert awq.gemm_plan(1, 63 * 1024, 4096, 128)[0] == binding.AWQ_PATH_DECODE
