@@ -242,6 +242,21 @@ def sweep(torch, awq, dev):
                     flush=True)
                 del r
                 torch.cuda.empty_cache()
+    # awq_dequant on its own (HBM-bound: packed words, zeros and scales in,
+    # the float16 weight out), at the two large weight shapes (W = 117 MB,
+    # written with ordinary stores) and at one whose W (470 MB) is larger
+    # than the last-level cache (nontemporal stores).
+    for (K, N) in ((8192, 7168), (14336, 4096), (8192, 28672)):
+        print(f"[sweep] awq_dequant K={K} N={N}", file=sys.stderr, flush=True)
+        d_us = dequant_time_us(torch, awq, K, N, dev)
+        G = K // 128
+        nbytes = K * N // 2 + G * N // 2 + G * N * 2 + K * N * 2
+        print(json.dumps({
+            "workload": f"awq_dequant_k{K}_n{N}_g128", "K": K, "N": N, "group_size": 128,
+            "kernel": "dequant", "us_per_call": round(d_us, 3),
+            "GB_per_s": round(nbytes / (d_us * 1e-6) / 1e9, 1), "bound": "hbm",
+            "frac": round(nbytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes}),
+            flush=True)
     # The unquantised float16 baseline at the single-token shapes the pages
     # name (FastLinear / FastLinearROCm: K = 8192, N = 1280 or 7168), timed
     # the same way; the W4A16 time at the same shape gives the speed-up.
@@ -378,6 +393,41 @@ def vendor_gemm_times_us(torch, awq, M, K, N, bias, dev, calls=30):
             ts.append(t0.elapsed_time(t1) * 1e3 / calls)
         out.append(sorted(ts)[1])
     return out[0], out[1]
+
+
+def dequant_time_us(torch, awq, K, N, dev, calls=100):
+    """awq_dequant per-call time, packed weights rotated through >= 512 MiB
+    (each copy writes its own float16 output)."""
+    import awq_inputs
+    p = awq_inputs.make_inputs(1, K, N, 128, seed=K + N)
+    nbytes = K * N // 2 + K * N * 2
+    R = max(2, -(-ROTATE_BYTES // nbytes))
+    base = {k: torch.from_numpy(p[k]).to(dev) for k in ("qweight", "qzeros", "scales")}
+    cps = [{k: v.clone() for k, v in base.items()} for _ in range(R)]
+    outs = [torch.empty((K, N), dtype=torch.float16, device=dev) for _ in range(R)]
+    stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(stream):
+        for i in range(5):
+            c = cps[i % R]
+            awq.dequant(c["qweight"], c["qzeros"], c["scales"], 128, out=outs[i % R])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(calls):
+            c = cps[i % R]
+            awq.dequant(c["qweight"], c["qzeros"], c["scales"], 128, out=outs[i % R])
+    graph.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    with torch.cuda.stream(stream):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / calls
+    del graph, cps, outs
+    torch.cuda.empty_cache()
+    return us
 
 
 def dense_time_us(torch, awq, M, K, N, dev, calls=200):

@@ -76,6 +76,24 @@ def test_dequant_gidx_bit_exact(K, N, G, kind):
     np.testing.assert_array_equal(w.cpu().numpy().view(np.uint16), ref.view(np.uint16))
 
 
+def test_dequant_gidx_streamed_output_sampled_rows():
+    """awq_dequant_gidx with a W larger than the last-level cache (K = 8192,
+    N = 14336; nontemporal-store form) under an activation-order map:
+    each row depends only on its packed row and its mapped group, so
+    sampled rows are checked bit for bit against the oracle on those rows."""
+    K, N, G = 8192, 14336, 64
+    say(f"dequant_gidx streamed K={K} N={N} G={G}")
+    p = problem(1, K, N, G, seed=31)
+    gi = awq_inputs.act_order_g_idx(K, K // G, seed=32)
+    w = awq.dequant_gidx(dev(p["qweight"]), dev(p["qzeros"]), dev(p["scales"]), dev(gi))
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(33).choice(K, size=512, replace=False))
+    rows[0], rows[-1] = 0, K - 1
+    got = w[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    ref = oracle.dequant_gidx(p["qweight"][rows], p["qzeros"], p["scales"], gi[rows])
+    np.testing.assert_array_equal(got.view(np.uint16), ref.view(np.uint16))
+
+
 def test_dequant_gidx_out_of_range_entries_give_zero_rows():
     """An entry outside [0, G) reads zero point 0 and scale 0: that row is
     +0 (documented behaviour of the device-side map; the host cannot check

@@ -150,6 +150,57 @@ def test_dequant_odd_shapes_and_signed_scales(K, N, g):
     np.testing.assert_array_equal(w.view(np.uint16), ref.view(np.uint16))
 
 
+@pytest.mark.parametrize("g", [128, -1])
+def test_dequant_streamed_output_sampled_groups(g):
+    """A W larger than the last-level cache (K = 8192, N = 14336: 235 MB)
+    takes the nontemporal-store form.  Each group of rows depends only on
+    its own packed rows and its zero/scale row, so whole sampled groups
+    (first, last and two seeded ones) are checked bit for bit against the
+    oracle on just those rows."""
+    K, N = 8192, 14336
+    say(f"awq_dequant streamed K={K} N={N} g={g}")
+    rng = np.random.default_rng(21)
+    qw = rng.integers(0, 2 ** 32, size=(K, N // 8), dtype=np.uint32).view(np.int32)
+    gs = K if g == -1 else g
+    G = K // gs
+    qz = rng.integers(0, 2 ** 32, size=(G, N // 8), dtype=np.uint32).view(np.int32)
+    sc = rng.uniform(-0.02, 0.02, size=(G, N)).astype(np.float16)
+    w = awq.dequant(torch.from_numpy(qw).to(DEV), torch.from_numpy(qz).to(DEV),
+                    torch.from_numpy(sc).to(DEV), g)
+    torch.cuda.synchronize()
+    for grp in sorted({0, G - 1, int(rng.integers(0, G)), int(rng.integers(0, G))}):
+        rows = slice(grp * gs, (grp + 1) * gs) if g != -1 else slice(0, 256)
+        got = w[rows].cpu().numpy()
+        ref = oracle.dequant(qw[rows], qz[grp:grp + 1], sc[grp:grp + 1],
+                             got.shape[0] if g == -1 else g)
+        np.testing.assert_array_equal(got.view(np.uint16), ref.view(np.uint16))
+
+
+def _offset_copy(a, words):
+    """A contiguous device copy of `a` that starts `words` elements into a
+    larger buffer (so it is not 16-byte aligned)."""
+    t = torch.from_numpy(np.ascontiguousarray(a)).reshape(-1)
+    buf = torch.zeros(t.numel() + words, dtype=t.dtype)
+    buf[words:] = t
+    return buf.to(DEV)[words:].view(a.shape)
+
+
+@pytest.mark.parametrize("qw_off,sc_off", [(0, 0), (1, 0), (0, 1), (3, 5)])
+def test_dequant_alignment_forms(qw_off, sc_off):
+    """awq_dequant takes its widest form (4 words per thread) only for 16-byte
+    aligned operands; offset operands take the narrower forms, bit for bit
+    the same."""
+    say(f"awq_dequant alignment qweight+{qw_off} scales+{sc_off}")
+    K, N, g = 256, 512, 64
+    p = awq_inputs.make_inputs(1, K, N, g, seed=11, scale_lo=-2.0, scale_hi=2.0)
+    qw = _offset_copy(p["qweight"], qw_off)
+    qz = _offset_copy(p["qzeros"], qw_off)
+    sc = _offset_copy(p["scales"], sc_off)
+    w = awq.dequant(qw, qz, sc, g).cpu().numpy()
+    ref = oracle.dequant(p["qweight"], p["qzeros"], p["scales"], g)
+    np.testing.assert_array_equal(w.view(np.uint16), ref.view(np.uint16))
+
+
 # ---------------------------------------------------------- config parity
 GEMM_CASES = [
     ("tiny_m4_k256_n128", 4, 4, 64, None),
