@@ -32,6 +32,8 @@
 //   per-step offset in an SGPR; prefetches past the last K step re-read the
 //   last step (in bounds, never used).  Only when K % 64 != 0 does the last
 //   step need per-lane masks (the KTAIL instantiation).
+// * The consumer waves run at a raised wave priority, so that an MFMA is
+//   never held back by producer work that could wait.
 // * Tile order: work-group ids are remapped so that each of the 8 XCDs (which
 //   receive ids round-robin) works on a contiguous range of tiles that share
 //   rows of x, keeping that slab resident in the XCD's L2.
@@ -768,6 +770,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Tile t = tile_of<BM, BN>(n_tiles, splits, kps, (K + BK - 1) / BK);
+  // Each SIMD runs one consumer and one producer wave, whose matrix-core
+  // and dequantisation instructions share the SIMD's vector issue port: the
+  // consumer goes first when both are ready, so the matrix cores are fed
+  // and the producer fills the cycles in between (3-11 % faster, most at
+  // M = 128-1024).
+  if (wave < 4) __builtin_amdgcn_s_setprio(1);
   // The partial plane is 16-byte aligned (workspace layout, N % 8 == 0).
   const int out_mode = splits == 1
                            ? ((reinterpret_cast<uintptr_t>(y) & 15) == 0 ? kOutStagedY : kOutDirect)
