@@ -3,7 +3,8 @@
 The compute lives in libawq_mi355x.so (hand-written HIP kernels behind the C
 ABI of include/awq.h); this package is its thin Python binding plus a
 WQLinear module with the interface of the page "Predibase Lorax AWQ WQLinear"
-(Signature, I/O Contract).
+(Signature, I/O Contract), and WQLinearGidx for weights under a row-to-group
+map.
 """
 from __future__ import annotations
 
@@ -54,3 +55,37 @@ class WQLinear(_module_base()):
         with torch.no_grad():
             return gemm(x, self.qweight, self.qzeros, self.scales, self.bias,
                         group_size=self.group_size)
+
+
+class WQLinearGidx(_module_base()):
+    """The same layer for weights whose rows map to groups through g_idx
+    (the row-to-group map of the GPTQ tuple on the page "Predibase Lorax
+    Linear Layer Factory", Description), with the packing of qweight and
+    qzeros unchanged.  The weight is rebuilt once, at construction, as a
+    grouped weight with its rows sorted by group (prepare_gidx); forward
+    brings the columns of x into the same order and runs the grouped
+    kernels (gemm_sorted).  Inference only.
+    """
+
+    def __init__(self, w_bit, qweight, qzeros, scales, g_idx, bias):
+        super().__init__()
+        if w_bit != 4:
+            raise ValueError("only 4-bit weights are supported")
+        self.w_bit = w_bit
+        self.in_features = qweight.shape[0]
+        self.out_features = qweight.shape[1] * 32 // w_bit
+        self.num_groups = scales.shape[0]
+        w = prepare_gidx(qweight, qzeros, scales, g_idx)
+        self.block_rows = w.block_rows
+        self.register_buffer("qweight", w.qweight)
+        self.register_buffer("qzeros", w.qzeros)
+        self.register_buffer("scales", w.scales)
+        self.register_buffer("perm", w.perm)
+        self.register_buffer("bias", bias)
+
+    def forward(self, x):
+        import torch
+        w = SortedWeight(self.qweight, self.qzeros, self.scales, self.perm, self.block_rows,
+                         self.in_features)
+        with torch.no_grad():
+            return gemm_sorted(x, w, self.bias)

@@ -211,6 +211,23 @@ def test_sorted_any_map_parity(M, K, N, G, bias):
     assert_within_tol(y, ref_of(p), f"sorted any map M={M} G={G}")
 
 
+@pytest.mark.parametrize("M,K,N,G", [(2, 1024, 256, 8), (64, 2048, 512, 23)])
+def test_wqlinear_gidx_module(M, K, N, G):
+    """WQLinearGidx: the map is taken at construction, forward flattens
+    leading dimensions and matches the oracle's forward under the map; the
+    module's buffers are the rebuilt weight."""
+    say(f"WQLinearGidx M={M} K={K} N={N} G={G}")
+    p = map_problem(M, K, N, G, seed=M + G, bias=True)
+    layer = awq.WQLinearGidx(4, dev(p["qweight"]), dev(p["qzeros"]), dev(p["scales"]),
+                             torch.from_numpy(p["g_idx"]), dev(p["bias"]))
+    assert (layer.in_features, layer.out_features, layer.num_groups) == (K, N, G)
+    assert layer.qweight.shape[0] == layer.perm.shape[0] >= K
+    y = layer(dev(p["x"]).reshape(2, M // 2, K))
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (2, M // 2, N)
+    assert_within_tol(y.reshape(M, N).cpu().numpy(), ref_of(p), "WQLinearGidx")
+
+
 @pytest.mark.parametrize("steps", [1, 2, 4, 8])
 @pytest.mark.parametrize("M", [1, 5])
 def test_sorted_decode_every_step_count(steps, M, monkeypatch):

@@ -285,6 +285,19 @@ def test_wqlinear_construction_checks():
         awq.WQLinear(4, 100, q, z, s, None)
 
 
+def test_wqlinear_gidx_construction_checks():
+    """WQLinearGidx rejects other bit widths and, with no CPU fallback,
+    tensors that are not on a HIP device (before any device work)."""
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((64, 4), dtype=torch.int32)
+    z = torch.zeros((2, 4), dtype=torch.int32)
+    s = torch.zeros((2, 32), dtype=torch.float16)
+    with pytest.raises(ValueError, match="4-bit"):
+        awq.WQLinearGidx(8, q, z, s, [0] * 64, None)
+    with pytest.raises(ValueError, match="HIP device"):
+        awq.WQLinearGidx(4, q, z, s, [0] * 64, None)
+
+
 def test_validation_under_sanitizers(tmp_path):
     """The HIP-free planning/validation translation unit, built with the host
     compiler under AddressSanitizer + UBSan and driven over a grid of
