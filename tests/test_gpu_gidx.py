@@ -76,6 +76,26 @@ def test_dequant_gidx_bit_exact(K, N, G, kind):
     np.testing.assert_array_equal(w.cpu().numpy().view(np.uint16), ref.view(np.uint16))
 
 
+def test_dequant_gidx_unaligned_scales():
+    """Scales that are not 16-byte aligned send awq_dequant_gidx to the
+    one-word-per-thread kernel: the same bits as the oracle, including
+    rows whose map entry is out of range (+0)."""
+    say("dequant_gidx unaligned scales")
+    K, N, G = 96, 72, 5
+    p = problem(1, K, N, G, seed=41)
+    gi = awq_inputs.random_g_idx(K, G, seed=42)
+    gi[7], gi[50] = G, -3
+    buf = torch.zeros(G * N + 1, dtype=torch.float16)
+    buf[1:] = torch.from_numpy(p["scales"]).reshape(-1)
+    sc = buf.to(DEV)[1:].view(G, N)
+    w = awq.dequant_gidx(dev(p["qweight"]), dev(p["qzeros"]), sc, dev(gi)).cpu().numpy()
+    good = gi.copy()
+    good[[7, 50]] = 0
+    ref = oracle.dequant_gidx(p["qweight"], p["qzeros"], p["scales"], good)
+    ref[[7, 50]] = 0
+    np.testing.assert_array_equal(w.view(np.uint16), ref.view(np.uint16))
+
+
 def test_dequant_gidx_streamed_output_sampled_rows():
     """awq_dequant_gidx with a W larger than the last-level cache (K = 8192,
     N = 14336; nontemporal-store form) under an activation-order map:
