@@ -50,6 +50,23 @@ def _shapes(n, seed):
 SHAPES = _shapes(40, 2024)
 
 
+def _large_shapes(n, seed):
+    """Larger K and N (several decode splits and prefill tiles, ragged
+    edges), batch sizes on both sides of every kernel boundary."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.choice([1, 4, 7, 16, 33, 64, 97, 128, 129, 255, 256, 511]))
+        g = int(rng.choice([32, 64, 128, -1]))
+        K = (g if g > 0 else 64) * int(rng.integers(8, 65))
+        N = 8 * int(rng.integers(64, 1025))
+        out.append((M, K, N, g, bool(rng.integers(0, 2))))
+    return out
+
+
+LARGE_SHAPES = _large_shapes(16, 77)
+
+
 def say(msg):
     print(f"\n[case] {msg}", flush=True)
     sys.stdout.flush()
@@ -83,6 +100,21 @@ def test_random_shape_gemm_and_dequant(M, K, N, g, bias):
     _check(y.cpu().numpy(), ref, f"gemm {path}")
     wref = oracle.dequant(p["qweight"], p["qzeros"], p["scales"], g)
     np.testing.assert_array_equal(w.cpu().numpy().view(np.uint16), wref.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,K,N,g,bias", LARGE_SHAPES)
+def test_large_random_shape_gemm(M, K, N, g, bias):
+    """Larger seeded shapes through the planner's choice, against the
+    float64 oracle on a sample of rows (first, last, and seeded ones)."""
+    path = awq.PATH_NAMES[awq.gemm_plan(M, K, N, g)[0]]
+    say(f"large random shape M={M} K={K} N={N} g={g} bias={bias} ({path})")
+    p = awq_inputs.make_inputs(M, K, N, g, seed=M + K + N, bias=bias)
+    t = {k: torch.from_numpy(v).to(DEV) for k, v in p.items() if isinstance(v, np.ndarray)}
+    y = awq.gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], t.get("bias"), g)
+    torch.cuda.synchronize()
+    rows = sorted({0, M - 1} | set(np.random.default_rng(M).integers(0, M, size=6).tolist()))
+    ref = oracle.awq_linear_ref(p["x"][rows], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
+    _check(y.cpu().numpy()[rows], ref, f"gemm {path}")
 
 
 @pytest.mark.parametrize("M,K,N,g,bias", SHAPES[:20])
