@@ -303,6 +303,9 @@ int gidx_layout(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* pe
         nb += (e - j + kGidxBlockRows - 1) / kGidxBlockRows;
         j = e;
       }
+      // An even block count keeps the row count a multiple of the prefill
+      // kernel's 64-row K step (no masked tail step): one null block more.
+      nb += nb & 1;
       *rows = nb * kGidxBlockRows;
       *block_rows = kGidxBlockRows;
       *blocks = nb;
@@ -325,6 +328,10 @@ int gidx_layout(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* pe
           perm[out++] = j + t < e ? order[static_cast<size_t>(j + t)] : -1;
         for (int64_t t = 0; t < nblk; ++t) block_group[b++] = grp;
         j = e;
+      }
+      if (b < *blocks) {   // the trailing null block (any valid group)
+        for (int64_t t = 0; t < kGidxBlockRows; ++t) perm[out++] = -1;
+        block_group[b] = block_group[b - 1];
       }
     }
   } catch (...) {

@@ -180,7 +180,9 @@ int awq_gemm_gidx(const void* x, const void* qweight, const void* qzeros, const 
  *     power of two >= 32 (activation order), one block per group, no rows
  *     added: *rows = K, *block_rows = K / num_groups, *blocks = num_groups;
  *   - otherwise blocks of 32 rows, each group's last block padded with null
- *     rows: *block_rows = 32, *rows = 32 * *blocks.
+ *     rows, and one block of null rows appended when the count is odd (with
+ *     the last group), so that *rows is a multiple of 64:
+ *     *block_rows = 32, *rows = 32 * *blocks.
  * perm (HOST int32, *rows entries): the input row placed j-th, or -1 for a
  * null row.  block_group (HOST int32, *blocks entries): the map's group of
  * each block.  Call with perm and block_group NULL to get the sizes; with

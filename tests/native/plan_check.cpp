@@ -117,14 +117,18 @@ int main() {
     const int32_t gi[6] = {2, 0, 1, 0, 2, 1};
     int64_t rows = 0, brows = 0, nblk = 0;
     EXPECT(gidx_layout(gi, 6, 3, nullptr, 0, nullptr, 0, &rows, &brows, &nblk) == AWQ_SUCCESS);
-    EXPECT(rows == 96 && brows == 32 && nblk == 3);
-    std::vector<int32_t> perm(96, 7), blk(3, 7);
-    EXPECT(gidx_layout(gi, 6, 3, perm.data(), 96, blk.data(), 3, &rows, &brows, &nblk) ==
+    // Three blocks, and a fourth of null rows so that rows % 64 == 0.
+    EXPECT(rows == 128 && brows == 32 && nblk == 4);
+    std::vector<int32_t> perm(128, 7), blk(4, 7);
+    EXPECT(gidx_layout(gi, 6, 3, perm.data(), 128, blk.data(), 4, &rows, &brows, &nblk) ==
            AWQ_SUCCESS);
     EXPECT(perm[0] == 1 && perm[1] == 3 && perm[2] == -1 && perm[31] == -1);
     EXPECT(perm[32] == 2 && perm[33] == 5 && perm[64] == 0 && perm[65] == 4 && perm[95] == -1);
-    EXPECT(blk[0] == 0 && blk[1] == 1 && blk[2] == 2);
-    EXPECT(gidx_layout(gi, 6, 3, perm.data(), 95, blk.data(), 3, &rows, &brows, &nblk) ==
+    EXPECT(perm[96] == -1 && perm[127] == -1);
+    EXPECT(blk[0] == 0 && blk[1] == 1 && blk[2] == 2 && blk[3] == 2);
+    EXPECT(gidx_layout(gi, 6, 3, perm.data(), 127, blk.data(), 4, &rows, &brows, &nblk) ==
+           AWQ_ERROR_SHAPE);
+    EXPECT(gidx_layout(gi, 6, 3, perm.data(), 128, blk.data(), 3, &rows, &brows, &nblk) ==
            AWQ_ERROR_SHAPE);
     // Activation order with 32-row groups: whole groups, no padding.
     std::vector<int32_t> ao(128);

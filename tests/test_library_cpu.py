@@ -381,7 +381,8 @@ def test_sorted_workspace_rules():
 def _layout_reference(g_idx, G):
     """The sorted layout restated independently: stable sort by group, then
     either whole groups (all of one power-of-two size >= 32) or 32-row
-    blocks padded with -1."""
+    blocks padded with -1, with one null block more when their count is
+    odd."""
     import numpy as np
     g_idx = [int(v) for v in g_idx]
     K = len(g_idx)
@@ -399,6 +400,9 @@ def _layout_reference(g_idx, G):
         nb = -(-len(rows) // 32)
         perm += rows + [-1] * (32 * nb - len(rows))
         blocks += [v] * nb
+    if len(blocks) % 2:        # an even block count: rows a multiple of 64
+        perm += [-1] * 32
+        blocks += [blocks[-1]]
     return np.array(perm), np.array(blocks), 32
 
 
@@ -427,10 +431,12 @@ def test_gidx_layout_matches_reference():
 
 def test_gidx_layout_memory_does_not_depend_on_group_count():
     """A map over a huge group range (most groups empty) sorts in O(K)
-    memory and comes out blocked."""
+    memory and comes out blocked (three blocks and a null one, so that the
+    row count is a multiple of 64)."""
     perm, blocks, b = awq.gidx_layout([3, 0, (1 << 30) - 1, 0], 1 << 30)
-    assert b == 32 and blocks.tolist() == [0, 3, (1 << 30) - 1]
+    assert b == 32 and blocks.tolist() == [0, 3, (1 << 30) - 1, (1 << 30) - 1]
     assert perm[:3].tolist() == [1, 3, -1] and perm[32] == 0 and perm[64] == 2
+    assert len(perm) == 128 and (perm[96:] == -1).all()
 
 
 @pytest.mark.parametrize("gi,G", [([0, 1, 3], 3), ([0, -1], 2), ([0, 0], 0)])
