@@ -87,7 +87,7 @@ def make_copies(torch, p, R, dev):
     return copies
 
 
-def run_leg(torch, awq, spec, steps, warmup, dev):
+def run_leg(torch, awq, spec, steps, warmup, dev, events=True, eager=True):
     import awq_inputs
     p = awq_inputs.workload_inputs(spec["source"], spec["M"], spec["group_size"])
     M = spec["M"]
@@ -133,16 +133,18 @@ def run_leg(torch, awq, spec, steps, warmup, dev):
             step(i)
     torch.cuda.synchronize()
 
-    # Kernel duration: HIP events around each launch, on the launching stream.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    with torch.cuda.stream(stream):
-        for i in range(steps):
-            ev[i][0].record(stream)
-            step(i)
-            ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    # Single launches: HIP events around each launch, on the launching stream.
+    kern_ms = [float("nan")]
+    if events:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        with torch.cuda.stream(stream):
+            for i in range(steps):
+                ev[i][0].record(stream)
+                step(i)
+                ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        kern_ms = [a.elapsed_time(b) for a, b in ev]
     kern_avg_ms = statistics.fmean(kern_ms)
 
     # Whole job: exactly `steps` steps captured in one graph, replayed once.
@@ -165,19 +167,124 @@ def run_leg(torch, awq, spec, steps, warmup, dev):
     ms_per_step = total_ms / steps
 
     # Eager loop for reference (host launch overhead included).
-    torch.cuda.synchronize()
-    e0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        for i in range(steps):
-            step(i)
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - e0) * 1e3 / steps
+    eager_ms = float("nan")
+    if eager:
+        torch.cuda.synchronize()
+        e0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for i in range(steps):
+                step(i)
+        torch.cuda.synchronize()
+        eager_ms = (time.perf_counter() - e0) * 1e3 / steps
+    del graph
 
     sorted_rows = copies[0]["w"].rows if act else K
     return dict(p=p, M=M, K=K, N=N, G=G, g=g, nbytes=nbytes, nflops=nflops, R=R,
                 sorted_rows=sorted_rows,
                 path=awq.PATH_NAMES[path], ms_per_step=ms_per_step, kern_avg_ms=kern_avg_ms,
                 kern_min_ms=min(kern_ms), eager_ms=eager_ms, ws_bytes=ws_bytes)
+
+
+# Every seeded workload point, in the order the workloads are listed, with
+# a short label: c0 tiny, c1 decode N=1280, c2 decode batch sweep, c3 the
+# prefill projection, c4 the down-projection at both group sizes.
+CONFIG_POINTS = (
+    [("c0", "tiny_m4_k256_n128", 4, 64), ("c1", "decode_k8192_n1280", 1, 128)]
+    + [("c2", "decode_sweep_k8192_n7168", M, 128) for M in (1, 4, 8, 16)]
+    + [("c3", "prefill_qkv_m2048_k4096_n12288", 2048, 128)]
+    + [("c4", "mlp_down_k14336_n4096", M, g) for g in (128, -1) for M in (1, 16, 256, 1024, 4096)]
+)
+
+
+def binding_roof(nbytes, nflops, sec):
+    """(bound, fraction of that roof): whichever of HBM bytes and matrix-core
+    flops takes longer at peak binds the point."""
+    gbs = nbytes / sec / 1e9
+    tfs = nflops / sec / 1e12
+    hbm = nbytes / HBM_PEAK_GBS >= nflops / FP16_MFMA_PEAK_TFLOPS / 1e3
+    return ("hbm", gbs / HBM_PEAK_GBS) if hbm else ("mfma", tfs / FP16_MFMA_PEAK_TFLOPS)
+
+
+def config_points(torch, awq, dev, steps_small, steps_large):
+    """Each seeded point timed like the headline legs (graph replay, weights
+    rotated past the last-level cache), against its binding roof."""
+    out = []
+    for label, name, M, g in CONFIG_POINTS:
+        print(f"[bench] config {label} {name} M={M} g={g}", file=sys.stderr, flush=True)
+        r = run_leg(torch, awq, dict(source=name, M=M, group_size=g),
+                    steps_small if M <= 16 else steps_large, 5, dev, events=False, eager=False)
+        sec = r["ms_per_step"] * 1e-3
+        bound, frac = binding_roof(r["nbytes"], r["nflops"], sec)
+        out.append({"config": label, "M": M, "K": r["K"], "N": r["N"], "g": g,
+                    "kernel": r["path"], "us": round(sec * 1e6, 3),
+                    "GB_per_s": round(r["nbytes"] / sec / 1e9, 1),
+                    "TFLOP_per_s": round(r["nflops"] / sec / 1e12, 2),
+                    "bound": bound, "frac": round(frac, 4)})
+        del r
+        torch.cuda.empty_cache()
+    return out
+
+
+def graph_time_us(torch, fn, calls, dev):
+    """Per-call time of fn(i) for i < calls, captured in one graph and
+    replayed once between HIP events on the capturing stream."""
+    stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            fn(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(calls):
+            fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    with torch.cuda.stream(stream):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return t0.elapsed_time(t1) * 1e3 / calls
+
+
+def same_box_references(torch, dev, decode_bytes):
+    """What this box does, in this process, on plain work of the headline
+    sizes: a read-only pass (torch's sum) and a device copy over the decode
+    step's byte count, rotated like the decode leg, and torch's float16
+    linear (the vendor GEMM) at the prefill projection's shape."""
+    n = decode_bytes // 4
+    R = max(2, -(-ROTATE_BYTES // decode_bytes))
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    bufs = [torch.randint(-2**31, 2**31 - 1, (n,), generator=gen, dtype=torch.int32).to(dev)
+            for _ in range(R)]
+    dst = [torch.empty_like(b) for b in bufs]
+    acc = torch.empty((), dtype=torch.int64, device=dev)
+    read_us = graph_time_us(torch, lambda i: torch.sum(bufs[i % R], dim=0, out=acc), 100, dev)
+    copy_us = graph_time_us(torch, lambda i: dst[i % R].copy_(bufs[i % R]), 100, dev)
+    del bufs, dst
+    torch.cuda.empty_cache()
+    M, K, N = 2048, 4096, 12288
+    x = torch.randn((M, K), generator=gen).to(torch.float16).to(dev)
+    ws = [(torch.randn((N, K), generator=gen) * 0.02).to(torch.float16).to(dev) for _ in range(2)]
+    b = (torch.randn((N,), generator=gen) * 0.1).to(torch.float16).to(dev)
+    lin_us = graph_time_us(torch, lambda i: torch.nn.functional.linear(x, ws[i % 2], b), 20, dev)
+    del x, ws, b
+    torch.cuda.empty_cache()
+    return {
+        "read_stream": {"op": "torch.sum over int32", "bytes": n * 4, "us": round(read_us, 3),
+                        "GB_per_s": round(n * 4 / read_us / 1e3, 1),
+                        "frac": round(n * 4 / read_us / 1e3 / HBM_PEAK_GBS, 4)},
+        "device_copy": {"op": "Tensor.copy_", "bytes_moved": 2 * n * 4, "us": round(copy_us, 3),
+                        "GB_per_s": round(2 * n * 4 / copy_us / 1e3, 1),
+                        "frac": round(2 * n * 4 / copy_us / 1e3 / HBM_PEAK_GBS, 4)},
+        "vendor_fp16_linear_prefill_shape": {
+            "op": "torch.nn.functional.linear, float16 weight (N, K), bias", "M": M, "K": K,
+            "N": N, "us": round(lin_us, 3),
+            "TFLOP_per_s": round(2 * M * N * K / lin_us / 1e6, 1),
+            "frac": round(2 * M * N * K / lin_us / 1e6 / FP16_MFMA_PEAK_TFLOPS, 4)},
+    }
 
 
 def blas_thread_count():
@@ -464,6 +571,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--legs", default="decode,prefill")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config points and the same-box references")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--sweep", action="store_true",
@@ -518,7 +627,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("decode"),
-                         "kernel_avg_us": round(r["ms_per_step"] * 1e3, 3),
+                         "graph_step_us": round(r["ms_per_step"] * 1e3, 3),
                          "single_launch_event_us": round(r["kern_avg_ms"] * 1e3, 3)},
         })
     if "prefill" in res:
@@ -532,7 +641,7 @@ def main():
                             "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(ktf / FP16_MFMA_PEAK_TFLOPS, 4),
                             "traffic": measured_traffic("prefill"),
-                            "kernel_avg_us": round(r["ms_per_step"] * 1e3, 3),
+                            "graph_step_us": round(r["ms_per_step"] * 1e3, 3),
                             "single_launch_event_us": round(r["kern_avg_ms"] * 1e3, 3)}}
         if "decode" not in res:
             out.update({"value": pre["value"], "unit": "TFLOP/s",
@@ -540,6 +649,11 @@ def main():
                         "config": {"workload": pre["workload"]}, "roofline": pre["roofline"]})
         out["prefill"] = pre
 
+    if not args.no_configs:
+        out["configs"] = config_points(torch, awq, dev, steps_small=200, steps_large=20)
+        print("[bench] same-box references", file=sys.stderr, flush=True)
+        out["references"] = same_box_references(
+            torch, dev, res["decode"]["nbytes"] if "decode" in res else 30537728)
     if not args.no_cpu_baseline and "decode" in res:
         r = res["decode"]
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

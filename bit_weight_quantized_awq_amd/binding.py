@@ -21,6 +21,18 @@ AWQ_ERROR_MISALIGNED = 3
 AWQ_ERROR_WORKSPACE = 4
 AWQ_ERROR_HIP = 5
 
+AWQ_OPT_FORCE_PATH = 1
+AWQ_OPT_DECODE_STEPS = 2
+AWQ_OPT_DECODE_GATHER_MAX_M = 3
+AWQ_OPT_PREFILL_BM = 4
+AWQ_OPT_PREFILL_BN = 5
+AWQ_OPT_PREFILL_SPLITS = 6
+AWQ_OPT_AUTO = -1
+OPTIONS = {"force_path": AWQ_OPT_FORCE_PATH, "decode_steps": AWQ_OPT_DECODE_STEPS,
+           "decode_gather_max_m": AWQ_OPT_DECODE_GATHER_MAX_M,
+           "prefill_bm": AWQ_OPT_PREFILL_BM, "prefill_bn": AWQ_OPT_PREFILL_BN,
+           "prefill_splits": AWQ_OPT_PREFILL_SPLITS}
+
 AWQ_PATH_DECODE = 1
 AWQ_PATH_PREFILL = 2
 AWQ_PATH_GENERIC = 3
@@ -33,6 +45,8 @@ _vp = ctypes.c_void_p
 SIGNATURES = {
     "awq_abi_version": (ctypes.c_int, []),
     "awq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "awq_set_option": (ctypes.c_int, [ctypes.c_int, _i64]),
+    "awq_get_option": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]),
     "awq_gemm_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64, _i64]),
     "awq_gemm_plan": (ctypes.c_int, [_i64, _i64, _i64, _i64, _vp, _vp, _vp,
                                      ctypes.POINTER(ctypes.c_int),
@@ -95,6 +109,78 @@ def gemm_workspace_size(M: int, K: int, N: int, group_size: int) -> int:
     return int(lib().awq_gemm_workspace_size(M, K, N, group_size))
 
 
+_ws_need: dict = {}
+
+
+def _gemm_workspace_need(M: int, K: int, N: int, group_size: int) -> int:
+    """awq_gemm_workspace_size, remembered per shape (it depends on the shape
+    only), so a forward makes a single C-ABI call."""
+    key = (M, K, N, group_size)
+    need = _ws_need.get(key)
+    if need is None:
+        need = _ws_need[key] = gemm_workspace_size(M, K, N, group_size)
+    return need
+
+
+def _option_id(name):
+    if isinstance(name, int):
+        return name
+    try:
+        return OPTIONS[name]
+    except KeyError:
+        raise ValueError(f"unknown option {name!r}; known: {sorted(OPTIONS)}") from None
+
+
+def _option_value(opt, value):
+    if value is None:
+        return AWQ_OPT_AUTO
+    if opt == AWQ_OPT_FORCE_PATH and isinstance(value, str):
+        names = {v: k for k, v in PATH_NAMES.items()}
+        if value not in names:
+            raise ValueError(f"unknown kernel family {value!r}")
+        return names[value]
+    return int(value)
+
+
+def set_option(name, value) -> None:
+    """awq_set_option: a process-wide planner override (tests and tuning).
+    name is an awq_option value or one of OPTIONS' keys; value None restores
+    the planner's own choice; force_path also takes a family name."""
+    opt = _option_id(name)
+    st = lib().awq_set_option(opt, _option_value(opt, value))
+    if st != AWQ_SUCCESS:
+        raise AwqError(st, f"awq_set_option({name!r}, {value!r})")
+
+
+def get_option(name) -> int:
+    """awq_get_option: the current override (AWQ_OPT_AUTO when none)."""
+    v = ctypes.c_int64(0)
+    st = lib().awq_get_option(_option_id(name), ctypes.byref(v))
+    if st != AWQ_SUCCESS:
+        raise AwqError(st, f"awq_get_option({name!r})")
+    return v.value
+
+
+class options:
+    """Context manager that sets planner overrides and restores the previous
+    values on exit: ``with options(force_path="prefill", prefill_bm=64): ...``."""
+
+    def __init__(self, **kw):
+        self._kw = kw
+        self._old = {}
+
+    def __enter__(self):
+        for k, v in self._kw.items():
+            self._old[k] = get_option(k)
+            set_option(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self._old.items():
+            lib().awq_set_option(_option_id(k), v)
+        return False
+
+
 def gemm_plan(M: int, K: int, N: int, group_size: int, x_ptr: int = 0,
               scales_ptr: int = 0, qweight_ptr: int = 0) -> tuple[int, int]:
     """(path, workspace bytes) that awq_gemm would use; pointers are only
@@ -145,13 +231,17 @@ def _torch():
 
 
 _workspaces: dict = {}
+_retired_workspaces: list = []
 _ws_lock = threading.Lock()
 
 
 def _workspace(device, stream_ptr: int, nbytes: int):
     """A zero-filled workspace per (device, stream), grown on demand.  The
     kernels leave it zeroed where it must start at zero, so one buffer serves
-    every later call on that stream."""
+    every later call on that stream.  A buffer replaced by a larger one is
+    kept alive until the process ends: a HIP graph captured earlier may still
+    hold its address, and freeing it would let the allocator hand that memory
+    to other tensors the replay would then overwrite."""
     torch = _torch()
     if nbytes == 0:
         return None
@@ -159,9 +249,17 @@ def _workspace(device, stream_ptr: int, nbytes: int):
     with _ws_lock:
         buf = _workspaces.get(key)
         if buf is None or buf.numel() < nbytes:
+            if buf is not None:
+                _retired_workspaces.append(buf)
             buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
             _workspaces[key] = buf
         return buf
+
+
+def _current_stream(device):
+    """The raw hipStream_t of the current stream on `device`."""
+    torch = _torch()
+    return torch._C._cuda_getCurrentRawStream(device.index)
 
 
 def _check_device(name, t, device):
@@ -221,14 +319,9 @@ def gemm(x, qweight, qzeros, scales, bias=None, group_size: int = 128, out=None,
         _check_device("out", out, device)
         if out.shape != (M, N) or out.dtype != torch.float16 or not out.is_contiguous():
             raise ValueError("out must be a contiguous float16 (M, N) tensor")
-    stream = torch.cuda.current_stream(device).cuda_stream
-    if M > 0:
-        _, need = gemm_plan(M, K, N, group_size, x2.data_ptr(), scales.data_ptr(),
-                            qweight.data_ptr())
-    else:
-        need = 0
+    stream = _current_stream(device)
     if workspace is None:
-        ws = _workspace(device, stream, need)
+        ws = _workspace(device, stream, _gemm_workspace_need(M, K, N, group_size) if M else 0)
     else:
         ws = workspace
     ws_ptr = ws.data_ptr() if ws is not None else None
@@ -270,7 +363,7 @@ def dense_gemv(x, w, bias=None, out=None):
         _check_device("out", out, device)
         if out.shape != (M, N) or out.dtype != torch.float16 or not out.is_contiguous():
             raise ValueError("out must be a contiguous float16 (M, N) tensor")
-    stream = torch.cuda.current_stream(device).cuda_stream
+    stream = _current_stream(device)
     st = lib().awq_dense_gemv(x2.data_ptr() if M else None, w.data_ptr(),
                               bias.data_ptr() if bias is not None else None,
                               y.data_ptr() if M else None, M, K, N, stream)
@@ -298,7 +391,7 @@ def dequant(qweight, qzeros, scales, group_size: int = 128, out=None):
         if out.shape != (K, N) or out.dtype != torch.float16 or not out.is_contiguous():
             raise ValueError("out must be a contiguous float16 (K, N) tensor")
     w = out if out is not None else torch.empty((K, N), dtype=torch.float16, device=device)
-    stream = torch.cuda.current_stream(device).cuda_stream
+    stream = _current_stream(device)
     st = lib().awq_dequant(qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
                            w.data_ptr(), K, N, group_size, stream)
     if st != AWQ_SUCCESS:
@@ -344,7 +437,7 @@ def dequant_gidx(qweight, qzeros, scales, g_idx, out=None):
         if out.shape != (K, N) or out.dtype != torch.float16 or not out.is_contiguous():
             raise ValueError("out must be a contiguous float16 (K, N) tensor")
     w = out if out is not None else torch.empty((K, N), dtype=torch.float16, device=device)
-    stream = torch.cuda.current_stream(device).cuda_stream
+    stream = _current_stream(device)
     st = lib().awq_dequant_gidx(qweight.data_ptr(), qzeros.data_ptr(), scales.data_ptr(),
                                 g_idx.data_ptr(), w.data_ptr(), K, N, G, stream)
     if st != AWQ_SUCCESS:
@@ -392,7 +485,7 @@ def gemm_gidx(x, qweight, qzeros, scales, g_idx, bias=None, out=None):
     M = x2.shape[0]
     y = _prep_out(out, M, N, device)
     qweight, qzeros, scales = qweight.contiguous(), qzeros.contiguous(), scales.contiguous()
-    stream = torch.cuda.current_stream(device).cuda_stream
+    stream = _current_stream(device)
     st = lib().awq_gemm_gidx(x2.data_ptr() if M else None, qweight.data_ptr(),
                              qzeros.data_ptr(), scales.data_ptr(), g_idx.data_ptr(),
                              bias.data_ptr() if bias is not None else None,
@@ -434,7 +527,7 @@ def gather_rows(src, idx, out=None):
         _check_device("out", out, device)
         if out.shape != (rows, src.shape[1]) or out.dtype != src.dtype or not out.is_contiguous():
             raise ValueError("out must be a contiguous tensor of shape (len(idx), src.shape[1])")
-    stream = torch.cuda.current_stream(device).cuda_stream
+    stream = _current_stream(device)
     st = lib().awq_gather_rows(src.data_ptr(), src.shape[0], idx.data_ptr(), out.data_ptr(),
                                rows, row_bytes, stream)
     if st != AWQ_SUCCESS:
@@ -506,7 +599,7 @@ def gemm_sorted(x, w, bias=None, out=None, workspace=None):
     lead, x2 = _prep_x(x, K_in)
     M = x2.shape[0]
     y = _prep_out(out, M, N, device)
-    stream = torch.cuda.current_stream(device).cuda_stream
+    stream = _current_stream(device)
     need = sorted_workspace_size(M, rows, N, w.block_rows) if M > 0 else 0
     ws = _workspace(device, stream, need) if workspace is None else workspace
     ws_ptr = ws.data_ptr() if ws is not None else None

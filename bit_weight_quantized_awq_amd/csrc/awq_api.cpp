@@ -28,6 +28,10 @@ const char* awq_status_string(int status) {
   }
 }
 
+int awq_set_option(int option, int64_t value) { return awq::set_option(option, value); }
+
+int awq_get_option(int option, int64_t* value) { return awq::get_option(option, value); }
+
 size_t awq_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size) {
   return awq::gemm_workspace_size(M, K, N, group_size);
 }
@@ -38,7 +42,7 @@ int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size, const voi
   Problem p;
   int st = awq::validate_shape(M, K, N, group_size, &p);
   if (st != AWQ_SUCCESS) return st;
-  const int force = awq::force_path_from_env();
+  const int force = awq::forced_path();
   if (force < 0) return AWQ_ERROR_INVALID_VALUE;
   Plan pl;
   const awq::Alignment al{awq::aligned(x, 16), awq::aligned(scales, 16),
@@ -60,17 +64,23 @@ namespace {
 // 0 where perm is outside [0, Kx): the LDS decode kernel gathers it itself
 // (small batches); every other kernel reads a copy reordered into xp first
 // (M x K float16, 16-byte aligned).
+// The plan awq_gemm follows for problem p with these operand addresses (a
+// reordered x is 16-byte aligned wherever it is read from).
+int plan_gemm(const Problem& p, const void* x, const void* qweight, const void* scales,
+              bool reordered_x, Plan* pl) {
+  const int force = awq::forced_path();
+  if (force < 0) return AWQ_ERROR_INVALID_VALUE;
+  const awq::Alignment al{reordered_x ? true : awq::aligned(x, 16), awq::aligned(scales, 16),
+                          awq::aligned(qweight, 16)};
+  return awq::make_plan(p, al, force, pl);
+}
+
 int run_gemm(const Problem& p, const void* x, const void* qweight, const void* qzeros,
              const void* scales, const void* bias, void* y, void* workspace,
              size_t workspace_bytes, const int32_t* perm, int64_t Kx, _Float16* xp,
              hipStream_t s) {
-  const int force = awq::force_path_from_env();
-  if (force < 0) return AWQ_ERROR_INVALID_VALUE;
   Plan pl;
-  // A reordered x is 16-byte aligned wherever it is read from.
-  const awq::Alignment al{perm ? true : awq::aligned(x, 16), awq::aligned(scales, 16),
-                          awq::aligned(qweight, 16)};
-  int st = awq::make_plan(p, al, force, &pl);
+  const int st = plan_gemm(p, x, qweight, scales, perm != nullptr, &pl);
   if (st != AWQ_SUCCESS) return st;
   if (pl.ws_bytes > 0) {
     if (!workspace || workspace_bytes < pl.ws_bytes) return AWQ_ERROR_WORKSPACE;

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 #include "awq.h"
@@ -116,36 +117,74 @@ bool prefill_supported(const Problem& p, const Alignment& al) {
          (p.G == 1 || (p.g >= 4 && log2_exact(p.g) >= 0));
 }
 
-// AWQ_PREFILL_BN (tuning and tests): 128 or 192 forces the prefill tile width.
-static int prefill_bn_override() {
-  const char* s = getenv("AWQ_PREFILL_BN");
-  if (!s) return 0;
-  const int v = atoi(s);
-  return (v == kPrefillBN || v == kPrefillWideBN) ? v : 0;
+// Planner overrides (awq_set_option).  Each starts from its environment
+// variable, read once on first use, and can be changed later through the
+// C ABI; planning reads them with relaxed atomic loads, so a call never
+// touches the environment.  kOptAuto means "the planner's own choice";
+// kOptInvalid marks an unrecognised AWQ_FORCE_PATH, which fails every plan.
+namespace {
+constexpr int kOptInvalid = -2;
+constexpr int kNumOptions = AWQ_OPT_PREFILL_SPLITS + 1;
+
+bool option_value_ok(int opt, int64_t v) {
+  if (v == kOptAuto) return true;
+  switch (opt) {
+    case AWQ_OPT_FORCE_PATH:
+      return v == AWQ_PATH_DECODE || v == AWQ_PATH_PREFILL || v == AWQ_PATH_GENERIC;
+    case AWQ_OPT_DECODE_STEPS: return v == 1 || v == 2 || v == 4 || v == 8;
+    case AWQ_OPT_DECODE_GATHER_MAX_M: return v >= 0 && v <= kDecodeMaxM;
+    case AWQ_OPT_PREFILL_BM: return v == kPrefillMinBM || v == 2 * kPrefillMinBM || v == kPrefillBM;
+    case AWQ_OPT_PREFILL_BN: return v == kPrefillBN || v == kPrefillWideBN;
+    case AWQ_OPT_PREFILL_SPLITS: return v >= 1 && v <= kPrefillMaxSplits;
+    default: return false;
+  }
 }
 
-// AWQ_PREFILL_BM (tuning and tests): 64, 128 or 256 forces the tile height.
-static int prefill_bm_override() {
-  const char* s = getenv("AWQ_PREFILL_BM");
-  if (!s) return 0;
-  const int v = atoi(s);
-  return (v == kPrefillMinBM || v == 2 * kPrefillMinBM || v == kPrefillBM) ? v : 0;
+int option_from_env(int opt) {
+  static const char* const names[kNumOptions] = {
+      nullptr, "AWQ_FORCE_PATH", "AWQ_DECODE_STEPS", "AWQ_DECODE_GATHER_MAX_M",
+      "AWQ_PREFILL_BM", "AWQ_PREFILL_BN", "AWQ_PREFILL_SPLITS"};
+  const char* s = getenv(names[opt]);
+  if (!s || !*s) return kOptAuto;
+  if (opt == AWQ_OPT_FORCE_PATH) {
+    if (!strcmp(s, "decode")) return AWQ_PATH_DECODE;
+    if (!strcmp(s, "prefill")) return AWQ_PATH_PREFILL;
+    if (!strcmp(s, "generic")) return AWQ_PATH_GENERIC;
+    return kOptInvalid;
+  }
+  const int v = atoi(s);   // unusable numeric values leave the automatic choice
+  return option_value_ok(opt, v) ? v : kOptAuto;
 }
 
-// AWQ_PREFILL_SPLITS (tuning and tests): 1..kPrefillMaxSplits overrides
-// the prefill split count (each split keeps at least one K step).
-static int prefill_splits_override() {
-  const char* s = getenv("AWQ_PREFILL_SPLITS");
-  if (!s) return 0;
-  const int v = atoi(s);
-  return (v >= 1 && v <= kPrefillMaxSplits) ? v : 0;
+std::atomic<int>* option_table() {
+  static std::atomic<int> table[kNumOptions];
+  static const bool loaded = [] {
+    for (int o = 1; o < kNumOptions; ++o) table[o].store(option_from_env(o));
+    return true;
+  }();
+  (void)loaded;
+  return table;
+}
+}  // namespace
+
+int option(int opt) { return option_table()[opt].load(std::memory_order_relaxed); }
+
+int set_option(int opt, int64_t value) {
+  if (opt < 1 || opt >= kNumOptions) return AWQ_ERROR_INVALID_VALUE;
+  if (!option_value_ok(opt, value)) return AWQ_ERROR_INVALID_VALUE;
+  option_table()[opt].store(static_cast<int>(value), std::memory_order_relaxed);
+  return AWQ_SUCCESS;
 }
 
-static int decode_steps_override() {
-  const char* s = getenv("AWQ_DECODE_STEPS");
-  if (!s) return 0;
-  int v = atoi(s);
-  return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 0;
+int get_option(int opt, int64_t* value) {
+  if (opt < 1 || opt >= kNumOptions || !value) return AWQ_ERROR_INVALID_VALUE;
+  *value = option(opt);
+  return AWQ_SUCCESS;
+}
+
+static int override_or_zero(int opt) {
+  const int v = option(opt);
+  return v > 0 ? v : 0;
 }
 
 int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
@@ -167,7 +206,7 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
   if (path == AWQ_PATH_DECODE) {
     pl.n_tiles = static_cast<int>(ceil_div(p.N, kDecodeCols));
     pl.decode_lds = (p.N % 32 == 0);
-    int steps = decode_steps_override();
+    int steps = override_or_zero(AWQ_OPT_DECODE_STEPS);
     if (steps != 0 && decode_splits(p, pl.decode_lds, steps) > kDecodeMaxSplits) steps = 0;
     if (steps == 0) {
       // The largest step count whose rows stay in one quantisation group and
@@ -198,7 +237,7 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
   } else if (path == AWQ_PATH_PREFILL) {
     pl.prefill_bm = p.M <= kPrefillMinBM ? kPrefillMinBM
                                          : (p.M <= 2 * kPrefillMinBM ? 2 * kPrefillMinBM : kPrefillBM);
-    if (const int o = prefill_bm_override()) pl.prefill_bm = o;
+    if (const int o = override_or_zero(AWQ_OPT_PREFILL_BM)) pl.prefill_bm = o;
     pl.m_tiles = static_cast<int>(ceil_div(p.M, pl.prefill_bm));
     // The wide tile (256 rows only) does 1.5x a narrow tile's work at a
     // little more speed per flop (fewer LDS bytes per flop): take it when it
@@ -210,7 +249,7 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
                      r_wide * 6 < r_narrow * 5)
                         ? kPrefillWideBN
                         : kPrefillBN;
-    if (const int o = prefill_bn_override()) pl.prefill_bn = o;
+    if (const int o = override_or_zero(AWQ_OPT_PREFILL_BN)) pl.prefill_bn = o;
     if (pl.prefill_bm != kPrefillBM) pl.prefill_bn = kPrefillBN;   // 192 needs 256 rows
     pl.n_tiles = static_cast<int>(ceil_div(p.N, pl.prefill_bn));
     pl.group_shift = p.G == 1 ? 31 : log2_exact(p.g);
@@ -224,7 +263,7 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
       if (splits > nkt / kPrefillMinSplitSteps) splits = nkt / kPrefillMinSplitSteps;
       if (splits < 2) splits = 1;
     }
-    if (const int o = prefill_splits_override()) splits = o < nkt ? o : nkt;
+    if (const int o = override_or_zero(AWQ_OPT_PREFILL_SPLITS)) splits = o < nkt ? o : nkt;
     const int64_t kps = ceil_div(nkt, splits);
     splits = ceil_div(nkt, kps);   // no empty split
     pl.splits = static_cast<int>(splits);
@@ -357,21 +396,14 @@ size_t sorted_workspace_size(int64_t M, int64_t rows, int64_t N, int64_t block_r
 }
 
 int decode_gather_max_m() {
-  const char* s = getenv("AWQ_DECODE_GATHER_MAX_M");
-  if (s && *s) {
-    const int v = atoi(s);
-    if (v >= 0 && v <= kDecodeMaxM) return v;
-  }
-  return kDecodeGatherMaxM;
+  const int v = option(AWQ_OPT_DECODE_GATHER_MAX_M);
+  return v >= 0 ? v : kDecodeGatherMaxM;
 }
 
-int force_path_from_env() {
-  const char* s = getenv("AWQ_FORCE_PATH");
-  if (!s || !*s) return 0;
-  if (!strcmp(s, "decode")) return AWQ_PATH_DECODE;
-  if (!strcmp(s, "prefill")) return AWQ_PATH_PREFILL;
-  if (!strcmp(s, "generic")) return AWQ_PATH_GENERIC;
-  return -1;
+int forced_path() {
+  const int v = option(AWQ_OPT_FORCE_PATH);
+  if (v == kOptInvalid) return -1;
+  return v > 0 ? v : 0;
 }
 
 }  // namespace awq

@@ -103,15 +103,25 @@ size_t gemm_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size);
 // force: 0 = automatic, otherwise an awq_path value.  Returns an awq_status.
 int make_plan(const Problem& p, const Alignment& al, int force, Plan* out);
 
+// Planner overrides for tests and tuning (awq_set_option / awq_get_option):
+// process-wide values, each initialised once from its environment variable
+// (AWQ_FORCE_PATH = decode | prefill | generic, AWQ_DECODE_STEPS,
+// AWQ_DECODE_GATHER_MAX_M, AWQ_PREFILL_BM, AWQ_PREFILL_BN,
+// AWQ_PREFILL_SPLITS) on first use.  kOptAuto = the planner's own choice.
+constexpr int kOptAuto = -1;
+int option(int opt);
+int set_option(int opt, int64_t value);
+int get_option(int opt, int64_t* value);
+
 // Largest batch for which the LDS decode kernel gathers an act-order x
 // itself (each column tile gathers its K range again, so the scattered loads
 // grow with M x N / 256; beyond this a separate reorder pass is cheaper).
-// AWQ_DECODE_GATHER_MAX_M overrides it (tuning and tests; 0 disables).
+// AWQ_OPT_DECODE_GATHER_MAX_M overrides it (0 disables).
 int decode_gather_max_m();
 
-// Parses AWQ_FORCE_PATH.  Returns 0 (unset/automatic), an awq_path value, or
-// -1 for an unrecognised value.
-int force_path_from_env();
+// The forced kernel family: 0 (automatic), an awq_path value, or -1 when
+// AWQ_FORCE_PATH held an unrecognised value.
+int forced_path();
 
 // Row-to-group map problems (awq_dequant_gidx, awq_gemm_gidx): M >= 0,
 // K > 0, N > 0 with N % 8 == 0, num_groups >= 1, every operand (including

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define AWQ_ABI_VERSION 4
+#define AWQ_ABI_VERSION 5
 
 /* Status codes returned by every entry point. */
 enum awq_status {
@@ -71,15 +71,44 @@ enum awq_path {
   AWQ_PATH_GENERIC = 3  /* any legal shape or alignment; slow */
 };
 
+/* Planner overrides, for tests and tuning (awq_set_option). */
+enum awq_option {
+  AWQ_OPT_FORCE_PATH = 1,          /* an awq_path value: run that kernel family */
+  AWQ_OPT_DECODE_STEPS = 2,        /* 1, 2, 4 or 8: 32-row steps per decode wave */
+  AWQ_OPT_DECODE_GATHER_MAX_M = 3, /* 0..16: largest batch whose sorted-weight
+                                      forward gathers x inside the decode kernel */
+  AWQ_OPT_PREFILL_BM = 4,          /* 64, 128 or 256: prefill tile rows */
+  AWQ_OPT_PREFILL_BN = 5,          /* 128 or 192: prefill tile columns */
+  AWQ_OPT_PREFILL_SPLITS = 6       /* 1..8: prefill work-groups along K per tile */
+};
+#define AWQ_OPT_AUTO (-1)          /* the planner's own choice */
+
 /* AWQ_ABI_VERSION of the built library. */
 int awq_abi_version(void);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* awq_status_string(int status);
 
+/* Sets a planner override, process-wide, for every later call from any
+ * thread (a relaxed atomic store; calls already planned are unaffected).
+ * value is AWQ_OPT_AUTO or one of the values listed with the option;
+ * anything else, or an unknown option, is AWQ_ERROR_INVALID_VALUE and
+ * changes nothing.  Each override starts from an environment variable read
+ * once, on the library's first planning call: AWQ_FORCE_PATH (decode |
+ * prefill | generic; any other text makes every awq_gemm and awq_gemm_plan
+ * call fail with AWQ_ERROR_INVALID_VALUE until the option is set),
+ * AWQ_DECODE_STEPS, AWQ_DECODE_GATHER_MAX_M, AWQ_PREFILL_BM,
+ * AWQ_PREFILL_BN, AWQ_PREFILL_SPLITS (numbers; unusable ones are ignored).
+ * No call reads the environment after that.  Host only. */
+int awq_set_option(int option, int64_t value);
+
+/* Writes the current value of an override (AWQ_OPT_AUTO when none) to
+ * *value.  Unknown option or NULL value: AWQ_ERROR_INVALID_VALUE. */
+int awq_get_option(int option, int64_t* value);
+
 /* Bytes of workspace awq_gemm needs for this problem whatever the pointers'
  * alignment and whichever kernel family runs it (also one forced through
- * AWQ_FORCE_PATH): the larger of the split-K decode and split-K prefill
+ * AWQ_OPT_FORCE_PATH): the larger of the split-K decode and split-K prefill
  * needs.  0 means none.  Returns 0 for invalid shapes (awq_gemm then reports
  * the error). */
 size_t awq_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_size);
@@ -87,10 +116,9 @@ size_t awq_gemm_workspace_size(int64_t M, int64_t K, int64_t N, int64_t group_si
 /* Host-only planning, no HIP call and no dereference of x, qweight or scales
  * (only their addresses' alignment is inspected; NULL counts as aligned).
  * Writes the kernel family awq_gemm would run to *path and its workspace need
- * to *workspace_bytes (either may be NULL).  The environment variable
- * AWQ_FORCE_PATH = decode | prefill | generic overrides the choice for
- * testing; a forced family that cannot run the problem yields
- * AWQ_ERROR_INVALID_VALUE. */
+ * to *workspace_bytes (either may be NULL).  AWQ_OPT_FORCE_PATH
+ * (awq_set_option) overrides the choice for testing; a forced family that
+ * cannot run the problem yields AWQ_ERROR_INVALID_VALUE. */
 int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size,
                   const void* x, const void* qweight, const void* scales, int* path,
                   size_t* workspace_bytes);
@@ -103,7 +131,10 @@ int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size,
  * NULL when that is 0.  It must be zero-filled once before its first use; the
  * kernels leave it re-usable (all counters back at zero) on exit, so the same
  * buffer serves later calls on the same stream.  Two calls that may run
- * concurrently (different streams) must not share a workspace.
+ * concurrently (different streams) must not share a workspace.  A HIP graph
+ * that captured a call keeps its workspace pointer: the buffer must stay
+ * allocated (and unused by anything else) for as long as the graph may be
+ * replayed.
  * M == 0 is a no-op that returns AWQ_SUCCESS (x and y may then be NULL). */
 int awq_gemm(const void* x, const void* qweight, const void* qzeros,
              const void* scales, const void* bias, void* y,

@@ -30,7 +30,6 @@ Functions:
     pack_int4 / unpack_int4
     dequant(...)           -- float16 (K, N) dequantised weight
     awq_linear_ref(...)    -- float64 forward, (*, K) -> (*, N)
-    awq_linear_ref_rows    -- the same for a chosen subset of input rows
     awq_linear_loops(...)  -- pure-Python triple loop, for tiny inputs only
     dense_linear_ref(...)  -- the unquantised float16 linear (baseline), float64
     dense_linear_loops     -- its pure-Python triple loop, for tiny inputs only
@@ -166,14 +165,6 @@ def awq_linear_ref(x, qweight, qzeros, scales, bias, group_size):
             raise ValueError("bias must have shape (out_features,)")
         y = y + b.astype(np.float64)[None, :]
     return y.reshape(*lead, N)
-
-
-def awq_linear_ref_rows(x, rows, qweight, qzeros, scales, bias, group_size):
-    """awq_linear_ref evaluated only for the input rows listed in `rows`
-    (x is (M, K)); used to check large problems at sampled rows."""
-    x = np.asarray(x)
-    return awq_linear_ref(x[np.asarray(rows)], qweight, qzeros, scales, bias,
-                          group_size)
 
 
 def awq_linear_loops(x, qweight, qzeros, scales, bias, group_size):

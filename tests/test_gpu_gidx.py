@@ -251,32 +251,33 @@ def test_wqlinear_gidx_module(M, K, N, G):
 
 @pytest.mark.parametrize("steps", [1, 2, 4, 8])
 @pytest.mark.parametrize("M", [1, 5])
-def test_sorted_decode_every_step_count(steps, M, monkeypatch):
+def test_sorted_decode_every_step_count(steps, M):
     """The LDS decode kernel gathers x through perm itself for 1, 2 and 4
     steps per wave (the load order differs with the step count); 8 steps
-    take the separate reorder.  Forced through AWQ_DECODE_STEPS; whole
-    groups and padded blocks."""
-    monkeypatch.setenv("AWQ_DECODE_STEPS", str(steps))
+    take the separate reorder.  Forced through the decode_steps option;
+    whole groups and padded blocks."""
     for p in (act_problem(M, 8192, 1024, 128, seed=steps * 10 + M, bias=True),
               map_problem(M, 8192, 1024, 50, seed=steps * 10 + M, bias=True)):
         say(f"sorted decode steps={steps} M={M} G={p['scales'].shape[0]}")
-        y, _ = run_sorted(p)
+        with awq.options(decode_steps=steps):
+            y, _ = run_sorted(p)
         assert_within_tol(y, ref_of(p), f"sorted decode steps={steps}")
 
 
 @pytest.mark.parametrize("M", [1, 4, 8, 16])
-def test_sorted_fused_and_separate_reorder(M, monkeypatch):
+def test_sorted_fused_and_separate_reorder(M):
     """Both forms of the decode's x reorder (gathered inside the decode
-    kernel, or a separate pass first), forced through
-    AWQ_DECODE_GATHER_MAX_M, match the oracle at every decode batch, for a
-    whole-group and a padded layout."""
+    kernel, or a separate pass first), forced through the
+    decode_gather_max_m option, match the oracle at every decode batch, for
+    a whole-group and a padded layout."""
     for p in (act_problem(M, 8192, 1280, 128, seed=70 + M, bias=True),
               map_problem(M, 8192, 1280, 70, seed=70 + M, bias=True)):
         ref = ref_of(p)
-        for limit in ("16", "0"):
+        for limit in (16, 0):
             say(f"sorted decode M={M} G={p['scales'].shape[0]} gather limit {limit}")
-            monkeypatch.setenv("AWQ_DECODE_GATHER_MAX_M", limit)
-            assert_within_tol(run_sorted(p)[0], ref, f"sorted M={M} limit {limit}")
+            with awq.options(decode_gather_max_m=limit):
+                y = run_sorted(p)[0]
+            assert_within_tol(y, ref, f"sorted M={M} limit {limit}")
 
 
 @pytest.mark.parametrize("M,K,N,g", [(8, 4096, 1024, 128), (256, 2048, 768, 64)])

@@ -64,24 +64,16 @@ def assert_within_tol(gpu, ref, what):
             f"gpu={gpu[tuple(i)]!r} ref={ref[tuple(i)]!r}; max err {err.max():.3e}")
 
 
-def run_gemm(d, path=None, M=None, env=None):
-    """awq_gemm on device inputs d; path forces a kernel family, env sets
-    further planning variables for the call only."""
+def run_gemm(d, path=None, M=None, opts=None):
+    """awq_gemm on device inputs d; path forces a kernel family, opts sets
+    further planner overrides (awq.options) for the call only."""
     x = d["x"] if M is None else d["x"][:M]
-    env = dict(env or {})
+    opts = dict(opts or {})
     if path is not None:
-        env["AWQ_FORCE_PATH"] = path
-    old = {k: os.environ.get(k) for k in env}
-    try:
-        os.environ.update(env)
+        opts["force_path"] = path
+    with awq.options(**opts):
         y = awq.gemm(x, d["qweight"], d["qzeros"], d["scales"], d["bias"], d["group_size"])
         torch.cuda.synchronize()
-    finally:
-        for k, v in old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
     return y.cpu().numpy()
 
 
@@ -90,14 +82,6 @@ def cached_problem(name, Mmax, g):
     p = awq_inputs.workload_inputs(name, Mmax, g)
     w = oracle.dequant(p["qweight"], p["qzeros"], p["scales"], g)
     return p, w
-
-
-def oracle_rows(p, w, rows):
-    x = p["x"][rows].astype(np.float64)
-    y = x @ w.astype(np.float64)
-    if p["bias"] is not None:
-        y = y + p["bias"].astype(np.float64)
-    return y
 
 
 # ------------------------------------------------------------------ golden
@@ -203,48 +187,46 @@ def test_dequant_alignment_forms(qw_off, sc_off):
 
 # ---------------------------------------------------------- config parity
 GEMM_CASES = [
-    ("tiny_m4_k256_n128", 4, 4, 64, None),
-    ("decode_k8192_n1280", 1, 1, 128, None),
-    ("decode_sweep_k8192_n7168", 16, 1, 128, None),
-    ("decode_sweep_k8192_n7168", 16, 4, 128, None),
-    ("decode_sweep_k8192_n7168", 16, 8, 128, None),
-    ("decode_sweep_k8192_n7168", 16, 16, 128, None),
-    ("mlp_down_k14336_n4096", 4096, 1, 128, None),
-    ("mlp_down_k14336_n4096", 4096, 16, 128, None),
-    ("mlp_down_k14336_n4096", 4096, 256, 128, None),
-    ("mlp_down_k14336_n4096", 4096, 1024, 128, 96),
-    ("mlp_down_k14336_n4096", 4096, 4096, 128, 96),
-    ("mlp_down_k14336_n4096", 4096, 1, -1, None),
-    ("mlp_down_k14336_n4096", 4096, 16, -1, None),
-    ("mlp_down_k14336_n4096", 4096, 256, -1, None),
-    ("mlp_down_k14336_n4096", 4096, 1024, -1, 96),
-    ("mlp_down_k14336_n4096", 4096, 4096, -1, 96),
-    ("prefill_qkv_m2048_k4096_n12288", 2048, 2048, 128, 96),
-    ("midm_k8192_n7168", 128, 32, 128, None),
-    ("midm_k8192_n7168", 128, 64, 128, None),
-    ("midm_k8192_n7168", 128, 128, 128, None),
+    ("tiny_m4_k256_n128", 4, 4, 64),
+    ("decode_k8192_n1280", 1, 1, 128),
+    ("decode_sweep_k8192_n7168", 16, 1, 128),
+    ("decode_sweep_k8192_n7168", 16, 4, 128),
+    ("decode_sweep_k8192_n7168", 16, 8, 128),
+    ("decode_sweep_k8192_n7168", 16, 16, 128),
+    ("mlp_down_k14336_n4096", 4096, 1, 128),
+    ("mlp_down_k14336_n4096", 4096, 16, 128),
+    ("mlp_down_k14336_n4096", 4096, 256, 128),
+    ("mlp_down_k14336_n4096", 4096, 1024, 128),
+    ("mlp_down_k14336_n4096", 4096, 4096, 128),
+    ("mlp_down_k14336_n4096", 4096, 1, -1),
+    ("mlp_down_k14336_n4096", 4096, 16, -1),
+    ("mlp_down_k14336_n4096", 4096, 256, -1),
+    ("mlp_down_k14336_n4096", 4096, 1024, -1),
+    ("mlp_down_k14336_n4096", 4096, 4096, -1),
+    ("prefill_qkv_m2048_k4096_n12288", 2048, 2048, 128),
+    ("midm_k8192_n7168", 128, 32, 128),
+    ("midm_k8192_n7168", 128, 64, 128),
+    ("midm_k8192_n7168", 128, 128, 128),
 ]
 
 
-@pytest.mark.parametrize("name,Mmax,M,g,nsample", GEMM_CASES)
-def test_gemm_config_parity(name, Mmax, M, g, nsample):
-    """Every workload point; rows sampled (first, last, and a seeded spread)
-    where the batch is large, all rows otherwise."""
+@pytest.mark.parametrize("name,Mmax,M,g", GEMM_CASES)
+def test_gemm_config_parity(name, Mmax, M, g):
+    """Every workload point, every output element, against the oracle's
+    forward (oracle.awq_linear_ref: float16 dequantisation, float64
+    contraction and bias)."""
     say(f"awq_gemm {name} M={M} g={g}")
-    p, w = cached_problem(name, Mmax, g)
+    p = awq_inputs.workload_inputs(name, Mmax, g)
     d = to_dev(p)
-    path, _ = awq.gemm_plan(M, w.shape[0], w.shape[1], g, d["x"].data_ptr(),
-                            d["scales"].data_ptr())
+    K, N = p["qweight"].shape[0], p["qweight"].shape[1] * 8
+    path, _ = awq.gemm_plan(M, K, N, g, d["x"].data_ptr(), d["scales"].data_ptr())
     expect_path = binding.AWQ_PATH_DECODE if M <= 16 else binding.AWQ_PATH_PREFILL
     assert path == expect_path
     y = run_gemm(d, M=M)
-    if nsample is None:
-        rows = np.arange(M)
-    else:
-        rng = np.random.default_rng(M)
-        rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, nsample, replace=False)]))
-    ref = oracle_rows(p, w, rows)
-    assert_within_tol(y[rows], ref, f"{name} M={M} g={g}")
+    del d
+    ref = oracle.awq_linear_ref(p["x"][:M], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
+    assert ref.shape == y.shape == (M, N)
+    assert_within_tol(y, ref, f"{name} M={M} g={g}")
 
 
 # ------------------------------------------------- exact special cases
@@ -333,7 +315,7 @@ def test_forced_path_and_tails(path, M, K, N, g, bias):
     assert_within_tol(y, ref, f"{path} M={M} K={K} N={N} g={g}")
 
 
-WIDE = {"AWQ_PREFILL_BN": "192"}
+WIDE = {"prefill_bn": 192}
 
 
 @pytest.mark.parametrize("M,K,N,g,bias", [
@@ -349,7 +331,7 @@ def test_prefill_wide_tile(M, K, N, g, bias):
     say(f"wide prefill M={M} K={K} N={N} g={g}")
     p = awq_inputs.make_inputs(M, K, N, g, seed=M + 3 * K + N, bias=bias)
     d = to_dev(p)
-    y = run_gemm(d, path="prefill", env=WIDE)
+    y = run_gemm(d, path="prefill", opts=WIDE)
     ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
     assert_within_tol(y, ref, f"wide M={M} K={K} N={N} g={g}")
 
@@ -367,12 +349,12 @@ def test_prefill_wide_tile_exact_cases():
     x = np.zeros((M, K), dtype=np.float16)
     x[np.arange(M), ks] = 1.0
     d = to_dev(dict(p, x=x, bias=None))
-    y = run_gemm(d, path="prefill", env=WIDE)
+    y = run_gemm(d, path="prefill", opts=WIDE)
     np.testing.assert_array_equal(y.view(np.uint16), w[ks].view(np.uint16))
     p = awq_inputs.make_inputs(M, K, N, g, seed=22, bias=True, scale_lo=-1, scale_hi=1)
     p["qweight"] = np.repeat(p["qzeros"], g, axis=0)
     d = to_dev(p)
-    y = run_gemm(d, path="prefill", env=WIDE)
+    y = run_gemm(d, path="prefill", opts=WIDE)
     np.testing.assert_array_equal(y.view(np.uint16),
                                   np.broadcast_to(p["bias"], (M, N)).view(np.uint16))
 
@@ -391,7 +373,7 @@ def test_prefill_short_tiles(bm, M, K, N, g, bias):
     say(f"prefill BM={bm} M={M} K={K} N={N} g={g}")
     p = awq_inputs.make_inputs(M, K, N, g, seed=bm + M + K + N, bias=bias)
     d = to_dev(p)
-    y = run_gemm(d, path="prefill", env={"AWQ_PREFILL_BM": str(bm)})
+    y = run_gemm(d, path="prefill", opts={"prefill_bm": bm})
     ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
     assert_within_tol(y, ref, f"BM={bm} M={M} K={K} N={N} g={g}")
 
@@ -402,17 +384,17 @@ def test_prefill_short_tiles_exact(bm):
     included: the reduction adds exact zeros)."""
     say(f"prefill BM={bm} exact cases")
     M, K, N, g = bm - 3, 2048, 520, 64
-    env = {"AWQ_PREFILL_BM": str(bm)}
+    opts = {"prefill_bm": bm}
     p = awq_inputs.make_inputs(M, K, N, g, seed=bm)
     w = oracle.dequant(p["qweight"], p["qzeros"], p["scales"], g)
     ks = np.random.default_rng(bm).choice(K, M)
     x = np.zeros((M, K), dtype=np.float16)
     x[np.arange(M), ks] = 1.0
-    y = run_gemm(to_dev(dict(p, x=x, bias=None)), path="prefill", env=env)
+    y = run_gemm(to_dev(dict(p, x=x, bias=None)), path="prefill", opts=opts)
     np.testing.assert_array_equal(y.view(np.uint16), w[ks].view(np.uint16))
     q = awq_inputs.make_inputs(M, K, N, g, seed=bm + 1, bias=True, scale_lo=-1, scale_hi=1)
     q["qweight"] = np.repeat(q["qzeros"], g, axis=0)
-    y = run_gemm(to_dev(q), path="prefill", env=env)
+    y = run_gemm(to_dev(q), path="prefill", opts=opts)
     np.testing.assert_array_equal(y.view(np.uint16),
                                   np.broadcast_to(q["bias"], (M, N)).view(np.uint16))
 

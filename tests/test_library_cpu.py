@@ -6,6 +6,7 @@ import os
 import re
 import shutil
 import subprocess
+import sys
 
 import pytest
 
@@ -208,18 +209,81 @@ def test_plan_unaligned_x_falls_back_to_generic():
         binding.AWQ_PATH_GENERIC
 
 
-def test_forced_path(monkeypatch):
-    monkeypatch.setenv("AWQ_FORCE_PATH", "prefill")
-    assert awq.gemm_plan(1, 8192, 7168, 128)[0] == binding.AWQ_PATH_PREFILL
-    monkeypatch.setenv("AWQ_FORCE_PATH", "generic")
-    assert awq.gemm_plan(2048, 4096, 12288, 128)[0] == binding.AWQ_PATH_GENERIC
-    monkeypatch.setenv("AWQ_FORCE_PATH", "decode")
-    with pytest.raises(awq.AwqError):
-        awq.gemm_plan(64, 4096, 4096, 128)          # decode handles M <= 16 only
-    monkeypatch.setenv("AWQ_FORCE_PATH", "bogus")
-    with pytest.raises(awq.AwqError):
-        awq.gemm_plan(1, 4096, 4096, 128)
-    assert _gemm(M=1, K=4096, N=4096, g=128) == binding.AWQ_ERROR_INVALID_VALUE
+def test_forced_path():
+    with awq.options(force_path="prefill"):
+        assert awq.gemm_plan(1, 8192, 7168, 128)[0] == binding.AWQ_PATH_PREFILL
+        assert awq.get_option("force_path") == binding.AWQ_PATH_PREFILL
+    assert awq.get_option("force_path") == binding.AWQ_OPT_AUTO
+    assert awq.gemm_plan(1, 8192, 7168, 128)[0] == binding.AWQ_PATH_DECODE
+    with awq.options(force_path="generic"):
+        assert awq.gemm_plan(2048, 4096, 12288, 128)[0] == binding.AWQ_PATH_GENERIC
+    with awq.options(force_path="decode"):
+        with pytest.raises(awq.AwqError):
+            awq.gemm_plan(64, 4096, 4096, 128)          # decode handles M <= 16 only
+
+
+def test_option_values_checked():
+    lib = binding.lib()
+    for opt, bad in [(binding.AWQ_OPT_FORCE_PATH, 4), (binding.AWQ_OPT_FORCE_PATH, 0),
+                     (binding.AWQ_OPT_DECODE_STEPS, 3), (binding.AWQ_OPT_DECODE_GATHER_MAX_M, 17),
+                     (binding.AWQ_OPT_PREFILL_BM, 96), (binding.AWQ_OPT_PREFILL_BN, 64),
+                     (binding.AWQ_OPT_PREFILL_SPLITS, 9), (0, 1), (7, 1)]:
+        assert lib.awq_set_option(opt, bad) == binding.AWQ_ERROR_INVALID_VALUE, (opt, bad)
+    assert lib.awq_get_option(7, None) == binding.AWQ_ERROR_INVALID_VALUE
+    assert lib.awq_get_option(binding.AWQ_OPT_PREFILL_BM, None) == binding.AWQ_ERROR_INVALID_VALUE
+    with awq.options(prefill_bm=64, prefill_splits=3):
+        assert awq.get_option("prefill_bm") == 64
+        assert awq.get_option("prefill_splits") == 3
+    assert awq.get_option("prefill_bm") == binding.AWQ_OPT_AUTO
+
+
+def _plan_in_subprocess(env_extra, code):
+    import subprocess
+    env = dict(os.environ)
+    for k in list(env):
+        if k.startswith("AWQ_"):
+            del env[k]
+    env.update(env_extra)
+    prog = ("import sys; sys.path.insert(0, %r)\n"
+            "import bit_weight_quantized_awq_amd as awq\n"
+            "from bit_weight_quantized_awq_amd import binding\n" % ROOT) + code
+    res = subprocess.run([sys.executable, "-c", prog], env=env, capture_output=True, text=True,
+                         timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
+    return res.stdout
+
+
+def test_environment_read_once():
+    """The AWQ_* variables seed the overrides on first use; changing the
+    environment afterwards changes nothing."""
+    out = _plan_in_subprocess({"AWQ_FORCE_PATH": "prefill", "AWQ_PREFILL_BM": "128"}, (
+        "import os\n"
+        "assert awq.gemm_plan(1, 8192, 7168, 128)[0] == binding.AWQ_PATH_PREFILL\n"
+        "assert awq.get_option('prefill_bm') == 128\n"
+        "os.environ['AWQ_FORCE_PATH'] = 'generic'\n"
+        "assert awq.gemm_plan(1, 8192, 7168, 128)[0] == binding.AWQ_PATH_PREFILL\n"
+        "awq.set_option('force_path', None)\n"
+        "assert awq.gemm_plan(1, 8192, 7168, 128)[0] == binding.AWQ_PATH_DECODE\n"
+        "print('ok')\n"))
+    assert out.strip() == "ok"
+
+
+def test_unrecognised_forced_path_fails_every_plan():
+    out = _plan_in_subprocess({"AWQ_FORCE_PATH": "bogus"}, (
+        "import ctypes\n"
+        "try:\n"
+        "    awq.gemm_plan(1, 4096, 4096, 128)\n"
+        "    raise SystemExit('no error')\n"
+        "except awq.AwqError as e:\n"
+        "    assert e.status == binding.AWQ_ERROR_INVALID_VALUE\n"
+        "lib = binding.lib()\n"
+        "A = 0x10000\n"
+        "st = lib.awq_gemm(A, A, A, A, None, A, 1, 4096, 4096, 128, None, 0, None)\n"
+        "assert st == binding.AWQ_ERROR_INVALID_VALUE, st\n"
+        "awq.set_option('force_path', None)\n"
+        "assert awq.gemm_plan(1, 4096, 4096, 128)[0] == binding.AWQ_PATH_DECODE\n"
+        "print('ok')\n"))
+    assert out.strip() == "ok"
 
 
 def test_decode_workspace_size_formula():
