@@ -249,19 +249,40 @@ def graph_time_us(torch, fn, calls, dev):
     return t0.elapsed_time(t1) * 1e3 / calls
 
 
+def read_stream_fn(torch, bufs, dev):
+    """A launcher of the plain read-stream kernel (libawq_bench.so, a
+    measurement aid built beside the library) over bufs[i % len(bufs)]."""
+    import ctypes
+    from bit_weight_quantized_awq_amd import build as _build
+    lib = ctypes.CDLL(_build.BENCH_LIB_PATH)
+    lib.awq_bench_read_stream.restype = ctypes.c_int
+    lib.awq_bench_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+
+    def fn(i):
+        st = lib.awq_bench_read_stream(bufs[i % len(bufs)].data_ptr(), nbytes, sink.data_ptr(),
+                                       1024, torch._C._cuda_getCurrentRawStream(dev.index))
+        if st != 0:
+            raise RuntimeError(f"awq_bench_read_stream: status {st}")
+    return fn
+
+
 def same_box_references(torch, dev, decode_bytes):
     """What this box does, in this process, on plain work of the headline
-    sizes: a read-only pass (torch's sum) and a device copy over the decode
-    step's byte count, rotated like the decode leg, and torch's float16
-    linear (the vendor GEMM) at the prefill projection's shape."""
-    n = decode_bytes // 4
+    sizes: a read-only stream (a plain kernel of 1024 work-groups, eight
+    16-byte loads in flight per thread) and a device copy over the decode
+    step's byte count (rounded down to 16 bytes), rotated like the decode
+    leg, and torch's float16 linear (the vendor GEMM) at the prefill
+    projection's shape."""
+    n = decode_bytes // 16 * 4
     R = max(2, -(-ROTATE_BYTES // decode_bytes))
     gen = torch.Generator(device="cpu").manual_seed(7)
     bufs = [torch.randint(-2**31, 2**31 - 1, (n,), generator=gen, dtype=torch.int32).to(dev)
             for _ in range(R)]
     dst = [torch.empty_like(b) for b in bufs]
-    acc = torch.empty((), dtype=torch.int64, device=dev)
-    read_us = graph_time_us(torch, lambda i: torch.sum(bufs[i % R], dim=0, out=acc), 100, dev)
+    read_us = graph_time_us(torch, read_stream_fn(torch, bufs, dev), 100, dev)
     copy_us = graph_time_us(torch, lambda i: dst[i % R].copy_(bufs[i % R]), 100, dev)
     del bufs, dst
     torch.cuda.empty_cache()
@@ -273,7 +294,7 @@ def same_box_references(torch, dev, decode_bytes):
     del x, ws, b
     torch.cuda.empty_cache()
     return {
-        "read_stream": {"op": "torch.sum over int32", "bytes": n * 4, "us": round(read_us, 3),
+        "read_stream": {"op": "plain read kernel (libawq_bench.so)", "bytes": n * 4, "us": round(read_us, 3),
                         "GB_per_s": round(n * 4 / read_us / 1e3, 1),
                         "frac": round(n * 4 / read_us / 1e3 / HBM_PEAK_GBS, 4)},
         "device_copy": {"op": "Tensor.copy_", "bytes_moved": 2 * n * 4, "us": round(copy_us, 3),

@@ -1,8 +1,11 @@
 """Build the C-ABI shared library libawq_mi355x.so for gfx950 with hipcc.
 
-Every source under csrc/ is compiled as HIP for gfx950 into _build/, then
-linked into the package directory, where the Python binding loads it from.
-Packed fp32 VALU instructions are disabled in device code.
+Every source of the library under csrc/ is compiled as HIP for gfx950 into
+_build/, then linked into the package directory, where the Python binding
+loads it from.  Packed fp32 VALU instructions are disabled in device code.
+A second, separate library, libawq_bench.so (csrc/bench_read.hip: a plain
+read stream that the benchmark uses as a same-box reference), is built the
+same way; the W4A16 path never loads it.
 """
 from __future__ import annotations
 
@@ -19,6 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libawq_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+BENCH_LIB_PATH = os.path.join(PKG_DIR, "libawq_bench.so")
+BENCH_SOURCES = ["bench_read.hip"]
 ARCH = "gfx950"
 
 SOURCES = [
@@ -67,16 +72,21 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, jobs: int
     os.makedirs(BUILD_DIR, exist_ok=True)
     extra = list(extra_flags or [])
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES + BENCH_SOURCES))
+    _link(objs[:len(SOURCES)], LIB_PATH, verbose)
+    _link(objs[len(SOURCES):], BENCH_LIB_PATH, verbose)
+    return LIB_PATH
+
+
+def _link(objs: list[str], path: str, verbose: bool) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {path}")
 
 
 if __name__ == "__main__":

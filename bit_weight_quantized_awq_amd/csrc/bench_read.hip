@@ -1,0 +1,48 @@
+// Measurement aid, not part of the W4A16 forward: a plain read-only stream
+// over a device buffer, built into its own small library (libawq_bench.so)
+// so that the benchmark can time, in the same process and on the same box,
+// what merely reading the decode step's bytes costs.  Every thread keeps
+// eight 16-byte loads in flight per grid-stride step and folds them into a
+// register, written out only on an impossible value (so the loads stay live).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kUnroll = 8;
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void read_stream_kernel(const uint4* __restrict__ p,
+                                                               size_t n16,
+                                                               uint32_t* __restrict__ sink) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * kThreads * kUnroll;
+  uint32_t acc = 0;
+  for (size_t base = static_cast<size_t>(blockIdx.x) * kThreads * kUnroll + threadIdx.x;
+       base < n16; base += stride) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const size_t i = base + static_cast<size_t>(u) * kThreads;
+      v[u] = i < n16 ? p[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+}  // namespace
+
+// Reads `bytes` bytes (a multiple of 16) at the 16-byte aligned device
+// pointer p on `stream` (a hipStream_t, NULL for the default stream), with
+// `blocks` work-groups of 256 threads; sink is a device word the kernel may
+// write.  Returns 0, 1 for bad arguments, 5 if the launch failed.
+extern "C" int awq_bench_read_stream(const void* p, size_t bytes, void* sink, int blocks,
+                                     void* stream) {
+  if (!p || !sink || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(p) % 16 != 0 || blocks <= 0)
+    return 1;
+  hipLaunchKernelGGL(read_stream_kernel, dim3(blocks), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(p), bytes / 16,
+                     static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
