@@ -12,7 +12,7 @@ from .binding import (  # noqa: F401
     AWQ_PATH_DECODE, AWQ_PATH_GENERIC, AWQ_PATH_PREFILL, AwqError, PATH_NAMES, abi_version,
     dense_gemv, dequant, gemm, gemm_plan, gemm_workspace_size, lib, status_string,
     SortedWeight, dequant_gidx, gather_rows, gemm_gidx, gemm_sorted, gidx_layout, prepare_gidx,
-    sorted_workspace_size, get_option, options, set_option,
+    sorted_workspace_size, get_option, options, set_option, gemm_noalloc,
 )
 
 

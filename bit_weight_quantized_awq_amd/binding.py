@@ -20,6 +20,8 @@ AWQ_ERROR_SHAPE = 2
 AWQ_ERROR_MISALIGNED = 3
 AWQ_ERROR_WORKSPACE = 4
 AWQ_ERROR_HIP = 5
+AWQ_ERROR_SCRATCH = 6
+AWQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 AWQ_OPT_FORCE_PATH = 1
 AWQ_OPT_DECODE_STEPS = 2
@@ -53,6 +55,8 @@ SIGNATURES = {
                                      ctypes.POINTER(ctypes.c_size_t)]),
     "awq_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                 _vp, ctypes.c_size_t, _vp]),
+    "awq_gemm_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                        _vp]),
     "awq_dequant": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "awq_dense_gemv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "awq_dequant_gidx": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
@@ -332,6 +336,40 @@ def gemm(x, qweight, qzeros, scales, bias=None, group_size: int = 128, out=None,
                         stream)
     if st != AWQ_SUCCESS:
         raise AwqError(st, "awq_gemm")
+    return y.reshape(*lead, N)
+
+
+def gemm_noalloc(x, qweight, qzeros, scales, bias=None, group_size: int = 128, out=None):
+    """gemm through awq_gemm_noalloc: no workspace, the library's fixed
+    per-device scratch instead (for code that cannot allocate, e.g. under
+    graph capture; pass `out` so that nothing is allocated here either).
+    Calls that may overlap on one device race on that scratch."""
+    torch = _torch()
+    device = qweight.device
+    for name, t in (("x", x), ("qweight", qweight), ("qzeros", qzeros), ("scales", scales)):
+        _check_device(name, t, device)
+    if x.dtype != torch.float16 or scales.dtype != torch.float16:
+        raise TypeError("x and scales must be float16")
+    if qweight.dtype != torch.int32 or qzeros.dtype != torch.int32:
+        raise TypeError("qweight and qzeros must be int32")
+    K = qweight.shape[0]
+    N = qweight.shape[1] * 8
+    if x.shape[-1] != K:
+        raise ValueError(f"x has {x.shape[-1]} features, qweight has {K}")
+    _check_group_shapes(K, N, group_size, qzeros, scales)
+    if not (qweight.is_contiguous() and qzeros.is_contiguous() and scales.is_contiguous()):
+        raise ValueError("qweight, qzeros and scales must be contiguous")
+    bias = _check_bias(bias, N, device)
+    lead, x2 = _prep_x(x, K)
+    M = x2.shape[0]
+    y = _prep_out(out, M, N, device)
+    st = lib().awq_gemm_noalloc(x2.data_ptr() if M else None, qweight.data_ptr(),
+                                qzeros.data_ptr(), scales.data_ptr(),
+                                bias.data_ptr() if bias is not None else None,
+                                y.data_ptr() if M else None, M, K, N, group_size,
+                                _current_stream(device))
+    if st != AWQ_SUCCESS:
+        raise AwqError(st, "awq_gemm_noalloc")
     return y.reshape(*lead, N)
 
 

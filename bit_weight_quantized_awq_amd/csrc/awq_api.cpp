@@ -1,6 +1,8 @@
 // C-ABI entry points (include/awq.h): host validation, planning, launch.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "awq.h"
 #include "awq_device.h"
 #include "awq_plan.h"
@@ -24,6 +26,9 @@ const char* awq_status_string(int status) {
     case AWQ_ERROR_MISALIGNED: return "pointer not aligned to its element size";
     case AWQ_ERROR_WORKSPACE: return "workspace missing or smaller than awq_gemm_workspace_size";
     case AWQ_ERROR_HIP: return "HIP launch error";
+    case AWQ_ERROR_SCRATCH:
+      return "problem needs more split-K workspace than awq_gemm_noalloc's fixed scratch "
+             "(AWQ_NOALLOC_SCRATCH_BYTES); use awq_gemm with a workspace";
     default: return "unknown status";
   }
 }
@@ -127,9 +132,88 @@ int run_gemm(const Problem& p, const void* x, const void* qweight, const void* q
   return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// awq_gemm_noalloc: awq_gemm for callers that cannot allocate (code under
+// HIP graph capture, serving loops, harnesses that forbid hipMalloc).  Its
+// split-K workspace is this file-scope array, one copy per device, held
+// until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): the per-device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current.
+constexpr size_t kScratchBytes = AWQ_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes >= awq::kTicketRegionBytes + awq::kAtomicRegionBytes,
+              "the scratch holds at least the exchange's fixed regions");
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  int status = AWQ_ERROR_HIP;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Zeroes n16 16-byte words at p (the exchange's ticket and accumulator
+// regions must start at zero; every exchange leaves them zero again).
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n16;
+       i += static_cast<size_t>(gridDim.x) * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The scratch address on the device of stream s, set up on first use: the
+// symbol's address with that device current, and a fill kernel on s that
+// zeroes the fixed regions before any exchange uses them.
+int scratch_for_stream(hipStream_t s, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return AWQ_ERROR_HIP;
+  int dev = cur;
+  if (s != nullptr && hipStreamGetDevice(s, &dev) != hipSuccess) return AWQ_ERROR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return AWQ_ERROR_INVALID_VALUE;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&] {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess && ptr != nullptr) {
+      const size_t n16 = (awq::kTicketRegionBytes + awq::kAtomicRegionBytes) / 16;
+      hipLaunchKernelGGL(zero_fill_kernel, dim3(256), dim3(256), 0, s,
+                         static_cast<uint4*>(ptr), n16);
+      if (hipGetLastError() == hipSuccess) {
+        slot.ptr = ptr;
+        slot.status = AWQ_SUCCESS;
+      }
+    }
+    if (dev != cur) (void)hipSetDevice(cur);
+  });
+  if (slot.status != AWQ_SUCCESS) return slot.status;
+  *out = slot.ptr;
+  return AWQ_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
+
+int awq_gemm_noalloc(const void* x, const void* qweight, const void* qzeros, const void* scales,
+                     const void* bias, void* y, int64_t M, int64_t K, int64_t N,
+                     int64_t group_size, void* stream) {
+  Problem p;
+  int st = awq::validate_shape(M, K, N, group_size, &p);
+  if (st != AWQ_SUCCESS) return st;
+  st = awq::validate_gemm_pointers(x, qweight, qzeros, scales, bias, y, M);
+  if (st != AWQ_SUCCESS) return st;
+  if (M == 0) return AWQ_SUCCESS;
+  Plan pl;
+  st = plan_gemm(p, x, qweight, scales, false, &pl);
+  if (st != AWQ_SUCCESS) return st;
+  if (pl.ws_bytes > kScratchBytes) return AWQ_ERROR_SCRATCH;
+  const auto s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  st = scratch_for_stream(s, &ws);
+  if (st != AWQ_SUCCESS) return st;
+  return run_gemm(p, x, qweight, qzeros, scales, bias, y, ws, kScratchBytes, nullptr, K,
+                  nullptr, s);
+}
 
 int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void* scales,
              const void* bias, void* y, int64_t M, int64_t K, int64_t N, int64_t group_size,

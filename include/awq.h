@@ -61,7 +61,9 @@ enum awq_status {
                                   or an operand with 2^31 or more elements */
   AWQ_ERROR_MISALIGNED = 3,    /* a pointer not aligned to its element size */
   AWQ_ERROR_WORKSPACE = 4,     /* workspace smaller than awq_gemm_workspace_size */
-  AWQ_ERROR_HIP = 5            /* a HIP launch reported an error */
+  AWQ_ERROR_HIP = 5,           /* a HIP launch reported an error */
+  AWQ_ERROR_SCRATCH = 6        /* awq_gemm_noalloc: the problem's split-K workspace
+                                  exceeds AWQ_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Kernel families that awq_gemm can run (see awq_gemm_plan). */
@@ -140,6 +142,27 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros,
              const void* scales, const void* bias, void* y,
              int64_t M, int64_t K, int64_t N, int64_t group_size,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): awq_gemm
+ * without a workspace argument.  The split-K workspace is the library's own
+ * file-scope device array of AWQ_NOALLOC_SCRATCH_BYTES (16 MiB), one copy per
+ * device, held from the library's first use on that device until the
+ * process ends; no call allocates or frees anything.  Same arguments,
+ * kernels, results (bit for bit), errors and stream behaviour as awq_gemm,
+ * plus AWQ_ERROR_SCRATCH when the problem's plan needs more workspace than
+ * the scratch holds (decode batches at the shapes this library targets fit;
+ * large split prefill problems may not).  The first call on a device looks
+ * up the array's address on that device (hipGetSymbolAddress) and enqueues
+ * a small fill kernel on `stream` that zeroes the exchange counters (inside
+ * a graph capture that kernel is captured too); every exchange leaves them
+ * zero again.  All calls on one device share the one array: calls that may
+ * run concurrently on that device (different streams, or graphs replayed
+ * concurrently) race and must not overlap. */
+#define AWQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int awq_gemm_noalloc(const void* x, const void* qweight, const void* qzeros,
+                     const void* scales, const void* bias, void* y,
+                     int64_t M, int64_t K, int64_t N, int64_t group_size, void* stream);
 
 /* The dequantised weight on its own: w[K, N] float16 with
  * w[k, n] = float16_RNE((q[k, n] - z[k / g, n]) * s[k / g, n]), bit-exact

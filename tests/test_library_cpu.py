@@ -529,3 +529,23 @@ def test_gather_rows_validation():
     assert lib.awq_gather_rows(A, 256, A, A, 256, 6, None) == binding.AWQ_ERROR_SHAPE
     assert lib.awq_gather_rows(A, 256, A + 2, A, 256, 64, None) == binding.AWQ_ERROR_MISALIGNED
     assert lib.awq_gather_rows(A, 256, A, A, 1 << 30, 64, None) == binding.AWQ_ERROR_SHAPE
+
+
+def _noalloc(x=A, qw=A, qz=A, sc=A, bias=None, y=A, M=4, K=256, N=128, g=64):
+    return awq.lib().awq_gemm_noalloc(x, qw, qz, sc, bias, y, M, K, N, g, None)
+
+
+def test_noalloc_host_checks():
+    """awq_gemm_noalloc validates like awq_gemm and refuses, before any HIP
+    call, a problem whose split-K workspace exceeds its fixed scratch."""
+    assert _noalloc(M=0, x=None, y=None) == binding.AWQ_SUCCESS
+    assert _noalloc(N=130) == binding.AWQ_ERROR_SHAPE
+    assert _noalloc(g=0) == binding.AWQ_ERROR_INVALID_VALUE
+    assert _noalloc(qw=None) == binding.AWQ_ERROR_INVALID_VALUE
+    assert _noalloc(x=A + 1) == binding.AWQ_ERROR_MISALIGNED
+    M, K, N, g = 256, 14336, 4096, 128
+    assert awq.gemm_workspace_size(M, K, N, g) > binding.AWQ_NOALLOC_SCRATCH_BYTES
+    assert _noalloc(M=M, K=K, N=N, g=g) == binding.AWQ_ERROR_SCRATCH
+    assert "scratch" in awq.status_string(binding.AWQ_ERROR_SCRATCH)
+    with awq.options(force_path="decode"):
+        assert _noalloc(M=64, K=4096, N=4096, g=128) == binding.AWQ_ERROR_INVALID_VALUE

@@ -1,0 +1,104 @@
+"""awq_gemm_noalloc -- awq_gemm without a workspace argument, its split-K
+workspace being the library's fixed per-device scratch -- against awq_gemm
+(the entry point it is a variant of) on the same seeded inputs, through the
+C ABI: bit-identical outputs, and both within the oracle's tolerance.  Two
+calls in a row, the second on a smaller problem, for each exchange the
+scratch serves."""
+import sys
+
+import numpy as np
+import pytest
+
+import awq_inputs
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import bit_weight_quantized_awq_amd as awq  # noqa: E402
+from bit_weight_quantized_awq_amd import binding  # noqa: E402
+
+DEV = "cuda:0"
+ATOL = RTOL = 1e-2
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert "gfx950" in torch.cuda.get_device_properties(0).gcnArchName
+    awq.lib()
+    yield
+
+
+def problem(M, K, N, g, seed, bias):
+    p = awq_inputs.make_inputs(M, K, N, g, seed=seed, bias=bias)
+    d = {k: (torch.from_numpy(v).to(DEV) if isinstance(v, np.ndarray) else v)
+         for k, v in p.items()}
+    return p, d
+
+
+def both(d, g):
+    """(awq_gemm output, awq_gemm_noalloc output) for device inputs d."""
+    ref = awq.gemm(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], g)
+    out = torch.full_like(ref, float("nan"))
+    got = awq.gemm_noalloc(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], g, out=out)
+    assert got.data_ptr() == out.data_ptr()
+    torch.cuda.synchronize()
+    return ref.cpu().numpy(), got.cpu().numpy()
+
+
+def check(p, g, a, b, what):
+    np.testing.assert_array_equal(b.view(np.uint16), a.view(np.uint16), err_msg=what)
+    ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
+    err = np.abs(b.astype(np.float64) - ref)
+    assert (err <= ATOL + RTOL * np.abs(ref)).all(), f"{what}: max err {err.max():.3e}"
+
+
+# (first problem, second smaller problem): the decode ticket exchange then
+# the decode atomic exchange; a split prefill (partials in the scratch) then
+# an unsplit tiny one; the atomic exchange then a single-split decode.
+PAIRS = [
+    ((16, 8192, 7168, 128, True), (1, 8192, 1280, 128, False)),
+    ((64, 8192, 7168, 128, True), (4, 256, 128, 64, True)),
+    ((4, 14336, 4096, -1, False), (2, 2048, 512, 128, True)),
+]
+
+
+@pytest.mark.parametrize("first,second", PAIRS)
+def test_noalloc_matches_gemm_two_calls(first, second):
+    for i, (M, K, N, g, bias) in enumerate((first, second)):
+        say(f"awq_gemm_noalloc call {i + 1}: M={M} K={K} N={N} g={g} bias={bias}")
+        p, d = problem(M, K, N, g, seed=M + K + N + i, bias=bias)
+        a, b = both(d, g)
+        check(p, g, a, b, f"call {i + 1} M={M} K={K} N={N} g={g}")
+
+
+def test_noalloc_repeats_are_identical():
+    """The scratch's counters are back at zero after every call: repeated
+    calls on one input give the same bits (ticket and atomic exchanges)."""
+    for (M, K, N, g) in ((8, 8192, 7168, 128), (1, 8192, 7168, 128)):
+        say(f"awq_gemm_noalloc repeats M={M} K={K} N={N}")
+        _, d = problem(M, K, N, g, seed=3, bias=False)
+        outs = [awq.gemm_noalloc(d["x"], d["qweight"], d["qzeros"], d["scales"], None, g)
+                for _ in range(5)]
+        torch.cuda.synchronize()
+        for o in outs[1:]:
+            assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_noalloc_rejects_problems_beyond_the_scratch():
+    """A split prefill whose partials exceed the fixed scratch is refused on
+    the host with AWQ_ERROR_SCRATCH; awq_gemm runs it with a workspace."""
+    M, K, N, g = 256, 14336, 4096, 128
+    assert awq.gemm_workspace_size(M, K, N, g) > binding.AWQ_NOALLOC_SCRATCH_BYTES
+    say(f"awq_gemm_noalloc over the limit M={M} K={K} N={N}")
+    _, d = problem(M, K, N, g, seed=9, bias=False)
+    with pytest.raises(awq.AwqError) as e:
+        awq.gemm_noalloc(d["x"], d["qweight"], d["qzeros"], d["scales"], None, g)
+    assert e.value.status == binding.AWQ_ERROR_SCRATCH
