@@ -29,11 +29,12 @@ AWQ_OPT_DECODE_GATHER_MAX_M = 3
 AWQ_OPT_PREFILL_BM = 4
 AWQ_OPT_PREFILL_BN = 5
 AWQ_OPT_PREFILL_SPLITS = 6
+AWQ_OPT_DECODE_WAVES = 7
 AWQ_OPT_AUTO = -1
 OPTIONS = {"force_path": AWQ_OPT_FORCE_PATH, "decode_steps": AWQ_OPT_DECODE_STEPS,
            "decode_gather_max_m": AWQ_OPT_DECODE_GATHER_MAX_M,
            "prefill_bm": AWQ_OPT_PREFILL_BM, "prefill_bn": AWQ_OPT_PREFILL_BN,
-           "prefill_splits": AWQ_OPT_PREFILL_SPLITS}
+           "prefill_splits": AWQ_OPT_PREFILL_SPLITS, "decode_waves": AWQ_OPT_DECODE_WAVES}
 
 AWQ_PATH_DECODE = 1
 AWQ_PATH_PREFILL = 2
@@ -118,7 +119,8 @@ _ws_need: dict = {}
 
 def _gemm_workspace_need(M: int, K: int, N: int, group_size: int) -> int:
     """awq_gemm_workspace_size, remembered per shape (it depends on the shape
-    only), so a forward makes a single C-ABI call."""
+    and the planner overrides only; set_option clears the memory), so a
+    forward makes a single C-ABI call."""
     key = (M, K, N, group_size)
     need = _ws_need.get(key)
     if need is None:
@@ -154,6 +156,7 @@ def set_option(name, value) -> None:
     st = lib().awq_set_option(opt, _option_value(opt, value))
     if st != AWQ_SUCCESS:
         raise AwqError(st, f"awq_set_option({name!r}, {value!r})")
+    _ws_need.clear()   # an override can change a shape's workspace need
 
 
 def get_option(name) -> int:
@@ -182,6 +185,7 @@ class options:
     def __exit__(self, *exc):
         for k, v in self._old.items():
             lib().awq_set_option(_option_id(k), v)
+        _ws_need.clear()
         return False
 
 

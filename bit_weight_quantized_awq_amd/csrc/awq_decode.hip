@@ -486,14 +486,15 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 // packed-word copies are split in two halves around the gathers, so the
 // dependent perm -> x round trip overlaps the first half of the weight
 // stream instead of delaying all of it.
-template <int STEPS, bool SINGLE_GROUP, bool GATHER>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void
+template <int STEPS, bool SINGLE_GROUP, bool GATHER, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
                   const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
                   const _Float16* __restrict__ bias, _Float16* __restrict__ y,
                   SplitK sk, int M, int K, int N, int g, int G, int splits,
                   const int32_t* __restrict__ perm, int Kx) {
   static_assert(!GATHER || STEPS <= 4, "gather loads must fit the load counter");
+  static_assert(WAVES == 4 || WAVES == 8, "four or eight waves along K");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   pin_arg(y);
   pin_arg(bias);
@@ -516,7 +517,7 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   const int col16 = lane & 15;  // MFMA column (B) / row (A) of this lane
   const int kb = lane >> 4;     // 8-row block within a 32-row step
   const int c0 = n_tile * 32;   // first word column of the tile
-  const int kw0 = split * (128 * STEPS) + wave * (32 * STEPS);
+  const int kw0 = split * (32 * WAVES * STEPS) + wave * (32 * STEPS);
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(qw, static_cast<uint32_t>(K) * NW * 4u);
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(qz, static_cast<uint32_t>(G) * NW * 4u);
@@ -746,8 +747,8 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
       }
     }
   }
-  // The four K-ranges meet in LDS (the copy regions are free once every wave
-  // is past its last step).  tot[h][j][i] is row 4*kb + i, local column
+  // The WAVES K-ranges meet in LDS (the copy regions are free once every
+  // wave is past its last step).  tot[h][j][i] is row 4*kb + i, local column
   // 8*(16h + col16) + j; with one row only element 0 is formed and stored.
   float* red = reinterpret_cast<float*>(smem);
   const int Mq = (M + 3) >> 2;
@@ -779,39 +780,57 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   }
   __syncthreads();
 
+  // One thread per column of the tile; with eight waves the upper half of
+  // the work-group is done (eight waves run only with the atomic exchange
+  // or one split, neither of which needs the whole work-group).
+  if (WAVES > 4 && tid >= kDecodeCols) return;
   const int n = n_tile * kDecodeCols + tid;
   const bool nvalid = n < N;
   float part[kDecodeMaxM];
-  red_sum<4>(red, Mq, M, tid, part);
+  red_sum<WAVES>(red, Mq, M, tid, part);
   if (splits == 1) {
     if (nvalid) store_rows(part, bias, y, M, N, n);
     return;
   }
   if (M <= kDecodeAtomicMaxM && N <= kDecodeAtomicMaxN) {
     if (nvalid) splitk_atomic(part, sk, bias, y, M, N, n, split, splits);
-  } else {
+  } else if constexpr (WAVES == 4) {
     splitk_ticket<32>(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
   }
+}
+
+template <int STEPS, bool GATHER, int WAVES>
+hipError_t launch_lds_waves(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
+                            const _Float16* scales, const _Float16* bias, _Float16* y,
+                            int M, int K, int N, int g, int G, int splits, int n_tiles,
+                            SplitK sk, const int32_t* perm, int Kx, hipStream_t stream) {
+  const size_t copy_bytes = WAVES * STEPS * 4 * kLdsBlockPitch;
+  const size_t red_bytes =
+      WAVES * static_cast<size_t>((M + 3) & ~3) * kDecodeCols * sizeof(float);
+  const size_t shmem = copy_bytes > red_bytes ? copy_bytes : red_bytes;
+  const bool single = (G == 1) || (g % (kDecodeRowsPerStep * STEPS) == 0);
+  if (single)
+    hipLaunchKernelGGL((decode_lds_kernel<STEPS, true, GATHER, WAVES>), dim3(n_tiles * splits),
+                       dim3(64 * WAVES), shmem, stream, x, qweight, qzeros, scales, bias, y, sk,
+                       M, K, N, g, G, splits, perm, Kx);
+  else
+    hipLaunchKernelGGL((decode_lds_kernel<STEPS, false, GATHER, WAVES>), dim3(n_tiles * splits),
+                       dim3(64 * WAVES), shmem, stream, x, qweight, qzeros, scales, bias, y, sk,
+                       M, K, N, g, G, splits, perm, Kx);
+  return hipGetLastError();
 }
 
 template <int STEPS, bool GATHER>
 hipError_t launch_lds_steps(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                             const _Float16* scales, const _Float16* bias, _Float16* y,
                             int M, int K, int N, int g, int G, int splits, int n_tiles,
-                            SplitK sk, const int32_t* perm, int Kx, hipStream_t stream) {
-  const size_t copy_bytes = 4 * STEPS * 4 * kLdsBlockPitch;
-  const size_t red_bytes = 4 * static_cast<size_t>((M + 3) & ~3) * kDecodeCols * sizeof(float);
-  const size_t shmem = copy_bytes > red_bytes ? copy_bytes : red_bytes;
-  const bool single = (G == 1) || (g % (kDecodeRowsPerStep * STEPS) == 0);
-  if (single)
-    hipLaunchKernelGGL((decode_lds_kernel<STEPS, true, GATHER>), dim3(n_tiles * splits),
-                       dim3(256), shmem, stream, x, qweight, qzeros, scales, bias, y, sk, M,
-                       K, N, g, G, splits, perm, Kx);
-  else
-    hipLaunchKernelGGL((decode_lds_kernel<STEPS, false, GATHER>), dim3(n_tiles * splits),
-                       dim3(256), shmem, stream, x, qweight, qzeros, scales, bias, y, sk, M,
-                       K, N, g, G, splits, perm, Kx);
-  return hipGetLastError();
+                            int waves, SplitK sk, const int32_t* perm, int Kx,
+                            hipStream_t stream) {
+  if (waves == 8)
+    return launch_lds_waves<STEPS, GATHER, 8>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
+                                              G, splits, n_tiles, sk, perm, Kx, stream);
+  return launch_lds_waves<STEPS, GATHER, 4>(x, qweight, qzeros, scales, bias, y, M, K, N, g, G,
+                                            splits, n_tiles, sk, perm, Kx, stream);
 }
 
 template <int STEPS>
@@ -839,8 +858,10 @@ hipError_t launch_steps(const _Float16* x, const uint32_t* qweight, const uint32
 hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                          const _Float16* scales, const _Float16* bias, _Float16* y,
                          int M, int K, int N, int g, int G, int steps, int splits,
-                         int n_tiles, bool lds_variant, void* workspace,
+                         int n_tiles, bool lds_variant, int waves, void* workspace,
                          const int32_t* perm, int Kx, hipStream_t stream) {
+  if (waves != 4 && !(lds_variant && waves == 8 && (splits == 1 || M <= kDecodeAtomicMaxM)))
+    return hipErrorInvalidValue;
   // Workspace: ticket region, accumulator region ([M][N] accumulators, then
   // [M][N] masks), then [splits][M][N] partials.
   char* ws = static_cast<char*>(workspace);
@@ -857,11 +878,11 @@ hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint3
   if (lds_variant && perm) {
     switch (steps) {
       case 1: return launch_lds_steps<1, true>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
-                                               G, splits, n_tiles, sk, perm, Kx, stream);
+                                               G, splits, n_tiles, waves, sk, perm, Kx, stream);
       case 2: return launch_lds_steps<2, true>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
-                                               G, splits, n_tiles, sk, perm, Kx, stream);
+                                               G, splits, n_tiles, waves, sk, perm, Kx, stream);
       case 4: return launch_lds_steps<4, true>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
-                                               G, splits, n_tiles, sk, perm, Kx, stream);
+                                               G, splits, n_tiles, waves, sk, perm, Kx, stream);
       default: return hipErrorInvalidValue;   // decode_gathers() is false for 8 steps
     }
   }
@@ -869,13 +890,13 @@ hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint3
   if (lds_variant) {
     switch (steps) {
       case 1: return launch_lds_steps<1, false>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
-                                                G, splits, n_tiles, sk, nullptr, K, stream);
+                                                G, splits, n_tiles, waves, sk, nullptr, K, stream);
       case 2: return launch_lds_steps<2, false>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
-                                                G, splits, n_tiles, sk, nullptr, K, stream);
+                                                G, splits, n_tiles, waves, sk, nullptr, K, stream);
       case 4: return launch_lds_steps<4, false>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
-                                                G, splits, n_tiles, sk, nullptr, K, stream);
+                                                G, splits, n_tiles, waves, sk, nullptr, K, stream);
       case 8: return launch_lds_steps<8, false>(x, qweight, qzeros, scales, bias, y, M, K, N, g,
-                                                G, splits, n_tiles, sk, nullptr, K, stream);
+                                                G, splits, n_tiles, waves, sk, nullptr, K, stream);
       default: return hipErrorInvalidValue;
     }
   }

@@ -84,9 +84,10 @@ static bool fits_32bit_offsets(const Problem& p) {
 }
 
 // Split-K work-groups per column tile for a step count: rows per work-group
-// are 4 waves (LDS variant) or 2 waves (register variant) x 32 x steps.
-static int64_t decode_splits(const Problem& p, bool lds, int steps) {
-  const int waves_k = lds ? 4 : 2;
+// are `waves` waves (LDS variant: 4 or 8) or 2 waves (register variant)
+// x 32 x steps.
+static int64_t decode_splits(const Problem& p, bool lds, int steps, int waves = 4) {
+  const int waves_k = lds ? waves : 2;
   return ceil_div(p.K, static_cast<int64_t>(waves_k) * kDecodeRowsPerStep * steps);
 }
 
@@ -124,7 +125,7 @@ bool prefill_supported(const Problem& p, const Alignment& al) {
 // kOptInvalid marks an unrecognised AWQ_FORCE_PATH, which fails every plan.
 namespace {
 constexpr int kOptInvalid = -2;
-constexpr int kNumOptions = AWQ_OPT_PREFILL_SPLITS + 1;
+constexpr int kNumOptions = AWQ_OPT_DECODE_WAVES + 1;
 
 bool option_value_ok(int opt, int64_t v) {
   if (v == kOptAuto) return true;
@@ -136,6 +137,7 @@ bool option_value_ok(int opt, int64_t v) {
     case AWQ_OPT_PREFILL_BM: return v == kPrefillMinBM || v == 2 * kPrefillMinBM || v == kPrefillBM;
     case AWQ_OPT_PREFILL_BN: return v == kPrefillBN || v == kPrefillWideBN;
     case AWQ_OPT_PREFILL_SPLITS: return v >= 1 && v <= kPrefillMaxSplits;
+    case AWQ_OPT_DECODE_WAVES: return v == 4 || v == 8;
     default: return false;
   }
 }
@@ -143,7 +145,7 @@ bool option_value_ok(int opt, int64_t v) {
 int option_from_env(int opt) {
   static const char* const names[kNumOptions] = {
       nullptr, "AWQ_FORCE_PATH", "AWQ_DECODE_STEPS", "AWQ_DECODE_GATHER_MAX_M",
-      "AWQ_PREFILL_BM", "AWQ_PREFILL_BN", "AWQ_PREFILL_SPLITS"};
+      "AWQ_PREFILL_BM", "AWQ_PREFILL_BN", "AWQ_PREFILL_SPLITS", "AWQ_DECODE_WAVES"};
   const char* s = getenv(names[opt]);
   if (!s || !*s) return kOptAuto;
   if (opt == AWQ_OPT_FORCE_PATH) {
@@ -206,8 +208,14 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
   if (path == AWQ_PATH_DECODE) {
     pl.n_tiles = static_cast<int>(ceil_div(p.N, kDecodeCols));
     pl.decode_lds = (p.N % 32 == 0);
+    // Eight waves per work-group only where its exchange needs no more than
+    // the column threads (the atomic exchange, M <= 4).
+    pl.decode_waves = 4;
+    if (pl.decode_lds && p.M <= kDecodeAtomicMaxM && override_or_zero(AWQ_OPT_DECODE_WAVES) == 8)
+      pl.decode_waves = 8;
+    const int waves = pl.decode_waves;
     int steps = override_or_zero(AWQ_OPT_DECODE_STEPS);
-    if (steps != 0 && decode_splits(p, pl.decode_lds, steps) > kDecodeMaxSplits) steps = 0;
+    if (steps != 0 && decode_splits(p, pl.decode_lds, steps, waves) > kDecodeMaxSplits) steps = 0;
     if (steps == 0) {
       // The largest step count whose rows stay in one quantisation group and
       // that still gives enough work-groups; failing that, the largest that
@@ -219,7 +227,7 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
       int single_enough = 0, enough = 0, most = 0;
       for (int s = 4; s >= 1; s /= 2) {
         const bool single = p.G == 1 || p.g % (kDecodeRowsPerStep * s) == 0;
-        const int64_t splits = decode_splits(p, pl.decode_lds, s);
+        const int64_t splits = decode_splits(p, pl.decode_lds, s, waves);
         if (splits > kDecodeMaxSplits) break;
         most = s;
         if (pl.n_tiles * splits >= target) {
@@ -229,8 +237,10 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
       }
       steps = single_enough ? single_enough : (enough ? enough : (most ? most : 8));
     }
+    // Eight waves of eight steps would need 272 KiB of LDS: four waves then.
+    if (pl.decode_waves == 8 && steps == 8) pl.decode_waves = 4;
     pl.steps = steps;
-    pl.splits = static_cast<int>(decode_splits(p, pl.decode_lds, steps));
+    pl.splits = static_cast<int>(decode_splits(p, pl.decode_lds, steps, pl.decode_waves));
     if (pl.splits > 1)
       pl.ws_bytes = kTicketRegionBytes + kAtomicRegionBytes +
                     static_cast<size_t>(pl.splits) * p.M * p.N * sizeof(float);

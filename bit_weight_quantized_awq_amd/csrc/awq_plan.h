@@ -68,6 +68,7 @@ struct Plan {
   int group_shift;    // prefill: log2(group size), or 31 for a single group
   int prefill_bn;     // prefill: tile width (kPrefillBN or kPrefillWideBN)
   int prefill_bm;     // prefill: tile height (64, 128 or kPrefillBM)
+  int decode_waves;   // decode, LDS variant: waves along K per work-group (4 or 8)
 };
 
 // Checks of the page's WQLinear construction (K % g == 0, N % 8 == 0, the -1

@@ -81,7 +81,9 @@ enum awq_option {
                                       forward gathers x inside the decode kernel */
   AWQ_OPT_PREFILL_BM = 4,          /* 64, 128 or 256: prefill tile rows */
   AWQ_OPT_PREFILL_BN = 5,          /* 128 or 192: prefill tile columns */
-  AWQ_OPT_PREFILL_SPLITS = 6       /* 1..8: prefill work-groups along K per tile */
+  AWQ_OPT_PREFILL_SPLITS = 6,      /* 1..8: prefill work-groups along K per tile */
+  AWQ_OPT_DECODE_WAVES = 7         /* 4 or 8: waves along K per decode work-group
+                                      (8 only for batches of at most 4 rows) */
 };
 #define AWQ_OPT_AUTO (-1)          /* the planner's own choice */
 
@@ -100,7 +102,8 @@ const char* awq_status_string(int status);
  * prefill | generic; any other text makes every awq_gemm and awq_gemm_plan
  * call fail with AWQ_ERROR_INVALID_VALUE until the option is set),
  * AWQ_DECODE_STEPS, AWQ_DECODE_GATHER_MAX_M, AWQ_PREFILL_BM,
- * AWQ_PREFILL_BN, AWQ_PREFILL_SPLITS (numbers; unusable ones are ignored).
+ * AWQ_PREFILL_BN, AWQ_PREFILL_SPLITS, AWQ_DECODE_WAVES (numbers; unusable
+ * ones are ignored).
  * No call reads the environment after that.  Host only. */
 int awq_set_option(int option, int64_t value);
 

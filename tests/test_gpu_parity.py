@@ -550,3 +550,23 @@ def test_dense_gemv_exact_cases():
     y0 = awq.dense_gemv(torch.zeros((0, K), dtype=torch.float16, device=DEV),
                         torch.from_numpy(w).to(DEV))
     assert y0.shape == (0, N)
+
+
+@pytest.mark.parametrize("M,K,N,g,steps", [(1, 8192, 7168, 128, 2), (3, 8192, 1280, 128, 1),
+                                           (4, 14336, 4096, -1, 4), (2, 4096, 2048, 32, 2)])
+def test_decode_eight_waves(M, K, N, g, steps):
+    """The decode work-group of eight waves along K (decode_waves=8, the
+    atomic exchange's batches) against the oracle, and one-hot rows exact."""
+    say(f"decode eight waves M={M} K={K} N={N} g={g} steps={steps}")
+    p = awq_inputs.make_inputs(M, K, N, g, seed=M + K + N + steps, bias=True)
+    d = to_dev(p)
+    opts = {"decode_waves": 8, "decode_steps": steps}
+    y = run_gemm(d, path="decode", opts=opts)
+    ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
+    assert_within_tol(y, ref, f"eight waves M={M} K={K} N={N}")
+    w = oracle.dequant(p["qweight"], p["qzeros"], p["scales"], g)
+    ks = np.random.default_rng(M).choice(K, M, replace=False)
+    x = np.zeros((M, K), dtype=np.float16)
+    x[np.arange(M), ks] = 1.0
+    y1 = run_gemm(to_dev(dict(p, x=x, bias=None)), path="decode", opts=opts)
+    np.testing.assert_array_equal(y1.view(np.uint16), w[ks].view(np.uint16))

@@ -227,9 +227,9 @@ def test_option_values_checked():
     for opt, bad in [(binding.AWQ_OPT_FORCE_PATH, 4), (binding.AWQ_OPT_FORCE_PATH, 0),
                      (binding.AWQ_OPT_DECODE_STEPS, 3), (binding.AWQ_OPT_DECODE_GATHER_MAX_M, 17),
                      (binding.AWQ_OPT_PREFILL_BM, 96), (binding.AWQ_OPT_PREFILL_BN, 64),
-                     (binding.AWQ_OPT_PREFILL_SPLITS, 9), (0, 1), (7, 1)]:
+                     (binding.AWQ_OPT_PREFILL_SPLITS, 9), (binding.AWQ_OPT_DECODE_WAVES, 6), (0, 1), (8, 1)]:
         assert lib.awq_set_option(opt, bad) == binding.AWQ_ERROR_INVALID_VALUE, (opt, bad)
-    assert lib.awq_get_option(7, None) == binding.AWQ_ERROR_INVALID_VALUE
+    assert lib.awq_get_option(8, None) == binding.AWQ_ERROR_INVALID_VALUE
     assert lib.awq_get_option(binding.AWQ_OPT_PREFILL_BM, None) == binding.AWQ_ERROR_INVALID_VALUE
     with awq.options(prefill_bm=64, prefill_splits=3):
         assert awq.get_option("prefill_bm") == 64
@@ -549,3 +549,32 @@ def test_noalloc_host_checks():
     assert "scratch" in awq.status_string(binding.AWQ_ERROR_SCRATCH)
     with awq.options(force_path="decode"):
         assert _noalloc(M=64, K=4096, N=4096, g=128) == binding.AWQ_ERROR_INVALID_VALUE
+
+
+def test_workspace_need_follows_overrides():
+    """An override that changes the split count changes the workspace the
+    binding sizes for a shape (its per-shape memory is cleared)."""
+    M, K, N, g = 1, 8192, 7168, 128
+    base = binding._gemm_workspace_need(M, K, N, g)
+    with awq.options(decode_steps=2):
+        more = binding._gemm_workspace_need(M, K, N, g)
+        assert more == awq.gemm_workspace_size(M, K, N, g) > base
+    assert binding._gemm_workspace_need(M, K, N, g) == base
+
+
+def test_eight_wave_decode_plan():
+    """decode_waves=8 halves the split count where it applies (the LDS
+    variant, M <= 4) and never pairs with eight steps per wave."""
+    K, N, g = 8192, 7168, 128
+    with awq.options(decode_waves=8, decode_steps=2):
+        _, ws8 = awq.gemm_plan(1, K, N, g)
+    with awq.options(decode_steps=2):
+        _, ws4 = awq.gemm_plan(1, K, N, g)
+    fixed = 65536 + 4 * 65536 * 16
+    assert (ws4 - fixed) == 2 * (ws8 - fixed) == 32 * N * 4
+    with awq.options(decode_waves=8, decode_steps=8):
+        _, ws = awq.gemm_plan(1, K, N, g)
+    assert ws - fixed == (K // (4 * 32 * 8)) * N * 4
+    with awq.options(decode_waves=8):
+        _, a = awq.gemm_plan(8, K, N, g)      # ticket exchange: four waves
+    assert a == awq.gemm_plan(8, K, N, g)[1]
