@@ -30,11 +30,13 @@ AWQ_OPT_PREFILL_BM = 4
 AWQ_OPT_PREFILL_BN = 5
 AWQ_OPT_PREFILL_SPLITS = 6
 AWQ_OPT_DECODE_WAVES = 7
+AWQ_OPT_PREFILL_PACKED = 8
 AWQ_OPT_AUTO = -1
 OPTIONS = {"force_path": AWQ_OPT_FORCE_PATH, "decode_steps": AWQ_OPT_DECODE_STEPS,
            "decode_gather_max_m": AWQ_OPT_DECODE_GATHER_MAX_M,
            "prefill_bm": AWQ_OPT_PREFILL_BM, "prefill_bn": AWQ_OPT_PREFILL_BN,
-           "prefill_splits": AWQ_OPT_PREFILL_SPLITS, "decode_waves": AWQ_OPT_DECODE_WAVES}
+           "prefill_splits": AWQ_OPT_PREFILL_SPLITS, "decode_waves": AWQ_OPT_DECODE_WAVES,
+           "prefill_packed": AWQ_OPT_PREFILL_PACKED}
 
 AWQ_PATH_DECODE = 1
 AWQ_PATH_PREFILL = 2

@@ -119,6 +119,11 @@ int run_gemm(const Problem& p, const void* x, const void* qweight, const void* q
                              fused_gather ? static_cast<int>(Kx) : iK, s);
       break;
     case AWQ_PATH_PREFILL:
+      if (pl.prefill_packed) {
+        e = awq::launch_prefill_packed(xh, qw, qz, sc, bh, yh, iM, iK, iN, pl.group_shift,
+                                       pl.prefill_bn, pl.packed_wm, pl.m_tiles, pl.n_tiles, s);
+        break;
+      }
       e = awq::launch_prefill(xh, qw, qz, sc, bh, yh, iM, iK, iN, pl.group_shift, pl.prefill_bm,
                               pl.prefill_bn, pl.m_tiles, pl.n_tiles, pl.splits, pl.steps,
                               workspace, s);

@@ -116,6 +116,11 @@ hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint
                           int M, int K, int N, int group_shift, int bm, int bn,
                           int m_tiles, int n_tiles, int splits, int ksteps, void* workspace,
                           hipStream_t stream);
+hipError_t launch_prefill_packed(const _Float16* x, const uint32_t* qweight,
+                                 const uint32_t* qzeros, const _Float16* scales,
+                                 const _Float16* bias, _Float16* y, int M, int K, int N,
+                                 int group_shift, int bn, int wm, int m_tiles, int n_tiles,
+                                 hipStream_t stream);
 hipError_t launch_dense_gemv(const _Float16* x, const _Float16* w, const _Float16* bias,
                              _Float16* y, int M, int K, int N, hipStream_t stream);
 }  // namespace awq

@@ -125,7 +125,7 @@ bool prefill_supported(const Problem& p, const Alignment& al) {
 // kOptInvalid marks an unrecognised AWQ_FORCE_PATH, which fails every plan.
 namespace {
 constexpr int kOptInvalid = -2;
-constexpr int kNumOptions = AWQ_OPT_DECODE_WAVES + 1;
+constexpr int kNumOptions = AWQ_OPT_PREFILL_PACKED + 1;
 
 bool option_value_ok(int opt, int64_t v) {
   if (v == kOptAuto) return true;
@@ -135,9 +135,10 @@ bool option_value_ok(int opt, int64_t v) {
     case AWQ_OPT_DECODE_STEPS: return v == 1 || v == 2 || v == 4 || v == 8;
     case AWQ_OPT_DECODE_GATHER_MAX_M: return v >= 0 && v <= kDecodeMaxM;
     case AWQ_OPT_PREFILL_BM: return v == kPrefillMinBM || v == 2 * kPrefillMinBM || v == kPrefillBM;
-    case AWQ_OPT_PREFILL_BN: return v == kPrefillBN || v == kPrefillWideBN;
+    case AWQ_OPT_PREFILL_BN: return v == kPrefillBN || v == kPrefillWideBN || v == kPackedBN;
     case AWQ_OPT_PREFILL_SPLITS: return v >= 1 && v <= kPrefillMaxSplits;
     case AWQ_OPT_DECODE_WAVES: return v == 4 || v == 8;
+    case AWQ_OPT_PREFILL_PACKED: return v >= 0 && v <= 3;
     default: return false;
   }
 }
@@ -145,7 +146,7 @@ bool option_value_ok(int opt, int64_t v) {
 int option_from_env(int opt) {
   static const char* const names[kNumOptions] = {
       nullptr, "AWQ_FORCE_PATH", "AWQ_DECODE_STEPS", "AWQ_DECODE_GATHER_MAX_M",
-      "AWQ_PREFILL_BM", "AWQ_PREFILL_BN", "AWQ_PREFILL_SPLITS", "AWQ_DECODE_WAVES"};
+      "AWQ_PREFILL_BM", "AWQ_PREFILL_BN", "AWQ_PREFILL_SPLITS", "AWQ_DECODE_WAVES", "AWQ_PREFILL_PACKED"};
   const char* s = getenv(names[opt]);
   if (!s || !*s) return kOptAuto;
   if (opt == AWQ_OPT_FORCE_PATH) {
@@ -245,6 +246,43 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
       pl.ws_bytes = kTicketRegionBytes + kAtomicRegionBytes +
                     static_cast<size_t>(pl.splits) * p.M * p.N * sizeof(float);
   } else if (path == AWQ_PATH_PREFILL) {
+    // The packed-weight tile where it applies and fills the CUs without a
+    // split; its width is the one whose rounds of work-groups over the CUs
+    // cost less (rounds x columns per tile).
+    const int packed_opt = option(AWQ_OPT_PREFILL_PACKED);
+    const int64_t m_tiles_p = ceil_div(p.M, kPackedBM);
+    const int64_t t256 = m_tiles_p * ceil_div(p.N, kPackedBN);
+    const int64_t t192 = m_tiles_p * ceil_div(p.N, kPackedNarrowBN);
+    // Automatic: where it applies and its tiles fill the CUs; forced (1):
+    // wherever it applies; 0: never.
+    const bool packed_fits = p.M > 2 * kPrefillMinBM && p.K % kPrefillBK == 0 &&
+                             p.N % 32 == 0 && al.qweight && (p.G == 1 || p.g % kPrefillBK == 0) &&
+                             override_or_zero(AWQ_OPT_PREFILL_SPLITS) <= 1 &&
+                             override_or_zero(AWQ_OPT_PREFILL_BM) == 0;
+    const bool packed_ok = packed_fits && (packed_opt >= 1 || (packed_opt == kOptAuto &&
+                                                               kPackedAuto &&
+                                                               t192 >= kPrefillTargetWGs));
+    if (packed_ok) {
+      const int64_t c256 = ceil_div(t256, kPrefillTargetWGs) * kPackedBN;
+      const int64_t c192 = ceil_div(t192, kPrefillTargetWGs) * kPackedNarrowBN;
+      int bn = c192 < c256 ? kPackedNarrowBN : kPackedBN;
+      const int o = override_or_zero(AWQ_OPT_PREFILL_BN);
+      if (o == kPackedBN || o == kPackedNarrowBN) bn = o;
+      pl.prefill_packed = true;
+      // Waves along M: one (each wave all 256 rows of 64 columns) for the
+      // 256-column tile, two for the 192-column one; option value 2 takes two
+      // for either (tuning).
+      pl.packed_wm = bn == kPackedNarrowBN ? 2 : (packed_opt >= 2 ? packed_opt : 1);
+      pl.prefill_bm = kPackedBM;
+      pl.prefill_bn = bn;
+      pl.m_tiles = static_cast<int>(m_tiles_p);
+      pl.n_tiles = static_cast<int>(ceil_div(p.N, bn));
+      pl.group_shift = p.G == 1 ? 31 : log2_exact(p.g);
+      pl.splits = 1;
+      pl.steps = static_cast<int>(p.K / kPrefillBK);
+      *out = pl;
+      return AWQ_SUCCESS;
+    }
     pl.prefill_bm = p.M <= kPrefillMinBM ? kPrefillMinBM
                                          : (p.M <= 2 * kPrefillMinBM ? 2 * kPrefillMinBM : kPrefillBM);
     if (const int o = override_or_zero(AWQ_OPT_PREFILL_BM)) pl.prefill_bm = o;
@@ -259,7 +297,8 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
                      r_wide * 6 < r_narrow * 5)
                         ? kPrefillWideBN
                         : kPrefillBN;
-    if (const int o = override_or_zero(AWQ_OPT_PREFILL_BN)) pl.prefill_bn = o;
+    if (const int o = override_or_zero(AWQ_OPT_PREFILL_BN); o == kPrefillBN || o == kPrefillWideBN)
+      pl.prefill_bn = o;
     if (pl.prefill_bm != kPrefillBM) pl.prefill_bn = kPrefillBN;   // 192 needs 256 rows
     pl.n_tiles = static_cast<int>(ceil_div(p.N, pl.prefill_bn));
     pl.group_shift = p.G == 1 ? 31 : log2_exact(p.g);

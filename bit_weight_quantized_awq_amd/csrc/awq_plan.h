@@ -50,6 +50,14 @@ constexpr int kPrefillBK = 64;
 constexpr int kPrefillTargetWGs = 256;
 constexpr int kPrefillMaxSplits = 8;
 constexpr int kPrefillMinSplitSteps = 8;
+// Packed-weight prefill tile (256 rows x 256 or 192 columns, packed words
+// staged in LDS, dequantised by the matrix-core waves): K % 64 == 0,
+// N % 32 == 0, qweight 16-byte aligned, groups of a multiple of 64 rows (or
+// one group), and at least kPrefillTargetWGs tiles (it does not split K).
+constexpr int kPackedBM = 256;
+constexpr int kPackedBN = 256;
+constexpr int kPackedNarrowBN = 192;
+constexpr bool kPackedAuto = false;   // chosen automatically (else only when forced)
 
 struct Problem {
   int64_t M, K, N;
@@ -69,6 +77,8 @@ struct Plan {
   int prefill_bn;     // prefill: tile width (kPrefillBN or kPrefillWideBN)
   int prefill_bm;     // prefill: tile height (64, 128 or kPrefillBM)
   int decode_waves;   // decode, LDS variant: waves along K per work-group (4 or 8)
+  bool prefill_packed;  // prefill: the packed-weight 256-row tile (one split)
+  int packed_wm;        // packed tile: waves along M (1 or 2)
 };
 
 // Checks of the page's WQLinear construction (K % g == 0, N % 8 == 0, the -1

@@ -827,7 +827,401 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float* __rest
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Packed-weight prefill tile: 256 rows x BN columns (BN = 256 or 192), four
+// waves, no producer waves.  The dequantised weight tile dominates the LDS
+// traffic of the tile above (written once, read by two waves), so here the
+// packed words themselves are staged -- a quarter of the bytes -- and each
+// wave dequantises the operands it multiplies.
+//
+// * Wave arrangements (WAVES waves, WM along M): four waves of 256 rows x
+//   64 columns (WM = 1: each dequantised weight fragment feeds eight MFMAs,
+//   the dequantisation work is about a quarter of the matrix-core time), four
+//   of 128 x BN/2 (WM = 2, the 192-column tile), or eight of 128 x 64 (two
+//   waves per SIMD, each weight dequantised by two waves).  Accumulators:
+//   256 (four waves) or 128 (eight) fp32 per lane.
+// * A 3-slot ring of K steps (64 k each), filled two steps ahead by 16-byte
+//   direct-to-LDS copies, the same eleven per wave per step: the x tile
+//   (256 rows of 128 bytes, chunks XOR-swizzled by (row / 2) % 8 as above),
+//   the packed rows (BN / 2 bytes per k-row, eight k-rows per KiB; the
+//   16-byte chunks of row r rotated by r / 2 (BN = 256) or r / 8 (BN = 192),
+//   which keeps the transposing reads below at most two-way bank conflicts)
+//   and the zero words and scales of the step's group (group size a
+//   multiple of 64, or one group; two waves copy each, the same bytes).
+// * The weight operand is read with the 4-bit transposing LDS read: the 16
+//   lanes of a group point at 16 consecutive k-rows of one 16-column unit,
+//   and lane i receives column i's 16 nibbles -- 16 consecutive k of its
+//   column, the operand of two MFMAs.  Lane halves cover k-rows 0-15 and
+//   16-31 of a 32-row pair, so MFMA e of pair p contracts k
+//   32p + 16h + 8e + (0..7) (h = lane / 32), and x is read with the same
+//   k order.
+// * Dequantisation: a byte shuffle places nibbles 2b and 2b+1 of the word
+//   (byte b of w and of w >> 4) in the two float16 halves, OR-ed into 1024.0
+//   (1024 + q, exact); a packed add of -(1024 + z) gives q - z exactly and a
+//   packed multiply by s rounds once: float16_RNE((q - z) * s), the value
+//   awq_dequant writes.
+// * One split only (the plan sends problems with fewer tiles than CUs to the
+//   split tile above).  Epilogue staged through LDS: float16(acc + bias)
+//   written as a row-major tile, copied out with 16-byte stores.
+// * Measured against the tile above (same box, same process): level at
+//   M = 4096, K = 14336, N = 4096 (444-448 us against 438-441 us for every
+//   arrangement) and slower at M = 2048, K = 4096, N = 12288 (241-247 us
+//   against 217-218 us), so the planner takes it only when asked
+//   (AWQ_OPT_PREFILL_PACKED).
+namespace pk {
+constexpr int kBM = 256;
+// WM waves along M (4 / WM along N): WM = 1 gives each wave all 256 rows
+// and 64 columns (every dequantised fragment feeds 8 MFMAs); WM = 2 gives
+// 128 rows and BN / 2 columns.
+template <int BN, int WM, int WAVES = 4>
+struct L {
+  static_assert(WAVES == 4 || WAVES == 8, "four or eight waves");
+  static_assert((BN == 256 && (WAVES == 4 || WM == 2)) || (BN == 192 && WM == 2 && WAVES == 4),
+                "packed tile shape");
+  static_assert(WM == 1 || WM == 2, "waves along M");
+  static constexpr int WN = WAVES / WM;
+  static constexpr int XPW = 32 / WAVES;        // x copies per wave per step
+  static constexpr int WPW = 8 / WAVES;         // packed-row copies per wave per step
+  static constexpr int kLoads = XPW + WPW + 1;  // loads per wave per step
+  static constexpr int NB = BN / WN / 32;       // 32-column blocks per wave
+  static constexpr int MI = 8 / WM;             // 32-row blocks per wave
+  static constexpr int WRow = BN / 2;           // packed bytes per k-row
+  static constexpr int WChunks = WRow / 16;     // 16-byte chunks per packed row: 8 or 6
+  static constexpr int XTile = kBM * BK * 2;    // 32 KiB
+  static constexpr int WTile = BK / 8 * 1024;   // 8 k-rows per KiB (BN = 192 leaves gaps)
+  static constexpr int ZOff = XTile + WTile;    // zero words (1 KiB area)
+  static constexpr int SOff = ZOff + 1024;      // scales (1 KiB area)
+  static constexpr int Slot = SOff + 1024;
+  static constexpr int S = 3;                   // copies run S - 1 steps ahead
+  static constexpr int OutPitch = BN * 2 + 16;  // staged output row, bytes
+  static constexpr int Ring = S * Slot;
+  static constexpr int Lds = Ring > kBM * OutPitch ? Ring : kBM * OutPitch;
+};
+static_assert(L<256, 1>::Lds <= 160 * 1024 && L<192, 2>::Lds <= 160 * 1024 &&
+                  L<256, 2, 8>::Lds <= 160 * 1024,
+              "LDS budget");
+
+// Physical 16-byte chunk of logical chunk c in packed k-row r (see above).
+template <int BN>
+__device__ __forceinline__ int w_chunk(int r, int c) {
+  if constexpr (BN == 256) return (c + (r >> 1)) & 7;
+  else return (c + (r >> 3)) % 6;
+}
+// Logical chunk held by physical chunk pc of k-row r (the inverse).
+template <int BN>
+__device__ __forceinline__ int w_logical(int r, int pc) {
+  if constexpr (BN == 256) return (pc - (r >> 1)) & 7;
+  else return (pc + 6 - (r >> 3) % 6) % 6;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+// Eight k of one column from a word of nibbles (k = 2b: low nibble of byte
+// b, k = 2b + 1: its high nibble), dequantised with zero pair zn =
+// -(1024 + z) and scale pair s2.
+__device__ __forceinline__ half8_t dequant8(uint32_t d, half2_t zn, half2_t s2) {
+  const uint32_t ds = d >> 4;
+  half8_t out;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t sel = 0x0C000C00u | (static_cast<uint32_t>(4 + b) << 16) | b;
+    const half2_t h = as_h2(magic_pair(__builtin_amdgcn_perm(ds, d, sel), 0));
+    const half2_t w = (h + zn) * s2;
+    out[2 * b] = w[0];
+    out[2 * b + 1] = w[1];
+  }
+  return out;
+}
+}  // namespace pk
+
+template <int BN, int WM, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void prefill_packed_kernel(
+    const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
+    const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
+    const _Float16* __restrict__ bias, _Float16* __restrict__ y, int M, int K, int N, int gsh,
+    int n_tiles) {
+  using C = pk::L<BN, WM, WAVES>;
+  constexpr int MI = C::MI, NB = C::NB, S = C::S, WN = C::WN;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  pin_arg(x);
+  pin_arg(qw);
+  pin_arg(qz);
+  pin_arg(sc);
+  pin_arg(bias);
+  pin_arg(y);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int nkt = K / BK;
+  const Tile t = tile_of<pk::kBM, BN>(n_tiles, 1, nkt, nkt);
+  const int NW = N >> 3;
+  const int G = gsh >= 31 ? 1 : (K >> gsh);
+  const v4i rx = raw_rsrc(x, static_cast<uint32_t>(M) * K * 2u);
+  const v4i rq = raw_rsrc(qw, static_cast<uint32_t>(K) * NW * 4u);
+  const v4i rz = raw_rsrc(qz, static_cast<uint32_t>(G) * NW * 4u);
+  const v4i rs = raw_rsrc(sc, static_cast<uint32_t>(G) * N * 2u);
+
+  // x copies: instruction i of this wave covers tile rows 8 * (XPW * wave + i)
+  // .. +7; lane -> row lane / 8, physical chunk lane % 8.  Rows past M are
+  // clamped (they only reach rows that are never stored).
+  uint32_t x_off[C::XPW];
+#pragma unroll
+  for (int i = 0; i < C::XPW; ++i) {
+    const int r = 8 * (C::XPW * wave + i) + (lane >> 3);
+    const int logical = (lane & 7) ^ ((r >> 1) & 7);
+    const int m = min(t.m0 + r, M - 1);
+    x_off[i] = static_cast<uint32_t>(m) * K * 2u + 16u * logical;
+  }
+  // Packed-row copies: instruction i (< WPW) of this wave covers k-rows
+  // 8 * (WPW * wave + i) .. +7 of the step, one KiB of LDS each; lane -> row
+  // lane / WChunks, physical chunk lane % WChunks.  When BN = 192 the lanes
+  // past 8 rows read out of range and write zeros into the gap after them.
+  constexpr int kWLanes = 8 * C::WChunks;
+  uint32_t w_off[C::WPW];
+#pragma unroll
+  for (int i = 0; i < C::WPW; ++i) {
+    const int r = 8 * (C::WPW * wave + i) + lane / C::WChunks;
+    const int logical = pk::w_logical<BN>(r, lane % C::WChunks);
+    w_off[i] = offset_or_oob(lane < kWLanes,
+                             (static_cast<uint32_t>(r) * NW + (t.n0 >> 3)) * 4u + 16u * logical);
+  }
+  // Even waves copy the zero words of the tile's columns, odd waves the
+  // scales (both copies of each write the same bytes; the lanes past them
+  // copy bytes that are never read, zeros past the end of a buffer).  The
+  // choices are wave-uniform selects, so every wave runs the same code.
+  const bool zs_scales = (wave & 1) != 0;
+  const v4i rzs = zs_scales ? rs : rz;
+  const uint32_t zs_off = zs_scales ? (static_cast<uint32_t>(t.n0) * 2u + 16u * lane)
+                                    : (static_cast<uint32_t>(t.n0 >> 3) * 4u + 16u * lane);
+  const uint32_t zs_row = zs_scales ? static_cast<uint32_t>(N) * 2u : static_cast<uint32_t>(NW) * 4u;
+  const uint32_t zs_dst = zs_scales ? C::SOff : C::ZOff;
+  auto copy_step = [&](int s) {   // the copies of K step s (clamped) into slot s % S
+    const int kstep = t.kt0 + min(s, nkt - 1);
+    const uint32_t slot = lds_addr(smem + (s % S) * C::Slot);
+#pragma unroll
+    for (int i = 0; i < C::XPW; ++i)
+      copy_to_lds(rx, x_off[i] + static_cast<uint32_t>(kstep) * (BK * 2), 0u,
+                  __builtin_amdgcn_readfirstlane(slot + 1024u * (C::XPW * wave + i)));
+#pragma unroll
+    for (int i = 0; i < C::WPW; ++i)
+      copy_to_lds(rq, w_off[i] + static_cast<uint32_t>(kstep) * (BK * NW * 4), 0u,
+                  __builtin_amdgcn_readfirstlane(slot + C::XTile +
+                                                 (C::WPW * wave + i) * 1024u));
+    const int grp = gsh >= 31 ? 0 : ((kstep * BK) >> gsh);
+    copy_to_lds(rzs, zs_off + static_cast<uint32_t>(grp) * zs_row, 0u,
+                __builtin_amdgcn_readfirstlane(slot + zs_dst));
+  };
+  // Loads per wave per step: XPW + WPW + 1 (kLoads).
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) copy_step(s);
+
+  floatx16 acc[MI][NB];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  const int half_l = lane >> 5;
+  int a_row[MI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) a_row[mi] = 32 * MI * wm + 32 * mi + (lane & 31);
+  int b_unit[NB], zs_col[NB];
+#pragma unroll
+  for (int ni = 0; ni < NB; ++ni) {
+    b_unit[ni] = 2 * (NB * wn + ni) + ((lane >> 4) & 1);
+    zs_col[ni] = 32 * (NB * wn + ni) + (lane & 31);
+  }
+
+  // Per-lane LDS byte offsets within a slot, computed once: the x operand
+  // of pair kp, MFMA e for row block 0 (row block mi adds 4096 * mi; the
+  // chunk swizzle (row / 2) % 8 is the same for all of the lane's rows), the
+  // weight operand of pair kp, column block ni, and the zero word and scale
+  // of column block ni.
+  const int sw = ((lane & 31) >> 1) & 7;
+  uint32_t a_off[2][2], b_off[2][NB], z_off[NB], z_sh[NB], s_off[NB];
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      a_off[kp][e] = static_cast<uint32_t>((32 * MI * wm + (lane & 31)) * 128 +
+                                           16 * ((4 * kp + 2 * half_l + e) ^ sw));
+    const int brow = 32 * kp + 16 * half_l + (lane & 15);
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni) {
+      const int u = b_unit[ni];
+      b_off[kp][ni] = static_cast<uint32_t>(C::XTile + (brow >> 3) * 1024 + (brow & 7) * C::WRow +
+                                            16 * pk::w_chunk<BN>(brow, u >> 1) + 8 * (u & 1));
+    }
+  }
+#pragma unroll
+  for (int ni = 0; ni < NB; ++ni) {
+    const int c = zs_col[ni];
+    z_off[ni] = static_cast<uint32_t>(C::ZOff + 4 * (c >> 3));
+    z_sh[ni] = static_cast<uint32_t>(4 * (c & 7));
+    s_off[ni] = static_cast<uint32_t>(C::SOff + 2 * c);
+  }
+
+  // Operands of one 32-k pair: x fragments of both MFMAs and the packed
+  // weight words of each column block.
+  struct Ops {
+    half8_t a[MI][2];
+    pk::v2i w[NB];
+  };
+  auto read_ops = [&](int j, int kp, Ops& o) {
+    const char* slot = smem + j * C::Slot;
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni)
+      o.w[ni] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+          (__attribute__((address_space(3))) pk::v2i*)(slot + b_off[kp][ni]));
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        o.a[mi][e] = *reinterpret_cast<const half8_t*>(slot + a_off[kp][e] + 4096 * mi);
+  };
+  half2_t zn[S][NB], s2[S][NB];
+  auto read_zs = [&](int j) {
+    const char* slot = smem + j * C::Slot;
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni) {
+      const uint32_t z = (*reinterpret_cast<const uint32_t*>(slot + z_off[ni]) >> z_sh[ni]) & 0xFu;
+      zn[j][ni] = as_h2(((0xE400u | z) << 16) | 0xE400u | z);
+      const uint32_t sb = *reinterpret_cast<const uint16_t*>(slot + s_off[ni]);
+      s2[j][ni] = as_h2((sb << 16) | sb);
+    }
+  };
+  // Step boundary: step k is in LDS (this wave's copies of it have landed,
+  // and the barrier covers the other waves'), every wave's reads of the
+  // previous slot are done, so that slot takes step k + S - 1.
+  auto step_sync = [&](int k) {
+    pk::wait_vm<(S - 2) * C::kLoads>();
+    __syncthreads();
+    copy_step(k + S - 1);
+  };
+
+  // Step kt sits in slot j = kt % S (static: the loop is unrolled by S).
+  // Its first pair's operands are in set 0 when it starts; the second
+  // pair's are read into set 1 at once, and halfway through the second
+  // pair's MFMAs the next step's boundary (wait, barrier, copies) is passed
+  // and its zero/scale pairs and first operands read into set 0, so the
+  // matrix cores keep queued work while the wave waits.  Units run x-block
+  // major (MFMA e of the pair, then column block ni); each is dequantised
+  // one unit ahead of its MFMAs.
+  constexpr int kUnits = 2 * NB;
+  Ops ops[2];
+  step_sync(0);
+  read_zs(0);
+  read_ops(0, 0, ops[0]);
+  // (The step boundary also runs after the last step: its copies re-read
+  // the last step, its reads go unused; the loop body stays branch-free.)
+  auto step = [&](int kt, int j) {
+    const int jn = (j + 1) % S;
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      Ops& cur = ops[kp];
+      if (kp == 0) read_ops(j, 1, ops[1]);
+      half8_t b = pk::dequant8(static_cast<uint32_t>(cur.w[0][0]), zn[j][0], s2[j][0]);
+#pragma unroll
+      for (int u = 0; u < kUnits; ++u) {
+        const int e = u / NB, ni = u % NB;
+        if (kp == 1 && u == kUnits / 2 && kt + 1 < nkt) {
+          step_sync(kt + 1);
+          read_zs(jn);
+          read_ops(jn, 0, ops[0]);
+        }
+        half8_t bn = b;
+        if (u + 1 < kUnits) {
+          const int e1 = (u + 1) / NB, ni1 = (u + 1) % NB;
+          bn = pk::dequant8(static_cast<uint32_t>(cur.w[ni1][e1]), zn[j][ni1], s2[j][ni1]);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[mi][e], b, acc[mi][ni], 0, 0, 0);
+        b = bn;
+      }
+    }
+  };
+  int kt = 0;
+  for (; kt + S <= nkt; kt += S) {
+    step(kt, 0);
+    step(kt + 1, 1);
+    step(kt + 2, 2);
+  }
+  if (kt < nkt) step(kt, 0);
+  if (kt + 1 < nkt) step(kt + 1, 1);
+  pk::wait_vm<0>();
+
+  // Epilogue: every wave is past its last LDS read; stage float16(acc +
+  // bias) as a row-major 256 x BN tile, then copy it out with 16-byte
+  // stores (y 16-byte aligned) or 2-byte stores.
+  __syncthreads();
+  char* stage = smem;
+#pragma unroll
+  for (int ni = 0; ni < NB; ++ni) {
+    const int lcol = (BN / WN) * wn + 32 * ni + (lane & 31);
+    const int col = t.n0 + lcol;
+    const float bv = (bias && col < N) ? static_cast<float>(bias[col]) : 0.f;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lrow = 32 * MI * wm + 32 * mi + 8 * (r >> 2) + 4 * half_l + (r & 3);
+        *reinterpret_cast<_Float16*>(stage + lrow * C::OutPitch + 2 * lcol) =
+            static_cast<_Float16>(acc[mi][ni][r] + bv);
+      }
+  }
+  __syncthreads();
+  constexpr int kChunksPerRow = BN / 8;
+  const bool y16 = (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+#pragma unroll 4
+  for (int c = tid; c < pk::kBM * kChunksPerRow; c += 64 * WAVES) {
+    const int lrow = c / kChunksPerRow;
+    const int lcol = 8 * (c - lrow * kChunksPerRow);
+    const int row = t.m0 + lrow;
+    const int col = t.n0 + lcol;
+    if (row >= M || col >= N) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + lrow * C::OutPitch + 2 * lcol);
+    _Float16* dst = y + static_cast<size_t>(row) * N + col;
+    if (y16) {
+      *reinterpret_cast<u32x4*>(dst) = v;
+    } else {
+      const half8_t hv = __builtin_bit_cast(half8_t, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) dst[q] = hv[q];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_prefill_packed(const _Float16* x, const uint32_t* qweight,
+                                 const uint32_t* qzeros, const _Float16* scales,
+                                 const _Float16* bias, _Float16* y, int M, int K, int N,
+                                 int group_shift, int bn, int wm, int m_tiles, int n_tiles,
+                                 hipStream_t stream) {
+  if (K % BK != 0) return hipErrorInvalidValue;
+  const dim3 grid(m_tiles * n_tiles);
+  auto go = [&](auto kernel, int lds, int waves) {
+    hipLaunchKernelGGL(kernel, grid, dim3(64 * waves), lds, stream, x, qweight, qzeros, scales,
+                       bias, y, M, K, N, group_shift, n_tiles);
+  };
+  // wm: 1 or 2 waves along M of four; 3: eight waves, two along M.
+  if (bn == 256 && wm == 1) go(prefill_packed_kernel<256, 1, 4>, pk::L<256, 1>::Lds, 4);
+  else if (bn == 256 && wm == 2) go(prefill_packed_kernel<256, 2, 4>, pk::L<256, 2>::Lds, 4);
+  else if (bn == 256 && wm == 3) go(prefill_packed_kernel<256, 2, 8>, pk::L<256, 2, 8>::Lds, 8);
+  else if (bn == 192 && wm == 2) go(prefill_packed_kernel<192, 2, 4>, pk::L<192, 2>::Lds, 4);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                           const _Float16* scales, const _Float16* bias, _Float16* y,

@@ -80,10 +80,14 @@ enum awq_option {
   AWQ_OPT_DECODE_GATHER_MAX_M = 3, /* 0..16: largest batch whose sorted-weight
                                       forward gathers x inside the decode kernel */
   AWQ_OPT_PREFILL_BM = 4,          /* 64, 128 or 256: prefill tile rows */
-  AWQ_OPT_PREFILL_BN = 5,          /* 128 or 192: prefill tile columns */
+  AWQ_OPT_PREFILL_BN = 5,          /* 128, 192 or 256: prefill tile columns
+                                      (256 for the packed-weight tile only) */
   AWQ_OPT_PREFILL_SPLITS = 6,      /* 1..8: prefill work-groups along K per tile */
-  AWQ_OPT_DECODE_WAVES = 7         /* 4 or 8: waves along K per decode work-group
+  AWQ_OPT_DECODE_WAVES = 7,        /* 4 or 8: waves along K per decode work-group
                                       (8 only for batches of at most 4 rows) */
+  AWQ_OPT_PREFILL_PACKED = 8       /* 0: never the packed-weight 256-row prefill
+                                      tile; 1: wherever it applies; 2: the same
+                                      with two waves along M (tuning) */
 };
 #define AWQ_OPT_AUTO (-1)          /* the planner's own choice */
 
@@ -102,8 +106,8 @@ const char* awq_status_string(int status);
  * prefill | generic; any other text makes every awq_gemm and awq_gemm_plan
  * call fail with AWQ_ERROR_INVALID_VALUE until the option is set),
  * AWQ_DECODE_STEPS, AWQ_DECODE_GATHER_MAX_M, AWQ_PREFILL_BM,
- * AWQ_PREFILL_BN, AWQ_PREFILL_SPLITS, AWQ_DECODE_WAVES (numbers; unusable
- * ones are ignored).
+ * AWQ_PREFILL_BN, AWQ_PREFILL_SPLITS, AWQ_DECODE_WAVES, AWQ_PREFILL_PACKED
+ * (numbers; unusable ones are ignored).
  * No call reads the environment after that.  Host only. */
 int awq_set_option(int option, int64_t value);
 

@@ -227,9 +227,9 @@ def test_option_values_checked():
     for opt, bad in [(binding.AWQ_OPT_FORCE_PATH, 4), (binding.AWQ_OPT_FORCE_PATH, 0),
                      (binding.AWQ_OPT_DECODE_STEPS, 3), (binding.AWQ_OPT_DECODE_GATHER_MAX_M, 17),
                      (binding.AWQ_OPT_PREFILL_BM, 96), (binding.AWQ_OPT_PREFILL_BN, 64),
-                     (binding.AWQ_OPT_PREFILL_SPLITS, 9), (binding.AWQ_OPT_DECODE_WAVES, 6), (0, 1), (8, 1)]:
+                     (binding.AWQ_OPT_PREFILL_SPLITS, 9), (binding.AWQ_OPT_DECODE_WAVES, 6), (binding.AWQ_OPT_PREFILL_PACKED, 4), (0, 1), (9, 1)]:
         assert lib.awq_set_option(opt, bad) == binding.AWQ_ERROR_INVALID_VALUE, (opt, bad)
-    assert lib.awq_get_option(8, None) == binding.AWQ_ERROR_INVALID_VALUE
+    assert lib.awq_get_option(9, None) == binding.AWQ_ERROR_INVALID_VALUE
     assert lib.awq_get_option(binding.AWQ_OPT_PREFILL_BM, None) == binding.AWQ_ERROR_INVALID_VALUE
     with awq.options(prefill_bm=64, prefill_splits=3):
         assert awq.get_option("prefill_bm") == 64
