@@ -195,14 +195,15 @@ __device__ __forceinline__ void splitk_atomic(const float (&part)[kDecodeMaxM], 
 // resets the ticket.
 // Final sum of a column tile's partials by the work-group holding the last
 // ticket: thread t covers the four columns 4*(t % 64) .. +3 of the tile and
-// the rows t / 64 + 4*i (i < MQ), reading each (split, row) as one 16-byte
+// the rows t / 64 + RG*i (i < MQ, RG = threads / 64 row groups), reading
+// each (split, row) as one 16-byte
 // load, so a round of BATCH splits moves 16 * BATCH * MQ bytes per thread
 // (the partials of a 16-row tile are 256 KiB: with one float per load the
 // load counter would cap a round at 63 x 4 bytes).  Sums run in split
 // order from zero.  The caller has invalidated this CU's caches (acquire),
 // so plain loads see every split's stores.  Indices past the last split
 // or row are clamped (the loads stay unconditional) and their values dropped.
-template <int BATCH, int MQ>
+template <int BATCH, int MQ, int RG>
 __device__ __forceinline__ void ticket_sum_store(const float* __restrict__ partial,
                                                  const _Float16* __restrict__ bias,
                                                  _Float16* __restrict__ y, int M, int N,
@@ -218,7 +219,7 @@ __device__ __forceinline__ void ticket_sum_store(const float* __restrict__ parti
       const int su = min(sp + u, splits - 1);
 #pragma unroll
       for (int i = 0; i < MQ; ++i) {
-        const int m = min(rq + 4 * i, M - 1);
+        const int m = min(rq + RG * i, M - 1);
         v[u][i] = *reinterpret_cast<const floatx4*>(partial + su * stride +
                                                     static_cast<size_t>(m) * N + n0);
       }
@@ -237,7 +238,7 @@ __device__ __forceinline__ void ticket_sum_store(const float* __restrict__ parti
   }
 #pragma unroll
   for (int i = 0; i < MQ; ++i) {
-    const int m = rq + 4 * i;
+    const int m = rq + RG * i;
     if (m < M) {
       half4_t o;
 #pragma unroll
@@ -247,8 +248,9 @@ __device__ __forceinline__ void ticket_sum_store(const float* __restrict__ parti
   }
 }
 
-// VREGS: 16-byte registers the final sum may hold in flight per thread.
-template <int VREGS>
+// VREGS: 16-byte registers the final sum may hold in flight per thread;
+// WAVES: waves of the work-group (all of them take part in the final sum).
+template <int VREGS, int WAVES = 4>
 __device__ __forceinline__ void splitk_ticket(const float (&part)[kDecodeMaxM], const SplitK& sk,
                                               const _Float16* __restrict__ bias,
                                               _Float16* __restrict__ y, int M, int N, int n,
@@ -278,11 +280,18 @@ __device__ __forceinline__ void splitk_ticket(const float (&part)[kDecodeMaxM], 
     const int n0 = n_tile * kDecodeCols + 4 * (threadIdx.x & 63);
     const int rq = threadIdx.x >> 6;
     if (n0 < N) {
-      switch ((M + 3) >> 2) {
-        case 1: ticket_sum_store<VREGS, 1>(sk.partial, bias, y, M, N, splits, n0, rq); break;
-        case 2: ticket_sum_store<VREGS / 2, 2>(sk.partial, bias, y, M, N, splits, n0, rq); break;
-        case 3: ticket_sum_store<VREGS / 3, 3>(sk.partial, bias, y, M, N, splits, n0, rq); break;
-        default: ticket_sum_store<VREGS / 4, 4>(sk.partial, bias, y, M, N, splits, n0, rq); break;
+      if constexpr (WAVES == 8) {
+        if (M > 8)
+          ticket_sum_store<VREGS / 2, 2, 8>(sk.partial, bias, y, M, N, splits, n0, rq);
+        else
+          ticket_sum_store<VREGS, 1, 8>(sk.partial, bias, y, M, N, splits, n0, rq);
+      } else {
+        switch ((M + 3) >> 2) {
+          case 1: ticket_sum_store<VREGS, 1, 4>(sk.partial, bias, y, M, N, splits, n0, rq); break;
+          case 2: ticket_sum_store<VREGS / 2, 2, 4>(sk.partial, bias, y, M, N, splits, n0, rq); break;
+          case 3: ticket_sum_store<VREGS / 3, 3, 4>(sk.partial, bias, y, M, N, splits, n0, rq); break;
+          default: ticket_sum_store<VREGS / 4, 4, 4>(sk.partial, bias, y, M, N, splits, n0, rq); break;
+        }
       }
     }
   }
@@ -780,22 +789,22 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   }
   __syncthreads();
 
-  // One thread per column of the tile; with eight waves the upper half of
-  // the work-group is done (eight waves run only with the atomic exchange
-  // or one split, neither of which needs the whole work-group).
-  if (WAVES > 4 && tid >= kDecodeCols) return;
+  // One thread per column of the tile holds its partial; with eight waves
+  // the upper half of the work-group only joins the ticket exchange's final
+  // sum.
+  const bool col_thread = WAVES == 4 || tid < kDecodeCols;
   const int n = n_tile * kDecodeCols + tid;
-  const bool nvalid = n < N;
+  const bool nvalid = col_thread && n < N;
   float part[kDecodeMaxM];
-  red_sum<WAVES>(red, Mq, M, tid, part);
+  if (col_thread) red_sum<WAVES>(red, Mq, M, tid, part);
   if (splits == 1) {
     if (nvalid) store_rows(part, bias, y, M, N, n);
     return;
   }
   if (M <= kDecodeAtomicMaxM && N <= kDecodeAtomicMaxN) {
     if (nvalid) splitk_atomic(part, sk, bias, y, M, N, n, split, splits);
-  } else if constexpr (WAVES == 4) {
-    splitk_ticket<32>(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
+  } else {
+    splitk_ticket<32, WAVES>(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
   }
 }
 
@@ -860,8 +869,7 @@ hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint3
                          int M, int K, int N, int g, int G, int steps, int splits,
                          int n_tiles, bool lds_variant, int waves, void* workspace,
                          const int32_t* perm, int Kx, hipStream_t stream) {
-  if (waves != 4 && !(lds_variant && waves == 8 && (splits == 1 || M <= kDecodeAtomicMaxM)))
-    return hipErrorInvalidValue;
+  if (waves != 4 && !(lds_variant && waves == 8)) return hipErrorInvalidValue;
   // Workspace: ticket region, accumulator region ([M][N] accumulators, then
   // [M][N] masks), then [splits][M][N] partials.
   char* ws = static_cast<char*>(workspace);

@@ -209,11 +209,9 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
   if (path == AWQ_PATH_DECODE) {
     pl.n_tiles = static_cast<int>(ceil_div(p.N, kDecodeCols));
     pl.decode_lds = (p.N % 32 == 0);
-    // Eight waves per work-group only where its exchange needs no more than
-    // the column threads (the atomic exchange, M <= 4).
     pl.decode_waves = 4;
-    if (pl.decode_lds && p.M <= kDecodeAtomicMaxM && override_or_zero(AWQ_OPT_DECODE_WAVES) == 8)
-      pl.decode_waves = 8;
+    const int waves_opt = override_or_zero(AWQ_OPT_DECODE_WAVES);
+    if (pl.decode_lds && waves_opt == 8) pl.decode_waves = 8;
     const int waves = pl.decode_waves;
     int steps = override_or_zero(AWQ_OPT_DECODE_STEPS);
     if (steps != 0 && decode_splits(p, pl.decode_lds, steps, waves) > kDecodeMaxSplits) steps = 0;
@@ -238,6 +236,13 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
       }
       steps = single_enough ? single_enough : (enough ? enough : (most ? most : 8));
     }
+    // The ticket exchange's final sum reads every split's partials, one
+    // work-group per column tile: past kDecodeTicketMaxSplits splits of four
+    // waves, eight waves of the same steps halve the splits (K = 14336,
+    // N = 4096, M = 16: 20.2 -> 16.7 us; at 16 splits four waves stay ahead).
+    if (pl.decode_lds && waves_opt == 0 && p.M > kDecodeAtomicMaxM && steps == 4 &&
+        decode_splits(p, true, steps, 4) > kDecodeTicketMaxSplits)
+      pl.decode_waves = 8;
     // Eight waves of eight steps would need 272 KiB of LDS: four waves then.
     if (pl.decode_waves == 8 && steps == 8) pl.decode_waves = 4;
     pl.steps = steps;

@@ -28,6 +28,7 @@ constexpr int kTicketMaxStrideBytes = 256;
 constexpr int kDecodeMaxSplits = 63;
 constexpr int kDecodeAtomicMaxM = 4;
 constexpr int kDecodeGatherMaxM = 4;
+constexpr int kDecodeTicketMaxSplits = 16;   // above: eight waves per work-group
 constexpr int kDecodeAtomicMaxN = 65536;
 constexpr size_t kAtomicRegionBytes = static_cast<size_t>(kDecodeAtomicMaxM) * kDecodeAtomicMaxN * 16;
 

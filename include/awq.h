@@ -83,8 +83,7 @@ enum awq_option {
   AWQ_OPT_PREFILL_BN = 5,          /* 128, 192 or 256: prefill tile columns
                                       (256 for the packed-weight tile only) */
   AWQ_OPT_PREFILL_SPLITS = 6,      /* 1..8: prefill work-groups along K per tile */
-  AWQ_OPT_DECODE_WAVES = 7,        /* 4 or 8: waves along K per decode work-group
-                                      (8 only for batches of at most 4 rows) */
+  AWQ_OPT_DECODE_WAVES = 7,        /* 4 or 8: waves along K per decode work-group */
   AWQ_OPT_PREFILL_PACKED = 8       /* 0: never the packed-weight 256-row prefill
                                       tile; 1: wherever it applies; 2: the same
                                       with two waves along M (tuning) */

@@ -70,7 +70,9 @@ int main() {
                 EXPECT(pl.splits >= 1 && pl.n_tiles * kDecodeCols >= N);
                 EXPECT(pl.decode_lds == (N % 32 == 0));
                 EXPECT(!pl.decode_lds || a.qweight);
-                const int waves_k = pl.decode_lds ? 4 : 2;
+                EXPECT(pl.decode_waves == 4 || (pl.decode_lds && pl.decode_waves == 8));
+                EXPECT(pl.decode_waves == 4 || pl.steps <= 4);
+                const int waves_k = pl.decode_lds ? pl.decode_waves : 2;
                 EXPECT((int64_t)pl.splits * waves_k * kDecodeRowsPerStep * pl.steps >= K);
                 EXPECT((int64_t)(pl.splits - 1) * waves_k * kDecodeRowsPerStep * pl.steps < K);
                 EXPECT(pl.splits <= kDecodeMaxSplits);

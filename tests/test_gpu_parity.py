@@ -553,10 +553,13 @@ def test_dense_gemv_exact_cases():
 
 
 @pytest.mark.parametrize("M,K,N,g,steps", [(1, 8192, 7168, 128, 2), (3, 8192, 1280, 128, 1),
-                                           (4, 14336, 4096, -1, 4), (2, 4096, 2048, 32, 2)])
+                                           (4, 14336, 4096, -1, 4), (2, 4096, 2048, 32, 2),
+                                           (5, 8192, 7168, 128, 4), (8, 4096, 1280, 64, 2),
+                                           (16, 14336, 4096, 128, 4), (13, 8192, 768, -1, 1)])
 def test_decode_eight_waves(M, K, N, g, steps):
-    """The decode work-group of eight waves along K (decode_waves=8, the
-    atomic exchange's batches) against the oracle, and one-hot rows exact."""
+    """The decode work-group of eight waves along K (decode_waves=8; the
+    atomic exchange up to 4 rows, the ticket exchange above) against the
+    oracle, and one-hot rows exact."""
     say(f"decode eight waves M={M} K={K} N={N} g={g} steps={steps}")
     p = awq_inputs.make_inputs(M, K, N, g, seed=M + K + N + steps, bias=True)
     d = to_dev(p)

@@ -564,7 +564,7 @@ def test_workspace_need_follows_overrides():
 
 def test_eight_wave_decode_plan():
     """decode_waves=8 halves the split count where it applies (the LDS
-    variant, M <= 4) and never pairs with eight steps per wave."""
+    variant) and never pairs with eight steps per wave."""
     K, N, g = 8192, 7168, 128
     with awq.options(decode_waves=8, decode_steps=2):
         _, ws8 = awq.gemm_plan(1, K, N, g)
@@ -575,6 +575,18 @@ def test_eight_wave_decode_plan():
     with awq.options(decode_waves=8, decode_steps=8):
         _, ws = awq.gemm_plan(1, K, N, g)
     assert ws - fixed == (K // (4 * 32 * 8)) * N * 4
-    with awq.options(decode_waves=8):
-        _, a = awq.gemm_plan(8, K, N, g)      # ticket exchange: four waves
-    assert a == awq.gemm_plan(8, K, N, g)[1]
+    with awq.options(decode_waves=8, decode_steps=4):
+        _, a = awq.gemm_plan(16, K, N, g)     # the ticket exchange too
+    assert a - fixed == (K // (8 * 32 * 4)) * 16 * N * 4
+
+
+def test_ticket_exchange_takes_eight_waves_past_sixteen_splits():
+    """Batches above four rows whose four-wave plan would have more than 16
+    splits (K = 14336: 28) run eight waves per work-group (14 splits);
+    K = 8192 (16 splits) and the atomic exchange's batches keep four."""
+    fixed = 65536 + 4 * 65536 * 16
+    for M, K, N, splits in [(16, 14336, 4096, 14), (5, 14336, 4096, 14), (16, 8192, 7168, 16),
+                            (1, 14336, 4096, 28), (4, 14336, 4096, 28)]:
+        path, ws = awq.gemm_plan(M, K, N, 128)
+        assert path == binding.AWQ_PATH_DECODE
+        assert ws - fixed == splits * M * N * 4, (M, K, N)
