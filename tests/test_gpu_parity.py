@@ -443,10 +443,11 @@ def test_deterministic_repeats(M):
     p = awq_inputs.make_inputs(M, 4096, 2048, 128, seed=M, bias=True)
     d = to_dev(p)
     first = awq.gemm(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], 128).clone()
-    for _ in range(20):
-        y = awq.gemm(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], 128)
-        assert torch.equal(y.view(torch.int16), first.view(torch.int16))
+    outs = [awq.gemm(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], 128)
+            for _ in range(100)]
     torch.cuda.synchronize()
+    for y in outs:
+        assert torch.equal(y.view(torch.int16), first.view(torch.int16))
 
 
 def test_workspace_reuse_across_shapes():
