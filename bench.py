@@ -339,6 +339,46 @@ def cpu_baseline(p, g, budget_s, sample_rows=None):
     return t, n, blas_thread_count()
 
 
+def sweep_point(torch, awq, dev, name, M, g):
+    """One workload point timed like the headline legs, printed as a JSON
+    line against its binding roof; returns its time per call (ms) and
+    whether it has a bias."""
+    spec = dict(source=name, M=M, group_size=g)
+    steps = 200 if M <= 16 else 50
+    print(f"[sweep] {name} M={M} g={g}", file=sys.stderr, flush=True)
+    r = run_leg(torch, awq, spec, steps, 10, dev)
+    sec = r["ms_per_step"] * 1e-3
+    gbs = r["nbytes"] / sec / 1e9
+    tfs = r["nflops"] / sec / 1e12
+    # The binding roof: whichever takes longer at peak.
+    hbm = r["nbytes"] / HBM_PEAK_GBS >= r["nflops"] / FP16_MFMA_PEAK_TFLOPS / 1e3
+    print(json.dumps({
+        "workload": name, "M": M, "K": r["K"], "N": r["N"], "group_size": g,
+        "bias": r["p"]["bias"] is not None, "kernel": r["path"],
+        "us_per_call": round(r["ms_per_step"] * 1e3, 3),
+        "GB_per_s": round(gbs, 1), "TFLOP_per_s": round(tfs, 2),
+        "bound": "hbm" if hbm else "mfma",
+        "frac": round(gbs / HBM_PEAK_GBS if hbm else tfs / FP16_MFMA_PEAK_TFLOPS, 4),
+        "bytes": r["nbytes"], "flops": r["nflops"], "copies_rotated": r["R"]}),
+        flush=True)
+    out = (r["ms_per_step"], r["K"], r["N"], r["p"]["bias"] is not None)
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
+def points(torch, awq, dev, specs):
+    """The points named on the command line: WORKLOAD:M[,M...][:GROUP_SIZE]."""
+    import awq_inputs
+    for spec in specs:
+        parts = spec.split(":")
+        if len(parts) not in (2, 3) or parts[0] not in awq_inputs.WORKLOADS:
+            raise SystemExit(f"--points: expected WORKLOAD:M[,M...][:GROUP_SIZE], got {spec!r}")
+        g = int(parts[2]) if len(parts) == 3 else awq_inputs.WORKLOADS[parts[0]].group_sizes[0]
+        for M in parts[1].split(","):
+            sweep_point(torch, awq, dev, parts[0], int(M), g)
+
+
 def sweep(torch, awq, dev):
     """Every point of every named workload, timed like the headline legs."""
     import awq_inputs
@@ -348,28 +388,9 @@ def sweep(torch, awq, dev):
             continue                    # launch-bound, a parity case only
         for g in w.group_sizes:
             for M in w.Ms:
-                spec = dict(source=name, M=M, group_size=g)
-                steps = 200 if M <= 16 else 50
-                print(f"[sweep] {name} M={M} g={g}", file=sys.stderr, flush=True)
-                r = run_leg(torch, awq, spec, steps, 10, dev)
+                ms, K, N, has_bias = sweep_point(torch, awq, dev, name, M, g)
                 if g == 128:
-                    fused[(name, M, r["K"], r["N"], r["p"]["bias"] is not None)] = r["ms_per_step"]
-                sec = r["ms_per_step"] * 1e-3
-                gbs = r["nbytes"] / sec / 1e9
-                tfs = r["nflops"] / sec / 1e12
-                # The binding roof: whichever takes longer at peak.
-                hbm = r["nbytes"] / HBM_PEAK_GBS >= r["nflops"] / FP16_MFMA_PEAK_TFLOPS / 1e3
-                print(json.dumps({
-                    "workload": name, "M": M, "K": r["K"], "N": r["N"], "group_size": g,
-                    "bias": r["p"]["bias"] is not None, "kernel": r["path"],
-                    "us_per_call": round(r["ms_per_step"] * 1e3, 3),
-                    "GB_per_s": round(gbs, 1), "TFLOP_per_s": round(tfs, 2),
-                    "bound": "hbm" if hbm else "mfma",
-                    "frac": round(gbs / HBM_PEAK_GBS if hbm else tfs / FP16_MFMA_PEAK_TFLOPS, 4),
-                    "bytes": r["nbytes"], "flops": r["nflops"], "copies_rotated": r["R"]}),
-                    flush=True)
-                del r
-                torch.cuda.empty_cache()
+                    fused[(name, M, K, N, has_bias)] = ms
     # awq_dequant on its own (HBM-bound: packed words, zeros and scales in,
     # the float16 weight out), at the two large weight shapes (W = 117 MB,
     # written with ordinary stores) and at one whose W (470 MB) is larger
@@ -596,6 +617,9 @@ def main():
                     help="skip the per-config points and the same-box references")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--points", nargs="+", metavar="WORKLOAD:M[,M...][:G]",
+                    help="instead of the headline line, time only these workload points "
+                         "(one JSON line each, like --sweep)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line, print one JSON line per point of "
                          "every named workload (all batch sizes and group sizes), each "
@@ -618,6 +642,9 @@ def main():
     awq.lib()
     if args.sweep:
         sweep(torch, awq, dev)
+        return
+    if args.points:
+        points(torch, awq, dev, args.points)
         return
     legs = args.legs.split(",")
     res = {}
