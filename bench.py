@@ -87,7 +87,23 @@ def make_copies(torch, p, R, dev):
     return copies
 
 
+# Timed work per point when the step count is left to run_leg: a graph
+# replay of a few milliseconds reads 10-18 % slow (the clocks are still
+# rising after the set-up pauses: K = 4096, N = 12288, M = 2048 took 206-217
+# us per call over 20 calls, 181-184 us over 100-500, on one box), so every
+# timed region lasts about this long.
+TIMED_SECONDS = 0.05
+
+
+def auto_steps(nbytes, nflops):
+    """Steps for about TIMED_SECONDS of timed work: the call's time
+    estimated from half the HBM and matrix-core peaks, 50 to 2000 steps."""
+    est = max(nbytes / (HBM_PEAK_GBS * 0.5e9), nflops / (FP16_MFMA_PEAK_TFLOPS * 0.4e12), 5e-6)
+    return int(min(2000, max(50, -(-TIMED_SECONDS // est))))
+
+
 def run_leg(torch, awq, spec, steps, warmup, dev, events=True, eager=True):
+    """One workload point timed (steps=None: auto_steps)."""
     import awq_inputs
     p = awq_inputs.workload_inputs(spec["source"], spec["M"], spec["group_size"])
     M = spec["M"]
@@ -95,6 +111,8 @@ def run_leg(torch, awq, spec, steps, warmup, dev, events=True, eager=True):
     K, N, G = problem_dims(p)
     nbytes = algorithmic_bytes(M, K, N, G, p["bias"] is not None)
     nflops = 2 * M * N * K
+    if steps is None:
+        steps = auto_steps(nbytes, nflops)
     act = spec.get("gidx")   # None, "act_order" or "uneven"
     if act:
         # The same weight under a row-to-group map: g_idx (K int32) is read
@@ -180,7 +198,7 @@ def run_leg(torch, awq, spec, steps, warmup, dev, events=True, eager=True):
 
     sorted_rows = copies[0]["w"].rows if act else K
     return dict(p=p, M=M, K=K, N=N, G=G, g=g, nbytes=nbytes, nflops=nflops, R=R,
-                sorted_rows=sorted_rows,
+                sorted_rows=sorted_rows, steps=steps,
                 path=awq.PATH_NAMES[path], ms_per_step=ms_per_step, kern_avg_ms=kern_avg_ms,
                 kern_min_ms=min(kern_ms), eager_ms=eager_ms, ws_bytes=ws_bytes)
 
@@ -205,18 +223,19 @@ def binding_roof(nbytes, nflops, sec):
     return ("hbm", gbs / HBM_PEAK_GBS) if hbm else ("mfma", tfs / FP16_MFMA_PEAK_TFLOPS)
 
 
-def config_points(torch, awq, dev, steps_small, steps_large):
+def config_points(torch, awq, dev):
     """Each seeded point timed like the headline legs (graph replay, weights
-    rotated past the last-level cache), against its binding roof."""
+    rotated past the last-level cache, about TIMED_SECONDS of timed work),
+    against its binding roof."""
     out = []
     for label, name, M, g in CONFIG_POINTS:
         print(f"[bench] config {label} {name} M={M} g={g}", file=sys.stderr, flush=True)
-        r = run_leg(torch, awq, dict(source=name, M=M, group_size=g),
-                    steps_small if M <= 16 else steps_large, 5, dev, events=False, eager=False)
+        r = run_leg(torch, awq, dict(source=name, M=M, group_size=g), None, 5, dev,
+                    events=False, eager=False)
         sec = r["ms_per_step"] * 1e-3
         bound, frac = binding_roof(r["nbytes"], r["nflops"], sec)
         out.append({"config": label, "M": M, "K": r["K"], "N": r["N"], "g": g,
-                    "kernel": r["path"], "us": round(sec * 1e6, 3),
+                    "kernel": r["path"], "us": round(sec * 1e6, 3), "steps": r["steps"],
                     "GB_per_s": round(r["nbytes"] / sec / 1e9, 1),
                     "TFLOP_per_s": round(r["nflops"] / sec / 1e12, 2),
                     "bound": bound, "frac": round(frac, 4)})
@@ -282,15 +301,17 @@ def same_box_references(torch, dev, decode_bytes):
     bufs = [torch.randint(-2**31, 2**31 - 1, (n,), generator=gen, dtype=torch.int32).to(dev)
             for _ in range(R)]
     dst = [torch.empty_like(b) for b in bufs]
-    read_us = graph_time_us(torch, read_stream_fn(torch, bufs, dev), 100, dev)
-    copy_us = graph_time_us(torch, lambda i: dst[i % R].copy_(bufs[i % R]), 100, dev)
+    read_us = graph_time_us(torch, read_stream_fn(torch, bufs, dev), auto_steps(n * 4, 0), dev)
+    copy_us = graph_time_us(torch, lambda i: dst[i % R].copy_(bufs[i % R]),
+                            auto_steps(2 * n * 4, 0), dev)
     del bufs, dst
     torch.cuda.empty_cache()
     M, K, N = 2048, 4096, 12288
     x = torch.randn((M, K), generator=gen).to(torch.float16).to(dev)
     ws = [(torch.randn((N, K), generator=gen) * 0.02).to(torch.float16).to(dev) for _ in range(2)]
     b = (torch.randn((N,), generator=gen) * 0.1).to(torch.float16).to(dev)
-    lin_us = graph_time_us(torch, lambda i: torch.nn.functional.linear(x, ws[i % 2], b), 20, dev)
+    lin_us = graph_time_us(torch, lambda i: torch.nn.functional.linear(x, ws[i % 2], b),
+                           auto_steps(2 * N * K, 2 * M * N * K), dev)
     del x, ws, b
     torch.cuda.empty_cache()
     return {
@@ -344,9 +365,8 @@ def sweep_point(torch, awq, dev, name, M, g):
     line against its binding roof; returns its time per call (ms) and
     whether it has a bias."""
     spec = dict(source=name, M=M, group_size=g)
-    steps = 200 if M <= 16 else 50
     print(f"[sweep] {name} M={M} g={g}", file=sys.stderr, flush=True)
-    r = run_leg(torch, awq, spec, steps, 10, dev)
+    r = run_leg(torch, awq, spec, None, 10, dev)
     sec = r["ms_per_step"] * 1e-3
     gbs = r["nbytes"] / sec / 1e9
     tfs = r["nflops"] / sec / 1e12
@@ -359,7 +379,8 @@ def sweep_point(torch, awq, dev, name, M, g):
         "GB_per_s": round(gbs, 1), "TFLOP_per_s": round(tfs, 2),
         "bound": "hbm" if hbm else "mfma",
         "frac": round(gbs / HBM_PEAK_GBS if hbm else tfs / FP16_MFMA_PEAK_TFLOPS, 4),
-        "bytes": r["nbytes"], "flops": r["nflops"], "copies_rotated": r["R"]}),
+        "bytes": r["nbytes"], "flops": r["nflops"], "copies_rotated": r["R"],
+        "steps": r["steps"]}),
         flush=True)
     out = (r["ms_per_step"], r["K"], r["N"], r["p"]["bias"] is not None)
     del r
@@ -413,7 +434,7 @@ def sweep(torch, awq, dev):
     for (K, N) in ((8192, 1280), (8192, 7168)):
         d_us = dense_time_us(torch, awq, 1, K, N, dev)
         name = "decode_k8192_n1280" if N == 1280 else "decode_sweep_k8192_n7168"
-        r = run_leg(torch, awq, dict(source=name, M=1, group_size=128), 200, 10, dev)
+        r = run_leg(torch, awq, dict(source=name, M=1, group_size=128), None, 10, dev)
         w4_us = r["ms_per_step"] * 1e3
         nbytes = K * N * 2 + K * 2 + N * 2
         t_cpu, n_cpu = dense_oracle_time(K, N)
@@ -438,7 +459,7 @@ def sweep(torch, awq, dev):
                           ("prefill_qkv_m2048_k4096_n12288", 2048, "uneven")):
         print(f"[sweep] {kind} map {name} M={M}", file=sys.stderr, flush=True)
         spec = dict(source=name, M=M, group_size=128, gidx=kind)
-        r = run_leg(torch, awq, spec, 200 if M <= 16 else 50, 10, dev)
+        r = run_leg(torch, awq, spec, None, 10, dev)
         sec = r["ms_per_step"] * 1e-3
         gbs = r["nbytes"] / sec / 1e9
         tfs = r["nflops"] / sec / 1e12
@@ -505,9 +526,11 @@ def gidx_oracle_time(p, rows):
     return t, n, rows
 
 
-def vendor_gemm_times_us(torch, awq, M, K, N, bias, dev, calls=30):
+def vendor_gemm_times_us(torch, awq, M, K, N, bias, dev, calls=None):
     """Median per-call times of torch's float16 linear on a random (N, K)
     weight, and of awq_dequant (g=128) followed by a float16 matmul."""
+    if calls is None:
+        calls = auto_steps(2 * N * K, 2 * M * N * K)
     gen = torch.Generator(device="cpu").manual_seed(M + K + N)
     x = torch.randn((M, K), generator=gen).to(torch.float16).to(dev)
     ws = [(torch.randn((N, K), generator=gen) * 0.02).to(torch.float16).to(dev) for _ in range(2)]
@@ -544,12 +567,14 @@ def vendor_gemm_times_us(torch, awq, M, K, N, bias, dev, calls=30):
     return out[0], out[1]
 
 
-def dequant_time_us(torch, awq, K, N, dev, calls=100):
+def dequant_time_us(torch, awq, K, N, dev, calls=None):
     """awq_dequant per-call time, packed weights rotated through >= 512 MiB
     (each copy writes its own float16 output)."""
     import awq_inputs
     p = awq_inputs.make_inputs(1, K, N, 128, seed=K + N)
     nbytes = K * N // 2 + K * N * 2
+    if calls is None:
+        calls = auto_steps(nbytes, 0)
     R = max(2, -(-ROTATE_BYTES // nbytes))
     base = {k: torch.from_numpy(p[k]).to(dev) for k in ("qweight", "qzeros", "scales")}
     cps = [{k: v.clone() for k, v in base.items()} for _ in range(R)]
@@ -579,10 +604,12 @@ def dequant_time_us(torch, awq, K, N, dev, calls=100):
     return us
 
 
-def dense_time_us(torch, awq, M, K, N, dev, calls=200):
+def dense_time_us(torch, awq, M, K, N, dev, calls=None):
     """awq_dense_gemv per-call time, weights rotated through >= 512 MiB."""
     gen = torch.Generator(device="cpu").manual_seed(K + N)
     nbytes = K * N * 2
+    if calls is None:
+        calls = auto_steps(nbytes, 0)
     R = max(2, -(-ROTATE_BYTES // nbytes))
     ws = [(torch.randn((N, K), generator=gen) * 0.02).to(torch.float16).to(dev) for _ in range(R)]
     x = torch.randn((M, K), generator=gen).to(torch.float16).to(dev)
@@ -698,7 +725,7 @@ def main():
         out["prefill"] = pre
 
     if not args.no_configs:
-        out["configs"] = config_points(torch, awq, dev, steps_small=200, steps_large=20)
+        out["configs"] = config_points(torch, awq, dev)
         print("[bench] same-box references", file=sys.stderr, flush=True)
         out["references"] = same_box_references(
             torch, dev, res["decode"]["nbytes"] if "decode" in res else 30537728)
