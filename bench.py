@@ -12,11 +12,15 @@ zeros, scales, x and y of each step rotate through enough distinct copies to
 exceed twice the 256 MiB Infinity Cache, so every step streams its weights
 from HBM.  W warmup steps, then exactly K steps recorded in a HIP graph and
 replayed once between device synchronisations (this removes host launch
-gaps, which are comparable to a decode kernel's duration).  HIP events on the
-launching stream bracket the replay; since the graph runs one kernel per step
-back to back, the replay time per step is the kernel's average duration and
-the roofline figures use it (it agrees with rocprofv3's kernel durations).
-Events around single launches are reported as well, for reference.
+gaps, which are comparable to a decode kernel's duration).  Right before the
+timed replay the same graph is replayed untimed for about 20 ms, enqueued
+back to back with it, so that the K timed steps run at the clocks of
+continuous work however few they are (`untimed_settle_ms` on the line).  HIP
+events on the launching stream bracket the timed replay; since the graph runs
+one kernel per step back to back, the replay time per step is the kernel's
+average duration and the roofline figures use it (it agrees with rocprofv3's
+kernel durations).  Events around single launches are reported as well, for
+reference.
 
 Prints one JSON line on stdout.  --gpus above 1 is refused: this build is the
 single-GPU share of the path.
@@ -93,6 +97,39 @@ def make_copies(torch, p, R, dev):
 # us per call over 20 calls, 181-184 us over 100-500, on one box), so every
 # timed region lasts about this long.
 TIMED_SECONDS = 0.05
+
+
+# Before every timed graph replay the same graph is replayed untimed for
+# about this long, enqueued back to back with the timed replay (no host
+# synchronisation in between), so that the timed steps run at the clocks of
+# continuous work whatever their number.  Without it a 20-step region right
+# after a synchronisation read 9 % slow at decode (10.66 against 9.78 us per
+# call) and 15 % at the prefill projection (210.5 against 178-184 us).
+SETTLE_SECONDS = 0.02
+
+
+def settled_replay_ms(torch, graph, stream, calls):
+    """Replays `graph` (already uploaded) untimed for about SETTLE_SECONDS,
+    then once more between HIP events on `stream`; returns (ms of the timed
+    replay, ms spent settling).  The caller synchronises before and after."""
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    with torch.cuda.stream(stream):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    probe_ms = max(t0.elapsed_time(t1), 1e-3)
+    n = int(min(10000, -(-SETTLE_SECONDS * 1e3 // probe_ms)))
+    with torch.cuda.stream(stream):
+        for _ in range(n):
+            graph.replay()
+    t0.record(stream)
+    with torch.cuda.stream(stream):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1), n * probe_ms
 
 
 def auto_steps(nbytes, nflops):
@@ -173,32 +210,32 @@ def run_leg(torch, awq, spec, steps, warmup, dev, events=True, eager=True):
     torch.cuda.synchronize()
     graph.replay()                      # first replay uploads the graph
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    with torch.cuda.stream(stream):
-        graph.replay()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
+    total_ms, settle_ms = settled_replay_ms(torch, graph, stream, steps)
     ms_per_step = total_ms / steps
 
-    # Eager loop for reference (host launch overhead included).
+    # Eager loop for reference (host launch overhead included), from an idle
+    # GPU, between HIP events: the time per call is the slower of the host's
+    # launch path and the kernel.  At least ~20 ms of calls, so that the
+    # clocks' rise at the start is a small share.
     eager_ms = float("nan")
     if eager:
+        n_eager = max(steps, int(-(-SETTLE_SECONDS // max(ms_per_step * 1e-3, 1e-7))))
+        n_eager = min(n_eager, 5000)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        e0 = time.perf_counter()
+        e0.record(stream)
         with torch.cuda.stream(stream):
-            for i in range(steps):
+            for i in range(n_eager):
                 step(i)
+        e1.record(stream)
         torch.cuda.synchronize()
-        eager_ms = (time.perf_counter() - e0) * 1e3 / steps
+        eager_ms = e0.elapsed_time(e1) / n_eager
     del graph
 
     sorted_rows = copies[0]["w"].rows if act else K
     return dict(p=p, M=M, K=K, N=N, G=G, g=g, nbytes=nbytes, nflops=nflops, R=R,
-                sorted_rows=sorted_rows, steps=steps,
+                sorted_rows=sorted_rows, steps=steps, settle_ms=settle_ms,
                 path=awq.PATH_NAMES[path], ms_per_step=ms_per_step, kern_avg_ms=kern_avg_ms,
                 kern_min_ms=min(kern_ms), eager_ms=eager_ms, ws_bytes=ws_bytes)
 
@@ -258,14 +295,9 @@ def graph_time_us(torch, fn, calls, dev):
             fn(i)
     graph.replay()
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    with torch.cuda.stream(stream):
-        graph.replay()
-    t1.record(stream)
-    torch.cuda.synchronize()
+    ms, _ = settled_replay_ms(torch, graph, stream, calls)
     del graph
-    return t0.elapsed_time(t1) * 1e3 / calls
+    return ms * 1e3 / calls
 
 
 def read_stream_fn(torch, bufs, dev):
@@ -592,13 +624,8 @@ def dequant_time_us(torch, awq, K, N, dev, calls=None):
             awq.dequant(c["qweight"], c["qzeros"], c["scales"], 128, out=outs[i % R])
     graph.replay()
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    with torch.cuda.stream(stream):
-        graph.replay()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    us = t0.elapsed_time(t1) * 1e3 / calls
+    ms, _ = settled_replay_ms(torch, graph, stream, calls)
+    us = ms * 1e3 / calls
     del graph, cps, outs
     torch.cuda.empty_cache()
     return us
@@ -625,13 +652,8 @@ def dense_time_us(torch, awq, M, K, N, dev, calls=None):
             awq.dense_gemv(x, ws[i % R], None, out=y)
     graph.replay()
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    with torch.cuda.stream(stream):
-        graph.replay()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) * 1e3 / calls
+    ms, _ = settled_replay_ms(torch, graph, stream, calls)
+    return ms * 1e3 / calls
 
 
 def main():
@@ -703,7 +725,8 @@ def main():
                          "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("decode"),
                          "graph_step_us": round(r["ms_per_step"] * 1e3, 3),
-                         "single_launch_event_us": round(r["kern_avg_ms"] * 1e3, 3)},
+                         "single_launch_event_us": round(r["kern_avg_ms"] * 1e3, 3),
+                         "untimed_settle_ms": round(r["settle_ms"], 1)},
         })
     if "prefill" in res:
         r = res["prefill"]
@@ -717,7 +740,8 @@ def main():
                             "frac": round(ktf / FP16_MFMA_PEAK_TFLOPS, 4),
                             "traffic": measured_traffic("prefill"),
                             "graph_step_us": round(r["ms_per_step"] * 1e3, 3),
-                            "single_launch_event_us": round(r["kern_avg_ms"] * 1e3, 3)}}
+                            "single_launch_event_us": round(r["kern_avg_ms"] * 1e3, 3),
+                            "untimed_settle_ms": round(r["settle_ms"], 1)}}
         if "decode" not in res:
             out.update({"value": pre["value"], "unit": "TFLOP/s",
                         "ms_per_step": pre["ms_per_step"],
