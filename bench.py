@@ -559,8 +559,9 @@ def gidx_oracle_time(p, rows):
 
 
 def vendor_gemm_times_us(torch, awq, M, K, N, bias, dev, calls=None):
-    """Median per-call times of torch's float16 linear on a random (N, K)
-    weight, and of awq_dequant (g=128) followed by a float16 matmul."""
+    """Per-call times of torch's float16 linear on a random (N, K) weight,
+    and of awq_dequant (g=128) followed by a float16 matmul, each captured in
+    a graph and replayed like the headline legs."""
     if calls is None:
         calls = auto_steps(2 * N * K, 2 * M * N * K)
     gen = torch.Generator(device="cpu").manual_seed(M + K + N)
@@ -581,22 +582,7 @@ def vendor_gemm_times_us(torch, awq, M, K, N, bias, dev, calls=None):
         y = torch.matmul(x, wkn)
         return y + b if b is not None else y
 
-    out = []
-    for fn in (linear, unfused):
-        for i in range(5):
-            fn(i)
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(3):
-            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            t0.record()
-            for i in range(calls):
-                fn(i)
-            t1.record()
-            torch.cuda.synchronize()
-            ts.append(t0.elapsed_time(t1) * 1e3 / calls)
-        out.append(sorted(ts)[1])
-    return out[0], out[1]
+    return graph_time_us(torch, linear, calls, dev), graph_time_us(torch, unfused, calls, dev)
 
 
 def dequant_time_us(torch, awq, K, N, dev, calls=None):
