@@ -209,6 +209,28 @@ def test_plan_unaligned_x_falls_back_to_generic():
         binding.AWQ_PATH_GENERIC
 
 
+def test_plan_size_limits():
+    """The fast kernels address operands with 32-bit byte offsets: x and y up
+    to 2^29 elements (1 GiB) take them; beyond, the general kernel (int
+    element indices, valid while every operand stays below 2^31 elements).
+    The largest packed weight (K * N just under 2^31) plans as decode with 8
+    steps per wave, 32 splits."""
+    assert awq.gemm_plan(1, 32768, 65504, 128)[0] == binding.AWQ_PATH_DECODE
+    assert awq.gemm_plan(200, 32768, 65504, 128)[0] == binding.AWQ_PATH_PREFILL
+    path, ws = awq.gemm_plan(1, 32768, 65504, 128)
+    assert ws == 65536 + 4 * 65536 * 16 + 32 * 1 * 65504 * 4
+    assert awq.gemm_plan(16384, 32768, 64, 128)[0] == binding.AWQ_PATH_PREFILL   # x = 1 GiB
+    assert awq.gemm_plan(16385, 32768, 64, 128)[0] == binding.AWQ_PATH_GENERIC
+    assert awq.gemm_plan(8192, 64, 65536, -1)[0] == binding.AWQ_PATH_PREFILL     # y = 1 GiB
+    assert awq.gemm_plan(8193, 64, 65536, -1)[0] == binding.AWQ_PATH_GENERIC
+    # The register decode variant (N % 32 != 0) has two waves along K: up to
+    # 63 splits of 8 steps, K <= 32256.
+    assert awq.gemm_plan(16, 32000, 65528, 128)[0] == binding.AWQ_PATH_DECODE
+    assert awq.gemm_plan(16, 32768, 65528, 128)[0] == binding.AWQ_PATH_PREFILL
+    with pytest.raises(awq.AwqError):
+        awq.gemm_plan(1, 65536, 32768, 128)                  # K * N = 2^31
+
+
 def test_forced_path():
     with awq.options(force_path="prefill"):
         assert awq.gemm_plan(1, 8192, 7168, 128)[0] == binding.AWQ_PATH_PREFILL
