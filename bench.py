@@ -647,7 +647,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--legs", default="decode,prefill")
+    ap.add_argument("--legs", default="decode,prefill",
+                    help="comma-separated: decode, prefill, and refs (the same-box references "
+                         "even with --no-configs)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-config points and the same-box references")
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -736,6 +738,7 @@ def main():
 
     if not args.no_configs:
         out["configs"] = config_points(torch, awq, dev)
+    if not args.no_configs or "refs" in legs:
         print("[bench] same-box references", file=sys.stderr, flush=True)
         out["references"] = same_box_references(
             torch, dev, res["decode"]["nbytes"] if "decode" in res else 30537728)
