@@ -146,8 +146,8 @@ int run_gemm(const Problem& p, const void* x, const void* qweight, const void* q
 // address comes from hipGetSymbolAddress, taken once per device with that
 // device current.
 constexpr size_t kScratchBytes = AWQ_NOALLOC_SCRATCH_BYTES;
-static_assert(kScratchBytes >= awq::kTicketRegionBytes + awq::kAtomicRegionBytes,
-              "the scratch holds at least the exchange's fixed regions");
+static_assert(kScratchBytes >= awq::kAtomicRegionBytes,
+              "the scratch holds at least the exchange's fixed region");
 __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -158,8 +158,8 @@ struct ScratchSlot {
 };
 ScratchSlot g_scratch[kMaxDevices];
 
-// Zeroes n16 16-byte words at p (the exchange's ticket and accumulator
-// regions must start at zero; every exchange leaves them zero again).
+// Zeroes n16 16-byte words at p (the atomic exchange's accumulator region
+// must start at zero; every exchange leaves it zero again).
 __global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ p, size_t n16) {
   for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n16;
        i += static_cast<size_t>(gridDim.x) * 256)
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ p, s
 
 // The scratch address on the device of stream s, set up on first use: the
 // symbol's address with that device current, and a fill kernel on s that
-// zeroes the fixed regions before any exchange uses them.
+// zeroes the fixed region before any exchange uses it.
 int scratch_for_stream(hipStream_t s, void** out) {
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) return AWQ_ERROR_HIP;
@@ -180,7 +180,7 @@ int scratch_for_stream(hipStream_t s, void** out) {
     if (dev != cur && hipSetDevice(dev) != hipSuccess) return;
     void* ptr = nullptr;
     if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess && ptr != nullptr) {
-      const size_t n16 = (awq::kTicketRegionBytes + awq::kAtomicRegionBytes) / 16;
+      const size_t n16 = awq::kAtomicRegionBytes / 16;
       hipLaunchKernelGGL(zero_fill_kernel, dim3(256), dim3(256), 0, s,
                          static_cast<uint4*>(ptr), n16);
       if (hipGetLastError() == hipSuccess) {

@@ -35,10 +35,10 @@
 //   with a contribution count, and the one whose returned sum shows every
 //   split has arrived writes y -- one atomic round trip.  For larger M the
 //   atomic count grows past what the memory-side atomic units sustain, so
-//   partials are stored, each work-group takes a ticket on its column tile,
-//   and the last one sums them in split order (splitk_ticket).  Every byte of
-//   the ticket and accumulator regions of the workspace is zero again when
-//   either exchange ends.
+//   each work-group stores its partials with plain stores and a second
+//   kernel on the same stream sums them in split order (decode_sum_kernel).
+//   The accumulator region of the workspace is zero again when the atomic
+//   exchange ends.
 // * Activation order (a row-to-group map whose groups were made contiguous
 //   by reordering the packed rows at load time): the LDS variant reads x
 //   through the same row order, gathering x[m, perm[k]] itself, so the
@@ -53,11 +53,10 @@ namespace {
 
 // Split-K exchange state in the workspace (all of it zero between calls).
 struct SplitK {
-  uint32_t* tickets;         // one per column tile, ticket_words apart (ticket exchange)
   unsigned long long* acc;   // [M][N]: fixed-point sum, contribution count (atomic exchange)
   unsigned long long* mask;  // [M][N]: splits that sent a float partial (atomic exchange)
-  float* partial;            // [splits][M][N]: partials (all for ticket, float ones for atomic)
-  int ticket_words;
+  float* partial;            // [splits][M][N]: partials (all of them for the two-launch
+                             // exchange, the float ones for the atomic exchange)
 };
 // acc layout: bits 0-51 sum of (v + 2^45) over fixed-point contributions,
 // v = rint(p * 2^24) with |p| < 2^21 (so each term is below 2^46 and up to
@@ -185,118 +184,15 @@ __device__ __forceinline__ void splitk_atomic(const float (&part)[kDecodeMaxM], 
   }
 }
 
-// Ticket exchange (M > 4), called by every thread of the work-group.
-// Partials are written with device-coherent stores and read back with
-// device-coherent loads (agent-scope atomic accesses bypass the per-XCD L2's
-// non-coherent state without a whole-L2 writeback); each thread waits for
-// its stores to be acknowledged before the barrier, so every partial of the
-// work-group is in place before its ticket is taken, and the work-group that
-// takes the last ticket sees all of them.  It sums them in split order and
-// resets the ticket.
-// Final sum of a column tile's partials by the work-group holding the last
-// ticket: thread t covers the four columns 4*(t % 64) .. +3 of the tile and
-// the rows t / 64 + RG*i (i < MQ, RG = threads / 64 row groups), reading
-// each (split, row) as one 16-byte
-// load, so a round of BATCH splits moves 16 * BATCH * MQ bytes per thread
-// (the partials of a 16-row tile are 256 KiB: with one float per load the
-// load counter would cap a round at 63 x 4 bytes).  Sums run in split
-// order from zero.  The caller has invalidated this CU's caches (acquire),
-// so plain loads see every split's stores.  Indices past the last split
-// or row are clamped (the loads stay unconditional) and their values dropped.
-template <int BATCH, int MQ, int RG>
-__device__ __forceinline__ void ticket_sum_store(const float* __restrict__ partial,
-                                                 const _Float16* __restrict__ bias,
-                                                 _Float16* __restrict__ y, int M, int N,
-                                                 int splits, int n0, int rq) {
-  const size_t stride = static_cast<size_t>(M) * N;
-  floatx4 sum[MQ];
+// Two-launch exchange (above the atomic exchange's rows): the thread of
+// column n stores the work-group's partial of each row with plain stores;
+// decode_sum_kernel, next on the stream, sums them.
+__device__ __forceinline__ void store_partials(const float (&part)[kDecodeMaxM],
+                                               float* __restrict__ partial, int M, int N, int n,
+                                               int split) {
 #pragma unroll
-  for (int i = 0; i < MQ; ++i) sum[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < splits; sp += BATCH) {
-    floatx4 v[BATCH][MQ];
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int su = min(sp + u, splits - 1);
-#pragma unroll
-      for (int i = 0; i < MQ; ++i) {
-        const int m = min(rq + RG * i, M - 1);
-        v[u][i] = *reinterpret_cast<const floatx4*>(partial + su * stride +
-                                                    static_cast<size_t>(m) * N + n0);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const bool ok = sp + u < splits;
-#pragma unroll
-      for (int i = 0; i < MQ; ++i) sum[i] += ok ? v[u][i] : floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-  floatx4 b = floatx4{0.f, 0.f, 0.f, 0.f};
-  if (bias) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = static_cast<float>(bias[n0 + j]);
-  }
-#pragma unroll
-  for (int i = 0; i < MQ; ++i) {
-    const int m = rq + RG * i;
-    if (m < M) {
-      half4_t o;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = static_cast<_Float16>(sum[i][j] + b[j]);
-      *reinterpret_cast<half4_t*>(y + static_cast<size_t>(m) * N + n0) = o;
-    }
-  }
-}
-
-// VREGS: 16-byte registers the final sum may hold in flight per thread;
-// WAVES: waves of the work-group (all of them take part in the final sum).
-template <int VREGS, int WAVES = 4>
-__device__ __forceinline__ void splitk_ticket(const float (&part)[kDecodeMaxM], const SplitK& sk,
-                                              const _Float16* __restrict__ bias,
-                                              _Float16* __restrict__ y, int M, int N, int n,
-                                              bool nvalid, int split, int splits, int n_tile) {
-  __shared__ int s_last;
-  if (nvalid) {
-#pragma unroll
-    for (int m = 0; m < kDecodeMaxM; ++m)
-      if (m < M)
-        __hip_atomic_store(sk.partial + (static_cast<size_t>(split) * M + m) * N + n, part[m],
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  uint32_t* ticket = sk.tickets + n_tile * sk.ticket_words;
-  if (threadIdx.x == 0)
-    s_last = (__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              static_cast<unsigned>(splits - 1));
-  __syncthreads();
-  if (!s_last) return;
-  // Acquire: drop this CU's and this XCD's cached copies, so the plain loads
-  // of the partials fetch what the other splits stored.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  {
-    // N % 8 == 0, so a group of four columns is all inside or all outside.
-    const int n0 = n_tile * kDecodeCols + 4 * (threadIdx.x & 63);
-    const int rq = threadIdx.x >> 6;
-    if (n0 < N) {
-      if constexpr (WAVES == 8) {
-        if (M > 8)
-          ticket_sum_store<VREGS / 2, 2, 8>(sk.partial, bias, y, M, N, splits, n0, rq);
-        else
-          ticket_sum_store<VREGS, 1, 8>(sk.partial, bias, y, M, N, splits, n0, rq);
-      } else {
-        switch ((M + 3) >> 2) {
-          case 1: ticket_sum_store<VREGS, 1, 4>(sk.partial, bias, y, M, N, splits, n0, rq); break;
-          case 2: ticket_sum_store<VREGS / 2, 2, 4>(sk.partial, bias, y, M, N, splits, n0, rq); break;
-          case 3: ticket_sum_store<VREGS / 3, 3, 4>(sk.partial, bias, y, M, N, splits, n0, rq); break;
-          default: ticket_sum_store<VREGS / 4, 4, 4>(sk.partial, bias, y, M, N, splits, n0, rq); break;
-        }
-      }
-    }
-  }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int m = 0; m < kDecodeMaxM; ++m)
+    if (m < M) partial[(static_cast<size_t>(split) * M + m) * N + n] = part[m];
 }
 
 // SINGLE_GROUP: every row a wave reads lies in one quantisation group (the
@@ -312,11 +208,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   extern __shared__ __attribute__((aligned(16))) float red[];  // see red_store
   pin_arg(y);
   pin_arg(bias);
-  pin_arg(sk.tickets);
   pin_arg(sk.acc);
   pin_arg(sk.mask);
   pin_arg(sk.partial);
-  pin_arg(sk.ticket_words);
 
   const int NW = N >> 3;
   const int tid = threadIdx.x;
@@ -435,11 +329,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     return;
   }
 
-  if (M <= kDecodeAtomicMaxM && N <= kDecodeAtomicMaxN) {
-    if (nvalid) splitk_atomic(part, sk, bias, y, M, N, n, split, splits);
-  } else {
-    splitk_ticket<8>(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
-  }
+  if (!nvalid) return;
+  if (decode_atomic_exchange(M, N))
+    splitk_atomic(part, sk, bias, y, M, N, n, split, splits);
+  else
+    store_partials(part, sk.partial, M, N, n, split);
 }
 
 // ---------------------------------------------------------------------------
@@ -507,11 +401,9 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   extern __shared__ __attribute__((aligned(16))) char smem[];
   pin_arg(y);
   pin_arg(bias);
-  pin_arg(sk.tickets);
   pin_arg(sk.acc);
   pin_arg(sk.mask);
   pin_arg(sk.partial);
-  pin_arg(sk.ticket_words);
   constexpr int kWaveBytes = STEPS * 4 * kLdsBlockPitch;
 
   const int NW = N >> 3;
@@ -790,8 +682,7 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   __syncthreads();
 
   // One thread per column of the tile holds its partial; with eight waves
-  // the upper half of the work-group only joins the ticket exchange's final
-  // sum.
+  // the upper half of the work-group is done.
   const bool col_thread = WAVES == 4 || tid < kDecodeCols;
   const int n = n_tile * kDecodeCols + tid;
   const bool nvalid = col_thread && n < N;
@@ -801,11 +692,62 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
     if (nvalid) store_rows(part, bias, y, M, N, n);
     return;
   }
-  if (M <= kDecodeAtomicMaxM && N <= kDecodeAtomicMaxN) {
-    if (nvalid) splitk_atomic(part, sk, bias, y, M, N, n, split, splits);
-  } else {
-    splitk_ticket<32, WAVES>(part, sk, bias, y, M, N, n, nvalid, split, splits, n_tile);
+  if (!nvalid) return;
+  if (decode_atomic_exchange(M, N))
+    splitk_atomic(part, sk, bias, y, M, N, n, split, splits);
+  else
+    store_partials(part, sk.partial, M, N, n, split);
+}
+
+// The two-launch exchange's sum: y = the split partials summed in split
+// order from zero, + bias.  64 threads per work-group, thread i takes the
+// four adjacent outputs 4i .. 4i+3 (N % 8 == 0: never across a row) with
+// 16-byte loads of each split's partials (the partial planes are 16-byte
+// aligned), eight splits' loads in flight at a time; loads past the last
+// split re-read it and are dropped.
+__global__ __launch_bounds__(64) void decode_sum_kernel(const float* __restrict__ partial,
+                                                        const _Float16* __restrict__ bias,
+                                                        _Float16* __restrict__ y, int M, int N,
+                                                        int splits) {
+  const size_t plane = static_cast<size_t>(M) * N;
+  const size_t e = (static_cast<size_t>(blockIdx.x) * 64 + threadIdx.x) * 4;
+  if (e >= plane) return;
+  floatx4 sum = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < splits; sp += 8) {
+    floatx4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = *reinterpret_cast<const floatx4*>(partial + min(sp + u, splits - 1) * plane + e);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+      sum += (sp + u < splits) ? v[u] : zero;
+    }
   }
+  if (bias) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sum[q] += static_cast<float>(bias[e % N + q]);
+  }
+  half4_t o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = static_cast<_Float16>(sum[q]);
+  if ((reinterpret_cast<uintptr_t>(y) & 7) == 0) {
+    *reinterpret_cast<half4_t*>(y + e) = o;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[e + q] = o[q];
+  }
+}
+
+// Launches the sum kernel after a split decode kernel whose exchange is the
+// two-launch one.
+hipError_t launch_sum(const SplitK& sk, const _Float16* bias, _Float16* y, int M, int N,
+                      int splits, hipStream_t stream) {
+  if (splits <= 1 || decode_atomic_exchange(M, N)) return hipSuccess;
+  const size_t quads = static_cast<size_t>(M) * N / 4;
+  hipLaunchKernelGGL(decode_sum_kernel, dim3(static_cast<unsigned>((quads + 63) / 64)), dim3(64), 0,
+                     stream, sk.partial, bias, y, M, N, splits);
+  return hipGetLastError();
 }
 
 template <int STEPS, bool GATHER, int WAVES>
@@ -826,7 +768,9 @@ hipError_t launch_lds_waves(const _Float16* x, const uint32_t* qweight, const ui
     hipLaunchKernelGGL((decode_lds_kernel<STEPS, false, GATHER, WAVES>), dim3(n_tiles * splits),
                        dim3(64 * WAVES), shmem, stream, x, qweight, qzeros, scales, bias, y, sk,
                        M, K, N, g, G, splits, perm, Kx);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_sum(sk, bias, y, M, N, splits, stream);
 }
 
 template <int STEPS, bool GATHER>
@@ -859,7 +803,9 @@ hipError_t launch_steps(const _Float16* x, const uint32_t* qweight, const uint32
     hipLaunchKernelGGL((decode_kernel<STEPS, false>), dim3(n_tiles * splits), dim3(256), shmem,
                        stream, x, qweight, qzeros, scales, bias, y, sk, M, K, N,
                        g, G, splits);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_sum(sk, bias, y, M, N, splits, stream);
 }
 
 }  // namespace
@@ -870,19 +816,13 @@ hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint3
                          int n_tiles, bool lds_variant, int waves, void* workspace,
                          const int32_t* perm, int Kx, hipStream_t stream) {
   if (waves != 4 && !(lds_variant && waves == 8)) return hipErrorInvalidValue;
-  // Workspace: ticket region, accumulator region ([M][N] accumulators, then
-  // [M][N] masks), then [splits][M][N] partials.
+  // Workspace: accumulator region ([M][N] accumulators, then [M][N] masks),
+  // then [splits][M][N] partials.
   char* ws = static_cast<char*>(workspace);
   const size_t mn = static_cast<size_t>(M) * N;
-  int tw = static_cast<int>(kTicketRegionBytes / 4 / n_tiles);
-  if (tw > kTicketMaxStrideBytes / 4) tw = kTicketMaxStrideBytes / 4;
-  const SplitK sk{reinterpret_cast<uint32_t*>(ws),
-                  ws ? reinterpret_cast<unsigned long long*>(ws + kTicketRegionBytes) : nullptr,
-                  ws ? reinterpret_cast<unsigned long long*>(ws + kTicketRegionBytes + mn * 8)
-                     : nullptr,
-                  ws ? reinterpret_cast<float*>(ws + kTicketRegionBytes + kAtomicRegionBytes)
-                     : nullptr,
-                  tw};
+  const SplitK sk{ws ? reinterpret_cast<unsigned long long*>(ws) : nullptr,
+                  ws ? reinterpret_cast<unsigned long long*>(ws + mn * 8) : nullptr,
+                  ws ? reinterpret_cast<float*>(ws + kAtomicRegionBytes) : nullptr};
   if (lds_variant && perm) {
     switch (steps) {
       case 1: return launch_lds_steps<1, true>(x, qweight, qzeros, scales, bias, y, M, K, N, g,

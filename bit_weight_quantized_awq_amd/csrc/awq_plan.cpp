@@ -95,13 +95,11 @@ bool decode_supported(const Problem& p, const Alignment& al) {
   // 16-byte x loads need K % 8 == 0; a group must not change inside a wave's
   // 32-row step; the LDS-streaming variant (N % 32 == 0) copies 16-byte row
   // segments; the split-K exchange counts at most kDecodeMaxSplits splits
-  // (at 8 steps per wave) and every column tile has a 4-byte ticket slot.
+  // (at 8 steps per wave).
   const bool lds = p.N % 32 == 0;
-  const int64_t n_tiles = ceil_div(p.N, kDecodeCols);
   return fits_32bit_offsets(p) && p.M <= kDecodeMaxM && p.K % 8 == 0 && al.x && al.scales &&
          (!lds || al.qweight) && (p.g % kDecodeRowsPerStep == 0 || p.G == 1) &&
-         decode_splits(p, lds, 8) <= kDecodeMaxSplits &&
-         n_tiles * 4 <= static_cast<int64_t>(kTicketRegionBytes);
+         decode_splits(p, lds, 8) <= kDecodeMaxSplits;
 }
 
 static int log2_exact(int64_t v) {
@@ -236,19 +234,19 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
       }
       steps = single_enough ? single_enough : (enough ? enough : (most ? most : 8));
     }
-    // The ticket exchange's final sum reads every split's partials, one
-    // work-group per column tile: past kDecodeTicketMaxSplits splits of four
-    // waves, eight waves of the same steps halve the splits (K = 14336,
-    // N = 4096, M = 16: 20.2 -> 16.7 us; at 16 splits four waves stay ahead).
-    if (pl.decode_lds && waves_opt == 0 && p.M > kDecodeAtomicMaxM && steps == 4 &&
-        decode_splits(p, true, steps, 4) > kDecodeTicketMaxSplits)
+    // Above the atomic exchange every split's partials are stored and read
+    // back by the sum kernel: past kDecodeFourWaveMaxSplits splits of four
+    // waves, eight waves of the same steps halve them (K = 14336, N = 4096,
+    // M = 16: 16.1 -> 15.3 us; at 16 splits four waves stay ahead).
+    if (pl.decode_lds && waves_opt == 0 && !decode_atomic_exchange(p.M, p.N) && steps == 4 &&
+        decode_splits(p, true, steps, 4) > kDecodeFourWaveMaxSplits)
       pl.decode_waves = 8;
     // Eight waves of eight steps would need 272 KiB of LDS: four waves then.
     if (pl.decode_waves == 8 && steps == 8) pl.decode_waves = 4;
     pl.steps = steps;
     pl.splits = static_cast<int>(decode_splits(p, pl.decode_lds, steps, pl.decode_waves));
     if (pl.splits > 1)
-      pl.ws_bytes = kTicketRegionBytes + kAtomicRegionBytes +
+      pl.ws_bytes = kAtomicRegionBytes +
                     static_cast<size_t>(pl.splits) * p.M * p.N * sizeof(float);
   } else if (path == AWQ_PATH_PREFILL) {
     // The packed-weight tile where it applies and fills the CUs without a
@@ -323,7 +321,7 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
     pl.splits = static_cast<int>(splits);
     pl.steps = static_cast<int>(kps);
     if (splits > 1)
-      pl.ws_bytes = kTicketRegionBytes + kAtomicRegionBytes +
+      pl.ws_bytes = kAtomicRegionBytes +
                     static_cast<size_t>(splits) * p.M * p.N * sizeof(float);
   }
   *out = pl;
@@ -438,7 +436,7 @@ size_t sorted_x_offset(int64_t M, int64_t rows, int64_t N, int64_t block_rows) {
   // this problem's own plan needs: the workspace may also serve awq_gemm
   // calls of other shapes.
   size_t base = gemm_workspace_size(M, rows, N, block_rows);
-  const size_t fixed = kTicketRegionBytes + kAtomicRegionBytes;
+  const size_t fixed = kAtomicRegionBytes;
   if (base < fixed) base = fixed;
   return round_up(base, 256);
 }

@@ -13,23 +13,26 @@ namespace awq {
 constexpr int kDecodeCols = 256;         // columns per work-group
 constexpr int kDecodeRowsPerStep = 32;   // rows one wave consumes per step
 constexpr int kDecodeMaxM = 16;          // rows of the 16x16 MFMA output
-// Split-K exchange workspace, in three parts:
-//  * a fixed ticket region: one ticket per column tile, up to 256 bytes apart
-//    (device-scope atomics on one cache line serialise);
+// Split-K exchange workspace, in two parts:
 //  * a fixed accumulator region for the atomic exchange (M <= 4, N <= 65536):
 //    an 8-byte fixed-point accumulator per output element, then an 8-byte
 //    mask (one bit per split) per output element;
-//  * 4 bytes per split per output element for partials.
-// The first two parts are zero between calls (each exchange resets what it
-// used) and no exchange writes partials into them, so calls of any shapes
-// can share one workspace.  The atomic exchange counts at most 63 splits.
-constexpr size_t kTicketRegionBytes = 65536;
-constexpr int kTicketMaxStrideBytes = 256;
+//  * 4 bytes per split per output element for partials (every split's for
+//    the two-launch exchange, only the float ones for the atomic exchange).
+// The first part is zero between calls (the atomic exchange resets what it
+// used) and no exchange writes partials into it, so calls of any shapes can
+// share one workspace.  The atomic exchange counts at most 63 splits.
 constexpr int kDecodeMaxSplits = 63;
 constexpr int kDecodeAtomicMaxM = 4;
 constexpr int kDecodeGatherMaxM = 4;
-constexpr int kDecodeTicketMaxSplits = 16;   // above: eight waves per work-group
+constexpr int kDecodeFourWaveMaxSplits = 16;   // above: eight waves per work-group
 constexpr int kDecodeAtomicMaxN = 65536;
+// The atomic exchange for at most kDecodeAtomicMaxM rows (one device-scope
+// atomic per output element and split); above, plain partial stores summed
+// by a second kernel.
+constexpr bool decode_atomic_exchange(int64_t M, int64_t N) {
+  return M <= kDecodeAtomicMaxM && N <= kDecodeAtomicMaxN;
+}
 constexpr size_t kAtomicRegionBytes = static_cast<size_t>(kDecodeAtomicMaxM) * kDecodeAtomicMaxN * 16;
 
 // Prefill kernel tile: 64, 128 or 256 rows (the smallest that covers the
@@ -46,8 +49,8 @@ constexpr int kPrefillBK = 64;
 // (one work-group per CU) split the K steps over up to kPrefillMaxSplits
 // work-groups per tile, each with at least kPrefillMinSplitSteps steps; a
 // second kernel sums the fp32 partials.  The workspace has the decode
-// exchange's layout (so one buffer serves both): the ticket and accumulator
-// regions (unused here, left zero), then [splits][M][N] partials.
+// exchange's layout (so one buffer serves both): the accumulator region
+// (unused here, left zero), then [splits][M][N] partials.
 constexpr int kPrefillTargetWGs = 256;
 constexpr int kPrefillMaxSplits = 8;
 constexpr int kPrefillMinSplitSteps = 8;
@@ -158,10 +161,9 @@ int gidx_layout(const int32_t* g_idx, int64_t K, int64_t num_groups, int32_t* pe
                 int64_t* rows, int64_t* block_rows, int64_t* blocks);
 
 // Workspace of awq_gemm_sorted: the awq_gemm workspace of the sorted problem
-// (M, rows, N, block_rows), at least the fixed ticket and accumulator
-// regions, rounded up to 256 bytes, then room for x with its columns
-// reordered (M x rows float16, rounded up to 256 bytes).  0 for M == 0 or
-// invalid shapes.
+// (M, rows, N, block_rows), at least the fixed accumulator region, rounded
+// up to 256 bytes, then room for x with its columns reordered (M x rows
+// float16, rounded up to 256 bytes).  0 for M == 0 or invalid shapes.
 size_t sorted_workspace_size(int64_t M, int64_t rows, int64_t N, int64_t block_rows);
 // Byte offset of the reordered x inside that workspace.
 size_t sorted_x_offset(int64_t M, int64_t rows, int64_t N, int64_t block_rows);

@@ -1229,11 +1229,10 @@ hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint
                           int m_tiles, int n_tiles, int splits, int ksteps, void* workspace,
                           hipStream_t stream) {
   // Workspace (split K only), laid out like the decode exchange's so that
-  // one buffer serves both: the ticket and accumulator regions (left
-  // untouched, they must stay zero), then [splits][M][N] partials.
+  // one buffer serves both: the accumulator region (left untouched, it must
+  // stay zero), then [splits][M][N] partials.
   char* ws = static_cast<char*>(workspace);
-  float* partial =
-      ws ? reinterpret_cast<float*>(ws + kTicketRegionBytes + kAtomicRegionBytes) : nullptr;
+  float* partial = ws ? reinterpret_cast<float*>(ws + kAtomicRegionBytes) : nullptr;
   const dim3 grid(m_tiles * n_tiles * splits);
   const bool tail = K % BK != 0;
   auto go = [&](auto kernel, int lds) {

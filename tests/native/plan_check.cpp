@@ -77,7 +77,7 @@ int main() {
                 EXPECT((int64_t)(pl.splits - 1) * waves_k * kDecodeRowsPerStep * pl.steps < K);
                 EXPECT(pl.splits <= kDecodeMaxSplits);
                 if (pl.splits > 1)
-                  EXPECT(pl.ws_bytes == kTicketRegionBytes + kAtomicRegionBytes +
+                  EXPECT(pl.ws_bytes == kAtomicRegionBytes +
                                         (size_t)pl.splits * M * N * 4);
                 else
                   EXPECT(pl.ws_bytes == 0);
@@ -98,7 +98,7 @@ int main() {
                                           pl.steps >= kPrefillMinSplitSteps));
                 EXPECT((tiles > 0 && tiles < kPrefillTargetWGs) || pl.splits == 1);
                 if (pl.splits > 1)
-                  EXPECT(pl.ws_bytes == kTicketRegionBytes + kAtomicRegionBytes +
+                  EXPECT(pl.ws_bytes == kAtomicRegionBytes +
                                         (size_t)pl.splits * M * N * 4);
                 else
                   EXPECT(pl.ws_bytes == 0);
@@ -156,7 +156,7 @@ int main() {
            AWQ_ERROR_INVALID_VALUE);
   }
   {
-    const size_t fixed = kTicketRegionBytes + kAtomicRegionBytes;
+    const size_t fixed = kAtomicRegionBytes;
     EXPECT(sorted_workspace_size(0, 256, 128, 64) == 0);
     EXPECT(sorted_workspace_size(4, 256, 128, 48) == 0);
     EXPECT(sorted_x_offset(4, 256, 128, 64) >= fixed);

@@ -23,7 +23,7 @@ from bit_weight_quantized_awq_amd import binding  # noqa: E402
 ATOL = 1e-2
 RTOL = 1e-2
 DEV = "cuda:0"
-ZERO_REGION = 65536 + 4 * 65536 * 16   # ticket + accumulator regions of a workspace
+ZERO_REGION = 4 * 65536 * 16   # accumulator region of a workspace
 
 
 def say(msg):
@@ -313,8 +313,8 @@ def test_sorted_full_size_sampled(M, K, N, g, rows):
 
 
 def test_sorted_shares_workspace_with_gemm():
-    """The reordered x sits after the regions that must stay zero, so one
-    workspace serves sorted and plain calls (atomic and ticket decode
+    """The reordered x sits after the region that must stay zero, so one
+    workspace serves sorted and plain calls (atomic and two-launch decode
     exchanges, split prefill) back to back."""
     say("sorted workspace sharing")
     shapes = [(1, 8192, 7168), (16, 8192, 7168), (256, 2048, 512), (2, 4096, 1024)]

@@ -4,8 +4,8 @@ inputs bit for bit (the kernels sum in a fixed order), with new inputs
 copied into the captured buffers, eager work and synchronisations between
 the replays.
 
-The split-K exchanges leave their workspace counters at zero on exit, so a
-graph can be replayed without clearing anything in between; the workspace is
+The atomic split-K exchange leaves its workspace accumulators at zero on
+exit, so a graph can be replayed without clearing anything in between; the workspace is
 zeroed once, eagerly, before capture (nothing is cleared inside the graph).
 awq_gemm_noalloc is called once eagerly first, so that its one-time scratch
 fill runs outside the capture.
@@ -65,7 +65,7 @@ def _replay_and_compare(fn_capture, fn_eager, x_static, y_static, M, K, seed):
 
 @pytest.mark.parametrize("M,K,N,g,bias", [
     (1, 8192, 7168, 128, False),      # decode, atomic exchange
-    (16, 4096, 2048, 64, True),       # decode, ticket exchange
+    (16, 4096, 2048, 64, True),       # decode, two-launch exchange
     (4, 14336, 4096, -1, False),      # decode, one group
     (256, 14336, 4096, 128, False),   # prefill, split K + reduce kernel
     (512, 2048, 4096, 128, True),     # prefill, one split
@@ -92,7 +92,7 @@ def test_graph_replay_matches_eager(M, K, N, g, bias):
                                 p["bias"], g)
     assert_within_tol(got.cpu().numpy(), ref, f"graph replay M={M}")
     if awq.gemm_plan(M, K, N, g)[0] == binding.AWQ_PATH_DECODE:
-        # The exchange left its tickets and accumulators at zero for the next replay.
+        # The exchange left its accumulators at zero for the next replay.
         assert torch.count_nonzero(ws[:min(ZERO_REGION, ws.numel())]).item() == 0
 
 

@@ -49,7 +49,7 @@ def to_dev(p):
     return d
 
 
-ZERO_REGION = 65536 + 4 * 65536 * 16   # ticket + accumulator regions of a decode workspace
+ZERO_REGION = 4 * 65536 * 16   # accumulator region of a decode workspace
 
 
 def assert_within_tol(gpu, ref, what):
@@ -452,8 +452,8 @@ def test_deterministic_repeats(M):
 
 def test_workspace_reuse_across_shapes():
     """One workspace serves decode calls of different shapes (both exchange
-    modes: M <= 4 atomic, M > 4 ticket) and split-K prefill calls back to
-    back: every call leaves the ticket and accumulator regions zero."""
+    modes: M <= 4 atomic, M > 4 two-launch) and split-K prefill calls back
+    to back: every call leaves the accumulator region zero."""
     say("workspace reuse")
     ws = torch.zeros(awq.gemm_workspace_size(16, 8192, 7168, 128), dtype=torch.uint8, device=DEV)
     shapes = [(16, 8192, 7168), (1, 8192, 1280), (256, 2048, 512), (4, 4096, 2048),
@@ -559,7 +559,7 @@ def test_dense_gemv_exact_cases():
                                            (16, 14336, 4096, 128, 4), (13, 8192, 768, -1, 1)])
 def test_decode_eight_waves(M, K, N, g, steps):
     """The decode work-group of eight waves along K (decode_waves=8; the
-    atomic exchange up to 4 rows, the ticket exchange above) against the
+    atomic exchange up to 4 rows, the two-launch exchange above) against the
     oracle, and one-hot rows exact."""
     say(f"decode eight waves M={M} K={K} N={N} g={g} steps={steps}")
     p = awq_inputs.make_inputs(M, K, N, g, seed=M + K + N + steps, bias=True)

@@ -193,12 +193,12 @@ def _prefill_splits_expected(M, K, N):
 ])
 def test_prefill_split_k_plan(M, K, N, g, splits):
     """Workspace of a split prefill, laid out like the decode exchange's: the
-    64 KiB ticket region, the 4 MiB accumulator region, then one fp32 partial
-    per split per output element; none without a split."""
+    4 MiB accumulator region, then one fp32 partial per split per output
+    element; none without a split."""
     assert _prefill_splits_expected(M, K, N) == splits
     path, ws = awq.gemm_plan(M, K, N, g)
     assert path == binding.AWQ_PATH_PREFILL
-    assert ws == (0 if splits == 1 else 65536 + 4 * 65536 * 16 + splits * M * N * 4)
+    assert ws == (0 if splits == 1 else 4 * 65536 * 16 + splits * M * N * 4)
     assert awq.gemm_workspace_size(M, K, N, g) == ws
 
 
@@ -218,7 +218,7 @@ def test_plan_size_limits():
     assert awq.gemm_plan(1, 32768, 65504, 128)[0] == binding.AWQ_PATH_DECODE
     assert awq.gemm_plan(200, 32768, 65504, 128)[0] == binding.AWQ_PATH_PREFILL
     path, ws = awq.gemm_plan(1, 32768, 65504, 128)
-    assert ws == 65536 + 4 * 65536 * 16 + 32 * 1 * 65504 * 4
+    assert ws == 4 * 65536 * 16 + 32 * 1 * 65504 * 4
     assert awq.gemm_plan(16384, 32768, 64, 128)[0] == binding.AWQ_PATH_PREFILL   # x = 1 GiB
     assert awq.gemm_plan(16385, 32768, 64, 128)[0] == binding.AWQ_PATH_GENERIC
     assert awq.gemm_plan(8192, 64, 65536, -1)[0] == binding.AWQ_PATH_PREFILL     # y = 1 GiB
@@ -309,15 +309,14 @@ def test_unrecognised_forced_path_fails_every_plan():
 
 
 def test_decode_workspace_size_formula():
-    """A fixed 64 KiB ticket region, a fixed 4 MiB accumulator region (an
-    8-byte accumulator and an 8-byte mask per element, for M <= 4 and
-    N <= 65536), then one fp32 slot per split per element; at most 63
-    splits."""
+    """A fixed 4 MiB accumulator region (an 8-byte accumulator and an 8-byte
+    mask per element, for M <= 4 and N <= 65536), then one fp32 slot per
+    split per element; at most 63 splits."""
     for (M, K, N, g) in [(4, 8192, 7168, 128), (1, 14336, 4096, 128), (16, 8192, 1280, -1)]:
         path, ws = awq.gemm_plan(M, K, N, g)
         assert path == binding.AWQ_PATH_DECODE
         assert ws == awq.gemm_workspace_size(M, K, N, g)
-        partial = ws - 65536 - 4 * 65536 * 16
+        partial = ws - 4 * 65536 * 16
         assert partial % (M * N * 4) == 0
         splits = partial // (M * N * 4)
         assert 2 <= splits <= 63
@@ -336,7 +335,7 @@ def test_decode_step_choice(M, K, N, g, splits):
     one with the most work-groups (fewer splits, less to exchange)."""
     path, ws = awq.gemm_plan(M, K, N, g)
     assert path == binding.AWQ_PATH_DECODE
-    assert (ws - 65536 - 4 * 65536 * 16) // (M * N * 4) == splits
+    assert (ws - 4 * 65536 * 16) // (M * N * 4) == splits
 
 
 def test_decode_split_limit():
@@ -447,10 +446,10 @@ def test_gidx_validation(fn, kwargs, status):
 
 def test_sorted_workspace_rules():
     """The reordered x (M x rows float16) sits after the awq_gemm workspace
-    of the sorted problem and never inside the fixed zero-filled regions
-    (64 KiB tickets + 4 MiB accumulators); the call checks size and 256-byte
-    alignment first."""
-    fixed = 65536 + 4 * 65536 * 16
+    of the sorted problem and never inside the fixed zero-filled region
+    (4 MiB of accumulators); the call checks size and 256-byte alignment
+    first."""
+    fixed = 4 * 65536 * 16
     for M, rows, N, b in [(1, 8192, 7168, 128), (16, 8192, 7168, 128), (2048, 4096, 12288, 128),
                           (4, 256, 128, 64), (3, 7968, 64, 32)]:
         need = awq.sorted_workspace_size(M, rows, N, b)
@@ -592,21 +591,22 @@ def test_eight_wave_decode_plan():
         _, ws8 = awq.gemm_plan(1, K, N, g)
     with awq.options(decode_steps=2):
         _, ws4 = awq.gemm_plan(1, K, N, g)
-    fixed = 65536 + 4 * 65536 * 16
+    fixed = 4 * 65536 * 16
     assert (ws4 - fixed) == 2 * (ws8 - fixed) == 32 * N * 4
     with awq.options(decode_waves=8, decode_steps=8):
         _, ws = awq.gemm_plan(1, K, N, g)
     assert ws - fixed == (K // (4 * 32 * 8)) * N * 4
     with awq.options(decode_waves=8, decode_steps=4):
-        _, a = awq.gemm_plan(16, K, N, g)     # the ticket exchange too
+        _, a = awq.gemm_plan(16, K, N, g)     # the two-launch exchange too
     assert a - fixed == (K // (8 * 32 * 4)) * 16 * N * 4
 
 
-def test_ticket_exchange_takes_eight_waves_past_sixteen_splits():
-    """Batches above four rows whose four-wave plan would have more than 16
-    splits (K = 14336: 28) run eight waves per work-group (14 splits);
-    K = 8192 (16 splits) and the atomic exchange's batches keep four."""
-    fixed = 65536 + 4 * 65536 * 16
+def test_two_launch_exchange_takes_eight_waves_past_sixteen_splits():
+    """Batches above four rows (the two-launch exchange) whose four-wave
+    plan would have more than 16 splits (K = 14336: 28) run eight waves per
+    work-group (14 splits); K = 8192 (16 splits) and the atomic exchange's
+    batches keep four."""
+    fixed = 4 * 65536 * 16
     for M, K, N, splits in [(16, 14336, 4096, 14), (5, 14336, 4096, 14), (16, 8192, 7168, 16),
                             (1, 14336, 4096, 28), (4, 14336, 4096, 28)]:
         path, ws = awq.gemm_plan(M, K, N, 128)

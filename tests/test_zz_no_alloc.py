@@ -60,7 +60,7 @@ def check(p, g, a, b, what):
     assert (err <= ATOL + RTOL * np.abs(ref)).all(), f"{what}: max err {err.max():.3e}"
 
 
-# (first problem, second smaller problem): the decode ticket exchange then
+# (first problem, second smaller problem): the decode two-launch exchange then
 # the decode atomic exchange; a split prefill (partials in the scratch) then
 # an unsplit tiny one; the atomic exchange then a single-split decode.
 PAIRS = [
@@ -81,7 +81,7 @@ def test_noalloc_matches_gemm_two_calls(first, second):
 
 def test_noalloc_repeats_are_identical():
     """The scratch's counters are back at zero after every call: repeated
-    calls on one input give the same bits (ticket and atomic exchanges)."""
+    calls on one input give the same bits (two-launch and atomic exchanges)."""
     for (M, K, N, g) in ((8, 8192, 7168, 128), (1, 8192, 7168, 128)):
         say(f"awq_gemm_noalloc repeats M={M} K={K} N={N}")
         _, d = problem(M, K, N, g, seed=3, bias=False)
