@@ -70,22 +70,29 @@ namespace {
 // (small batches); every other kernel reads a copy reordered into xp first
 // (M x K float16, 16-byte aligned).
 // The plan awq_gemm follows for problem p with these operand addresses (a
-// reordered x is 16-byte aligned wherever it is read from).
+// reordered x is 16-byte aligned wherever it is read from).  ws_limit: the
+// workspace the caller can offer at most (awq_gemm_noalloc's scratch); a
+// two-block decode plan (17-32 rows) that needs more falls back to the
+// prefill kernel, whose split partials are fewer.
 int plan_gemm(const Problem& p, const void* x, const void* qweight, const void* scales,
-              bool reordered_x, Plan* pl) {
+              bool reordered_x, size_t ws_limit, Plan* pl) {
   const int force = awq::forced_path();
   if (force < 0) return AWQ_ERROR_INVALID_VALUE;
   const awq::Alignment al{reordered_x ? true : awq::aligned(x, 16), awq::aligned(scales, 16),
                           awq::aligned(qweight, 16)};
-  return awq::make_plan(p, al, force, pl);
+  const int st = awq::make_plan(p, al, force, pl);
+  if (st != AWQ_SUCCESS || force != 0 || pl->ws_bytes <= ws_limit ||
+      pl->path != AWQ_PATH_DECODE || p.M <= awq::kDecodeBlockM || !awq::prefill_supported(p, al))
+    return st;
+  return awq::make_plan(p, al, AWQ_PATH_PREFILL, pl);
 }
 
 int run_gemm(const Problem& p, const void* x, const void* qweight, const void* qzeros,
              const void* scales, const void* bias, void* y, void* workspace,
              size_t workspace_bytes, const int32_t* perm, int64_t Kx, _Float16* xp,
-             hipStream_t s) {
+             size_t ws_limit, hipStream_t s) {
   Plan pl;
-  const int st = plan_gemm(p, x, qweight, scales, perm != nullptr, &pl);
+  const int st = plan_gemm(p, x, qweight, scales, perm != nullptr, ws_limit, &pl);
   if (st != AWQ_SUCCESS) return st;
   if (pl.ws_bytes > 0) {
     if (!workspace || workspace_bytes < pl.ws_bytes) return AWQ_ERROR_WORKSPACE;
@@ -209,7 +216,7 @@ int awq_gemm_noalloc(const void* x, const void* qweight, const void* qzeros, con
   if (st != AWQ_SUCCESS) return st;
   if (M == 0) return AWQ_SUCCESS;
   Plan pl;
-  st = plan_gemm(p, x, qweight, scales, false, &pl);
+  st = plan_gemm(p, x, qweight, scales, false, kScratchBytes, &pl);
   if (st != AWQ_SUCCESS) return st;
   if (pl.ws_bytes > kScratchBytes) return AWQ_ERROR_SCRATCH;
   const auto s = static_cast<hipStream_t>(stream);
@@ -217,7 +224,7 @@ int awq_gemm_noalloc(const void* x, const void* qweight, const void* qzeros, con
   st = scratch_for_stream(s, &ws);
   if (st != AWQ_SUCCESS) return st;
   return run_gemm(p, x, qweight, qzeros, scales, bias, y, ws, kScratchBytes, nullptr, K,
-                  nullptr, s);
+                  nullptr, kScratchBytes, s);
 }
 
 int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void* scales,
@@ -230,7 +237,7 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros, const void*
   if (st != AWQ_SUCCESS) return st;
   if (M == 0) return AWQ_SUCCESS;
   return run_gemm(p, x, qweight, qzeros, scales, bias, y, workspace, workspace_bytes, nullptr,
-                  K, nullptr, static_cast<hipStream_t>(stream));
+                  K, nullptr, SIZE_MAX, static_cast<hipStream_t>(stream));
 }
 
 int awq_dense_gemv(const void* x, const void* w, const void* bias, void* y, int64_t M, int64_t K,
@@ -347,7 +354,8 @@ int awq_gemm_sorted(const void* x, const void* perm, const void* qweight_sorted,
   const size_t xoff = awq::sorted_x_offset(M, rows, N, block_rows);
   auto* xp = reinterpret_cast<_Float16*>(static_cast<char*>(workspace) + xoff);
   return run_gemm(p, x, qweight_sorted, qzeros_sorted, scales_sorted, bias, y, workspace, xoff,
-                  static_cast<const int32_t*>(perm), K_in, xp, static_cast<hipStream_t>(stream));
+                  static_cast<const int32_t*>(perm), K_in, xp, SIZE_MAX,
+                  static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -1,4 +1,4 @@
-// Decode W4A16 skinny GEMM (M <= 16): split-K over the input dimension,
+// Decode W4A16 skinny GEMM (M <= 32): split-K over the input dimension,
 // matrix cores for the multiply-accumulate, deterministic cross-work-group
 // reduction with the bias epilogue fused in.
 //
@@ -22,7 +22,9 @@
 //   (1024 + z) gives the exact integers q - z as float16.
 // * MFMA v_mfma_f32_16x16x32_f16: A = 16 rows of x (rows >= M are zero),
 //   B = (q - z) for 16 columns x 32 rows, one MFMA per nibble position j, so
-//   MFMA j covers columns 8*word + j.  Accumulation is fp32.
+//   MFMA j covers columns 8*word + j.  Accumulation is fp32.  Batches of
+//   17-32 rows (streaming variant, one group per wave) take two 16-row
+//   blocks of x, each multiplied with the same dequantised operands.
 // * The scale is applied once per group to the fp32 group partial:
 //   sum_k x*(q - z)*s = s * sum_k x*(q - z) exactly in real arithmetic; this
 //   differs from rounding each dequantised weight to float16 only by that
@@ -87,9 +89,9 @@ __device__ __forceinline__ void red_store(float* red, int wave, int Mq, int kb, 
 __device__ __forceinline__ void red_store1(float* red, int wave, int col, float v) {
   red[(wave * kDecodeCols + red_col(col)) * 4] = v;
 }
+// Sums one pass of M <= kDecodeBlockM rows into part[0 .. M).
 template <int WAVES>
-__device__ __forceinline__ void red_sum(const float* red, int Mq, int M, int col,
-                                        float (&part)[kDecodeMaxM]) {
+__device__ __forceinline__ void red_sum(const float* red, int Mq, int M, int col, float* part) {
   if (M == 1) {
     const int pc = red_col(col);
     float v = red[pc * 4];
@@ -99,7 +101,7 @@ __device__ __forceinline__ void red_sum(const float* red, int Mq, int M, int col
     return;
   }
 #pragma unroll
-  for (int c4 = 0; c4 < kDecodeMaxM / 4; ++c4) {
+  for (int c4 = 0; c4 < kDecodeBlockM / 4; ++c4) {
     if (4 * c4 < M) {
       const int pc = red_col(col);
       floatx4 v = *reinterpret_cast<const floatx4*>(red + (c4 * kDecodeCols + pc) * 4);
@@ -112,12 +114,13 @@ __device__ __forceinline__ void red_sum(const float* red, int Mq, int M, int col
   }
 }
 // Output of a work-group that covers all of K (no exchange).
-__device__ __forceinline__ void store_rows(const float (&part)[kDecodeMaxM],
+template <int MM>
+__device__ __forceinline__ void store_rows(const float (&part)[MM],
                                            const _Float16* __restrict__ bias,
                                            _Float16* __restrict__ y, int M, int N, int n) {
   const float b = bias ? static_cast<float>(bias[n]) : 0.f;
 #pragma unroll
-  for (int m = 0; m < kDecodeMaxM; ++m)
+  for (int m = 0; m < MM; ++m)
     if (m < M) y[m * N + n] = static_cast<_Float16>(part[m] + b);
 }
 
@@ -125,14 +128,16 @@ __device__ __forceinline__ void store_rows(const float (&part)[kDecodeMaxM],
 // the work-group's partial for row m < M.  All atomics of the thread are issued
 // before any result is used.  Partials are exact multiples of 2^-24 whenever
 // the scales are (every float16 is), so a one-hot row stays exact.
-__device__ __forceinline__ void splitk_atomic(const float (&part)[kDecodeMaxM], const SplitK& sk,
+template <int MM>
+__device__ __forceinline__ void splitk_atomic(const float (&part)[MM], const SplitK& sk,
                                               const _Float16* __restrict__ bias,
                                               _Float16* __restrict__ y, int M, int N, int n,
                                               int split, int splits) {
-  unsigned long long add[kDecodeMaxM], old[kDecodeMaxM];
+  constexpr int R = MM < kDecodeAtomicMaxM ? MM : kDecodeAtomicMaxM;   // M <= R
+  unsigned long long add[R], old[R];
   bool published = false;
 #pragma unroll
-  for (int m = 0; m < kDecodeMaxM; ++m) {
+  for (int m = 0; m < R; ++m) {
     if (m < M) {
       const float p = part[m];
       if (fabsf(p) < kFxLimit) {   // false for NaN
@@ -155,13 +160,13 @@ __device__ __forceinline__ void splitk_atomic(const float (&part)[kDecodeMaxM], 
   if (published) __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
-  for (int m = 0; m < kDecodeMaxM; ++m)
+  for (int m = 0; m < R; ++m)
     if (m < M)
       old[m] = __hip_atomic_fetch_add(sk.acc + static_cast<size_t>(m) * N + n, add[m],
                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const float b = bias ? static_cast<float>(bias[n]) : 0.f;
 #pragma unroll
-  for (int m = 0; m < kDecodeMaxM; ++m) {
+  for (int m = 0; m < R; ++m) {
     if (m >= M) continue;
     const unsigned long long tot = old[m] + add[m];
     if (static_cast<int>((tot >> 52) & 63u) != splits) continue;
@@ -187,11 +192,12 @@ __device__ __forceinline__ void splitk_atomic(const float (&part)[kDecodeMaxM], 
 // Two-launch exchange (above the atomic exchange's rows): the thread of
 // column n stores the work-group's partial of each row with plain stores;
 // decode_sum_kernel, next on the stream, sums them.
-__device__ __forceinline__ void store_partials(const float (&part)[kDecodeMaxM],
+template <int MM>
+__device__ __forceinline__ void store_partials(const float (&part)[MM],
                                                float* __restrict__ partial, int M, int N, int n,
                                                int split) {
 #pragma unroll
-  for (int m = 0; m < kDecodeMaxM; ++m)
+  for (int m = 0; m < MM; ++m)
     if (m < M) partial[(static_cast<size_t>(split) * M + m) * N + n] = part[m];
 }
 
@@ -322,7 +328,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 
   const int n = n_tile * kDecodeCols + tid;
   const bool nvalid = n < N;
-  float part[kDecodeMaxM];
+  float part[kDecodeBlockM];
   red_sum<2>(red, Mq, M, tid, part);
   if (splits == 1) {
     if (nvalid) store_rows(part, bias, y, M, N, n);
@@ -389,7 +395,11 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 // packed-word copies are split in two halves around the gathers, so the
 // dependent perm -> x round trip overlaps the first half of the weight
 // stream instead of delaying all of it.
-template <int STEPS, bool SINGLE_GROUP, bool GATHER, int WAVES>
+//
+// RB: MFMA row blocks of 16 rows (2 for 17-32 rows): the dequantised weight
+// operands of a step feed one MFMA per block, and the LDS reduction runs
+// once per block.
+template <int STEPS, bool SINGLE_GROUP, bool GATHER, int WAVES, int RB>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
                   const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
@@ -398,6 +408,8 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
                   const int32_t* __restrict__ perm, int Kx) {
   static_assert(!GATHER || STEPS <= 4, "gather loads must fit the load counter");
   static_assert(WAVES == 4 || WAVES == 8, "four or eight waves along K");
+  static_assert(RB == 1 || (RB == 2 && SINGLE_GROUP && !GATHER),
+                "two row blocks only for one group per wave, without a gather");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   pin_arg(y);
   pin_arg(bias);
@@ -468,15 +480,19 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   // Steps whose copies precede the x gathers (GATHER only).
   constexpr int kEarly = GATHER ? (STEPS + 1) / 2 : 0;
 
-  half8_t xa[STEPS];
+  // xa[rb][s]: rows 16 * rb + col16 of x (zero past M), k 8 * kb .. +7 of step s.
+  half8_t xa[RB][STEPS];
   if (!GATHER) {
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      const int kr = kw0 + 32 * s + 8 * kb;
-      const uint32_t xoff =
-          offset_or_oob(col16 < M && kr < K, static_cast<uint32_t>(col16 * K + kr) * 2u);
-      xa[s] = __builtin_bit_cast(half8_t, buf_load_u32x4(rx, xoff));
-    }
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) {
+        const int kr = kw0 + 32 * s + 8 * kb;
+        const int row = kDecodeBlockM * rb + col16;
+        const uint32_t xoff =
+            offset_or_oob(row < M && kr < K, static_cast<uint32_t>(row * K + kr) * 2u);
+        xa[rb][s] = __builtin_bit_cast(half8_t, buf_load_u32x4(rx, xoff));
+      }
     // Nothing may be scheduled between here and the waits below except the
     // LDS copies: the waits count outstanding copies.
     __builtin_amdgcn_sched_barrier(0);
@@ -496,7 +512,7 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
     for (int s = 0; s < STEPS; ++s) {
       pv[s][0] = u32x4{0u, 0u, 0u, 0u};
       pv[s][1] = u32x4{0u, 0u, 0u, 0u};
-      xa[s] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      xa[0][s] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
     }
     if (row_lane) {
 #pragma unroll
@@ -521,7 +537,7 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
           const uint32_t src = pv[s][i >> 2][i & 3];
           const uint32_t off = offset_or_oob(kr < K && src < kmax,
                                              static_cast<uint32_t>(col16) * kmax * 2u + src * 2u);
-          xa[s][i] =
+          xa[0][s][i] =
               __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rxg, off, 0, 0));
         }
       }
@@ -544,20 +560,22 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   // The operands are kept normal because the matrix cores align subnormal
   // products without normalising them, which costs bits next to a large
   // activation.  q == z and one-hot rows stay exact.
-  floatx4 acc_e[2][4], acc_f[2][4];
-  floatx4 tot[2][8];
+  floatx4 acc_e[RB][2][4], acc_f[RB][2][4];
+  floatx4 tot[RB][2][8];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc_e[h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
-      acc_f[h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc_e[rb][h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+        acc_f[rb][h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+      if (!SINGLE_GROUP) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tot[rb][h][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
     }
-    if (!SINGLE_GROUP) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) tot[h][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
 
   // -(zero byte) * 2^-9 and -(low zero nibble) * 2^-9 pairs of byte b of zero
   // word zw (exact: the subnormal byte times -2^15).
@@ -569,7 +587,7 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   };
   // Scale the group partials of set h into the totals, elements 0..R-1 (rows
   // 4*kb + i): added for one group per step, assigned for one group per wave.
-  auto fold = [&](int h, half8_t svh, auto rows) {
+  auto fold = [&](int rb, int h, half8_t svh, auto rows) {
     constexpr int R = decltype(rows)::value;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -577,14 +595,14 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
       const float so = static_cast<float>(svh[2 * q + 1]) * 0x1p5f;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const float ve = se * acc_e[h][q][i];
-        const float vo = so * (acc_f[h][q][i] - acc_e[h][q][i]);
+        const float ve = se * acc_e[rb][h][q][i];
+        const float vo = so * (acc_f[rb][h][q][i] - acc_e[rb][h][q][i]);
         if (SINGLE_GROUP) {
-          tot[h][2 * q][i] = ve;
-          tot[h][2 * q + 1][i] = vo;
+          tot[rb][h][2 * q][i] = ve;
+          tot[rb][h][2 * q + 1][i] = vo;
         } else {
-          tot[h][2 * q][i] += ve;
-          tot[h][2 * q + 1][i] += vo;
+          tot[rb][h][2 * q][i] += ve;
+          tot[rb][h][2 * q + 1][i] += vo;
         }
       }
     }
@@ -632,62 +650,76 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
           be[2 * p] = e[0];
           be[2 * p + 1] = e[1];
         }
-        acc_e[h][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], be, acc_e[h][q], 0, 0, 0);
-        acc_f[h][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], bf, acc_f[h][q], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          acc_e[rb][h][q] =
+              __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rb][s], be, acc_e[rb][h][q], 0, 0, 0);
+          acc_f[rb][h][q] =
+              __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rb][s], bf, acc_f[rb][h][q], 0, 0, 0);
+        }
       }
-      if (!SINGLE_GROUP) {
+      if (!SINGLE_GROUP) {   // RB == 1
         if (one_row)
-          fold(h, sv[s][h], OneRow{});
+          fold(0, h, sv[s][h], OneRow{});
         else
-          fold(h, sv[s][h], FourRows{});
+          fold(0, h, sv[s][h], FourRows{});
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          acc_e[h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
-          acc_f[h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+          acc_e[0][h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+          acc_f[0][h][q] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
       }
     }
   }
   // The WAVES K-ranges meet in LDS (the copy regions are free once every
-  // wave is past its last step).  tot[h][j][i] is row 4*kb + i, local column
-  // 8*(16h + col16) + j; with one row only element 0 is formed and stored.
+  // wave is past its last step), one pass per row block.  tot[rb][h][j][i]
+  // is row 16*rb + 4*kb + i, local column 8*(16h + col16) + j; with one row
+  // only element 0 is formed and stored.  One thread per column of the tile
+  // then holds its partial; with eight waves the upper half of the
+  // work-group is done.
   float* red = reinterpret_cast<float*>(smem);
-  const int Mq = (M + 3) >> 2;
+  const bool col_thread = WAVES == 4 || tid < kDecodeCols;
+  const int n = n_tile * kDecodeCols + tid;
+  const bool nvalid = col_thread && n < N;
+  float part[kDecodeBlockM * RB];
   if (one_row) {
     if (SINGLE_GROUP) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) fold(h, sv[0][h], OneRow{});
+      for (int h = 0; h < 2; ++h) fold(0, h, sv[0][h], OneRow{});
     }
     __syncthreads();
     if (kb == 0) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) red_store1(red, wave, 8 * (16 * h + col16) + j, tot[h][j][0]);
+        for (int j = 0; j < 8; ++j)
+          red_store1(red, wave, 8 * (16 * h + col16) + j, tot[0][h][j][0]);
     }
+    __syncthreads();
+    if (col_thread) red_sum<WAVES>(red, 1, 1, tid, part);
   } else {
     if (SINGLE_GROUP) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) fold(h, sv[0][h], FourRows{});
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) fold(rb, h, sv[0][h], FourRows{});
     }
-    __syncthreads();
-    if (4 * kb < M) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+    for (int rb = 0; rb < RB; ++rb) {
+      const int Mr = min(M - kDecodeBlockM * rb, kDecodeBlockM);   // rows of this pass
+      const int Mq = (Mr + 3) >> 2;
+      __syncthreads();   // the copy regions, or the previous pass, are done with
+      if (4 * kb < Mr) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          red_store(red, wave, Mq, kb, 8 * (16 * h + col16) + j, tot[h][j]);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            red_store(red, wave, Mq, kb, 8 * (16 * h + col16) + j, tot[rb][h][j]);
+      }
+      __syncthreads();
+      if (col_thread) red_sum<WAVES>(red, Mq, Mr, tid, part + kDecodeBlockM * rb);
     }
   }
-  __syncthreads();
-
-  // One thread per column of the tile holds its partial; with eight waves
-  // the upper half of the work-group is done.
-  const bool col_thread = WAVES == 4 || tid < kDecodeCols;
-  const int n = n_tile * kDecodeCols + tid;
-  const bool nvalid = col_thread && n < N;
-  float part[kDecodeMaxM];
-  if (col_thread) red_sum<WAVES>(red, Mq, M, tid, part);
   if (splits == 1) {
     if (nvalid) store_rows(part, bias, y, M, N, n);
     return;
@@ -755,19 +787,33 @@ hipError_t launch_lds_waves(const _Float16* x, const uint32_t* qweight, const ui
                             const _Float16* scales, const _Float16* bias, _Float16* y,
                             int M, int K, int N, int g, int G, int splits, int n_tiles,
                             SplitK sk, const int32_t* perm, int Kx, hipStream_t stream) {
+  // The LDS holds the weight copies, then one reduction pass (at most 16 rows).
   const size_t copy_bytes = WAVES * STEPS * 4 * kLdsBlockPitch;
-  const size_t red_bytes =
-      WAVES * static_cast<size_t>((M + 3) & ~3) * kDecodeCols * sizeof(float);
+  const int pass_rows = M < kDecodeBlockM ? ((M + 3) & ~3) : kDecodeBlockM;
+  const size_t red_bytes = WAVES * static_cast<size_t>(pass_rows) * kDecodeCols * sizeof(float);
   const size_t shmem = copy_bytes > red_bytes ? copy_bytes : red_bytes;
   const bool single = (G == 1) || (g % (kDecodeRowsPerStep * STEPS) == 0);
-  if (single)
-    hipLaunchKernelGGL((decode_lds_kernel<STEPS, true, GATHER, WAVES>), dim3(n_tiles * splits),
-                       dim3(64 * WAVES), shmem, stream, x, qweight, qzeros, scales, bias, y, sk,
-                       M, K, N, g, G, splits, perm, Kx);
-  else
-    hipLaunchKernelGGL((decode_lds_kernel<STEPS, false, GATHER, WAVES>), dim3(n_tiles * splits),
-                       dim3(64 * WAVES), shmem, stream, x, qweight, qzeros, scales, bias, y, sk,
-                       M, K, N, g, G, splits, perm, Kx);
+  const dim3 grid(n_tiles * splits), block(64 * WAVES);
+  if (M > kDecodeBlockM) {
+    // Two row blocks: the planner takes this variant only with one group per
+    // wave and no gather.
+    if constexpr (!GATHER) {
+      if (!single) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((decode_lds_kernel<STEPS, true, false, WAVES, 2>), grid, block, shmem,
+                         stream, x, qweight, qzeros, scales, bias, y, sk, M, K, N, g, G, splits,
+                         perm, Kx);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (single) {
+    hipLaunchKernelGGL((decode_lds_kernel<STEPS, true, GATHER, WAVES, 1>), grid, block, shmem,
+                       stream, x, qweight, qzeros, scales, bias, y, sk, M, K, N, g, G, splits,
+                       perm, Kx);
+  } else {
+    hipLaunchKernelGGL((decode_lds_kernel<STEPS, false, GATHER, WAVES, 1>), grid, block, shmem,
+                       stream, x, qweight, qzeros, scales, bias, y, sk, M, K, N, g, G, splits,
+                       perm, Kx);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_sum(sk, bias, y, M, N, splits, stream);
@@ -816,6 +862,7 @@ hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint3
                          int n_tiles, bool lds_variant, int waves, void* workspace,
                          const int32_t* perm, int Kx, hipStream_t stream) {
   if (waves != 4 && !(lds_variant && waves == 8)) return hipErrorInvalidValue;
+  if (M > kDecodeBlockM && (!lds_variant || perm)) return hipErrorInvalidValue;
   // Workspace: accumulator region ([M][N] accumulators, then [M][N] masks),
   // then [splits][M][N] partials.
   char* ws = static_cast<char*>(workspace);

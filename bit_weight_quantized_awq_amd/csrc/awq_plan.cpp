@@ -91,6 +91,21 @@ static int64_t decode_splits(const Problem& p, bool lds, int steps, int waves = 
   return ceil_div(p.K, static_cast<int64_t>(waves_k) * kDecodeRowsPerStep * steps);
 }
 
+// Whether every wave's rows lie in one quantisation group at `steps` steps
+// per wave (work-group row ranges start at multiples of the wave's rows).
+static bool decode_single_group(const Problem& p, int steps) {
+  return p.G == 1 || p.g % (static_cast<int64_t>(kDecodeRowsPerStep) * steps) == 0;
+}
+
+// More than one MFMA row block (17-32 rows) runs only in the LDS variant
+// with one group per wave: some step count must give that within the split
+// limit.
+static bool decode_two_blocks_fit(const Problem& p) {
+  for (int s = 8; s >= 1; s /= 2)
+    if (decode_single_group(p, s) && decode_splits(p, true, s) <= kDecodeMaxSplits) return true;
+  return false;
+}
+
 bool decode_supported(const Problem& p, const Alignment& al) {
   // 16-byte x loads need K % 8 == 0; a group must not change inside a wave's
   // 32-row step; the LDS-streaming variant (N % 32 == 0) copies 16-byte row
@@ -99,7 +114,8 @@ bool decode_supported(const Problem& p, const Alignment& al) {
   const bool lds = p.N % 32 == 0;
   return fits_32bit_offsets(p) && p.M <= kDecodeMaxM && p.K % 8 == 0 && al.x && al.scales &&
          (!lds || al.qweight) && (p.g % kDecodeRowsPerStep == 0 || p.G == 1) &&
-         decode_splits(p, lds, 8) <= kDecodeMaxSplits;
+         decode_splits(p, lds, 8) <= kDecodeMaxSplits &&
+         (p.M <= kDecodeBlockM || (lds && decode_two_blocks_fit(p)));
 }
 
 static int log2_exact(int64_t v) {
@@ -131,7 +147,7 @@ bool option_value_ok(int opt, int64_t v) {
     case AWQ_OPT_FORCE_PATH:
       return v == AWQ_PATH_DECODE || v == AWQ_PATH_PREFILL || v == AWQ_PATH_GENERIC;
     case AWQ_OPT_DECODE_STEPS: return v == 1 || v == 2 || v == 4 || v == 8;
-    case AWQ_OPT_DECODE_GATHER_MAX_M: return v >= 0 && v <= kDecodeMaxM;
+    case AWQ_OPT_DECODE_GATHER_MAX_M: return v >= 0 && v <= kDecodeBlockM;
     case AWQ_OPT_PREFILL_BM: return v == kPrefillMinBM || v == 2 * kPrefillMinBM || v == kPrefillBM;
     case AWQ_OPT_PREFILL_BN: return v == kPrefillBN || v == kPrefillWideBN || v == kPackedBN;
     case AWQ_OPT_PREFILL_SPLITS: return v >= 1 && v <= kPrefillMaxSplits;
@@ -195,7 +211,18 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
   const bool pre = prefill_supported(p, al);
   int path;
   if (force == 0) {
-    path = dec ? AWQ_PATH_DECODE : (pre ? AWQ_PATH_PREFILL : AWQ_PATH_GENERIC);
+    // 17-32 rows: the decode kernel's two-block form where the weight is
+    // large and its split partials (written, then read back by the sum
+    // kernel) are at most half the packed weight's bytes, else the prefill
+    // kernel.
+    bool dec_auto = dec;
+    if (dec && pre && p.M > kDecodeBlockM) {
+      Plan d;
+      dec_auto = p.K * p.N >= kDecodeTwoBlockMinWeights &&
+                 make_plan(p, al, AWQ_PATH_DECODE, &d) == AWQ_SUCCESS &&
+                 16 * static_cast<int64_t>(d.splits) * p.M <= p.K;
+    }
+    path = dec_auto ? AWQ_PATH_DECODE : (pre ? AWQ_PATH_PREFILL : AWQ_PATH_GENERIC);
   } else {
     path = force;
     if ((force == AWQ_PATH_DECODE && !dec) || (force == AWQ_PATH_PREFILL && !pre))
@@ -211,8 +238,12 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
     const int waves_opt = override_or_zero(AWQ_OPT_DECODE_WAVES);
     if (pl.decode_lds && waves_opt == 8) pl.decode_waves = 8;
     const int waves = pl.decode_waves;
+    // Two row blocks need one group per wave.
+    const bool two_blocks = p.M > kDecodeBlockM;
     int steps = override_or_zero(AWQ_OPT_DECODE_STEPS);
-    if (steps != 0 && decode_splits(p, pl.decode_lds, steps, waves) > kDecodeMaxSplits) steps = 0;
+    if (steps != 0 && (decode_splits(p, pl.decode_lds, steps, waves) > kDecodeMaxSplits ||
+                       (two_blocks && !decode_single_group(p, steps))))
+      steps = 0;
     if (steps == 0) {
       // The largest step count whose rows stay in one quantisation group and
       // that still gives enough work-groups; failing that, the largest that
@@ -223,9 +254,10 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
       const int64_t target = pl.decode_lds ? kDecodeLdsTargetWGs : kDecodeTargetWGs;
       int single_enough = 0, enough = 0, most = 0;
       for (int s = 4; s >= 1; s /= 2) {
-        const bool single = p.G == 1 || p.g % (kDecodeRowsPerStep * s) == 0;
+        const bool single = decode_single_group(p, s);
         const int64_t splits = decode_splits(p, pl.decode_lds, s, waves);
         if (splits > kDecodeMaxSplits) break;
+        if (two_blocks && !single) continue;
         most = s;
         if (pl.n_tiles * splits >= target) {
           if (single && single_enough == 0) single_enough = s;

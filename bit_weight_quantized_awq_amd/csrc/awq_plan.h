@@ -12,7 +12,15 @@ namespace awq {
 // the K range of the work-group, waves 0/2 and 1/3 split its 256 columns.
 constexpr int kDecodeCols = 256;         // columns per work-group
 constexpr int kDecodeRowsPerStep = 32;   // rows one wave consumes per step
-constexpr int kDecodeMaxM = 16;          // rows of the 16x16 MFMA output
+constexpr int kDecodeBlockM = 16;        // rows of one 16x16 MFMA output block
+// Rows of the decode kernels: one MFMA row block, or two for the LDS
+// variant when each wave's rows lie in one quantisation group.
+constexpr int kDecodeMaxM = 32;
+// The planner takes the two-block decode by itself only for weights of at
+// least this many elements (16 MiB packed) whose split partials are at most
+// half the packed bytes; the prefill kernel runs the others faster
+// (K = 4096, N = 4096, g = 64, M = 20: 10.9 against 12.1 us).
+constexpr int64_t kDecodeTwoBlockMinWeights = int64_t{1} << 25;
 // Split-K exchange workspace, in two parts:
 //  * a fixed accumulator region for the atomic exchange (M <= 4, N <= 65536):
 //    an 8-byte fixed-point accumulator per output element, then an 8-byte

@@ -158,9 +158,12 @@ int awq_gemm(const void* x, const void* qweight, const void* qzeros,
  * device, held from the library's first use on that device until the
  * process ends; no call allocates or frees anything.  Same arguments,
  * kernels, results (bit for bit), errors and stream behaviour as awq_gemm,
- * plus AWQ_ERROR_SCRATCH when the problem's plan needs more workspace than
- * the scratch holds (decode batches at the shapes this library targets fit;
- * large split prefill problems may not).  The first call on a device looks
+ * with two exceptions: a batch of 17-32 rows whose decode plan needs more
+ * workspace than the scratch holds runs awq_gemm's prefill kernel instead
+ * (same tolerance, other rounding), and AWQ_ERROR_SCRATCH when the plan
+ * still needs more workspace than the scratch holds (decode batches at the
+ * shapes this library targets fit; large split prefill problems may not).
+ * The first call on a device looks
  * up the array's address on that device (hipGetSymbolAddress) and enqueues
  * a small fill kernel on `stream` that zeroes the exchange counters (inside
  * a graph capture that kernel is captured too); every exchange leaves them

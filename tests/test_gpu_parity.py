@@ -220,7 +220,9 @@ def test_gemm_config_parity(name, Mmax, M, g):
     d = to_dev(p)
     K, N = p["qweight"].shape[0], p["qweight"].shape[1] * 8
     path, _ = awq.gemm_plan(M, K, N, g, d["x"].data_ptr(), d["scales"].data_ptr())
-    expect_path = binding.AWQ_PATH_DECODE if M <= 16 else binding.AWQ_PATH_PREFILL
+    # Up to 16 rows the decode kernel; 17-32 rows (here M = 32 of the 29 MB
+    # weight) its two-block form; above, the prefill kernel.
+    expect_path = binding.AWQ_PATH_DECODE if M <= 32 else binding.AWQ_PATH_PREFILL
     assert path == expect_path
     y = run_gemm(d, M=M)
     del d
@@ -236,6 +238,7 @@ def test_gemm_config_parity(name, Mmax, M, g):
     ("mlp_down_k14336_n4096", 4096, -1, 3),
     ("prefill_qkv_m2048_k4096_n12288", 2048, 128, 256),
     ("mlp_down_k14336_n4096", 4096, 128, 256),
+    ("midm_k8192_n7168", 128, 128, 32),   # decode, two row blocks
 ])
 def test_one_hot_rows_exact(name, Mmax, g, M):
     """x rows one-hot at k_i, no bias: y[i] must equal the float16
@@ -313,6 +316,31 @@ def test_forced_path_and_tails(path, M, K, N, g, bias):
     y = run_gemm(d, path=path)
     ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
     assert_within_tol(y, ref, f"{path} M={M} K={K} N={N} g={g}")
+
+
+# Decode with two 16-row MFMA blocks (17-32 rows): the streaming variant with
+# one quantisation group per wave, split K summed by the second kernel.
+@pytest.mark.parametrize("M,K,N,g,bias,opts", [
+    (17, 8192, 7168, 128, True, None),                  # planner's choice: 4 steps, 16 splits
+    (32, 8192, 7168, 128, False, None),
+    (24, 14336, 4096, -1, True, None),                  # eight waves (14 splits), one group
+    (32, 4096, 4096, 64, True, {"force_path": "decode"}),                   # 2 steps per wave
+    (29, 2080, 96, 32, True, {"force_path": "decode"}),  # 1 step, K tail, one partial tile
+    (31, 1024, 512, 128, True, {"force_path": "decode", "decode_steps": 4}),
+    (18, 2048, 256, 128, True, {"force_path": "decode", "decode_waves": 8}),
+    (32, 256, 64, -1, True, {"force_path": "decode"}),   # one split: no exchange
+    (20, 4096, 2048, 64, False, {"force_path": "decode", "decode_steps": 4}),  # 4 would span
+                                                                               # groups: 2 taken
+])
+def test_decode_two_row_blocks(M, K, N, g, bias, opts):
+    say(f"decode two blocks M={M} K={K} N={N} g={g} opts={opts}")
+    p = awq_inputs.make_inputs(M, K, N, g, seed=M * 3 + K + N, bias=bias)
+    d = to_dev(p)
+    with awq.options(**(opts or {})):
+        assert awq.gemm_plan(M, K, N, g)[0] == binding.AWQ_PATH_DECODE
+    y = run_gemm(d, opts=opts)
+    ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
+    assert_within_tol(y, ref, f"decode two blocks M={M} K={K} N={N} g={g}")
 
 
 WIDE = {"prefill_bn": 192}
@@ -436,7 +464,7 @@ def test_empty_batch_and_leading_dims():
     assert_within_tol(y3.reshape(6, 128).cpu().numpy(), ref, "leading dims")
 
 
-@pytest.mark.parametrize("M", [1, 16, 256, 2048])
+@pytest.mark.parametrize("M", [1, 16, 32, 256, 2048])
 def test_deterministic_repeats(M):
     """Split-K partials are summed in a fixed order: repeats are bitwise equal."""
     say(f"determinism M={M}")

@@ -196,10 +196,16 @@ def test_prefill_split_k_plan(M, K, N, g, splits):
     4 MiB accumulator region, then one fp32 partial per split per output
     element; none without a split."""
     assert _prefill_splits_expected(M, K, N) == splits
-    path, ws = awq.gemm_plan(M, K, N, g)
+    with awq.options(force_path="prefill"):
+        path, ws = awq.gemm_plan(M, K, N, g)
     assert path == binding.AWQ_PATH_PREFILL
     assert ws == (0 if splits == 1 else 4 * 65536 * 16 + splits * M * N * 4)
-    assert awq.gemm_workspace_size(M, K, N, g) == ws
+    # The workspace size covers every kernel family that can run the problem:
+    # up to 32 rows the decode kernel's too.
+    if M > 32:
+        assert awq.gemm_workspace_size(M, K, N, g) == ws
+    else:
+        assert awq.gemm_workspace_size(M, K, N, g) >= ws
 
 
 def test_plan_unaligned_x_falls_back_to_generic():
@@ -612,3 +618,48 @@ def test_two_launch_exchange_takes_eight_waves_past_sixteen_splits():
         path, ws = awq.gemm_plan(M, K, N, 128)
         assert path == binding.AWQ_PATH_DECODE
         assert ws - fixed == splits * M * N * 4, (M, K, N)
+
+
+@pytest.mark.parametrize("M,K,N,g,path", [
+    (17, 8192, 7168, 128, binding.AWQ_PATH_DECODE),
+    (32, 8192, 7168, 128, binding.AWQ_PATH_DECODE),
+    (32, 14336, 4096, -1, binding.AWQ_PATH_DECODE),
+    (33, 8192, 7168, 128, binding.AWQ_PATH_PREFILL),    # above two row blocks
+    (20, 4096, 4096, 64, binding.AWQ_PATH_PREFILL),     # weight below 2^25 elements
+    (32, 4096, 12288, 32, binding.AWQ_PATH_PREFILL),    # one group per wave: 32 splits, partials
+                                                        # above half the packed weight
+    (32, 8192, 7176, 128, binding.AWQ_PATH_PREFILL),    # N % 32 != 0: no streaming variant
+])
+def test_plan_two_block_decode(M, K, N, g, path):
+    """17-32 rows run the decode kernel's two-block form where the weight has
+    at least 2^25 elements and the split partials are at most half the
+    packed weight's bytes (16 * splits * M <= K); otherwise the prefill
+    kernel."""
+    got, ws = awq.gemm_plan(M, K, N, g)
+    assert got == path
+    if path == binding.AWQ_PATH_DECODE:
+        splits = (ws - 4 * 65536 * 16) // (M * N * 4)
+        assert ws == 4 * 65536 * 16 + splits * M * N * 4
+        assert 16 * splits * M <= K
+
+
+def test_plan_two_block_decode_limits():
+    """Forcing the decode kernel: 33 rows cannot run it; 17-32 rows take a
+    step count whose rows stay in one group (an override that would span
+    groups is ignored); the fused x gather stays within one row block."""
+    with awq.options(force_path="decode"):
+        with pytest.raises(awq.AwqError):
+            awq.gemm_plan(33, 8192, 7168, 128)
+        with pytest.raises(awq.AwqError):
+            awq.gemm_plan(20, 8192, 7176, 128)     # register variant: 16 rows at most
+        _, ws = awq.gemm_plan(20, 4096, 7168, 64)
+        assert ws == 4 * 65536 * 16 + (4096 // (4 * 32 * 2)) * 20 * 7168 * 4   # 2 steps
+        with awq.options(decode_steps=4):
+            _, ws4 = awq.gemm_plan(20, 4096, 7168, 64)
+            assert ws4 == ws
+            _, ws16 = awq.gemm_plan(16, 4096, 7168, 64)                     # one block: taken
+            assert ws16 == 4 * 65536 * 16 + (4096 // (4 * 32 * 4)) * 16 * 7168 * 4
+    with pytest.raises(awq.AwqError):
+        awq.set_option("decode_gather_max_m", 17)
+    awq.set_option("decode_gather_max_m", 16)
+    awq.set_option("decode_gather_max_m", None)

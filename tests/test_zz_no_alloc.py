@@ -67,6 +67,7 @@ PAIRS = [
     ((16, 8192, 7168, 128, True), (1, 8192, 1280, 128, False)),
     ((64, 8192, 7168, 128, True), (4, 256, 128, 64, True)),
     ((4, 14336, 4096, -1, False), (2, 2048, 512, 128, True)),
+    ((24, 14336, 4096, 128, True), (17, 8192, 7168, 128, False)),   # two-block decode
 ]
 
 
@@ -90,6 +91,23 @@ def test_noalloc_repeats_are_identical():
         torch.cuda.synchronize()
         for o in outs[1:]:
             assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_noalloc_two_block_decode_beyond_the_scratch_runs_prefill():
+    """17-32 rows whose decode plan needs more workspace than the scratch
+    holds: awq_gemm_noalloc runs the prefill kernel instead, bit for bit
+    what awq_gemm computes with that kernel forced, and within the oracle's
+    tolerance."""
+    M, K, N, g = 32, 8192, 14336, 128
+    path, ws = awq.gemm_plan(M, K, N, g)
+    assert path == binding.AWQ_PATH_DECODE and ws > binding.AWQ_NOALLOC_SCRATCH_BYTES
+    say(f"awq_gemm_noalloc two-block decode over the scratch M={M} K={K} N={N}")
+    p, d = problem(M, K, N, g, seed=13, bias=True)
+    got = awq.gemm_noalloc(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], g)
+    with awq.options(force_path="prefill"):
+        ref = awq.gemm(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], g)
+    torch.cuda.synchronize()
+    check(p, g, ref.cpu().numpy(), got.cpu().numpy(), "noalloc fallback to prefill")
 
 
 def test_noalloc_rejects_problems_beyond_the_scratch():
