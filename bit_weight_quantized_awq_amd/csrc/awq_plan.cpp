@@ -240,7 +240,8 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
     const int waves = pl.decode_waves;
     // Two row blocks need one group per wave.
     const bool two_blocks = p.M > kDecodeBlockM;
-    int steps = override_or_zero(AWQ_OPT_DECODE_STEPS);
+    const int steps_opt = override_or_zero(AWQ_OPT_DECODE_STEPS);
+    int steps = steps_opt;
     if (steps != 0 && (decode_splits(p, pl.decode_lds, steps, waves) > kDecodeMaxSplits ||
                        (two_blocks && !decode_single_group(p, steps))))
       steps = 0;
@@ -267,12 +268,23 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
       steps = single_enough ? single_enough : (enough ? enough : (most ? most : 8));
     }
     // Above the atomic exchange every split's partials are stored and read
-    // back by the sum kernel: past kDecodeFourWaveMaxSplits splits of four
-    // waves, eight waves of the same steps halve them (K = 14336, N = 4096,
-    // M = 16: 16.1 -> 15.3 us; at 16 splits four waves stay ahead).
-    if (pl.decode_lds && waves_opt == 0 && !decode_atomic_exchange(p.M, p.N) && steps == 4 &&
-        decode_splits(p, true, steps, 4) > kDecodeFourWaveMaxSplits)
-      pl.decode_waves = 8;
+    // back by the sum kernel, so eight waves of four steps (half the splits
+    // of four waves, one group per wave) are taken whenever their work-groups
+    // make one resident round that fills the CUs: K = 8192, N = 7168, M = 16:
+    // 14.7 -> 14.0 us, M = 32: 19.6 -> 18.2 us; K = 4096, N = 11008, M = 16
+    // (against 2 steps of four waves): 16.5 -> 13.3 us; K = 14336, N = 4096,
+    // M = 16: 16.1 -> 15.3 us.  Two rounds (K = 8192, N = 14336, 448
+    // work-groups) or idle CUs (56-64 work-groups) lose.
+    if (pl.decode_lds && waves_opt == 0 && steps_opt == 0 && !decode_atomic_exchange(p.M, p.N) &&
+        decode_single_group(p, 4)) {
+      const int64_t s8 = decode_splits(p, true, 4, 8);
+      const int64_t wg8 = pl.n_tiles * s8;
+      if (s8 <= kDecodeMaxSplits && wg8 >= kDecodeEightWaveMinWGs &&
+          wg8 <= kDecodeEightWaveMaxWGs) {
+        steps = 4;
+        pl.decode_waves = 8;
+      }
+    }
     // Eight waves of eight steps would need 272 KiB of LDS: four waves then.
     if (pl.decode_waves == 8 && steps == 8) pl.decode_waves = 4;
     pl.steps = steps;

@@ -33,7 +33,10 @@ constexpr int64_t kDecodeTwoBlockMinWeights = int64_t{1} << 25;
 constexpr int kDecodeMaxSplits = 63;
 constexpr int kDecodeAtomicMaxM = 4;
 constexpr int kDecodeGatherMaxM = 4;
-constexpr int kDecodeFourWaveMaxSplits = 16;   // above: eight waves per work-group
+// Eight waves of four steps for the two-launch exchange when they give this
+// many work-groups (one resident round of 139 KiB work-groups, one per CU).
+constexpr int64_t kDecodeEightWaveMinWGs = 160;
+constexpr int64_t kDecodeEightWaveMaxWGs = 256;
 constexpr int kDecodeAtomicMaxN = 65536;
 // The atomic exchange for at most kDecodeAtomicMaxM rows (one device-scope
 // atomic per output element and split); above, plain partial stores summed

@@ -607,15 +607,25 @@ def test_eight_wave_decode_plan():
     assert a - fixed == (K // (8 * 32 * 4)) * 16 * N * 4
 
 
-def test_two_launch_exchange_takes_eight_waves_past_sixteen_splits():
-    """Batches above four rows (the two-launch exchange) whose four-wave
-    plan would have more than 16 splits (K = 14336: 28) run eight waves per
-    work-group (14 splits); K = 8192 (16 splits) and the atomic exchange's
-    batches keep four."""
+def test_two_launch_exchange_takes_eight_waves_filling_one_round():
+    """Batches above four rows (the two-launch exchange) run eight waves of
+    four steps per work-group (half the splits) when that gives 160-256
+    work-groups with one group per wave; otherwise, and for the atomic
+    exchange's batches, the four-wave plan."""
     fixed = 4 * 65536 * 16
-    for M, K, N, splits in [(16, 14336, 4096, 14), (5, 14336, 4096, 14), (16, 8192, 7168, 16),
-                            (1, 14336, 4096, 28), (4, 14336, 4096, 28)]:
-        path, ws = awq.gemm_plan(M, K, N, 128)
+    for M, K, N, splits in [
+            (16, 14336, 4096, 14),   # 16 tiles x 14 = 224 work-groups
+            (5, 14336, 4096, 14),
+            (16, 8192, 7168, 8),     # 28 x 8 = 224
+            (32, 8192, 7168, 8),     # two row blocks
+            (16, 4096, 11008, 4),    # 43 x 4 = 172 (four waves would take 2 steps, 16 splits)
+            (12, 8192, 14336, 16),   # eight waves: 448 work-groups, two rounds: four waves
+            (8, 4096, 4096, 32),     # eight waves: 64 work-groups: four waves of 1 step
+            (16, 4096, 7168, 16),    # g = 64 below: 4 steps would span groups
+            (1, 14336, 4096, 28),    # atomic exchange: four waves
+            (4, 8192, 7168, 16)]:
+        g = 64 if (M, K, N) == (16, 4096, 7168) else 128
+        path, ws = awq.gemm_plan(M, K, N, g)
         assert path == binding.AWQ_PATH_DECODE
         assert ws - fixed == splits * M * N * 4, (M, K, N)
 
