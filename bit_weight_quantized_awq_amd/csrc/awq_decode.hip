@@ -205,8 +205,17 @@ __device__ __forceinline__ void store_partials(const float (&part)[MM],
 // group size is a multiple of the wave's 32*STEPS rows, or there is one
 // group), so the scale is applied once after all steps.  Otherwise each
 // 32-row step (which never straddles a group) is scaled on its own.
+// Four waves per SIMD cap a wave at 128 registers; the plans that hold
+// more words in flight (eight steps, or four steps scaled per step) take
+// two, which keeps them from spilling.
 template <int STEPS, bool SINGLE_GROUP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_kernel(
+constexpr int decode_kernel_min_waves() {
+  return (STEPS >= 8 || (STEPS >= 4 && !SINGLE_GROUP)) ? 2 : 4;
+}
+
+template <int STEPS, bool SINGLE_GROUP>
+__global__ __launch_bounds__(256) __attribute__((
+    amdgpu_waves_per_eu(decode_kernel_min_waves<STEPS, SINGLE_GROUP>(), 8))) void decode_kernel(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint32_t* __restrict__ qz, const _Float16* __restrict__ sc,
     const _Float16* __restrict__ bias, _Float16* __restrict__ y,
