@@ -66,6 +66,7 @@ def _replay_and_compare(fn_capture, fn_eager, x_static, y_static, M, K, seed):
 @pytest.mark.parametrize("M,K,N,g,bias", [
     (1, 8192, 7168, 128, False),      # decode, atomic exchange
     (16, 4096, 2048, 64, True),       # decode, two-launch exchange
+    (24, 8192, 7168, 128, True),      # decode, two row blocks, eight waves
     (4, 14336, 4096, -1, False),      # decode, one group
     (256, 14336, 4096, 128, False),   # prefill, split K + reduce kernel
     (512, 2048, 4096, 128, True),     # prefill, one split
@@ -96,7 +97,7 @@ def test_graph_replay_matches_eager(M, K, N, g, bias):
         assert torch.count_nonzero(ws[:min(ZERO_REGION, ws.numel())]).item() == 0
 
 
-@pytest.mark.parametrize("M,K,N", [(4, 8192, 7168), (64, 8192, 7168)])
+@pytest.mark.parametrize("M,K,N", [(4, 8192, 7168), (17, 8192, 7168), (64, 8192, 7168)])
 def test_graph_replay_noalloc(M, K, N):
     say(f"graph replay noalloc M={M} K={K} N={N}")
     g = 128
