@@ -660,7 +660,8 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line, print one JSON line per point of "
                          "every named workload (all batch sizes and group sizes), each "
-                         "against its binding roof: HBM for M <= 16, MFMA for larger M")
+                         "against its binding roof: whichever of HBM bytes and MFMA flops "
+                         "takes longer at peak")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -68,7 +68,7 @@ enum awq_status {
 
 /* Kernel families that awq_gemm can run (see awq_gemm_plan). */
 enum awq_path {
-  AWQ_PATH_DECODE = 1,  /* split-K MFMA skinny GEMM, M <= 16 */
+  AWQ_PATH_DECODE = 1,  /* split-K MFMA skinny GEMM, M <= 16 (17-32 on large weights) */
   AWQ_PATH_PREFILL = 2, /* LDS-tiled MFMA GEMM with dequantisation into LDS */
   AWQ_PATH_GENERIC = 3  /* any legal shape or alignment; slow */
 };

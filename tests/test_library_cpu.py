@@ -247,7 +247,7 @@ def test_forced_path():
         assert awq.gemm_plan(2048, 4096, 12288, 128)[0] == binding.AWQ_PATH_GENERIC
     with awq.options(force_path="decode"):
         with pytest.raises(awq.AwqError):
-            awq.gemm_plan(64, 4096, 4096, 128)          # decode handles M <= 16 only
+            awq.gemm_plan(64, 4096, 4096, 128)          # decode handles M <= 32 only
 
 
 def test_option_values_checked():
