@@ -7,24 +7,21 @@
 // stream of packed weights from HBM (0.5 byte per weight), so the kernel is
 // built around keeping that stream saturated:
 //
-// * Work-group = 4 waves covering 256 output columns (32 packed words per row,
-//   128 contiguous bytes) and 2 x 32*STEPS input rows.  Waves 0/2 take words
-//   0..15 of the tile, waves 1/3 words 16..31; waves 0/1 take the first half
-//   of the rows, 2/3 the second.
-// * Lane l of a wave owns word column (l % 16) and the 8-row block (l / 16) of
-//   each 32-row step: it loads 8 words (one per row) of its column.  Each
-//   row's 16 words are one 64-byte contiguous segment, and the two waves on
-//   a row make it a full 128-byte line.  All loads of a wave are issued
-//   before any arithmetic.
-// * Unpack: two rows' words are byte-shuffled so that nibble j of both sits
-//   in the two halves of one register; OR-ing into float16 1024.0 gives the
-//   exact pair (1024 + q_k, 1024 + q_k+1), and a packed subtraction of
-//   (1024 + z) gives the exact integers q - z as float16.
+// * Two variants.  Streaming (N % 32 == 0, decode_lds_kernel): 4 or 8 waves
+//   over the same 256 output columns (32 packed words, 128 contiguous bytes
+//   per row) and consecutive 32*STEPS-row K ranges; each wave copies its rows
+//   HBM -> LDS with 16-byte direct-to-LDS loads, all issued before any
+//   arithmetic, and reads back per 32-row step the 8 rows of its word column.
+//   Register (other N, decode_kernel): 2 x 2 waves, each lane loading the 8
+//   words of its column and 8-row block per step into registers.
+// * Unpack: the streaming variant forms exact normal float16 operands from
+//   byte pairs of two rows with four VALU ops per four weights (see
+//   decode_lds_kernel); the register variant ORs nibble pairs into float16
+//   1024.0 and subtracts (1024 + z), giving the exact integers q - z.
 // * MFMA v_mfma_f32_16x16x32_f16: A = 16 rows of x (rows >= M are zero),
-//   B = (q - z) for 16 columns x 32 rows, one MFMA per nibble position j, so
-//   MFMA j covers columns 8*word + j.  Accumulation is fp32.  Batches of
-//   17-32 rows (streaming variant, one group per wave) take two 16-row
-//   blocks of x, each multiplied with the same dequantised operands.
+//   B = dequantised weights for 16 columns x 32 rows.  Accumulation is fp32.
+//   Batches of 17-32 rows (streaming variant, one group per wave) take two
+//   16-row blocks of x, each multiplied with the same dequantised operands.
 // * The scale is applied once per group to the fp32 group partial:
 //   sum_k x*(q - z)*s = s * sum_k x*(q - z) exactly in real arithmetic; this
 //   differs from rounding each dequantised weight to float16 only by that
@@ -53,7 +50,8 @@
 namespace awq {
 namespace {
 
-// Split-K exchange state in the workspace (all of it zero between calls).
+// Split-K exchange state in the workspace (acc and mask are zero between
+// calls; partials are overwritten by every call that uses them).
 struct SplitK {
   unsigned long long* acc;   // [M][N]: fixed-point sum, contribution count (atomic exchange)
   unsigned long long* mask;  // [M][N]: splits that sent a float partial (atomic exchange)
@@ -359,10 +357,10 @@ __global__ __launch_bounds__(256) __attribute__((
 // word column -- the transposition the MFMA operand layout needs -- without
 // the packed words ever occupying registers in flight.
 //
-// Work-group: 4 waves over the same 256 columns (two MFMA column sets of 16
-// words per wave) and consecutive 32*STEPS-row ranges; the four K-ranges
-// meet in LDS, the work-groups of a column tile meet through the split-K
-// exchange.  The 8-row blocks sit 1088 bytes apart in LDS so that the 64
+// Work-group: 4 or 8 waves (WAVES) over the same 256 columns (two MFMA
+// column sets of 16 words per wave) and consecutive 32*STEPS-row ranges; the
+// K-ranges meet in LDS, the work-groups of a column tile meet through the
+// split-K exchange.  The 8-row blocks sit 1088 bytes apart in LDS so that the 64
 // lanes of a transposed read (16 word columns x 4 row blocks) hit 64 distinct
 // banks.
 constexpr int kLdsBlockPitch = 1088;  // 8 rows x 128 bytes + 64-byte skew
