@@ -121,7 +121,8 @@ int run_gemm(const Problem& p, const void* x, const void* qweight, const void* q
   switch (pl.path) {
     case AWQ_PATH_DECODE:
       e = awq::launch_decode(xh, qw, qz, sc, bh, yh, iM, iK, iN, ig, iG, pl.steps, pl.splits,
-                             pl.n_tiles, pl.decode_lds, pl.decode_waves, workspace,
+                             pl.n_tiles, pl.decode_lds, pl.decode_waves, pl.decode_atomic,
+                             workspace,
                              fused_gather ? perm : nullptr,
                              fused_gather ? static_cast<int>(Kx) : iK, s);
       break;

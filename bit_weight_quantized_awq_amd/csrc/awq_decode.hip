@@ -29,11 +29,12 @@
 //   float16 dequantised weight exactly.
 // * Reduction: the K-ranges of a work-group meet in LDS; the work-groups of a
 //   column tile then meet in the workspace, deterministically in either of
-//   two ways.  For M <= 4, one 64-bit device-scope atomic per output element
+//   two ways, chosen by the planner.  For M <= 4 and few enough atomics per
+//   call, one 64-bit device-scope atomic per output element
 //   (splitk_atomic): each adds its partial as a 2^-24 fixed-point integer
 //   with a contribution count, and the one whose returned sum shows every
-//   split has arrived writes y -- one atomic round trip.  For larger M the
-//   atomic count grows past what the memory-side atomic units sustain, so
+//   split has arrived writes y -- one atomic round trip.  Past that, the
+//   atomic count outgrows what the memory-side atomic units sustain, so
 //   each work-group stores its partials with plain stores and a second
 //   kernel on the same stream sums them in split order (decode_sum_kernel).
 //   The accumulator region of the workspace is zero again when the atomic
@@ -57,6 +58,7 @@ struct SplitK {
   unsigned long long* mask;  // [M][N]: splits that sent a float partial (atomic exchange)
   float* partial;            // [splits][M][N]: partials (all of them for the two-launch
                              // exchange, the float ones for the atomic exchange)
+  int atomic;                // the planner's exchange: 1 atomic, 0 two launches
 };
 // acc layout: bits 0-51 sum of (v + 2^45) over fixed-point contributions,
 // v = rint(p * 2^24) with |p| < 2^21 (so each term is below 2^46 and up to
@@ -224,6 +226,7 @@ __global__ __launch_bounds__(256) __attribute__((
   pin_arg(sk.acc);
   pin_arg(sk.mask);
   pin_arg(sk.partial);
+  pin_arg(sk.atomic);
 
   const int NW = N >> 3;
   const int tid = threadIdx.x;
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(256) __attribute__((
   }
 
   if (!nvalid) return;
-  if (decode_atomic_exchange(M, N))
+  if (sk.atomic)
     splitk_atomic(part, sk, bias, y, M, N, n, split, splits);
   else
     store_partials(part, sk.partial, M, N, n, split);
@@ -423,6 +426,7 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   pin_arg(sk.acc);
   pin_arg(sk.mask);
   pin_arg(sk.partial);
+  pin_arg(sk.atomic);
   constexpr int kWaveBytes = STEPS * 4 * kLdsBlockPitch;
 
   const int NW = N >> 3;
@@ -732,7 +736,7 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
     return;
   }
   if (!nvalid) return;
-  if (decode_atomic_exchange(M, N))
+  if (sk.atomic)
     splitk_atomic(part, sk, bias, y, M, N, n, split, splits);
   else
     store_partials(part, sk.partial, M, N, n, split);
@@ -782,7 +786,7 @@ __global__ __launch_bounds__(64) void decode_sum_kernel(const float* __restrict_
 // two-launch one.
 hipError_t launch_sum(const SplitK& sk, const _Float16* bias, _Float16* y, int M, int N,
                       int splits, hipStream_t stream) {
-  if (splits <= 1 || decode_atomic_exchange(M, N)) return hipSuccess;
+  if (splits <= 1 || sk.atomic) return hipSuccess;
   const size_t quads = static_cast<size_t>(M) * N / 4;
   hipLaunchKernelGGL(decode_sum_kernel, dim3(static_cast<unsigned>((quads + 63) / 64)), dim3(64), 0,
                      stream, sk.partial, bias, y, M, N, splits);
@@ -866,17 +870,19 @@ hipError_t launch_steps(const _Float16* x, const uint32_t* qweight, const uint32
 hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                          const _Float16* scales, const _Float16* bias, _Float16* y,
                          int M, int K, int N, int g, int G, int steps, int splits,
-                         int n_tiles, bool lds_variant, int waves, void* workspace,
-                         const int32_t* perm, int Kx, hipStream_t stream) {
+                         int n_tiles, bool lds_variant, int waves, bool atomic,
+                         void* workspace, const int32_t* perm, int Kx, hipStream_t stream) {
   if (waves != 4 && !(lds_variant && waves == 8)) return hipErrorInvalidValue;
   if (M > kDecodeBlockM && (!lds_variant || perm)) return hipErrorInvalidValue;
+  if (atomic && !decode_atomic_capable(M, N)) return hipErrorInvalidValue;
   // Workspace: accumulator region ([M][N] accumulators, then [M][N] masks),
   // then [splits][M][N] partials.
   char* ws = static_cast<char*>(workspace);
   const size_t mn = static_cast<size_t>(M) * N;
   const SplitK sk{ws ? reinterpret_cast<unsigned long long*>(ws) : nullptr,
                   ws ? reinterpret_cast<unsigned long long*>(ws + mn * 8) : nullptr,
-                  ws ? reinterpret_cast<float*>(ws + kAtomicRegionBytes) : nullptr};
+                  ws ? reinterpret_cast<float*>(ws + kAtomicRegionBytes) : nullptr,
+                  atomic ? 1 : 0};
   if (lds_variant && perm) {
     switch (steps) {
       case 1: return launch_lds_steps<1, true>(x, qweight, qzeros, scales, bias, y, M, K, N, g,

@@ -109,8 +109,8 @@ hipError_t launch_gather_cols(const _Float16* x, const int32_t* perm, _Float16* 
 hipError_t launch_decode(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                          const _Float16* scales, const _Float16* bias, _Float16* y,
                          int M, int K, int N, int g, int G, int steps, int splits,
-                         int n_tiles, bool lds_variant, int waves, void* workspace,
-                         const int32_t* perm, int Kx, hipStream_t stream);
+                         int n_tiles, bool lds_variant, int waves, bool atomic,
+                         void* workspace, const int32_t* perm, int Kx, hipStream_t stream);
 hipError_t launch_prefill(const _Float16* x, const uint32_t* qweight, const uint32_t* qzeros,
                           const _Float16* scales, const _Float16* bias, _Float16* y,
                           int M, int K, int N, int group_shift, int bm, int bn,

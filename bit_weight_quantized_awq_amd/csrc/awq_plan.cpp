@@ -275,7 +275,10 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
     // (against 2 steps of four waves): 16.5 -> 13.3 us; K = 14336, N = 4096,
     // M = 16: 16.1 -> 15.3 us.  Two rounds (K = 8192, N = 14336, 448
     // work-groups) or idle CUs (56-64 work-groups) lose.
-    if (pl.decode_lds && waves_opt == 0 && steps_opt == 0 && !decode_atomic_exchange(p.M, p.N) &&
+    pl.decode_atomic = decode_atomic_capable(p.M, p.N) &&
+                       decode_splits(p, pl.decode_lds, steps, pl.decode_waves) * p.M * p.N <
+                           kDecodeAtomicMaxOps;
+    if (pl.decode_lds && waves_opt == 0 && steps_opt == 0 && !pl.decode_atomic &&
         decode_single_group(p, 4)) {
       const int64_t s8 = decode_splits(p, true, 4, 8);
       const int64_t wg8 = pl.n_tiles * s8;

@@ -38,10 +38,15 @@ constexpr int kDecodeGatherMaxM = 4;
 constexpr int64_t kDecodeEightWaveMinWGs = 160;
 constexpr int64_t kDecodeEightWaveMaxWGs = 256;
 constexpr int kDecodeAtomicMaxN = 65536;
-// The atomic exchange for at most kDecodeAtomicMaxM rows (one device-scope
-// atomic per output element and split); above, plain partial stores summed
-// by a second kernel.
-constexpr bool decode_atomic_exchange(int64_t M, int64_t N) {
+// The atomic exchange (one device-scope atomic per output element and
+// split) is possible for at most kDecodeAtomicMaxM rows, and the planner takes
+// it while a call issues fewer than kDecodeAtomicMaxOps atomics; otherwise
+// plain partial stores summed by a second kernel.  Same box, two launches
+// against atomics: K = 4096, N = 4096, M = 4 (524K atomics): 8.5 against
+// 10.4 us; K = 8192, N = 7168, M = 4 (458K): 12.3 against 12.7 us; M = 3
+// (344K): 12.2 against 11.9 us; M = 1 (115K): 11.7 against 10.0 us.
+constexpr int64_t kDecodeAtomicMaxOps = 380000;
+constexpr bool decode_atomic_capable(int64_t M, int64_t N) {
   return M <= kDecodeAtomicMaxM && N <= kDecodeAtomicMaxN;
 }
 constexpr size_t kAtomicRegionBytes = static_cast<size_t>(kDecodeAtomicMaxM) * kDecodeAtomicMaxN * 16;
@@ -92,6 +97,7 @@ struct Plan {
   int prefill_bn;     // prefill: tile width (kPrefillBN or kPrefillWideBN)
   int prefill_bm;     // prefill: tile height (64, 128 or kPrefillBM)
   int decode_waves;   // decode, LDS variant: waves along K per work-group (4 or 8)
+  bool decode_atomic; // decode, split K: the atomic exchange (else two launches)
   bool prefill_packed;  // prefill: the packed-weight 256-row tile (one split)
   int packed_wm;        // packed tile: waves along M (1 or 2)
 };

@@ -142,9 +142,11 @@ int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size,
  * concurrently (different streams) must not share a workspace.  A HIP graph
  * that captured a call keeps its workspace pointer: the buffer must stay
  * allocated (and unused by anything else) for as long as the graph may be
- * replayed.  A split decode call of more than four rows, and a split prefill
- * call, enqueue two kernels on `stream` (the second sums the fp32 split
- * partials in split order); every other call enqueues one.
+ * replayed.  A split prefill call, and a split decode call of more than
+ * four rows or of so many splits x rows x columns that the atomic exchange
+ * would issue 380K or more atomics, enqueue two kernels on `stream` (the
+ * second sums the fp32 split partials in split order); every other call
+ * enqueues one.
  * M == 0 is a no-op that returns AWQ_SUCCESS (x and y may then be NULL). */
 int awq_gemm(const void* x, const void* qweight, const void* qzeros,
              const void* scales, const void* bias, void* y,

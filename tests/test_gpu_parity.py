@@ -343,6 +343,32 @@ def test_decode_two_row_blocks(M, K, N, g, bias, opts):
     assert_within_tol(y, ref, f"decode two blocks M={M} K={K} N={N} g={g}")
 
 
+# The split-K exchange the planner picks: the atomic exchange for at most
+# four rows while a call issues fewer than 380K atomics, else two launches
+# (also for M <= 4).  Each case against the oracle and 20 repeats bitwise.
+@pytest.mark.parametrize("M,K,N,g,bias", [
+    (3, 8192, 7168, 128, True),     # 344K atomics: atomic exchange
+    (4, 8192, 7168, 128, False),    # 459K: two launches, eight waves
+    (4, 4096, 4096, 128, True),     # 524K: two launches, four waves of one step
+    (4, 4096, 12288, 64, False),    # two launches; g = 64: two steps, four waves
+    (2, 14336, 4096, -1, True),     # 229K: atomic exchange, one group
+])
+def test_decode_exchange_choice(M, K, N, g, bias):
+    say(f"decode exchange M={M} K={K} N={N} g={g}")
+    p = awq_inputs.make_inputs(M, K, N, g, seed=M + K + N + 7, bias=bias)
+    d = to_dev(p)
+    assert awq.gemm_plan(M, K, N, g)[0] == binding.AWQ_PATH_DECODE
+    y = run_gemm(d)
+    ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
+    assert_within_tol(y, ref, f"decode exchange M={M} K={K} N={N} g={g}")
+    first = awq.gemm(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], g).clone()
+    outs = [awq.gemm(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], g)
+            for _ in range(20)]
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), first.view(torch.int16))
+
+
 WIDE = {"prefill_bn": 192}
 
 

@@ -608,10 +608,11 @@ def test_eight_wave_decode_plan():
 
 
 def test_two_launch_exchange_takes_eight_waves_filling_one_round():
-    """Batches above four rows (the two-launch exchange) run eight waves of
-    four steps per work-group (half the splits) when that gives 160-256
-    work-groups with one group per wave; otherwise, and for the atomic
-    exchange's batches, the four-wave plan."""
+    """Batches on the two-launch exchange (above four rows, or when the atomic
+    exchange would issue 380K or more atomics) run eight waves of four steps
+    per work-group (half the splits) when that gives 160-256 work-groups with
+    one group per wave; otherwise, and for the atomic exchange's batches, the
+    four-wave plan."""
     fixed = 4 * 65536 * 16
     for M, K, N, splits in [
             (16, 14336, 4096, 14),   # 16 tiles x 14 = 224 work-groups
@@ -623,7 +624,9 @@ def test_two_launch_exchange_takes_eight_waves_filling_one_round():
             (8, 4096, 4096, 32),     # eight waves: 64 work-groups: four waves of 1 step
             (16, 4096, 7168, 16),    # g = 64 below: 4 steps would span groups
             (1, 14336, 4096, 28),    # atomic exchange: four waves
-            (4, 8192, 7168, 16)]:
+            (3, 8192, 7168, 16),     # atomic: 16 x 3 x 7168 = 344K atomics
+            (4, 8192, 7168, 8),      # 16 x 4 x 7168 = 459K atomics: two launches, eight waves
+            (4, 4096, 4096, 32)]:    # 524K atomics: two launches (eight waves: 64 work-groups)
         g = 64 if (M, K, N) == (16, 4096, 7168) else 128
         path, ws = awq.gemm_plan(M, K, N, g)
         assert path == binding.AWQ_PATH_DECODE
