@@ -35,8 +35,9 @@
 // * The consumer waves run at a raised wave priority, so that an MFMA is
 //   never held back by producer work that could wait.
 // * Tile order: work-group ids are remapped so that each of the 8 XCDs (which
-//   receive ids round-robin) works on a contiguous range of tiles that share
-//   rows of x, keeping that slab resident in the XCD's L2.
+//   receive ids round-robin) works on a block of the tile grid (tile_of), so
+//   the tiles resident on one XCD share rows of x and columns of the weight
+//   through its L2.
 #include "awq_device.h"
 #include "awq_plan.h"
 
@@ -147,9 +148,13 @@ struct Frag {
   half8_t b[NB];
 };
 
-// Tile coordinates and K range of this work-group.  Work-group ids are
-// remapped so that each of the 8 XCDs (which receive ids round-robin) works
-// on a contiguous range of ids; ids run over the tiles of split 0, then of
+// Tile coordinates and K range of this work-group.  The 8 XCDs receive
+// work-group ids round-robin.  Without a split, each XCD takes one block of
+// the tile grid, 2 or 4 row tiles by the matching share of column tiles, so
+// that every column tile's weights reach 2 or 4 XCDs' L2 instead of all
+// eight (M = 2048, K = 4096, N = 12288: 252 -> 181 MB fetched per call, same
+// time); within the block row tiles run fastest.  Otherwise each XCD takes a
+// contiguous range of ids, which run over the tiles of split 0, then of
 // split 1, ..., so an XCD's tiles share rows of x and the same K range.
 struct Tile {
   int m0, n0;    // first row and column
@@ -161,9 +166,30 @@ template <int BM, int BN>
 __device__ __forceinline__ Tile tile_of(int n_tiles, int splits, int kps, int nkt) {
   int bid = blockIdx.x;
   const int nb = gridDim.x;
-  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
   const int tiles = nb / splits;
   Tile t;
+  // XCD blocks: XM x (8 / XM) XCDs over the (m_tiles, n_tiles) grid.
+  const int m_tiles = tiles / n_tiles;
+  int xm = 0;
+  if (splits == 1 && (nb & 7) == 0) {
+    if (m_tiles % 4 == 0 && n_tiles % 2 == 0) xm = 4;
+    else if (m_tiles % 2 == 0 && n_tiles % 4 == 0) xm = 2;
+  }
+  if (xm != 0) {
+    const int xn = 8 / xm;
+    const int xcd = bid & 7, r = bid >> 3;
+    const int mt_per = m_tiles / xm, nt_per = n_tiles / xn;
+    const int mt = (xcd / xn) * mt_per + r % mt_per;
+    const int nt = (xcd % xn) * nt_per + r / mt_per;
+    t.sp = 0;
+    t.tile = mt * n_tiles + nt;
+    t.m0 = mt * BM;
+    t.n0 = nt * BN;
+    t.kt0 = 0;
+    t.nks = min(kps, nkt);
+    return t;
+  }
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
   t.sp = bid / tiles;
   t.tile = bid - t.sp * tiles;
   const int mt = t.tile / n_tiles;
