@@ -3,31 +3,39 @@
 //
 // The product of the page "Predibase Lorax AWQ WQLinear" (Description, forward
 // step 2) is compute-bound at prefill sizes, so the dequantisation must be
-// amortised over many rows of x: each 256 x 128 output tile dequantises its
-// 64 x 128 weight slab once per K step into LDS and feeds it to all 256 rows.
+// amortised over many rows of x: each BM x BN output tile (up to 256 x 192)
+// dequantises its 64 x BN weight slab once per K step into LDS and feeds it
+// to all BM rows.
 //
-// * Work-group: 256 threads = 4 waves in a 2 x 2 grid; each wave owns a
-//   128 x 64 sub-tile = 4 x 2 blocks of v_mfma_f32_32x32x16_f16 (fp32
-//   accumulators, 128 per lane).  One work-group per CU (LDS-limited), so
-//   each SIMD runs one wave and all latency hiding is explicit.
-// * x tiles (256 rows x 64 k) move HBM -> LDS directly (16-byte buffer loads
+// * Work-group: 512 threads = 8 waves, 4 consumers in a 2 x 2 grid of
+//   (BM/2) x (BN/2) sub-tiles (fp32 accumulators in registers) and 4
+//   producers.  One work-group per CU (LDS-limited); each SIMD runs one
+//   consumer and one producer wave.
+// * Matrix instruction: 256-row tiles use v_mfma_f32_16x16x32_f16, the 64-
+//   and 128-row tiles v_mfma_f32_32x32x16_f16.  With random operands the
+//   chip runs this kernel at its power limit (about 1.46 GHz against 2.2 GHz
+//   for constant data), and the 16x16x32 form finishes the same flops with
+//   less energy: it reads and writes a quarter of the accumulator registers
+//   per product.
+// * x tiles (BM rows x 64 k) move HBM -> LDS directly (16-byte buffer loads
 //   with an LDS destination; no registers) into a 3-stage ring, two K steps
 //   ahead of the matrix cores.  Within each 128-byte row the eight 16-byte
 //   chunks are XOR-swizzled by (row / 2) % 8, so the 16-byte operand reads of
 //   16 consecutive rows hit 16 distinct bank groups.
-// * Packed weights (one word, four rows per thread), zeros and scales are
-//   loaded into registers two K steps ahead and dequantised one step ahead:
+// * Packed weights, zeros and scales are loaded by the producers into
+//   registers three K steps ahead and dequantised one step ahead:
 //   float16_RNE((q - z) * s), exactly the value awq_dequant writes, for two
 //   adjacent columns per packed float16 operation (byte shuffles place
 //   nibbles 2b and 2b+1 in the two halves, OR-ing into float16 1024.0 gives
 //   1024 + q exactly, then one packed subtract and one packed multiply).
 //   The weight tile is stored k-major ([k][n], 16-byte writes of 8 adjacent
-//   columns: conflict-free) in a 3-buffer ring and read back with
-//   ds_read_b64_tr_b16, whose 16-lane transpose turns four k-rows of four
-//   adjacent columns into the k-contiguous operand the matrix cores need.
-// * A K step runs as 16 sub-blocks, each two MFMAs with the LDS operand reads
-//   of the next k slice, one dequantised float16 pair and at most one global
-//   load placed between them, so that no unit's queue fills in a burst.
+//   columns: conflict-free) and read back with ds_read_b64_tr_b16, whose
+//   16-lane transpose turns four k-rows of four adjacent columns into the
+//   k-contiguous operand the matrix cores need.
+// * Consumers read each operand well before its MFMA and replace it in place
+//   after its last use; the last operands of a K step are multiplied after
+//   the next step's barrier, overlapping that step's first reads.  One
+//   barrier per K step.
 // * Every global load takes a thread-constant lane offset plus a uniform
 //   per-step offset in an SGPR; prefetches past the last K step re-read the
 //   last step (in bounds, never used).  Only when K % 64 != 0 does the last
@@ -58,12 +66,23 @@ struct Cfg {
   static_assert((BM == 64 || BM == 128 || BM == 256) && (BN == 128 || (BN == 192 && BM == 256)),
                 "tile shape");
   static constexpr int MI = BM / 64, NB = BN / 64, BST = BN == 192 ? 2 : 3, NDMA = BM / 32;
+  // 256-row tiles multiply with v_mfma_f32_16x16x32_f16 (MR x NC blocks of
+  // 16 x 16 per consumer wave), the smaller ones with 32x32x16 (MI x NB
+  // blocks of 32 x 32).
+  static constexpr bool MF16 = BM == 256;
+  static constexpr int MR = BM / 32, NC = BN / 32;
   static constexpr int kATileBytes = BM * BK * 2;
   static constexpr int kLoadsPerStep = 6 + NDMA;   // weight words/zeros/scales, x copies
 };
 template <int BN> constexpr int b_pitch() { return BN * 2 + 64; }   // bytes per k-row
 template <int BN> constexpr int b_tile_bytes() { return BK * b_pitch<BN>(); }
-template <int BM, int BN> constexpr int lds_bytes() {
+// Byte shift of weight-tile row k for the 16x16x32 operand reads: rows 8
+// apart are read by one transposing-read pass and would hit the same banks
+// at this pitch, so every other 8-row block sits 32 bytes further along its
+// row (inside the row's 64 padding bytes).
+template <int BM, int BN> __host__ __device__ constexpr int w_shift(int k) {
+  return Cfg<BM, BN>::MF16 ? ((k >> 3) & 1) * 32 : 0;
+}template <int BM, int BN> constexpr int lds_bytes() {
   return kAStages * Cfg<BM, BN>::kATileBytes + Cfg<BM, BN>::BST * b_tile_bytes<BN>();
 }
 static_assert(lds_bytes<256, 128>() == 156 * 1024 && lds_bytes<256, 192>() == 152 * 1024,
@@ -436,7 +455,9 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
   for (int r = 0; r < WR; ++r) q_off[r] = static_cast<uint32_t>((wrow + r) * NW + wcol) * 4u;
   const uint32_t z_off = static_cast<uint32_t>((wrow >> gsh) * NW + wcol) * 4u;
   const uint32_t s_off = static_cast<uint32_t>((wrow >> gsh) * N + 8 * wcol) * 2u;
-  char* const b_wr0 = b_ring + wrow * kBPitch + (BN == 128 ? 16 * (pt & 15) : 48 * (pt & 7));
+  // A thread's k-rows lie in one 8-row block, so they share one row shift.
+  char* const b_wr0 = b_ring + wrow * kBPitch + w_shift<BM, BN>(wrow) +
+                      (BN == 128 ? 16 * (pt & 15) : 48 * (pt & 7));
 
   // Per-step load parameters: uniform offsets of step k (clamped to the last
   // step; prefetches past the end re-read it and are never used) and, for a
@@ -767,6 +788,208 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
   }
 }
 
+// The 256-row tiles' consumers: the same 2 x 2 grid of (BM/2) x (BN/2)
+// sub-tiles, as MR x NC blocks of v_mfma_f32_16x16x32_f16 over 32-k slices.
+// Under the chip's power limit (random operands) this instruction finishes
+// the same flops sooner than 32x32x16: it moves a quarter of the accumulator
+// registers per product.
+//
+// Operands (lane = 16 * grp + i): x block rb: row 16*rb + i, k 8*grp .. +7 of
+// the slice (one 16-byte read); weight block cb: column 16*cb + i, the same
+// k (two transposing reads of four k-rows each; source lane i of a 16-lane
+// group reads k-row i/4 (+4), columns 4*(i%4) .. +3).  Accumulator register r
+// of block (rb, cb): row 16*rb + 4*grp + r, column 16*cb + i.
+//
+// Order: x-block major.  The NC weight blocks of a slice stay in registers
+// while the x blocks stream through two registers (block rb+1 is read during
+// the NC MFMAs of block rb); during the slice's last x block each weight
+// block is replaced by the next slice's right after its MFMA.  At the end of
+// a K step that last x block is multiplied after the next step's barrier,
+// overlapping that step's first reads.  Registers: 4*MR*NC accumulators
+// (192 for 256 x 192) + 4*NC + 8 operands.
+template <int BM, int BN>
+__device__ __forceinline__ void stage_tile16(const floatx4 (&acc)[BM / 32][BN / 32],
+                                             const _Float16* __restrict__ bias, char* stage,
+                                             int N, Tile t, int wave, int lane) {
+  constexpr int MR = BM / 32, NC = BN / 32;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+#pragma unroll
+  for (int cb = 0; cb < NC; ++cb) {
+    const int lcol = (BN / 2) * wn + 16 * cb + (lane & 15);
+    const int col = t.n0 + lcol;
+    const float b = (bias && col < N) ? static_cast<float>(bias[col]) : 0.f;
+#pragma unroll
+    for (int rb = 0; rb < MR; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lrow = (BM / 2) * wm + 16 * rb + 4 * (lane >> 4) + r;
+        *reinterpret_cast<_Float16*>(stage + lrow * out_pitch<BN>() + 2 * lcol) =
+            static_cast<_Float16>(acc[rb][cb][r] + b);
+      }
+    }
+  }
+}
+template <int BM, int BN>
+__device__ __forceinline__ void stage_partial16(const floatx4 (&acc)[BM / 32][BN / 32],
+                                                char* stage, int wave, int lane) {
+  constexpr int MR = BM / 32, NC = BN / 32;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+#pragma unroll
+  for (int cb = 0; cb < NC; ++cb) {
+    const int lcol = (BN / 2) * wn + 16 * cb + (lane & 15);
+#pragma unroll
+    for (int rb = 0; rb < MR; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lrow = (BM / 2) * wm + 16 * rb + 4 * (lane >> 4) + r;
+        *reinterpret_cast<float*>(stage + lrow * part_pitch<BN>() + 4 * lcol) = acc[rb][cb][r];
+      }
+    }
+  }
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void consumer16(const _Float16* __restrict__ bias,
+                                           _Float16* __restrict__ y, float* __restrict__ partial,
+                                           int M, int N, int splits, Tile t, char* a_ring,
+                                           const char* b_ring, int wave, int lane, int out_mode) {
+  using C = Cfg<BM, BN>;
+  constexpr int MR = C::MR;
+  constexpr int NC = C::NC;
+  constexpr int kBPitch = b_pitch<BN>();
+  constexpr int kBTileBytes = b_tile_bytes<BN>();
+  constexpr int kATileBytes = C::kATileBytes;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const int nkt = t.nks;
+  const int li = lane & 15;
+  const int grp = lane >> 4;
+
+  floatx4 acc[MR][NC];
+#pragma unroll
+  for (int rb = 0; rb < MR; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) acc[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  half8_t b[NC];
+#pragma unroll
+  for (int cb = 0; cb < NC; ++cb) b[cb] = half8_t{};
+
+  half8_t a_cur = half8_t{}, a_nxt = half8_t{};
+  // Operand addresses: a per-lane byte offset plus compile-time constants.
+  // x: row (BM/2)*wm + 16*rb + li, 16-byte chunk (4*ks + grp) ^ ((row/2) % 8),
+  // where (row/2) % 8 = (li/2) % 8 for every rb.  Weights: k-row 32*ks +
+  // 8*grp + li/4 (+4), shifted as its 8-row block, column (BN/2)*wn + 16*cb +
+  // 4*(li%4).
+  const int a_row = (BM / 2) * wm + li;
+  const uint32_t a_off0 = a_row * 128 + 16 * (grp ^ ((li >> 1) & 7));
+  const uint32_t a_off1 = a_row * 128 + 16 * ((4 + grp) ^ ((li >> 1) & 7));
+  const int b_krow = 8 * grp + (li >> 2);
+  const uint32_t b_off =
+      b_krow * kBPitch + w_shift<BM, BN>(b_krow) + 2 * ((BN / 2) * wn + 4 * (li & 3));
+  auto a_src = [&](const char* a_slot, int ks, int rb) {
+    return reinterpret_cast<const half8_t*>(a_slot + (ks ? a_off1 : a_off0) + 2048 * rb);
+  };
+  auto b_read = [&](const char* b_buf, int ks, int cb) {
+    const char* p = b_buf + b_off + 32 * ks * kBPitch + 32 * cb;
+    const short4_t lo = read_tr16(p);
+    const short4_t hi = read_tr16(p + 4 * kBPitch);
+    return __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // Rows 0 .. MR-2 of the slice held in b / a_cur: each row's x block for
+  // the next row is read while the row's NC MFMAs run.
+  auto body_rows = [&](const char* a_slot, int ks) {
+#pragma unroll
+    for (int rb = 0; rb + 1 < MR; ++rb) {
+      a_nxt = *a_src(a_slot, ks, rb + 1);
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb) {
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur, b[cb], acc[rb][cb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      a_cur = a_nxt;
+    }
+  };
+  // Last row of the slice held in b / a_cur, each weight block replaced by
+  // slice ks of (a_slot, b_buf) right after its MFMA, and the first x block of
+  // that slice read at the start.  In the first step the operands are still
+  // zero and the MFMAs add nothing.
+  auto last_row = [&](const char* a_slot, const char* b_buf, int ks) {
+    a_nxt = *a_src(a_slot, ks, 0);
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) {
+      acc[MR - 1][cb] =
+          __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur, b[cb], acc[MR - 1][cb], 0, 0, 0);
+      b[cb] = b_read(b_buf, ks, cb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    a_cur = a_nxt;
+  };
+  // Step with x slot j and weight buffer jb: the previous step's last row
+  // (after the barrier: its operands are in registers), then slice 0, the
+  // transition to slice 1, and slice 1 up to its last row.
+  auto cstep = [&](int j, int jb) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of step kt-1 done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const char* a_slot = a_ring + static_cast<uint32_t>(j) * kATileBytes;
+    const char* b_buf = b_ring + static_cast<uint32_t>(jb) * kBTileBytes;
+    last_row(a_slot, b_buf, 0);
+    body_rows(a_slot, 0);
+    last_row(a_slot, b_buf, 1);
+    body_rows(a_slot, 1);
+  };
+  {
+    int j = 0;
+#pragma unroll 1
+    for (int kt = 0; kt < nkt; ++kt) {
+      cstep(__builtin_amdgcn_readfirstlane(j), __builtin_amdgcn_readfirstlane(kt % C::BST));
+      j = j == 2 ? 0 : j + 1;
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < NC; ++cb)
+    acc[MR - 1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur, b[cb], acc[MR - 1][cb], 0, 0, 0);
+
+  if (out_mode == kOutStagedY) {
+    __syncthreads();   // every wave is done with the LDS
+    stage_tile16<BM, BN>(acc, bias, a_ring, N, t, wave, lane);
+    __syncthreads();
+    store_tile<BM, BN>(a_ring, y, M, N, t, 64 * wave + lane);
+    return;
+  }
+  if constexpr (partial_stages<BM, BN>()) {
+    if (out_mode == kOutStagedPartial) {
+      __syncthreads();   // every wave is done with the LDS
+      stage_partial16<BM, BN>(acc, a_ring, wave, lane);
+      __syncthreads();
+      store_partial<BM, BN>(a_ring, partial + static_cast<size_t>(t.sp) * M * N, M, N, t,
+                            64 * wave + lane);
+      return;
+    }
+  }
+  float* const pp = partial + static_cast<size_t>(t.sp) * M * N;
+#pragma unroll
+  for (int cb = 0; cb < NC; ++cb) {
+    const int col = t.n0 + (BN / 2) * wn + 16 * cb + li;
+    if (col >= N) continue;
+    const float bv = (bias && splits == 1) ? static_cast<float>(bias[col]) : 0.f;
+#pragma unroll
+    for (int rb = 0; rb < MR; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = t.m0 + (BM / 2) * wm + 16 * rb + 4 * grp + r;
+        if (row >= M) continue;
+        if (splits == 1)
+          y[row * N + col] = static_cast<_Float16>(acc[rb][cb][r] + bv);
+        else
+          pp[static_cast<size_t>(row) * N + col] = acc[rb][cb][r];
+      }
+    }
+  }
+}
+
 // 512 threads = 8 waves: waves 0-3 consume (MFMA), waves 4-7 produce (loads
 // and dequantisation).  Waves are spread over the 4 SIMDs round-robin, so
 // each SIMD runs one of each and the producer's vector work co-issues with
@@ -809,6 +1032,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   if (wave >= 4)
     producer<BM, BN, KTAIL>(x, qw, qz, sc, y, M, K, N, gsh, t, a_ring, b_ring, wave - 4,
                             tid - 256, out_mode, partial);
+  else if constexpr (Cfg<BM, BN>::MF16)
+    consumer16<BM, BN>(bias, y, partial, M, N, splits, t, a_ring, b_ring, wave, tid & 63, out_mode);
   else
     consumer<BM, BN>(bias, y, partial, M, N, splits, t, a_ring, b_ring, wave, tid & 63, out_mode);
 }
