@@ -463,6 +463,31 @@ def test_mid_batch_tails(M):
     assert_within_tol(y, ref, f"M={M}")
 
 
+@pytest.mark.parametrize("M,K,N,g,bm,bn,bias", [
+    (300, 1024, 768, 128, 256, 192, True),   # 16x16x32 wide tile, ragged rows
+    (256, 2048, 520, 64, 256, 128, False),   # 16x16x32 narrow tile, ragged columns
+    (260, 1000, 384, -1, 256, 192, True),    # 16x16x32, partial last K step
+    (100, 1024, 256, 128, 128, 128, True),   # 32x32x16 tile
+])
+def test_prefill_unaligned_out_direct_stores(M, K, N, g, bm, bn, bias):
+    """y only 2-byte aligned: with one split the prefill stores each element
+    from its accumulators instead of staging the tile in LDS."""
+    say(f"prefill unaligned out M={M} K={K} N={N} g={g} tile {bm}x{bn}")
+    p = awq_inputs.make_inputs(M, K, N, g, seed=M + N, bias=bias)
+    d = to_dev(p)
+    buf = torch.full((M * N + 1,), float("nan"), dtype=torch.float16, device=DEV)
+    y = buf[1:].view(M, N)
+    assert y.data_ptr() % 16 != 0
+    with awq.options(force_path=binding.AWQ_PATH_PREFILL, prefill_bm=bm, prefill_bn=bn,
+                     prefill_splits=1):
+        assert awq.gemm_plan(M, K, N, g)[0] == binding.AWQ_PATH_PREFILL
+        awq.gemm(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], g, out=y)
+        torch.cuda.synchronize()
+    ref = oracle.awq_linear_ref(p["x"], p["qweight"], p["qzeros"], p["scales"], p["bias"], g)
+    assert_within_tol(y.cpu().numpy(), ref, f"unaligned out {bm}x{bn}")
+    assert torch.isnan(buf[0]).item()   # nothing written before y
+
+
 def test_unaligned_x_takes_general_kernel():
     say("unaligned x")
     p = awq_inputs.make_inputs(3, 512, 256, 128, seed=31, bias=True)
