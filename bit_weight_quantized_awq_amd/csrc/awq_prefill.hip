@@ -612,27 +612,25 @@ __device__ __forceinline__ void producer(const _Float16* __restrict__ x, const u
     store_partial<BM, BN>(a_ring, partial + static_cast<size_t>(t.sp) * M * N, M, N, t, 256 + pt);
 }
 
-// Consumer waves (4 of the 8, a 2 x 2 grid): LDS operand reads and the
-// matrix-core work for a (BM/2) x (BN/2) sub-tile each (MI x NB blocks of
-// 32 x 32), then the epilogue.  LDS operands are read one k slice ahead of
-// the MFMAs; the last slice of a step is multiplied after the next step's
-// barrier, overlapping that step's first reads.  Each slice runs as four
-// sub-blocks of LDS reads (one x block, and the weight blocks spread over
-// the four) and NB MFMAs.
+// Consumer waves of the 64- and 128-row tiles (4 of the 8, a 2 x 2 grid):
+// LDS operand reads and the matrix-core work for a (BM/2) x 64 sub-tile each
+// (MI x 2 blocks of 32 x 32), then the epilogue.  Two operand sets: LDS
+// operands are read one k slice ahead of the MFMAs; the last slice of a step
+// is multiplied after the next step's barrier, overlapping that step's
+// first reads.  Each slice runs as MI sub-blocks of LDS reads (one x block,
+// and the four weight reads spread over them) and two MFMAs.
 template <int BM, int BN>
 __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Float16* __restrict__ y,
                                          float* __restrict__ partial, int M, int N, int splits,
                                          Tile t, char* a_ring, const char* b_ring, int wave,
                                          int lane, int out_mode) {
   using C = Cfg<BM, BN>;
+  static_assert(!C::MF16 && BN == 128 && C::BST == 3, "64- and 128-row tiles");
   constexpr int MI = C::MI;
   constexpr int NB = C::NB;
   constexpr int kBPitch = b_pitch<BN>();
   constexpr int kBTileBytes = b_tile_bytes<BN>();
   constexpr int kATileBytes = C::kATileBytes;
-  // The narrow tile keeps two operand sets (reads a slice ahead into nxt);
-  // the wide one's 4 x 3 accumulator blocks (192 registers) leave room for
-  // one, replaced in place.
   const int wm = wave >> 1;
   const int wn = wave & 1;
   const int nkt = t.nks;
@@ -662,10 +660,8 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
 #pragma unroll
   for (int ni = 0; ni < NB; ++ni) cur.b[ni] = half8_t{};
 
-  // Weight read number q (0 .. 2*NB-1) of a slice: block q / 2, k-rows +4*(q%2).
-  // Step with x slot j and weight buffer jb: static for the narrow tile
-  // (loop unrolled by 3), computed per step for the wide one, whose
-  // registers leave no room for an address per slot.
+  // Weight read number q (0 .. 3) of a slice: block q / 2, k-rows +4*(q%2).
+  // Step with x slot j and weight buffer jb.
   auto cstep = [&](int j, int jb) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of step kt-1 done
     __builtin_amdgcn_s_barrier();
@@ -682,64 +678,36 @@ __device__ __forceinline__ void consumer(const _Float16* __restrict__ bias, _Flo
       auto b_src = [&](int q) {
         return b_rd + 16 * ks * kBPitch + 64 * (q >> 1) + (q & 1) * 4 * kBPitch;
       };
-      if constexpr (NB == 2) {
-        // The four weight reads of a slice spread over the MI sub-blocks.
-        short4_t raw[4];
+      // The four weight reads of a slice spread over the MI sub-blocks.
+      short4_t raw[4];
 #pragma unroll
-        for (int sub = 0; sub < MI; ++sub) {
-          nxt.a[sub] = *a_src(sub);
+      for (int sub = 0; sub < MI; ++sub) {
+        nxt.a[sub] = *a_src(sub);
 #pragma unroll
-          for (int q = sub * 4 / MI; q < (sub + 1) * 4 / MI; ++q) raw[q] = read_tr16(b_src(q));
-#pragma unroll
-          for (int ni = 0; ni < NB; ++ni)
-            acc[sub][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[sub], cur.b[ni],
-                                                                  acc[sub][ni], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int q = sub * 4 / MI; q < (sub + 1) * 4 / MI; ++q) raw[q] = read_tr16(b_src(q));
 #pragma unroll
         for (int ni = 0; ni < NB; ++ni)
-          nxt.b[ni] = __builtin_bit_cast(
-              half8_t, __builtin_shufflevector(raw[2 * ni], raw[2 * ni + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-        cur = nxt;
-      } else {
-        // Weight-block major, every operand replaced in place by the next
-        // slice's as soon as its last MFMA of this slice is issued: block ni
-        // after its four MFMAs, x block sub after the last block's.
-#pragma unroll
-        for (int ni = 0; ni < NB; ++ni) {
-#pragma unroll
-          for (int sub = 0; sub < MI; ++sub) {
-            acc[sub][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[sub], cur.b[ni],
-                                                                  acc[sub][ni], 0, 0, 0);
-            if (ni == NB - 1) cur.a[sub] = *a_src(sub);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          const short4_t lo = read_tr16(b_src(2 * ni));
-          const short4_t hi = read_tr16(b_src(2 * ni + 1));
-          cur.b[ni] =
-              __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          __builtin_amdgcn_sched_barrier(0);
-        }
+          acc[sub][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[sub], cur.b[ni],
+                                                                acc[sub][ni], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int ni = 0; ni < NB; ++ni)
+        nxt.b[ni] = __builtin_bit_cast(
+            half8_t, __builtin_shufflevector(raw[2 * ni], raw[2 * ni + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+      cur = nxt;
     }
   };
-  if constexpr (C::BST == 3) {
-    int kt = 0;
-    for (; kt + 2 < nkt; kt += 3) {
-      cstep(0, 0);
-      cstep(1, 1);
-      cstep(2, 2);
-    }
-    if (kt < nkt) cstep(0, 0);
-    if (kt + 1 < nkt) cstep(1, 1);
-  } else {
-    int j = 0;
-#pragma unroll 1
-    for (int kt = 0; kt < nkt; ++kt) {
-      cstep(__builtin_amdgcn_readfirstlane(j), kt & 1);
-      j = j == 2 ? 0 : j + 1;
-    }
+  // x slot and weight buffer of step kt are both kt % 3 (static: the loop
+  // is unrolled by three).
+  int kt = 0;
+  for (; kt + 2 < nkt; kt += 3) {
+    cstep(0, 0);
+    cstep(1, 1);
+    cstep(2, 2);
   }
+  if (kt < nkt) cstep(0, 0);
+  if (kt + 1 < nkt) cstep(1, 1);
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
