@@ -85,10 +85,6 @@ __device__ __forceinline__ void red_store(float* red, int wave, int Mq, int kb, 
                                           floatx4 v) {
   *reinterpret_cast<floatx4*>(red + ((wave * Mq + kb) * kDecodeCols + red_col(col)) * 4) = v;
 }
-// M == 1: only row 0 (element 0 of the kb == 0 lanes) is stored and read.
-__device__ __forceinline__ void red_store1(float* red, int wave, int col, float v) {
-  red[(wave * kDecodeCols + red_col(col)) * 4] = v;
-}
 // Sums one pass of M <= kDecodeBlockM rows into part[0 .. M).
 template <int WAVES>
 __device__ __forceinline__ void red_sum(const float* red, int Mq, int M, int col, float* part) {
@@ -682,12 +678,14 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
       }
     }
   }
-  // The WAVES K-ranges meet in LDS (the copy regions are free once every
-  // wave is past its last step), one pass per row block.  tot[rb][h][j][i]
-  // is row 16*rb + 4*kb + i, local column 8*(16h + col16) + j; with one row
-  // only element 0 is formed and stored.  One thread per column of the tile
-  // then holds its partial; with eight waves the upper half of the
-  // work-group is done.
+  // The WAVES K-ranges meet in LDS, one pass per row block.  tot[rb][h][j][i]
+  // is row 16*rb + 4*kb + i, local column 8*(16h + col16) + j.  With one
+  // row only element 0 is formed, and it goes to a region of its own after
+  // the copy regions ([wave][j][word column], WAVES KiB), so each wave
+  // stores as soon as its steps are done and one barrier suffices; more
+  // rows reuse the copy regions, free once every wave is past its last step.
+  // One thread per column of the tile then holds its partial; with eight
+  // waves the upper half of the work-group is done.
   float* red = reinterpret_cast<float*>(smem);
   const bool col_thread = WAVES == 4 || tid < kDecodeCols;
   const int n = n_tile * kDecodeCols + tid;
@@ -698,16 +696,22 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
 #pragma unroll
       for (int h = 0; h < 2; ++h) fold(0, h, sv[0][h], OneRow{});
     }
-    __syncthreads();
+    float* red1 = reinterpret_cast<float*>(smem + WAVES * kWaveBytes);
     if (kb == 0) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          red_store1(red, wave, 8 * (16 * h + col16) + j, tot[0][h][j][0]);
+        for (int j = 0; j < 8; ++j) red1[(wave * 8 + j) * 32 + 16 * h + col16] = tot[0][h][j][0];
     }
     __syncthreads();
-    if (col_thread) red_sum<WAVES>(red, 1, 1, tid, part);
+    if (col_thread) {
+      // Column tid: word column tid / 8, nibble j = tid % 8; waves in order.
+      const int at = (tid & 7) * 32 + ((tid & (kDecodeCols - 1)) >> 3);
+      float v = red1[at];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) v += red1[w * 256 + at];
+      part[0] = v;
+    }
   } else {
     if (SINGLE_GROUP) {
 #pragma unroll
@@ -798,11 +802,14 @@ hipError_t launch_lds_waves(const _Float16* x, const uint32_t* qweight, const ui
                             const _Float16* scales, const _Float16* bias, _Float16* y,
                             int M, int K, int N, int g, int G, int splits, int n_tiles,
                             SplitK sk, const int32_t* perm, int Kx, hipStream_t stream) {
-  // The LDS holds the weight copies, then one reduction pass (at most 16 rows).
+  // The LDS holds the weight copies, then one reduction pass (at most 16
+  // rows) in the same bytes; one row has a reduction region of its own after
+  // the copies.
   const size_t copy_bytes = WAVES * STEPS * 4 * kLdsBlockPitch;
   const int pass_rows = M < kDecodeBlockM ? ((M + 3) & ~3) : kDecodeBlockM;
   const size_t red_bytes = WAVES * static_cast<size_t>(pass_rows) * kDecodeCols * sizeof(float);
-  const size_t shmem = copy_bytes > red_bytes ? copy_bytes : red_bytes;
+  const size_t shmem = M == 1 ? copy_bytes + WAVES * kDecodeCols * sizeof(float)
+                              : (copy_bytes > red_bytes ? copy_bytes : red_bytes);
   const bool single = (G == 1) || (g % (kDecodeRowsPerStep * STEPS) == 0);
   const dim3 grid(n_tiles * splits), block(64 * WAVES);
   if (M > kDecodeBlockM) {
