@@ -320,13 +320,32 @@ def read_stream_fn(torch, bufs, dev):
     return fn
 
 
+def empty_launch_fn(torch, dev, blocks, threads):
+    """A launcher of a kernel that does nothing (libawq_bench.so), with the
+    decode kernel's grid shape: the per-call floor of a graph replay."""
+    import ctypes
+    from bit_weight_quantized_awq_amd import build as _build
+    lib = ctypes.CDLL(_build.BENCH_LIB_PATH)
+    lib.awq_bench_empty.restype = ctypes.c_int
+    lib.awq_bench_empty.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def fn(i):
+        st = lib.awq_bench_empty(sink.data_ptr(), blocks, threads,
+                                 torch._C._cuda_getCurrentRawStream(dev.index))
+        if st != 0:
+            raise RuntimeError(f"awq_bench_empty: status {st}")
+    return fn
+
+
 def same_box_references(torch, dev, decode_bytes):
     """What this box does, in this process, on plain work of the headline
     sizes: a read-only stream (a plain kernel of 1024 work-groups, eight
     16-byte loads in flight per thread) and a device copy over the decode
     step's byte count (rounded down to 16 bytes), rotated like the decode
-    leg, and torch's float16 linear (the vendor GEMM) at the prefill
-    projection's shape."""
+    leg; a kernel that does nothing, launched with the decode grid (what
+    one launch costs per call of a graph replay); and torch's float16
+    linear (the vendor GEMM) at the prefill projection's shape."""
     n = decode_bytes // 16 * 4
     R = max(2, -(-ROTATE_BYTES // decode_bytes))
     gen = torch.Generator(device="cpu").manual_seed(7)
@@ -334,6 +353,7 @@ def same_box_references(torch, dev, decode_bytes):
             for _ in range(R)]
     dst = [torch.empty_like(b) for b in bufs]
     read_us = graph_time_us(torch, read_stream_fn(torch, bufs, dev), auto_steps(n * 4, 0), dev)
+    empty_us = graph_time_us(torch, empty_launch_fn(torch, dev, 448, 256), 2000, dev)
     copy_us = graph_time_us(torch, lambda i: dst[i % R].copy_(bufs[i % R]),
                             auto_steps(2 * n * 4, 0), dev)
     del bufs, dst
@@ -350,6 +370,8 @@ def same_box_references(torch, dev, decode_bytes):
         "read_stream": {"op": "plain read kernel (libawq_bench.so)", "bytes": n * 4, "us": round(read_us, 3),
                         "GB_per_s": round(n * 4 / read_us / 1e3, 1),
                         "frac": round(n * 4 / read_us / 1e3 / HBM_PEAK_GBS, 4)},
+        "empty_launch": {"op": "kernel that does nothing, 448 work-groups of 256 threads (libawq_bench.so)",
+                         "us": round(empty_us, 3)},
         "device_copy": {"op": "Tensor.copy_", "bytes_moved": 2 * n * 4, "us": round(copy_us, 3),
                         "GB_per_s": round(2 * n * 4 / copy_us / 1e3, 1),
                         "frac": round(2 * n * 4 / copy_us / 1e3 / HBM_PEAK_GBS, 4)},

@@ -1,7 +1,7 @@
-// Measurement aid, not part of the W4A16 forward: a plain read-only stream
-// over a device buffer, built into its own small library (libawq_bench.so)
-// so that the benchmark can time, in the same process and on the same box,
-// what merely reading the decode step's bytes costs.  Every thread keeps
+// Measurement aids, not part of the W4A16 forward, built into their own small
+// library (libawq_bench.so) so that the benchmark can time, in the same
+// process and on the same box, what merely reading the decode step's bytes
+// costs, and what one kernel launch costs when it does nothing.  Every thread keeps
 // eight 16-byte loads in flight per grid-stride step and folds them into a
 // register, written out only on an impossible value (so the loads stay live).
 #include <hip/hip_runtime.h>
@@ -31,6 +31,12 @@ __global__ __launch_bounds__(kThreads) void read_stream_kernel(const uint4* __re
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
+// Does nothing (the store is never taken): the launch and completion cost
+// of one kernel.
+__global__ void empty_kernel(uint32_t* sink) {
+  if (threadIdx.x == 0x7fffffffu) sink[1] = 1u;
+}
+
 }  // namespace
 
 // Reads `bytes` bytes (a multiple of 16) at the 16-byte aligned device
@@ -43,6 +49,16 @@ extern "C" int awq_bench_read_stream(const void* p, size_t bytes, void* sink, in
     return 1;
   hipLaunchKernelGGL(read_stream_kernel, dim3(blocks), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint4*>(p), bytes / 16,
+                     static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+// One launch of a kernel that does nothing, with `blocks` work-groups of
+// `threads` threads (1..1024) on `stream`; sink is a device word.  Returns 0,
+// 1 for bad arguments, 5 if the launch failed.
+extern "C" int awq_bench_empty(void* sink, int blocks, int threads, void* stream) {
+  if (!sink || blocks <= 0 || threads <= 0 || threads > 1024) return 1;
+  hipLaunchKernelGGL(empty_kernel, dim3(blocks), dim3(threads), 0, static_cast<hipStream_t>(stream),
                      static_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
