@@ -181,7 +181,11 @@ __device__ __forceinline__ void splitk_atomic(const float (&part)[MM], const Spl
       __hip_atomic_store(sk.mask + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     y[e] = static_cast<_Float16>(r + b);
-    __hip_atomic_store(sk.acc + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Every split has been counted, so nothing else touches this word in
+    // this call, and the next call on the stream sees the zero through the
+    // kernel boundary: a plain store resets it (a device-scope store would
+    // go out to memory and hold up the end of the kernel).
+    sk.acc[e] = 0ull;
   }
 }
 
