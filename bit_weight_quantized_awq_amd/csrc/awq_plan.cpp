@@ -288,6 +288,18 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
         pl.decode_waves = 8;
       }
     }
+    // One row on the atomic exchange: four waves of four steps become eight
+    // waves of two (the same work-groups and splits), so the arithmetic left
+    // when the last copies land is at most two steps per wave.  Same box:
+    // K = 14336, N = 4096: 10.06 -> 9.62 us; K = 4096, N = 12288: 9.62 ->
+    // 9.46 us; K = 28672, N = 8192: 28.9 -> 28.1 us; K = 8192, N = 28672:
+    // 29.2 -> 28.8 us; K = 8192, N = 7168: 9.38 -> 9.43 us.  Not for more
+    // rows (M = 2, 3: 0.4 us slower) nor from two steps to one (slower).
+    if (pl.decode_lds && waves_opt == 0 && steps_opt == 0 && pl.decode_atomic && p.M == 1 &&
+        steps == 4 && decode_single_group(p, 2)) {
+      steps = 2;
+      pl.decode_waves = 8;
+    }
     // Eight waves of eight steps would need 272 KiB of LDS: four waves then.
     if (pl.decode_waves == 8 && steps == 8) pl.decode_waves = 4;
     pl.steps = steps;

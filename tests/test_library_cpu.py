@@ -623,7 +623,7 @@ def test_two_launch_exchange_takes_eight_waves_filling_one_round():
             (12, 8192, 14336, 16),   # eight waves: 448 work-groups, two rounds: four waves
             (8, 4096, 4096, 32),     # eight waves: 64 work-groups: four waves of 1 step
             (16, 4096, 7168, 16),    # g = 64 below: 4 steps would span groups
-            (1, 14336, 4096, 28),    # atomic exchange: four waves
+            (1, 14336, 4096, 28),    # atomic exchange, one row: eight waves of two steps, same splits
             (3, 8192, 7168, 16),     # atomic: 16 x 3 x 7168 = 344K atomics
             (4, 8192, 7168, 8),      # 16 x 4 x 7168 = 459K atomics: two launches, eight waves
             (4, 4096, 4096, 32)]:    # 524K atomics: two launches (eight waves: 64 work-groups)
