@@ -72,38 +72,37 @@ constexpr float kFxScale = 16777216.0f;   // 2^24
 constexpr float kFxLimit = 2097152.0f;    // 2^21
 static_assert(kDecodeMaxSplits <= 63, "six-bit contribution counts");
 
-// Cross-wave reduction in LDS.  Layout [wave][row group of 4][column][4 rows]
-// (row groups below M only): the lane holding rows 4*kb .. 4*kb+3 of a column
-// writes them as one 16-byte store, and the thread of a column reads each
-// row group of each wave as one 16-byte load.  Columns are XOR-swizzled
-// within groups of 16 (bits 1-3 ^= bits 4-6): the 16 lanes of one store
-// instruction (columns 8 apart) then spread over 8 bank groups instead of 2,
-// and 16 consecutive columns still cover 16 distinct bank groups for the
-// loads.
+// Cross-wave reduction in LDS.  Each wave's region (`stride` floats apart)
+// is laid out [row group of 4][column][4 rows] (row groups below M only):
+// the lane holding rows 4*kb .. 4*kb+3 of a column writes them as one
+// 16-byte store, and the thread of a column reads each row group of each
+// wave as one 16-byte load.  Columns are XOR-swizzled within groups of 16
+// (bits 1-3 ^= bits 4-6): the 16 lanes of one store instruction (columns 8
+// apart) then spread over 8 bank groups instead of 2, and 16 consecutive
+// columns still cover 16 distinct bank groups for the loads.
 __device__ __forceinline__ int red_col(int col) { return col ^ (((col >> 4) & 7) << 1); }
-__device__ __forceinline__ void red_store(float* red, int wave, int Mq, int kb, int col,
+__device__ __forceinline__ void red_store(float* red, int stride, int wave, int kb, int col,
                                           floatx4 v) {
-  *reinterpret_cast<floatx4*>(red + ((wave * Mq + kb) * kDecodeCols + red_col(col)) * 4) = v;
+  *reinterpret_cast<floatx4*>(red + wave * stride + (kb * kDecodeCols + red_col(col)) * 4) = v;
 }
-// Sums one pass of M <= kDecodeBlockM rows into part[0 .. M).
+// Sums one pass of M <= kDecodeBlockM rows into part[0 .. M), waves in order.
 template <int WAVES>
-__device__ __forceinline__ void red_sum(const float* red, int Mq, int M, int col, float* part) {
+__device__ __forceinline__ void red_sum(const float* red, int stride, int M, int col, float* part) {
+  const int pc = red_col(col);
   if (M == 1) {
-    const int pc = red_col(col);
     float v = red[pc * 4];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) v += red[(w * kDecodeCols + pc) * 4];
+    for (int w = 1; w < WAVES; ++w) v += red[w * stride + pc * 4];
     part[0] = v;
     return;
   }
 #pragma unroll
   for (int c4 = 0; c4 < kDecodeBlockM / 4; ++c4) {
     if (4 * c4 < M) {
-      const int pc = red_col(col);
       floatx4 v = *reinterpret_cast<const floatx4*>(red + (c4 * kDecodeCols + pc) * 4);
 #pragma unroll
       for (int w = 1; w < WAVES; ++w)
-        v += *reinterpret_cast<const floatx4*>(red + ((w * Mq + c4) * kDecodeCols + pc) * 4);
+        v += *reinterpret_cast<const floatx4*>(red + w * stride + (c4 * kDecodeCols + pc) * 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) part[4 * c4 + i] = v[i];
     }
@@ -330,16 +329,17 @@ __global__ __launch_bounds__(256) __attribute__((
   // tot[j][i] is row 4*kb + i, column 8*c + j.  Meet the other K-half in LDS.
   const int Mq = (M + 3) >> 2;
   const int lcol = 8 * (wn * 16 + col16);
+  const int stride = Mq * kDecodeCols * 4;
   if (4 * kb < M) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) red_store(red, wk, Mq, kb, lcol + j, tot[j]);
+    for (int j = 0; j < 8; ++j) red_store(red, stride, wk, kb, lcol + j, tot[j]);
   }
   __syncthreads();
 
   const int n = n_tile * kDecodeCols + tid;
   const bool nvalid = n < N;
   float part[kDecodeBlockM];
-  red_sum<2>(red, Mq, M, tid, part);
+  red_sum<2>(red, stride, M, tid, part);
   if (splits == 1) {
     if (nvalid) store_rows(part, bias, y, M, N, n);
     return;
@@ -727,16 +727,20 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
     for (int rb = 0; rb < RB; ++rb) {
       const int Mr = min(M - kDecodeBlockM * rb, kDecodeBlockM);   // rows of this pass
       const int Mq = (Mr + 3) >> 2;
-      __syncthreads();   // the copy regions, or the previous pass, are done with
+      // A pass that fits a wave's own copy region goes there: the wave is
+      // past its last step, so it stores without waiting for the others.
+      const bool own = Mq * kDecodeCols * 16 <= kWaveBytes;
+      const int stride = own ? kWaveBytes / 4 : Mq * kDecodeCols * 4;
+      if (!own || rb > 0) __syncthreads();   // the copy regions, or the previous pass, are done with
       if (4 * kb < Mr) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            red_store(red, wave, Mq, kb, 8 * (16 * h + col16) + j, tot[rb][h][j]);
+            red_store(red, stride, wave, kb, 8 * (16 * h + col16) + j, tot[rb][h][j]);
       }
       __syncthreads();
-      if (col_thread) red_sum<WAVES>(red, Mq, Mr, tid, part + kDecodeBlockM * rb);
+      if (col_thread) red_sum<WAVES>(red, stride, Mr, tid, part + kDecodeBlockM * rb);
     }
   }
   if (splits == 1) {
