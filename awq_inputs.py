@@ -37,8 +37,9 @@ class Workload:
 
 # The seeded workloads: a tiny case, the two decode shapes of the ROCm
 # skinny-GEMM dispatch (K=8192, N in {1280, 7168}), a fused-QKV prefill
-# projection, an MLP down-projection, and batches between decode and prefill
-# at the larger decode shape.
+# projection, an MLP down-projection, batches between decode and prefill
+# at the larger decode shape, and one GPU's shard of the two tensor-parallel
+# layers.
 WORKLOADS = {
     "tiny_m4_k256_n128": Workload(
         "tiny_m4_k256_n128", (4,), 256, 128, (64,), 0, 0.002, 0.02, True,
@@ -58,6 +59,15 @@ WORKLOADS = {
     "midm_k8192_n7168": Workload(
         "midm_k8192_n7168", (32, 64, 128), 8192, 7168, (128,), 5, 0.001, 0.01, False,
         "batches between decode and prefill"),
+    # One GPU's share of an 8-way tensor-parallel layer: a column shard of the
+    # fused-QKV projection (N / 8 output columns) and a row shard of the
+    # down-projection (K / 8 input rows, 14 groups of 128).
+    "tp8_col_shard_qkv_m2048_k4096_n1536": Workload(
+        "tp8_col_shard_qkv_m2048_k4096_n1536", (2048,), 4096, 1536, (128,), 6, 0.001, 0.01,
+        True, "8-way column shard of the fused-QKV projection"),
+    "tp8_row_shard_down_k1792_n4096": Workload(
+        "tp8_row_shard_down_k1792_n4096", (1, 16, 256, 1024, 4096), 1792, 4096, (128,), 7,
+        0.001, 0.01, False, "8-way row shard of the MLP down-projection"),
 }
 
 

@@ -345,35 +345,70 @@ int make_plan(const Problem& p, const Alignment& al, int force, Plan* out) {
       *out = pl;
       return AWQ_SUCCESS;
     }
-    pl.prefill_bm = p.M <= kPrefillMinBM ? kPrefillMinBM
-                                         : (p.M <= 2 * kPrefillMinBM ? 2 * kPrefillMinBM : kPrefillBM);
-    if (const int o = override_or_zero(AWQ_OPT_PREFILL_BM)) pl.prefill_bm = o;
-    pl.m_tiles = static_cast<int>(ceil_div(p.M, pl.prefill_bm));
-    // The wide tile (256 rows only) does 1.5x a narrow tile's work at a
-    // little more speed per flop (fewer LDS bytes per flop): take it when it
-    // needs no split and its rounds of work-groups over the CUs cost less.
-    const int64_t r_narrow = ceil_div(pl.m_tiles * ceil_div(p.N, kPrefillBN), kPrefillTargetWGs);
-    const int64_t wide_tiles = pl.m_tiles * ceil_div(p.N, kPrefillWideBN);
-    const int64_t r_wide = ceil_div(wide_tiles, kPrefillTargetWGs);
-    pl.prefill_bn = (pl.prefill_bm == kPrefillBM && wide_tiles >= kPrefillTargetWGs &&
-                     r_wide * 6 < r_narrow * 5)
-                        ? kPrefillWideBN
-                        : kPrefillBN;
-    if (const int o = override_or_zero(AWQ_OPT_PREFILL_BN); o == kPrefillBN || o == kPrefillWideBN)
-      pl.prefill_bn = o;
-    if (pl.prefill_bm != kPrefillBM) pl.prefill_bn = kPrefillBN;   // 192 needs 256 rows
-    pl.n_tiles = static_cast<int>(ceil_div(p.N, pl.prefill_bn));
-    pl.group_shift = p.G == 1 ? 31 : log2_exact(p.g);
-    // Split K when the tiles alone leave CUs idle and K is long enough.
+    // Tile width and split count for a tile height: the wide tile (256 rows
+    // only) does 1.5x a narrow tile's work at a little more speed per flop
+    // (fewer LDS bytes per flop): take it when it needs no split and its
+    // rounds of work-groups over the CUs cost less.  Split K when the tiles
+    // alone leave CUs idle and K is long enough.
     const int64_t nkt = ceil_div(p.K, kPrefillBK);
-    const int64_t tiles = static_cast<int64_t>(pl.m_tiles) * pl.n_tiles;
-    int64_t splits = 1;
-    if (tiles > 0 && tiles < kPrefillTargetWGs) {
-      splits = kPrefillTargetWGs / tiles;
-      if (splits > kPrefillMaxSplits) splits = kPrefillMaxSplits;
-      if (splits > nkt / kPrefillMinSplitSteps) splits = nkt / kPrefillMinSplitSteps;
-      if (splits < 2) splits = 1;
+    auto shape_for = [&](int bm, int* bn, int64_t* tiles, int64_t* splits) {
+      const int64_t m_tiles = ceil_div(p.M, bm);
+      const int64_t r_narrow = ceil_div(m_tiles * ceil_div(p.N, kPrefillBN), kPrefillTargetWGs);
+      const int64_t wide_tiles = m_tiles * ceil_div(p.N, kPrefillWideBN);
+      const int64_t r_wide = ceil_div(wide_tiles, kPrefillTargetWGs);
+      *bn = (bm == kPrefillBM && wide_tiles >= kPrefillTargetWGs && r_wide * 6 < r_narrow * 5)
+                ? kPrefillWideBN
+                : kPrefillBN;
+      if (const int o = override_or_zero(AWQ_OPT_PREFILL_BN); o == kPrefillBN || o == kPrefillWideBN)
+        *bn = o;
+      if (bm != kPrefillBM) *bn = kPrefillBN;   // 192 needs 256 rows
+      *tiles = m_tiles * ceil_div(p.N, *bn);
+      *splits = 1;
+      if (*tiles > 0 && *tiles < kPrefillTargetWGs) {
+        *splits = kPrefillTargetWGs / *tiles;
+        if (*splits > kPrefillMaxSplits) *splits = kPrefillMaxSplits;
+        if (*splits > nkt / kPrefillMinSplitSteps) *splits = nkt / kPrefillMinSplitSteps;
+        if (*splits < 2) *splits = 1;
+      }
+    };
+    int bm = p.M <= kPrefillMinBM ? kPrefillMinBM
+                                  : (p.M <= 2 * kPrefillMinBM ? 2 * kPrefillMinBM : kPrefillBM);
+    const int bm_opt = override_or_zero(AWQ_OPT_PREFILL_BM);
+    if (bm_opt) bm = bm_opt;
+    int bn;
+    int64_t tiles, splits;
+    shape_for(bm, &bn, &tiles, &splits);
+    // Short K (at most kPrefillShortKSteps steps): a split's partials and
+    // the second kernel cost more than lower tiles lose, so when the
+    // 256-row plan splits, take the tallest lower tile (128, or 64 for at most 256 rows)
+    // whose tiles fill three quarters of the CUs without a split, else the
+    // lowest allowed one with its own split.  Same box (us, before -> after):
+    // K=1792 N=4096 M=256 21.3 -> 16.9, M=1024 30.1 -> 20.8; K=4096 N=4096
+    // M=256 28.5 -> 22.1, M=512 30.6 -> 28.7; K=2048 N=8192 M=256 29.0 ->
+    // 18.5, M=512 31.6 -> 24.0; K=4096 N=1536 M=2048 36.3 -> 35.2; K=4096
+    // N=12288 M=256 37.2 -> 36.8.  Longer K keeps the tall split tile
+    // (K=14336 N=4096 M=1024: 114 us split against 134 us at 128 rows).
+    if (!bm_opt && override_or_zero(AWQ_OPT_PREFILL_SPLITS) == 0 && bm == kPrefillBM &&
+        nkt <= kPrefillShortKSteps && splits > 1) {
+      int pick = 0;
+      for (int c = bm / 2; c >= kPrefillMinBM; c /= 2) {
+        if (c == kPrefillMinBM && p.M > kPrefillMinBM * 4) break;
+        int cbn;
+        int64_t ct, cs;
+        shape_for(c, &cbn, &ct, &cs);
+        pick = c;
+        if (ct * 4 >= kPrefillTargetWGs * 3) break;
+      }
+      if (pick) {
+        bm = pick;
+        shape_for(bm, &bn, &tiles, &splits);
+      }
     }
+    pl.prefill_bm = bm;
+    pl.prefill_bn = bn;
+    pl.m_tiles = static_cast<int>(ceil_div(p.M, bm));
+    pl.n_tiles = static_cast<int>(ceil_div(p.N, bn));
+    pl.group_shift = p.G == 1 ? 31 : log2_exact(p.g);
     if (const int o = override_or_zero(AWQ_OPT_PREFILL_SPLITS)) splits = o < nkt ? o : nkt;
     const int64_t kps = ceil_div(nkt, splits);
     splits = ceil_div(nkt, kps);   // no empty split

@@ -70,6 +70,9 @@ constexpr int kPrefillBK = 64;
 constexpr int kPrefillTargetWGs = 256;
 constexpr int kPrefillMaxSplits = 8;
 constexpr int kPrefillMinSplitSteps = 8;
+// At most this many K steps (K <= 4096) the planner prefers lower tiles
+// without a split to the 256-row tile with one.
+constexpr int64_t kPrefillShortKSteps = 64;
 // Packed-weight prefill tile (256 rows x 256 or 192 columns, packed words
 // staged in LDS, dequantised by the matrix-core waves): K % 64 == 0,
 // N % 32 == 0, qweight 16-byte aligned, groups of a multiple of 64 rows (or

@@ -85,11 +85,17 @@ int main() {
                 EXPECT(pl.prefill_bm == 64 || pl.prefill_bm == 128 || pl.prefill_bm == kPrefillBM);
                 EXPECT(pl.prefill_bn == kPrefillBN || pl.prefill_bm == kPrefillBM);
                 EXPECT((int64_t)pl.m_tiles * pl.prefill_bm >= M);
-                EXPECT(M <= 64 ? pl.prefill_bm == 64 : (M <= 128 ? pl.prefill_bm == 128 : pl.prefill_bm == 256));
+                const int64_t nkt = (K + kPrefillBK - 1) / kPrefillBK;
+                // The smallest of 64 / 128 / 256 rows covering M; for short K
+                // (a 256-row plan that would split) also 128, or 64 for at
+                // most 256 rows.
+                const int def_bm = M <= 64 ? 64 : (M <= 128 ? 128 : 256);
+                EXPECT(pl.prefill_bm == def_bm ||
+                       (def_bm == 256 && nkt <= kPrefillShortKSteps &&
+                        (pl.prefill_bm == 128 || (pl.prefill_bm == 64 && M <= 256))));
                 EXPECT(pl.prefill_bn == kPrefillBN || pl.prefill_bn == kPrefillWideBN);
                 EXPECT((int64_t)pl.n_tiles * pl.prefill_bn >= N);
                 EXPECT((int64_t)(pl.n_tiles - 1) * pl.prefill_bn < N);
-                const int64_t nkt = (K + kPrefillBK - 1) / kPrefillBK;
                 const int64_t tiles = (int64_t)pl.m_tiles * pl.n_tiles;
                 EXPECT(pl.splits >= 1 && pl.splits <= kPrefillMaxSplits);
                 EXPECT((int64_t)pl.splits * pl.steps >= nkt);

@@ -231,6 +231,28 @@ def test_gemm_config_parity(name, Mmax, M, g):
     assert_within_tol(y, ref, f"{name} M={M} g={g}")
 
 
+@pytest.mark.parametrize("name,Mmax,M", [
+    ("tp8_col_shard_qkv_m2048_k4096_n1536", 2048, 2048),
+    ("tp8_row_shard_down_k1792_n4096", 4096, 1),
+    ("tp8_row_shard_down_k1792_n4096", 4096, 16),
+    ("tp8_row_shard_down_k1792_n4096", 4096, 256),
+    ("tp8_row_shard_down_k1792_n4096", 4096, 1024),
+    ("tp8_row_shard_down_k1792_n4096", 4096, 4096),
+])
+def test_gemm_tensor_parallel_shard_parity(name, Mmax, M):
+    """One GPU's shard of an 8-way tensor-parallel layer (column shard of
+    the QKV projection, row shard of the down-projection), every output
+    element against the oracle's forward."""
+    say(f"awq_gemm shard {name} M={M}")
+    p = awq_inputs.workload_inputs(name, Mmax, 128)
+    d = to_dev(p)
+    y = run_gemm(d, M=M)
+    del d
+    ref = oracle.awq_linear_ref(p["x"][:M], p["qweight"], p["qzeros"], p["scales"], p["bias"], 128)
+    assert ref.shape == y.shape
+    assert_within_tol(y, ref, f"{name} M={M}")
+
+
 # ------------------------------------------------- exact special cases
 @pytest.mark.parametrize("name,Mmax,g,M", [
     ("decode_sweep_k8192_n7168", 16, 128, 16),
