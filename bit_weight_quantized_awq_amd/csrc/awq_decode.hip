@@ -685,11 +685,12 @@ decode_lds_kernel(const _Float16* __restrict__ x, const uint32_t* __restrict__ q
   // The WAVES K-ranges meet in LDS, one pass per row block.  tot[rb][h][j][i]
   // is row 16*rb + 4*kb + i, local column 8*(16h + col16) + j.  With one
   // row only element 0 is formed, and it goes to a region of its own after
-  // the copy regions ([wave][j][word column], WAVES KiB), so each wave
-  // stores as soon as its steps are done and one barrier suffices; more
-  // rows reuse the copy regions, free once every wave is past its last step.
-  // One thread per column of the tile then holds its partial; with eight
-  // waves the upper half of the work-group is done.
+  // the copy regions ([wave][j][word column], WAVES KiB); more rows go to
+  // the wave's own copy region when the pass fits there, else to the copy
+  // regions of all waves once every wave is past its last step.  In the
+  // first two cases each wave stores as soon as its steps are done and one
+  // barrier precedes the sum.  One thread per column of the tile then holds
+  // its partial; with eight waves the upper half of the work-group is done.
   float* red = reinterpret_cast<float*>(smem);
   const bool col_thread = WAVES == 4 || tid < kDecodeCols;
   const int n = n_tile * kDecodeCols + tid;
