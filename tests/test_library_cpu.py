@@ -676,3 +676,22 @@ def test_plan_two_block_decode_limits():
         awq.set_option("decode_gather_max_m", 17)
     awq.set_option("decode_gather_max_m", 16)
     awq.set_option("decode_gather_max_m", None)
+
+
+@pytest.mark.parametrize("M,K,N,splits", [
+    (1024, 1792, 4096, 1),    # 128-row tiles fill the CUs: no split (256 rows would split 2 ways)
+    (256, 1792, 4096, 2),     # 64-row tiles, 128 of them: two splits (256 rows: three)
+    (512, 4096, 4096, 2),     # 64-row tiles not taken above 256 rows: 128-row tiles, two splits
+    (2048, 4096, 1536, 1),    # 128-row tiles, 192 of them: no split
+    (1024, 14336, 4096, 2),   # long K keeps the split 256-row tile
+    (256, 14336, 4096, 8),
+])
+def test_prefill_short_k_prefers_lower_tiles(M, K, N, splits):
+    """With at most 64 K steps the planner trades the split 256-row tile for
+    a lower one that needs fewer (or no) splits; longer K keeps the split
+    tall tile.  Seen through the workspace need: the fixed exchange region
+    plus one float partial plane per split, or nothing without a split."""
+    path, ws = awq.gemm_plan(M, K, N, 128)
+    assert path == binding.AWQ_PATH_PREFILL
+    fixed = 4 * 65536 * 16
+    assert ws == (fixed + splits * M * N * 4 if splits > 1 else 0), (M, K, N, ws)
