@@ -256,6 +256,10 @@ def test_gemm_tensor_parallel_shard_parity(name, Mmax, M):
 # ------------------------------------------------- exact special cases
 @pytest.mark.parametrize("name,Mmax,g,M", [
     ("decode_sweep_k8192_n7168", 16, 128, 16),
+    ("decode_sweep_k8192_n7168", 16, 128, 1),   # one row: eight waves of two steps
+    ("mlp_down_k14336_n4096", 4096, 128, 1),
+    ("mlp_down_k14336_n4096", 4096, -1, 1),
+    ("decode_sweep_k8192_n7168", 16, 128, 3),   # the atomic exchange, several rows
     ("decode_k8192_n1280", 1, 128, 1),
     ("mlp_down_k14336_n4096", 4096, -1, 3),
     ("prefill_qkv_m2048_k4096_n12288", 2048, 128, 256),
@@ -277,7 +281,8 @@ def test_one_hot_rows_exact(name, Mmax, g, M):
     np.testing.assert_array_equal(y.view(np.uint16), w[ks].view(np.uint16))
 
 
-@pytest.mark.parametrize("M,K,N,g", [(1, 8192, 1280, 128), (16, 4096, 1024, 64),
+@pytest.mark.parametrize("M,K,N,g", [(1, 8192, 1280, 128), (1, 8192, 7168, 128),
+                                     (1, 14336, 4096, -1), (16, 4096, 1024, 64),
                                      (5, 512, 40, 32), (300, 1024, 640, 128),
                                      (64, 512, 256, -1)])
 def test_q_equal_z_gives_bias_exactly(M, K, N, g):
